@@ -1,0 +1,133 @@
+"""fp64 CPU oracle for volumetric delay-and-sum (DAS).
+
+TEST INFRASTRUCTURE ONLY.  The tests, the package smoke check and the
+benchmark's CPU-baseline leg are the only users; the GPU library never imports,
+links or runs anything here, and this package imports nothing from it.
+
+``das_sum`` wraps the plain C implementation in ``das_oracle.c`` (single
+threaded, fp64, compiled -O2 without fast-math).  The permute references are
+numpy transposes: the permute is a pure relayout, so the library primitive is
+its definition ("ffdas: volumetric ultrasound reconstruction at warp speed",
+Section 3, batch-inner tiling: B x Q x M x K becomes K x Q x M x B; ffdas docs,
+"How It Works", ALG2: the batch index moves to the innermost position).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "das_oracle.c")
+_LIB = os.path.join(_HERE, "libdas_oracle.so")
+_lib = None
+
+
+class _Geometry(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("Q", ctypes.c_int32), ("M", ctypes.c_int32), ("K", ctypes.c_int32),
+        ("nx", ctypes.c_int32), ("ny", ctypes.c_int32), ("nz", ctypes.c_int32),
+        ("complex_iq", ctypes.c_int32),
+        ("origin", ctypes.c_double * 3), ("spacing", ctypes.c_double * 3),
+        ("fs", ctypes.c_double), ("c", ctypes.c_double), ("t0", ctypes.c_double),
+        ("f_number", ctypes.c_double), ("f_demod", ctypes.c_double),
+    ]
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle into ``oracle/libdas_oracle.so`` with gcc -O2."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math",
+                        "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        lib.das_oracle_sum.restype = ctypes.c_int
+        lib.das_oracle_sum.argtypes = [
+            ctypes.POINTER(_Geometry), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+            ctypes.c_void_p]
+        lib.das_oracle_rx_weight.restype = ctypes.c_double
+        lib.das_oracle_rx_weight.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double]
+        _lib = lib
+    return _lib
+
+
+def _as_f32(a, name):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.float32:
+        raise TypeError(f"{name} must be float32, got {a.dtype}")
+    return a
+
+
+def das_sum(fields: dict, rf, rx_pos, tau_tx, w_tx,
+            voxels: Optional[Sequence[int]] = None,
+            frames: Optional[Sequence[int]] = None) -> np.ndarray:
+    """fp64 DAS of the given voxels and frames.
+
+    fields: B, Q, M, K, nx, ny, nz, origin, spacing, fs, c, t0, f_number,
+            f_demod, iq (as made by ``das_synth.problem_fields``).
+    rf: float32 B x Q x M x K (IQ: B x Q x M x K x 2).  The frame axis of rf
+        must hold all B frames (frame indices address it directly).
+    Returns float64 (n_frames, n_voxels), or complex128 for IQ.
+    """
+    lib = _load()
+    g = _Geometry()
+    for key in ("B", "Q", "M", "K", "nx", "ny", "nz"):
+        setattr(g, key, int(fields[key]))
+    g.complex_iq = 1 if fields.get("iq") else 0
+    g.origin[:] = [float(v) for v in fields["origin"]]
+    g.spacing[:] = [float(v) for v in fields["spacing"]]
+    g.fs, g.c, g.t0 = float(fields["fs"]), float(fields["c"]), float(fields["t0"])
+    g.f_number, g.f_demod = float(fields["f_number"]), float(fields.get("f_demod", 0.0))
+
+    rf = _as_f32(rf, "rf")
+    rx_pos = _as_f32(rx_pos, "rx_pos")
+    tau_tx = _as_f32(tau_tx, "tau_tx")
+    w_tx = _as_f32(w_tx, "w_tx")
+    n_total = g.nx * g.ny * g.nz
+    expect_rf = g.B * g.Q * g.M * g.K * (2 if g.complex_iq else 1)
+    if rf.size != expect_rf:
+        raise ValueError(f"rf has {rf.size} values, expected {expect_rf}")
+    if rx_pos.size != 3 * g.M or tau_tx.size != g.Q * n_total or w_tx.size != g.Q * n_total:
+        raise ValueError("rx_pos / tau_tx / w_tx sizes do not match the problem")
+    vox = np.arange(n_total, dtype=np.int64) if voxels is None else np.ascontiguousarray(voxels, dtype=np.int64)
+    frm = np.arange(g.B, dtype=np.int32) if frames is None else np.ascontiguousarray(frames, dtype=np.int32)
+    comps = 2 if g.complex_iq else 1
+    out = np.zeros((frm.size, vox.size, comps), dtype=np.float64)
+    rc = lib.das_oracle_sum(ctypes.byref(g), rf.ctypes.data, rx_pos.ctypes.data, tau_tx.ctypes.data,
+                            w_tx.ctypes.data, vox.ctypes.data, vox.size, frm.ctypes.data, frm.size,
+                            out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (code {rc})")
+    if g.complex_iq:
+        return out[..., 0] + 1j * out[..., 1]
+    return out[..., 0]
+
+
+def rx_weight(rho: float, dz: float, f_number: float) -> float:
+    """The oracle's receive apodization for one (rho, dz) offset."""
+    return _load().das_oracle_rx_weight(float(rho), float(dz), float(f_number))
+
+
+def permute_kqmb(x: np.ndarray) -> np.ndarray:
+    """B x Q x M x K (x 2 for IQ) -> K x Q x M x B (x 2): y[k,q,m,b] = x[b,q,m,k]."""
+    axes = (3, 1, 2, 0) + ((4,) if x.ndim == 5 else ())
+    return np.ascontiguousarray(np.transpose(x, axes))
+
+
+def permute_qmkb(x: np.ndarray) -> np.ndarray:
+    """B x Q x M x K (x 2 for IQ) -> Q x M x K x B (x 2): batch moved innermost."""
+    axes = (1, 2, 3, 0) + ((4,) if x.ndim == 5 else ())
+    return np.ascontiguousarray(np.transpose(x, axes))
