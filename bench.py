@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Throughput of volumetric delay-and-sum on one MI355X.
+
+One step is one pass of the whole hot path over one volume of the workload:
+das_permute (B x Q x M x K -> frames-innermost layout) followed by
+das_beamform with the batch-inner kernel, inputs already resident in HBM.
+
+Prints ONE JSON line.  `value` is accumulations (voxels x receivers x
+transmit events x frames) per second of whole steps; the roofline object
+describes the beamform kernel, timed with HIP events on the stream it runs on;
+cpu_baseline times the fp64 oracle on one depth slab of the same volume on the
+host.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_TFLOPS = 157.3        # MI355X vector fp32 (published)
+PEAK_HBM_GBS = 8000.0
+
+
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources; a stored counter reading is valid only for the same hash."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "volumetric_delay_sum_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it matches these sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        rec = data.get(f"{kernel}:{workload}")
+        if rec and rec.get("source_hash") == kernel_source_hash():
+            return rec.get("hbm_bytes_per_launch")
+    except Exception:
+        return None
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="main", help="workload: tiny, mid, main, main-c64")
+    ap.add_argument("--layout", default="kqmb", choices=["kqmb", "qmkb"])
+    ap.add_argument("--algorithm", default="batch_inner", choices=["batch_inner", "baseline"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-voxels", type=int, default=0, help="oracle sample size (0: one depth slab)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the q-sharded multi-GPU design is described but not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import das_synth
+    import volumetric_delay_sum_amd as das
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    das.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cfg = das_synth.get_config(args.config)
+    fields = das_synth.problem_fields(cfg)
+    print(f"[bench] generating {cfg.name}", file=sys.stderr, flush=True)
+    rx = das_synth.array_positions(cfg)
+    tau, w = das_synth.tx_tables(cfg)
+    rf = das_synth.rf(cfg, device=dev)
+    rx_d = torch.from_numpy(rx).to(dev)
+    tau_d = torch.from_numpy(tau).to(dev)
+    w_d = torch.from_numpy(w).to(dev)
+
+    plan = das.plan_from_fields(fields, algorithm=args.algorithm, layout=args.layout)
+    out = torch.empty(plan.output_shape(), dtype=torch.float32, device=dev)
+    bi = plan.batch_inner
+    perm = torch.empty(plan.permuted_shape(), dtype=torch.float32, device=dev) if bi else None
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if bi:
+            if ev is not None:
+                ev[0].record(stream)
+            plan.permute(rf, perm, 0, cfg.Q, stream=stream)
+            if ev is not None:
+                ev[1].record(stream)
+            plan.beamform(perm, rx_d, tau_d, w_d, out, 0, cfg.Q, stream=stream)
+            if ev is not None:
+                ev[2].record(stream)
+        else:
+            if ev is not None:
+                ev[0].record(stream)
+                ev[1].record(stream)
+            plan.beamform(rf, rx_d, tau_d, w_d, out, 0, cfg.Q, stream=stream)
+            if ev is not None:
+                ev[2].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    perm_ms = [e[0].elapsed_time(e[1]) for e in events]
+    kern_ms = [e[1].elapsed_time(e[2]) for e in events]
+    print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    accs = das_synth.accumulations(cfg)
+    ms_step = wall * 1e3 / args.steps
+    value = accs / (ms_step * 1e-3) / 1e9
+    kern_avg = float(np.mean(kern_ms))
+    perm_avg = float(np.mean(perm_ms))
+    flops_per_acc = 8 if cfg.iq else 4          # 2 FMA (real) or 8 FMA (complex) per accumulation
+    achieved = accs * flops_per_acc / (kern_avg * 1e-3) / 1e12
+    kernel_name = "das_batch_inner_kernel" if bi else "das_baseline_kernel"
+    traffic = stored_traffic(kernel_name, cfg.name)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        nx, ny, nz = cfg.grid
+        iz = nz // 2
+        vox = np.arange(iz * nx * ny, (iz + 1) * nx * ny, dtype=np.int64)
+        if args.cpu_voxels:
+            vox = vox[: args.cpu_voxels]
+        print(f"[bench] cpu baseline: oracle on {vox.size} voxels", file=sys.stderr, flush=True)
+        rf_host = rf.cpu().numpy()
+        t1 = time.perf_counter()
+        ref = oracle.das_sum(fields, rf_host, rx, tau, w, voxels=vox)
+        cpu_s = time.perf_counter() - t1
+        cpu_acc = vox.size * cfg.M * cfg.Q * cfg.B
+        y = out.cpu().numpy().astype(np.float64)
+        y = (y[..., 0] + 1j * y[..., 1]) if cfg.iq else y
+        y = y[:, vox]
+        comps = [(y.real, ref.real), (y.imag, ref.imag)] if cfg.iq else [(y, ref)]
+        parity = [(float(np.abs(g - r).max() / np.abs(r).max()), float(np.linalg.norm(g - r) / np.linalg.norm(r)))
+                  for g, r in comps]
+        cpu = {"value": cpu_acc / cpu_s / 1e9, "unit": "G acc/s", "cores": 1, "kind": "oracle",
+               "sample": f"{cfg.name}: depth slab iz={iz} ({vox.size} voxels) x all {cfg.Q} events x "
+                         f"{cfg.M} receivers x {cfg.B} frames = {cpu_acc:.3e} accumulations in {cpu_s:.1f} s, "
+                         "single-threaded fp64 C oracle",
+               "gpu_parity_on_sample": {"max_rel": max(p[0] for p in parity), "l2_rel": max(p[1] for p in parity)}}
+
+    info = plan.info
+    rec = {
+        "metric": "G voxel·receiver·transmit·frame accumulations/s (fp32), % of bounding roofline",
+        "value": value,
+        "unit": "G acc/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "c64" if cfg.iq else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{cfg.name}: {cfg.grid[0]}x{cfg.grid[1]}x{cfg.grid[2]} voxels, "
+                         f"{cfg.array[0]}x{cfg.array[1]} array (M={cfg.M}), Q={cfg.Q} "
+                         f"{'plane' if cfg.tx == 'plane' else 'diverging'} waves, K={cfg.K}, B={cfg.B}, "
+                         f"{'complex64 IQ' if cfg.iq else 'fp32 RF'}"),
+            "step": ("das_permute + das_beamform (batch-inner, layout "
+                     f"{args.layout.upper()})" if bi else "das_beamform (baseline)"),
+            "accumulations_per_step": accs,
+            "frames_per_lane": info["frames_per_lane"],
+        },
+        "roofline": {
+            "bound": "alu",
+            "achieved": achieved,
+            "peak": PEAK_FP32_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_FP32_TFLOPS,
+            "traffic": traffic,
+            "kernel": kernel_name,
+            "kernel_ms": kern_avg,
+            "kernel_gacc_s": accs / (kern_avg * 1e-3) / 1e9,
+            "flops_per_accumulation": flops_per_acc,
+        },
+        "permute_ms": perm_avg if bi else None,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * das.h -- C ABI of libdas: volumetric delay-and-sum (DAS) beamforming on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("ffdas: volumetric ultrasound reconstruction at warp speed",
+ * Section 3, baseline paragraph: transmit delays and weights are per-voxel
+ * tables, receive delays and weights are computed in the kernel from the
+ * receiver geometry; tensor-core paragraphs: each voxel uses the two samples
+ * k and k+1 of each receiver with an interpolation weight per sample; ffdas
+ * docs, "How It Works", The computational challenge: interpolate and sum the
+ * aligned samples of every receiver and transmit event for each voxel):
+ *
+ *   y[b,n] = sum_q sum_m  w_tx[q,n] * w_rx[m,n] * v(b,q,m,n)
+ *   tau    = tau_tx[q,n] + |r_n - p_m| / c
+ *   s      = (tau - t0) * fs,  k = floor(s),  f = s - k
+ *   v      = (1-f) x[b,q,m,k] + f x[b,q,m,k+1]  if 0 <= k <= K-2, else 0
+ *   IQ:      v *= exp(+j 2 pi f_demod tau)
+ *   w_rx   = 0.5 (1 + cos(pi theta / theta_max)) if dz > 0 and theta < theta_max,
+ *            else 0, with theta = atan2(rho, dz) the angle from the array normal
+ *            (rho = lateral offset, dz = depth offset voxel - receiver) and
+ *            theta_max = atan(1 / (2 f_number)); f_number <= 0 gives w_rx = 1.
+ *   r_n    = origin + (ix, iy, iz) * spacing,  n = (iz*ny + iy)*nx + ix.
+ *
+ * Conventions for every entry point:
+ *  - All data pointers are DEVICE pointers owned by the caller; the library
+ *    allocates no device memory.  Base pointers must be 16-byte aligned.
+ *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the default
+ *    stream) and the call returns without synchronizing.  A device fault
+ *    surfaces at the caller's next synchronization.
+ *  - Every function returns a das_status; nothing throws across the ABI.
+ *    Arguments are validated on the host before any launch, so a non-OK
+ *    return means nothing was enqueued (except DAS_ERR_LAUNCH).
+ *  - Sizes are NOT known to the library beyond the plan: the caller must pass
+ *    buffers of the sizes stated below.
+ *  - Plans are immutable host objects; one plan may be used from several
+ *    streams and threads at once.
+ */
+#ifndef DAS_H
+#define DAS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DAS_ABI_VERSION 1
+
+typedef enum das_status {
+    DAS_OK = 0,
+    DAS_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, bad range, bad enum   */
+    DAS_ERR_UNSUPPORTED = 2,      /* valid request this build cannot serve          */
+    DAS_ERR_ALIGNMENT = 3,        /* a base pointer is not 16-byte aligned          */
+    DAS_ERR_NO_DEVICE = 4,        /* no HIP device, or the device is not gfx950     */
+    DAS_ERR_LAUNCH = 5            /* the HIP runtime refused a launch               */
+} das_status;
+
+/* Sample type.  DAS_F32: real float32 RF.  DAS_C64: complex64 IQ data, stored
+ * as interleaved (re, im) float32 pairs; requires f_demod > 0. */
+enum { DAS_F32 = 0, DAS_C64 = 1 };
+
+/* Kernel family.
+ *  DAS_ALG_BASELINE     one lane per voxel, a tile of frames per lane, reading
+ *                       the B x Q x M x K input directly (the paper's baseline,
+ *                       Section 3; the docs' ALG1).
+ *  DAS_ALG_BATCH_INNER  frames innermost: reads the permuted layout made by
+ *                       das_permute, a group of lanes shares one voxel and
+ *                       reads consecutive frames at one (k, q, m) (the paper's
+ *                       batch-inner tiling, Section 3; the docs' ALG2).
+ *  DAS_ALG_DEFAULT      the baseline, as the docs' DEFAULT dispatch.          */
+enum { DAS_ALG_DEFAULT = 0, DAS_ALG_BASELINE = 1, DAS_ALG_BATCH_INNER = 2 };
+
+/* Frames-innermost layout made by das_permute and read by the batch-inner
+ * kernel, for a chunk of q_count transmit events:
+ *  DAS_LAYOUT_KQMB  K x q_count x M x B  (the paper, Section 3 batch-inner)
+ *  DAS_LAYOUT_QMKB  q_count x M x K x B  (the docs' ALG2 ordering: batch moved
+ *                   innermost, the other axes kept in order)               */
+enum { DAS_LAYOUT_KQMB = 0, DAS_LAYOUT_QMKB = 1 };
+
+typedef struct das_problem {
+    int32_t B, Q, M, K;      /* frames, transmit events, receivers, samples (K >= 2)   */
+    int32_t nx, ny, nz;      /* voxel grid; n = (iz*ny + iy)*nx + ix                   */
+    int32_t dtype;           /* DAS_F32 | DAS_C64                                      */
+    int32_t algorithm;       /* DAS_ALG_DEFAULT | DAS_ALG_BASELINE | DAS_ALG_BATCH_INNER */
+    int32_t layout;          /* DAS_LAYOUT_KQMB | DAS_LAYOUT_QMKB (batch-inner only)    */
+    double  origin[3];       /* metres: centre of voxel (0,0,0)                         */
+    double  spacing[3];      /* metres: voxel pitch along x, y, z (> 0)                 */
+    double  fs;              /* Hz, sampling rate (> 0)                                 */
+    double  c;               /* m/s, speed of sound (> 0)                               */
+    double  t0;              /* s, time of sample k = 0                                 */
+    double  f_number;        /* receive Hann over angle; <= 0 gives w_rx = 1            */
+    double  f_demod;         /* Hz: 0 with DAS_F32, > 0 with DAS_C64                    */
+} das_problem;
+
+typedef struct das_plan das_plan_t;
+
+/* What a plan chose, for reporting. */
+typedef struct das_plan_info {
+    int32_t algorithm;          /* resolved: DAS_ALG_BASELINE or DAS_ALG_BATCH_INNER */
+    int32_t layout;
+    int32_t elem_bytes;         /* 4 (f32) or 8 (c64) per sample                     */
+    int32_t frames_per_lane;    /* batch-inner: frames one lane loads per vector load;
+                                   baseline: frames one lane accumulates             */
+    int32_t lanes_per_voxel;    /* batch-inner: 16; baseline: 1                      */
+    int32_t voxels_per_group;   /* voxels one workgroup covers                       */
+    int64_t N;                  /* nx * ny * nz                                      */
+} das_plan_info;
+
+/* Validate a problem and build a host-side plan.  Host only: no HIP call, no
+ * device memory.  On success *out receives a plan the caller frees with
+ * das_plan_destroy.
+ * Errors: DAS_ERR_INVALID_ARGUMENT for null pointers, non-positive sizes,
+ * K < 2, non-finite or non-positive fs / c / spacing, unknown enums;
+ * DAS_ERR_UNSUPPORTED for dtype / f_demod mismatch (C64 needs f_demod > 0,
+ * F32 needs f_demod == 0) or N, B*Q*M*K beyond 2^31 elements per axis. */
+das_status das_plan(const das_problem *problem, das_plan_t **out);
+
+void das_plan_destroy(das_plan_t *plan);
+
+das_status das_plan_get_info(const das_plan_t *plan, das_plan_info *info);
+
+/* Bytes of the permuted buffer that holds q_count transmit events
+ * (K * q_count * M * B * elem_bytes, in either layout).  0 on a bad argument. */
+size_t das_permuted_bytes(const das_plan_t *plan, int32_t q_count);
+
+/* Permute transmit events [q_begin, q_begin + q_count) of the B x Q x M x K
+ * input into the plan's frames-innermost layout ("ffdas: volumetric
+ * ultrasound reconstruction at warp speed", Section 3, batch-inner tiling:
+ * frames become the contiguous axis; ffdas docs, ALG2).  Bit-exact relayout.
+ *   rf_bqmk   B x Q x M x K samples (all Q), elem_bytes each
+ *   rf_perm   das_permuted_bytes(plan, q_count) bytes; event q is stored at
+ *             local index q - q_begin
+ * Errors: DAS_ERR_INVALID_ARGUMENT (null pointer, empty or out-of-range q
+ * range, rf_perm overlapping rf_bqmk is not checked: do not alias);
+ * DAS_ERR_ALIGNMENT; DAS_ERR_NO_DEVICE; DAS_ERR_LAUNCH. */
+das_status das_permute(const das_plan_t *plan, const void *rf_bqmk, void *rf_perm,
+                       int32_t q_begin, int32_t q_count, void *hip_stream);
+
+/* Beamform transmit events [q_begin, q_begin + q_count) into out.
+ *   rf       baseline: the B x Q x M x K input (all Q, indexed by absolute q);
+ *            batch-inner: the permuted chunk made by das_permute with the same
+ *            q_begin / q_count
+ *   rx_pos   M x 3 float32 receiver positions (x, y, z), metres
+ *   tau_tx   Q x N float32 transmit delays, seconds (absolute q)
+ *   w_tx     Q x N float32 transmit weights (absolute q)
+ *   out      B x N float32 (DAS_C64: B x N interleaved re/im float32 pairs)
+ *   accumulate  0: out is overwritten; 1: the chunk's sum is added to out
+ *               (to sum a volume over several q chunks)
+ * Errors: DAS_ERR_INVALID_ARGUMENT (null pointer, bad q range, accumulate not
+ * 0/1); DAS_ERR_UNSUPPORTED (batch-inner KQMB chunk larger than 4 GiB: use
+ * a smaller q_count or the QMKB layout); DAS_ERR_ALIGNMENT;
+ * DAS_ERR_NO_DEVICE; DAS_ERR_LAUNCH. */
+das_status das_beamform(const das_plan_t *plan, const void *rf, const float *rx_pos,
+                        const float *tau_tx, const float *w_tx, void *out,
+                        int32_t q_begin, int32_t q_count, int32_t accumulate,
+                        void *hip_stream);
+
+/* Static text for a status code (never NULL). */
+const char *das_error_string(int status);
+
+/* DAS_ABI_VERSION of the loaded library. */
+int32_t das_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DAS_H */

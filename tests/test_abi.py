@@ -1,0 +1,213 @@
+"""C-ABI contract of libdas.so on the host: it loads, exports every declared
+symbol, and rejects bad arguments with the documented status before touching
+a device.  No kernel runs here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import volumetric_delay_sum_amd as das
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "das.h")
+
+OK, INVALID, UNSUPPORTED, ALIGNMENT, NO_DEVICE, LAUNCH = 0, 1, 2, 3, 4, 5
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return das.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(das_[a-z_0-9]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("das_plan", "das_permute", "das_beamform", "das_plan_destroy", "das_error_string",
+                     "das_permuted_bytes"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"libdas.so does not export {name}"
+
+
+def test_abi_version(lib):
+    text = open(HEADER).read()
+    v = int(re.search(r"#define DAS_ABI_VERSION (\d+)", text).group(1))
+    assert lib.das_abi_version() == v
+
+
+def _c_layout(struct, fields, tmp_path):
+    """sizeof and field offsets of a header struct, as the C compiler lays it out."""
+    src = tmp_path / "layout.c"
+    body = "".join(f'printf("%zu ", offsetof({struct}, {f}));' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "das.h"\n'
+                   f'int main(void){{printf("%zu ", sizeof({struct}));{body}return 0;}}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    return [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
+
+
+@pytest.mark.parametrize("cls,struct", [(das._Problem, "das_problem"), (das._PlanInfo, "das_plan_info")])
+def test_ctypes_mirrors_match_the_header(cls, struct, tmp_path):
+    fields = [f for f, _ in cls._fields_]
+    got = _c_layout(struct, fields, tmp_path)
+    assert got[0] == ctypes.sizeof(cls)
+    assert got[1:] == [getattr(cls, f).offset for f in fields]
+
+
+def _problem(**kw):
+    base = dict(B=4, Q=2, M=8, K=64, nx=4, ny=4, nz=2, origin=(0.0, 0.0, 5e-3), spacing=(2e-4,) * 3,
+                fs=20e6, c=1540.0, t0=0.0, f_number=1.0, f_demod=0.0, dtype="f32", algorithm="batch_inner",
+                layout="kqmb")
+    base.update(kw)
+    return base
+
+
+def _status(**kw):
+    try:
+        das.Plan(**_problem(**kw))
+        return OK
+    except das.DasError as e:
+        return e.code
+
+
+@pytest.mark.parametrize("field,value", [("B", 0), ("Q", 0), ("M", 0), ("K", 1), ("nx", 0), ("ny", -1),
+                                         ("nz", 0), ("fs", 0.0), ("c", -1.0), ("fs", float("nan")),
+                                         ("t0", float("inf")), ("algorithm", 7), ("layout", 3), ("dtype", 5)])
+def test_plan_rejects_invalid_problems(field, value):
+    assert _status(**{field: value}) == INVALID
+
+
+def test_plan_rejects_nonfinite_geometry():
+    assert _status(origin=(0.0, float("nan"), 0.0)) == INVALID
+    assert _status(spacing=(1e-4, float("inf"), 1e-4)) == INVALID
+
+
+def test_plan_dtype_demod_mismatch_is_unsupported():
+    assert _status(dtype="f32", f_demod=5e6) == UNSUPPORTED
+    assert _status(dtype="c64", f_demod=0.0) == UNSUPPORTED
+    assert _status(dtype="c64", f_demod=5e6) == OK
+
+
+def test_plan_rejects_sizes_beyond_addressing():
+    assert _status(nx=2048, ny=2048, nz=1024) == UNSUPPORTED          # N > 2^31
+    assert _status(K=1 << 20, B=512) == UNSUPPORTED                   # 16 K B elem > 4 GiB
+
+
+def test_plan_null_pointers(lib):
+    h = ctypes.c_void_p()
+    assert lib.das_plan(None, ctypes.byref(h)) == INVALID
+    p = das._Problem()
+    assert lib.das_plan(ctypes.byref(p), None) == INVALID
+
+
+def test_plan_info_and_sizes():
+    pl = das.Plan(**_problem(B=32, dtype="c64", f_demod=5e6))
+    assert pl.info["algorithm"] == das.ALG_BATCH_INNER
+    assert pl.info["elem_bytes"] == 8
+    assert pl.info["frames_per_lane"] == 2
+    assert pl.info["lanes_per_voxel"] == 16
+    assert pl.info["N"] == 32
+    assert pl.permuted_bytes(1) == 64 * 1 * 8 * 32 * 8
+    assert pl.permuted_bytes(2) == 2 * pl.permuted_bytes(1)
+    assert pl.permuted_bytes(3) == 0
+    assert pl.permuted_bytes(0) == 0
+    assert pl.permuted_shape(1) == (64, 1, 8, 32, 2)
+    pl2 = das.Plan(**_problem(algorithm="default"))
+    assert pl2.info["algorithm"] == das.ALG_BASELINE       # DEFAULT dispatches to the baseline
+    pl3 = das.Plan(**_problem(layout="qmkb"))
+    assert pl3.permuted_shape(2) == (2, 8, 64, 4)
+
+
+@pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (24, 1), (32, 2), (48, 2), (64, 4), (96, 4), (66, 2)])
+def test_frames_per_lane_choice(B, fl):
+    assert das.Plan(**_problem(B=B)).info["frames_per_lane"] == fl
+
+
+def test_error_strings(lib):
+    for code in range(0, 7):
+        s = lib.das_error_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert lib.das_error_string(-3) == b"unknown status"
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_permute_argument_errors(lib):
+    pl = das.Plan(**_problem())
+    h = pl._h
+    good = _fake(0x10000)
+    assert lib.das_permute(None, good, good, 0, 1, None) == INVALID
+    assert lib.das_permute(h, None, good, 0, 1, None) == INVALID
+    assert lib.das_permute(h, good, None, 0, 1, None) == INVALID
+    assert lib.das_permute(h, good, good, -1, 1, None) == INVALID
+    assert lib.das_permute(h, good, good, 0, 0, None) == INVALID
+    assert lib.das_permute(h, good, good, 1, 2, None) == INVALID          # past Q
+    assert lib.das_permute(h, _fake(0x10004), good, 0, 1, None) == ALIGNMENT
+    assert lib.das_permute(h, good, _fake(0x10008), 0, 1, None) == ALIGNMENT
+
+
+def test_beamform_argument_errors(lib):
+    pl = das.Plan(**_problem())
+    h = pl._h
+    g = _fake(0x10000)
+    bad = _fake(0x10004)
+    assert lib.das_beamform(None, g, g, g, g, g, 0, 1, 0, None) == INVALID
+    for i in range(5):
+        args = [g] * 5
+        args[i] = None
+        assert lib.das_beamform(h, *args, 0, 1, 0, None) == INVALID
+    assert lib.das_beamform(h, g, g, g, g, g, 0, 3, 0, None) == INVALID
+    assert lib.das_beamform(h, g, g, g, g, g, 2, 1, 0, None) == INVALID
+    assert lib.das_beamform(h, g, g, g, g, g, 0, 1, 2, None) == INVALID       # accumulate not 0/1
+    for i in range(5):
+        args = [g] * 5
+        args[i] = bad
+        assert lib.das_beamform(h, *args, 0, 1, 0, None) == ALIGNMENT
+
+
+def test_batch_inner_kqmb_chunk_limit(lib):
+    # K * q_count * M * B * 4 > 4 GiB: the KQMB batch-inner kernel needs a smaller chunk
+    pl = das.Plan(**_problem(B=64, Q=16, M=1024, K=4096))
+    g = _fake(0x10000)
+    assert lib.das_beamform(pl._h, g, g, g, g, g, 0, 16, 0, None) == UNSUPPORTED
+    assert lib.das_beamform(pl._h, g, g, g, g, g, 0, 4, 0, None) == UNSUPPORTED
+    # a 1-event chunk passes validation (and then needs a device)
+    rc = lib.das_beamform(pl._h, g, g, g, g, g, 0, 1, 0, None) if not _gpu() else NO_DEVICE
+    assert rc == NO_DEVICE
+
+
+def _gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu(), reason="checks the no-device path")
+def test_no_device_is_reported(lib):
+    pl = das.Plan(**_problem())
+    g = _fake(0x10000)
+    assert lib.das_permute(pl._h, g, g, 0, 1, None) == NO_DEVICE
+    assert lib.das_beamform(pl._h, g, g, g, g, g, 0, 1, 0, None) == NO_DEVICE
+
+
+def test_binding_checks_tensor_sizes_before_the_call():
+    torch = pytest.importorskip("torch")
+    pl = das.Plan(**_problem())
+    cpu = torch.zeros(10)
+    with pytest.raises(TypeError):
+        pl.beamform(cpu, cpu, cpu, cpu, cpu)

@@ -1,0 +1,171 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  Bar: max|err| <= 1e-4 max|oracle| and relative L2 <= 1e-5,
+complex data per component.
+
+Small ragged shapes are compared element by element over every voxel and
+frame; the named full-size configurations are compared on a seeded voxel
+sample (all scatterer voxels, the grid corners, random voxels) in the launch
+configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+
+import das_synth
+from das_testing import Inputs, assert_parity, oracle_ref, run_gpu, sample_voxels, to_numpy
+
+pytestmark = pytest.mark.gpu
+
+ALGS = [("baseline", "kqmb"), ("batch_inner", "kqmb"), ("batch_inner", "qmkb")]
+
+
+def _ragged(iq=False, B=12, array=(37, 1), grid=(13, 7, 3), K=300, sources=None, **kw):
+    sources = sources or ((0.0, 0.0), (1.5e-3, -0.5e-3), (-1e-3, 1e-3))
+    return das_synth.custom_config("tiny", name="ragged", seed=17, array=array, grid=grid, K=K, B=B,
+                                   tx="diverging", sources=sources, iq=iq, n_scatterers=0, **kw)
+
+
+@pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])
+@pytest.mark.parametrize("alg,layout", ALGS)
+@pytest.mark.parametrize("B", [12, 32, 40])
+def test_ragged_full_compare(gpu, iq, alg, layout, B):
+    cfg = _ragged(iq=iq, B=B)
+    inp = Inputs(cfg, w_tx="uniform")
+    y = to_numpy(run_gpu(inp, alg, layout), iq)
+    ref = oracle_ref(inp)
+    assert_parity(y, ref, f"{alg}/{layout} B={B} iq={iq}")
+
+
+@pytest.mark.parametrize("alg,layout", ALGS)
+def test_tiny_full_compare(gpu, alg, layout):
+    cfg = das_synth.get_config("tiny")
+    inp = Inputs(cfg)
+    y = to_numpy(run_gpu(inp, alg, layout), False)
+    assert_parity(y, oracle_ref(inp), f"tiny {alg}/{layout}")
+
+
+@pytest.mark.parametrize("alg,layout", ALGS)
+def test_tiny_iq_full_compare(gpu, alg, layout):
+    cfg = das_synth.custom_config("tiny", iq=True, seed=8)
+    inp = Inputs(cfg)
+    y = to_numpy(run_gpu(inp, alg, layout), True)
+    assert_parity(y, oracle_ref(inp), f"tiny-iq {alg}/{layout}")
+
+
+@pytest.mark.parametrize("alg,layout", ALGS)
+def test_degenerate_shapes(gpu, alg, layout):
+    # one voxel, one receiver, one event, one frame, K = 2
+    cfg = das_synth.custom_config("tiny", name="deg", array=(1, 1), grid=(1, 1, 1), K=2, B=1, n_scatterers=0,
+                                  z0=1e-3, f_number=0.0, fs=1e6)
+    inp = Inputs(cfg, w_tx="uniform")
+    y = to_numpy(run_gpu(inp, alg, layout), False)
+    ref = oracle_ref(inp)
+    # s = 2 * 1e-3 / 1540 * 1e6 = 1.3 > K-2: the only term is dropped, the result is exactly 0
+    assert np.all(ref == 0.0) and np.all(y == 0.0)
+
+
+@pytest.mark.parametrize("alg,layout", ALGS)
+def test_terms_off_the_record_end(gpu, alg, layout):
+    # K short enough that deep voxels lose part of their (q, m) terms
+    cfg = _ragged(K=140, B=16)
+    inp = Inputs(cfg, w_tx="uniform")
+    y = to_numpy(run_gpu(inp, alg, layout), False)
+    ref = oracle_ref(inp)
+    assert_parity(y, ref, f"short record {alg}/{layout}")
+
+
+@pytest.mark.parametrize("alg,layout", ALGS)
+def test_accumulate_adds_into_out(gpu, alg, layout):
+    import torch
+    cfg = _ragged(B=16)
+    inp = Inputs(cfg, w_tx="uniform")
+    ref = oracle_ref(inp)
+    start = torch.linspace(-3.0, 3.0, cfg.B * cfg.N, device="cuda").reshape(cfg.B, cfg.N)
+    out = run_gpu(inp, alg, layout, out=start.clone(), accumulate_into=True)
+    y = out.cpu().numpy().astype(np.float64) - start.cpu().numpy()
+    assert_parity(y, ref, f"accumulate {alg}/{layout}")
+
+
+@pytest.mark.parametrize("alg,layout", ALGS)
+def test_q_chunks_sum_to_the_whole(gpu, alg, layout):
+    cfg = _ragged(B=32)
+    inp = Inputs(cfg)
+    y = to_numpy(run_gpu(inp, alg, layout, q_chunk=1), False)
+    assert_parity(y, oracle_ref(inp), f"q chunks {alg}/{layout}")
+
+
+def test_baseline_and_batch_inner_agree(gpu):
+    cfg = das_synth.get_config("tiny")
+    inp = Inputs(cfg)
+    a = to_numpy(run_gpu(inp, "baseline"), False)
+    b = to_numpy(run_gpu(inp, "batch_inner", "kqmb"), False)
+    c = to_numpy(run_gpu(inp, "batch_inner", "qmkb"), False)
+    assert_parity(a, b.astype(np.float64), "BL vs BI")
+    # the two batch-inner layouts run the same arithmetic in the same order
+    assert np.array_equal(b, c)
+
+
+# --------------------------------------------------------------------------
+# Named configurations at full size, sampled voxels
+# --------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def mid_inputs(gpu):
+    return Inputs(das_synth.get_config("mid"))
+
+
+@pytest.mark.parametrize("alg,layout", ALGS)
+def test_mid_sampled(mid_inputs, alg, layout):
+    inp = mid_inputs
+    vox = sample_voxels(inp.cfg, 400)
+    y = to_numpy(run_gpu(inp, alg, layout), False)[:, vox]
+    assert_parity(y, oracle_ref(inp, voxels=vox), f"mid {alg}/{layout}")
+
+
+@pytest.fixture(scope="module")
+def main_inputs(gpu):
+    return Inputs(das_synth.get_config("main"))
+
+
+@pytest.mark.parametrize("alg,layout", ALGS)
+def test_main_sampled(main_inputs, alg, layout):
+    inp = main_inputs
+    vox = sample_voxels(inp.cfg, 192)
+    y = to_numpy(run_gpu(inp, alg, layout), False)[:, vox]
+    assert_parity(y, oracle_ref(inp, voxels=vox), f"main {alg}/{layout}")
+
+
+def test_main_scatterers_peak(main_inputs):
+    """End to end on the GPU: each scatterer is the brightest voxel of its 5^3 neighbourhood."""
+    inp = main_inputs
+    cfg = inp.cfg
+    y = np.abs(to_numpy(run_gpu(inp, "batch_inner", "kqmb"), False)[0]).reshape(cfg.grid[::-1])
+    nx, ny, nz = cfg.grid
+    sv = das_synth.scatterer_voxels(cfg)
+    idx = np.stack([sv % nx, (sv // nx) % ny, sv // (nx * ny)], axis=-1)
+    checked = 0
+    for i, n in enumerate(sv):
+        # a scatterer within 4 voxels of another may sit in its brighter neighbour's blur
+        others = np.delete(idx, i, axis=0)
+        if others.size and np.abs(others - idx[i]).max(axis=1).min() <= 4:
+            continue
+        ix, iy, iz = idx[i]
+        nb = y[max(iz - 2, 0): iz + 3, max(iy - 2, 0): iy + 3, max(ix - 2, 0): ix + 3]
+        assert y[iz, iy, ix] == nb.max(), n
+        checked += 1
+    assert checked >= 20
+
+
+def test_main_noise_only(gpu):
+    """Worst case for relative error: no scatterer energy to dilute it."""
+    inp = Inputs(das_synth.get_config("main"), scatterers=False)
+    vox = sample_voxels(inp.cfg, 128, seed=3)
+    y = to_numpy(run_gpu(inp, "batch_inner", "kqmb"), False)[:, vox]
+    assert_parity(y, oracle_ref(inp, voxels=vox), "main noise-only")
+
+
+@pytest.mark.parametrize("alg,layout", ALGS)
+def test_main_c64_sampled(gpu, alg, layout):
+    inp = Inputs(das_synth.get_config("main-c64"))
+    vox = sample_voxels(inp.cfg, 128)
+    y = to_numpy(run_gpu(inp, alg, layout), True)[:, vox]
+    assert_parity(y, oracle_ref(inp, voxels=vox), f"main-c64 {alg}/{layout}")

@@ -1,0 +1,178 @@
+// Device helpers for the DAS kernels: voxel and receive geometry, sample
+// position split, and row-broadcast DPP arithmetic for gfx950 wave64.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "das_internal.h"
+
+namespace das {
+
+// Compile-time integer sequence (for fully unrolled, immediate-indexed loops).
+template <int... Is> struct iseq {};
+template <int N, int... Is> struct make_iseq : make_iseq<N - 1, N - 1, Is...> {};
+template <int... Is> struct make_iseq<0, Is...> { using type = iseq<Is...>; };
+template <int I> struct ic { static constexpr int value = I; };
+template <class F, int... Is>
+__device__ __forceinline__ void unroll_impl(F &&f, iseq<Is...>) { (f(ic<Is>{}), ...); }
+template <int N, class F>
+__device__ __forceinline__ void unroll(F &&f) { unroll_impl(f, typename make_iseq<N>::type{}); }
+
+// Voxel centre in fp64: origin + index * pitch.
+__device__ __forceinline__ void voxel_centre(const DasKParams &P, int ix, int iy, int iz,
+                                             double &x, double &y, double &z) {
+    x = P.ox + (double)ix * P.sx;
+    y = P.oy + (double)iy * P.sy;
+    z = P.oz + (double)iz * P.sz;
+}
+
+// sqrt in fp64 from the fp32 reciprocal-square-root estimate plus one Newton
+// step (relative error about 1e-14, ample for sample positions near 1e3).
+__device__ __forceinline__ double sqrt_f64(double x) {
+    float r = __builtin_amdgcn_rsqf((float)x);
+    double y = (double)r;
+    double s = x * y;
+    double e = __builtin_fma(-s, s, x);
+    s = __builtin_fma(e, 0.5 * y, s);
+    return x > 0.0 ? s : 0.0;
+}
+
+// Receive apodization: Hann over the angle from the array normal,
+// 0.5 (1 + cos(pi theta / theta_max)) = cos^2(pi/2 theta / theta_max) for
+// dz > 0 and theta < theta_max, else 0.  fp32 is enough for a weight.
+__device__ __forceinline__ float rx_weight(const DasKParams &P, float rho, float dz) {
+    float th = atan2f(rho, dz);
+    float u = th * P.inv_theta_max;
+    float c = cospif(0.5f * u);
+    float w = c * c;
+    w = (dz > 0.0f && u < 1.0f) ? w : 0.0f;
+    return P.apod ? w : 1.0f;
+}
+
+// Receive part of one (voxel, receiver) pair: fp64 sample offset, weight,
+// and (IQ) the unit phasor exp(+j 2 pi f0 d / c).
+struct RxTerm {
+    double s_rx;
+    float w;
+    float pc, ps;
+};
+
+template <bool IQ>
+__device__ __forceinline__ RxTerm rx_term(const DasKParams &P, double vx, double vy, double vz,
+                                          float px, float py, float pz) {
+    const double dx = vx - (double)px, dy = vy - (double)py, dz = vz - (double)pz;
+    const double d2 = __builtin_fma(dx, dx, __builtin_fma(dy, dy, dz * dz));
+    const double d = sqrt_f64(d2);
+    RxTerm t;
+    t.s_rx = d * P.fs_over_c;
+    const float rho = sqrtf((float)__builtin_fma(dx, dx, dy * dy));
+    t.w = rx_weight(P, rho, (float)dz);
+    t.pc = 1.0f;
+    t.ps = 0.0f;
+    if constexpr (IQ) {
+        double cyc = d * P.f0_over_c;
+        cyc -= __builtin_floor(cyc);
+        float sn, cs;
+        sincospif(2.0f * (float)cyc, &sn, &cs);
+        t.pc = cs;
+        t.ps = sn;
+    }
+    return t;
+}
+
+// Transmit part of one (voxel, event) pair: fp64 sample offset (tau_tx - t0) fs
+// and (IQ) the unit phasor exp(+j 2 pi f0 tau_tx).
+struct TxTerm {
+    double s_tx;
+    float w;
+    float pc, ps;
+};
+
+template <bool IQ>
+__device__ __forceinline__ TxTerm tx_term(const DasKParams &P, float tau, float w) {
+    TxTerm t;
+    t.s_tx = __builtin_fma((double)tau, P.fs, -P.t0fs);
+    t.w = w;
+    t.pc = 1.0f;
+    t.ps = 0.0f;
+    if constexpr (IQ) {
+        double cyc = (double)tau * P.f0;
+        cyc -= __builtin_floor(cyc);
+        float sn, cs;
+        sincospif(2.0f * (float)cyc, &sn, &cs);
+        t.pc = cs;
+        t.ps = sn;
+    }
+    return t;
+}
+
+// Split s into k = floor(s) and f = s - k.  A term is kept iff 0 <= k <= K-2;
+// a dropped term gets weight 0 and k = 0 so every address stays inside the row.
+struct Lerp {
+    uint32_t k;
+    float a, b;        // real: (1-f) w and f w
+    float ai, bi;      // IQ: imaginary parts of the phase-rotated weights
+};
+
+template <bool IQ>
+__device__ __forceinline__ Lerp lerp_coeffs(double s, float w, float pc, float ps, int32_t K) {
+    const double kf = __builtin_floor(s);
+    const int32_t ki = (int32_t)kf;
+    const bool ok = (kf >= 0.0) && (kf <= (double)(K - 2));
+    const float f = (float)(s - kf);
+    const float wv = ok ? w : 0.0f;
+    Lerp L;
+    L.k = ok ? (uint32_t)ki : 0u;
+    const float bw = wv * f;
+    const float aw = wv - bw;
+    if constexpr (IQ) {
+        L.a = aw * pc;
+        L.ai = aw * ps;
+        L.b = bw * pc;
+        L.bi = bw * ps;
+    } else {
+        L.a = aw;
+        L.b = bw;
+        L.ai = 0.0f;
+        L.bi = 0.0f;
+    }
+    return L;
+}
+
+// ---------------------------------------------------------------------------
+// Row broadcast on wave64: DPP row_newbcast:J hands lane J of each 16-lane row
+// to every lane of that row (gfx90a and later).
+// ---------------------------------------------------------------------------
+template <int J>
+__device__ __forceinline__ uint32_t row_bcast(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x150 + J, 0xF, 0xF, true);
+}
+
+// acc += coef[lane J of the row] * x, as one v_fmac_f32_dpp.  The compiler
+// does not fold a DPP move into v_fmac (tied accumulator), so this is written
+// out.  Every coefficient read this way must have been written by a VALU op
+// at least two wait states earlier: see settle().
+template <int J>
+__device__ __forceinline__ void fmac_bcast(float &acc, float coef, float x) {
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc) : "v"(coef), "v"(x), "n"(J));
+}
+// acc -= coef[lane J of the row] * x
+template <int J>
+__device__ __forceinline__ void fnmac_bcast(float &acc, float coef, float x) {
+    asm("v_fmac_f32_dpp %0, -%1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc) : "v"(coef), "v"(x), "n"(J));
+}
+
+// Two wait states after the last VALU write of the given registers, so that
+// DPP reads of them that follow are safe (VALU write -> DPP read hazard).
+// The build scans the generated code for this hazard as well.
+__device__ __forceinline__ void settle(float &a, float &b) {
+    asm volatile("s_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void settle(float &a, float &b, float &c, float &d) {
+    asm volatile("s_nop 1" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
+}  // namespace das

@@ -1,0 +1,44 @@
+// Internal declarations shared by the host entry points and the kernels of
+// libdas.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "das.h"
+
+// Kernel-side constants of one beamform launch, passed by value.
+struct DasKParams {
+    double ox, oy, oz;        // voxel (0,0,0) centre, metres
+    double sx, sy, sz;        // voxel pitch, metres
+    double fs;                // Hz
+    double t0fs;              // t0 * fs (samples)
+    double fs_over_c;         // samples per metre of path
+    double f0;                // IQ demodulation frequency, Hz
+    double f0_over_c;         // IQ phase cycles per metre of path
+    float inv_theta_max;      // 1 / theta_max (receive Hann)
+    int32_t apod;             // 0: w_rx = 1
+    int32_t nx, ny, nz, N;
+    int32_t B, Q, M, K;
+    int32_t q_begin, q_count; // transmit events of this launch (absolute q)
+    int32_t accumulate;       // 0 overwrite, 1 add
+};
+
+struct das_plan {
+    das_problem p;
+    int64_t N;
+    int32_t alg;              // resolved algorithm
+    int32_t elem_bytes;       // 4 or 8
+    int32_t fl;               // batch-inner: frames per lane
+    int32_t bt;               // baseline: frames per lane
+};
+
+// Launchers (defined next to their kernels).  They assume validated input.
+hipError_t das_launch_permute(const das_plan_t &plan, const void *rf, void *out,
+                              int32_t q_begin, int32_t q_count, hipStream_t stream);
+hipError_t das_launch_baseline(const das_plan_t &plan, const DasKParams &kp, const float *rf,
+                               const float *rx, const float *tau_tx, const float *w_tx,
+                               float *out, hipStream_t stream);
+hipError_t das_launch_batch_inner(const das_plan_t &plan, const DasKParams &kp, const float *rf,
+                                  const float *rx, const float *tau_tx, const float *w_tx,
+                                  float *out, hipStream_t stream);
