@@ -61,6 +61,8 @@ def main():
     ap.add_argument("--config", default="main", help="workload: tiny, mid, main, main-c64")
     ap.add_argument("--layout", default="kqmb", choices=["kqmb", "qmkb"])
     ap.add_argument("--algorithm", default="batch_inner", choices=["batch_inner", "baseline"])
+    ap.add_argument("--q-chunk", type=int, default=0,
+                    help="transmit events per permute/beamform pair (0: as many as the plan allows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-voxels", type=int, default=0, help="oracle sample size (0: one depth slab)")
     args = ap.parse_args()
@@ -96,47 +98,53 @@ def main():
     plan = das.plan_from_fields(fields, algorithm=args.algorithm, layout=args.layout)
     out = torch.empty(plan.output_shape(), dtype=torch.float32, device=dev)
     bi = plan.batch_inner
-    perm = torch.empty(plan.permuted_shape(), dtype=torch.float32, device=dev) if bi else None
+    # events per das_permute / das_beamform pair (all Q unless the layout's
+    # 32-bit offsets need chunks); chunks after the first accumulate into out
+    qc = plan.max_q_chunk() if bi else cfg.Q
+    if args.q_chunk > 0:
+        qc = min(qc, args.q_chunk)
+    chunks = [(q0, min(qc, cfg.Q - q0)) for q0 in range(0, cfg.Q, qc)]
+    perm = torch.empty(plan.permuted_shape(qc), dtype=torch.float32, device=dev) if bi else None
+    per_event = perm.numel() // qc if bi else 0
     stream = torch.cuda.current_stream(dev)
 
     def step(ev=None):
-        if bi:
-            if ev is not None:
-                ev[0].record(stream)
-            plan.permute(rf, perm, 0, cfg.Q, stream=stream)
-            if ev is not None:
-                ev[1].record(stream)
-            plan.beamform(perm, rx_d, tau_d, w_d, out, 0, cfg.Q, stream=stream)
-            if ev is not None:
-                ev[2].record(stream)
-        else:
-            if ev is not None:
-                ev[0].record(stream)
-                ev[1].record(stream)
-            plan.beamform(rf, rx_d, tau_d, w_d, out, 0, cfg.Q, stream=stream)
-            if ev is not None:
-                ev[2].record(stream)
+        """ev: list of (start, mid, end) event triples, one per chunk."""
+        for i, (q0, n) in enumerate(chunks):
+            e = ev[i] if ev is not None else None
+            if e is not None:
+                e[0].record(stream)
+            if bi:
+                view = perm.view(-1)[: per_event * n]
+                plan.permute(rf, view, q0, n, stream=stream)
+            if e is not None:
+                e[1].record(stream)
+            plan.beamform(view if bi else rf, rx_d, tau_d, w_d, out, q0, n, accumulate=(i > 0), stream=stream)
+            if e is not None:
+                e[2].record(stream)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in chunks] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    perm_ms = [e[0].elapsed_time(e[1]) for e in events]
-    kern_ms = [e[1].elapsed_time(e[2]) for e in events]
+    perm_ms = [sum(e[0].elapsed_time(e[1]) for e in ev) for ev in events]
+    kern_ms = [sum(e[1].elapsed_time(e[2]) for e in ev) for ev in events]
+    launch_ms = [e[1].elapsed_time(e[2]) for ev in events for e in ev]
     print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
     accs = das_synth.accumulations(cfg)
     ms_step = wall * 1e3 / args.steps
     value = accs / (ms_step * 1e-3) / 1e9
-    kern_avg = float(np.mean(kern_ms))
+    kern_avg = float(np.mean(kern_ms))              # beamform time per step (all chunks)
+    launch_avg = float(np.mean(launch_ms))          # per beamform launch
     perm_avg = float(np.mean(perm_ms))
     flops_per_acc = 8 if cfg.iq else 4          # 2 FMA (real) or 8 FMA (complex) per accumulation
     achieved = accs * flops_per_acc / (kern_avg * 1e-3) / 1e12
@@ -189,8 +197,8 @@ def main():
                          f"{cfg.array[0]}x{cfg.array[1]} array (M={cfg.M}), Q={cfg.Q} "
                          f"{'plane' if cfg.tx == 'plane' else 'diverging'} waves, K={cfg.K}, B={cfg.B}, "
                          f"{'complex64 IQ' if cfg.iq else 'fp32 RF'}"),
-            "step": ("das_permute + das_beamform (batch-inner, layout "
-                     f"{args.layout.upper()})" if bi else "das_beamform (baseline)"),
+            "step": ((f"das_permute + das_beamform (batch-inner, layout {args.layout.upper()}"
+                      f", {len(chunks)} chunk(s) of <= {qc} events)") if bi else "das_beamform (baseline)"),
             "accumulations_per_step": accs,
             "frames_per_lane": info["frames_per_lane"],
         },
@@ -202,7 +210,9 @@ def main():
             "frac": achieved / PEAK_FP32_TFLOPS,
             "traffic": traffic,
             "kernel": kernel_name,
-            "kernel_ms": kern_avg,
+            "kernel_ms_per_step": kern_avg,
+            "kernel_ms_per_launch": launch_avg,
+            "launches_per_step": len(chunks),
             "kernel_gacc_s": accs / (kern_avg * 1e-3) / 1e9,
             "flops_per_accumulation": flops_per_acc,
         },

@@ -105,6 +105,9 @@ typedef struct das_plan_info {
     int32_t lanes_per_voxel;    /* batch-inner: 16; baseline: 1                      */
     int32_t voxels_per_group;   /* voxels one workgroup covers                       */
     int64_t N;                  /* nx * ny * nz                                      */
+    int32_t staged;             /* batch-inner: 1 if frame rows are staged through LDS
+                                   (8 x 8 voxel tiles per 1024-thread workgroup), 0 if
+                                   every lane loads its rows from memory             */
 } das_plan_info;
 
 /* Validate a problem and build a host-side plan.  Host only: no HIP call, no
@@ -123,6 +126,13 @@ das_status das_plan_get_info(const das_plan_t *plan, das_plan_info *info);
 /* Bytes of the permuted buffer that holds q_count transmit events
  * (K * q_count * M * B * elem_bytes, in either layout).  0 on a bad argument. */
 size_t das_permuted_bytes(const das_plan_t *plan, int32_t q_count);
+
+/* Largest q_count one das_beamform call accepts with this plan: Q, except
+ * for the batch-inner kernel on the KQMB layout, whose chunk of K x q_count x
+ * M x B samples must stay below 4 GiB (32-bit sample offsets).  0 if even one
+ * event does not fit (then use DAS_LAYOUT_QMKB).  Stream a volume through
+ * das_permute / das_beamform in chunks of at most this many events. */
+int32_t das_max_q_chunk(const das_plan_t *plan);
 
 /* Permute transmit events [q_begin, q_begin + q_count) of the B x Q x M x K
  * input into the plan's frames-innermost layout ("ffdas: volumetric

@@ -72,7 +72,8 @@ def run_gpu(inp: Inputs, algorithm: str, layout: str = "kqmb", q_chunk: int | No
     Q = inp.cfg.Q
     first_acc = accumulate_into is not None
     if plan.batch_inner:
-        qc = Q if q_chunk is None else q_chunk
+        qc = min(Q if q_chunk is None else q_chunk, plan.max_q_chunk())
+        assert qc >= 1
         perm = torch.empty(plan.permuted_shape(qc), dtype=torch.float32, device=inp.rf_d.device)
         for q0 in range(0, Q, qc):
             n = min(qc, Q - q0)

@@ -125,13 +125,23 @@ def test_plan_info_and_sizes():
     assert pl.permuted_shape(1) == (64, 1, 8, 32, 2)
     pl2 = das.Plan(**_problem(algorithm="default"))
     assert pl2.info["algorithm"] == das.ALG_BASELINE       # DEFAULT dispatches to the baseline
+    assert pl.info["staged"] == 0                           # IQ: direct-load kernel
+    assert das.Plan(**_problem(B=32)).info["staged"] == 1      # fp32, B % 32 == 0: LDS-staged
+    assert das.Plan(**_problem(B=16)).info["staged"] == 0
+    assert das.Plan(**_problem(B=32, algorithm="baseline")).info["staged"] == 0
     pl3 = das.Plan(**_problem(layout="qmkb"))
     assert pl3.permuted_shape(2) == (2, 8, 64, 4)
 
 
-@pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (24, 1), (32, 2), (48, 2), (64, 4), (96, 4), (66, 2)])
+@pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (24, 1), (32, 2), (48, 1), (64, 4), (96, 4), (66, 1),
+                                  (160, 4)])
 def test_frames_per_lane_choice(B, fl):
     assert das.Plan(**_problem(B=B)).info["frames_per_lane"] == fl
+
+
+@pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (31, 1), (32, 2), (40, 2), (64, 2)])
+def test_frames_per_lane_choice_iq(B, fl):
+    assert das.Plan(**_problem(B=B, dtype="c64", f_demod=5e6)).info["frames_per_lane"] == fl
 
 
 def test_error_strings(lib):
@@ -184,6 +194,13 @@ def test_batch_inner_kqmb_chunk_limit(lib):
     g = _fake(0x10000)
     assert lib.das_beamform(pl._h, g, g, g, g, g, 0, 16, 0, None) == UNSUPPORTED
     assert lib.das_beamform(pl._h, g, g, g, g, g, 0, 4, 0, None) == UNSUPPORTED
+    assert lib.das_max_q_chunk(pl._h) == 3
+    assert pl.max_q_chunk() == 3
+    assert das.Plan(**_problem(B=64, Q=16, M=1024, K=4096, layout="qmkb")).max_q_chunk() == 16
+    assert das.Plan(**_problem(B=64, Q=16, M=1024, K=4096, algorithm="baseline")).max_q_chunk() == 16
+    assert lib.das_max_q_chunk(None) == 0
+    # Main-c64: 8 events of 2048 x 1024 x 32 complex samples are exactly 4 GiB, 7 fit
+    assert das.Plan(**_problem(B=32, Q=9, M=1024, K=2048, dtype="c64", f_demod=5e6)).max_q_chunk() == 7
     # a 1-event chunk passes validation (and then needs a device)
     rc = lib.das_beamform(pl._h, g, g, g, g, g, 0, 1, 0, None) if not _gpu() else NO_DEVICE
     assert rc == NO_DEVICE

@@ -57,7 +57,7 @@ class _PlanInfo(ctypes.Structure):
     _fields_ = [
         ("algorithm", ctypes.c_int32), ("layout", ctypes.c_int32), ("elem_bytes", ctypes.c_int32),
         ("frames_per_lane", ctypes.c_int32), ("lanes_per_voxel", ctypes.c_int32),
-        ("voxels_per_group", ctypes.c_int32), ("N", ctypes.c_int64),
+        ("voxels_per_group", ctypes.c_int32), ("N", ctypes.c_int64), ("staged", ctypes.c_int32),
     ]
 
 
@@ -87,6 +87,8 @@ def load_library():
     lib.das_permute.restype = ctypes.c_int
     lib.das_beamform.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
     lib.das_beamform.restype = ctypes.c_int
+    lib.das_max_q_chunk.argtypes = [vp]
+    lib.das_max_q_chunk.restype = i32
     lib.das_error_string.argtypes = [ctypes.c_int]
     lib.das_error_string.restype = ctypes.c_char_p
     lib.das_abi_version.argtypes = []
@@ -155,6 +157,10 @@ class Plan:
 
     def permuted_bytes(self, q_count: Optional[int] = None) -> int:
         return int(self._lib.das_permuted_bytes(self._h, self.problem.Q if q_count is None else int(q_count)))
+
+    def max_q_chunk(self) -> int:
+        """Most transmit events one beamform call accepts (see das_max_q_chunk)."""
+        return int(self._lib.das_max_q_chunk(self._h))
 
     def permuted_shape(self, q_count: Optional[int] = None) -> tuple:
         p = self.problem

@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 
@@ -42,14 +43,32 @@ das_status check_device() {
     return st == 1 ? DAS_OK : DAS_ERR_NO_DEVICE;
 }
 
-// Frames per lane of the batch-inner kernel: the widest vector (4, 2 or 1
-// frames) that divides B without leaving most of a 16-lane row idle.
-int32_t pick_fl(int32_t B) {
-    for (int32_t f : {4, 2}) {
-        if (B % f == 0 && 16 * f <= B)
-            return f;
-    }
+// Frames per lane of the batch-inner kernel.  fp32: 4 adjacent frames (one
+// 128-bit load) when B is a multiple of 4 and at least 64; 2 frames 16 apart
+// (two dword loads) when B is a multiple of 32; else 1.  IQ: 2 adjacent
+// complex frames (128-bit) when B is even and at least 32; else 1.
+int32_t pick_fl(int32_t B, int32_t dtype) {
+    if (dtype == DAS_C64)
+        return (B % 2 == 0 && B >= 32) ? 2 : 1;
+    if (B % 4 == 0 && B >= 64)
+        return 4;
+    if (B % 32 == 0)
+        return 2;
     return 1;
+}
+
+// Transmit events per receiver sweep of the batch-inner kernel: enough to
+// amortize the receive geometry, few enough that the frame rows a die touches
+// at once stay in its 4 MB L2.  DAS_Q_GROUP overrides (tuning sweeps).
+int32_t pick_q_group(const das_problem &p, int32_t elem) {
+    const char *env = std::getenv("DAS_Q_GROUP");
+    if (env) {
+        const int v = std::atoi(env);
+        if (v >= 1)
+            return v;
+    }
+    const int64_t row = (int64_t)p.B * elem;
+    return row <= 128 ? 3 : (row <= 256 ? 2 : 1);
 }
 
 DasKParams make_params(const das_plan_t &pl, int32_t q_begin, int32_t q_count, int32_t accumulate) {
@@ -78,11 +97,35 @@ DasKParams make_params(const das_plan_t &pl, int32_t q_begin, int32_t q_count, i
     k.K = p.K;
     k.q_begin = q_begin;
     k.q_count = q_count;
+    k.q_group = pl.q_group;
     k.accumulate = accumulate;
     return k;
 }
 
 bool valid_plan(const das_plan_t *plan) { return plan != nullptr; }
+
+// The batch-inner KQMB kernel addresses a chunk with 32-bit byte offsets from
+// the first row of a 16-receiver block.
+bool kqmb_chunk_fits(const das_plan_t *plan, int64_t q_count) {
+    const das_problem &p = plan->p;
+    const uint64_t row = (uint64_t)p.B * plan->elem_bytes;
+    const uint64_t chunk = (uint64_t)p.K * q_count * p.M * row;
+    return chunk + 16ull * row <= (uint64_t)UINT32_MAX;
+}
+
+int32_t max_q_chunk(const das_plan_t *plan) {
+    if (plan->alg != DAS_ALG_BATCH_INNER || plan->p.layout != DAS_LAYOUT_KQMB)
+        return plan->p.Q;
+    int32_t lo = 0, hi = plan->p.Q;
+    while (lo < hi) {
+        const int32_t mid = lo + (hi - lo + 1) / 2;
+        if (kqmb_chunk_fits(plan, mid))
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
 
 }  // namespace
 
@@ -151,8 +194,16 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
     pl->N = N;
     pl->alg = (p.algorithm == DAS_ALG_BATCH_INNER) ? DAS_ALG_BATCH_INNER : DAS_ALG_BASELINE;
     pl->elem_bytes = elem;
-    pl->fl = pick_fl(p.B);
+    pl->fl = pick_fl(p.B, p.dtype);
     pl->bt = 8;
+    pl->q_group = pick_q_group(p, elem);
+    // LDS-staged batch-inner kernel where it is built; DAS_BI_KERNEL=direct
+    // selects the direct-load kernel (comparisons).
+    const char *kv = std::getenv("DAS_BI_KERNEL");
+    pl->staged = (pl->alg == DAS_ALG_BATCH_INNER && das_staged_supported(*pl) &&
+                  !(kv && std::strcmp(kv, "direct") == 0)) ? 1 : 0;
+    const char *vv = std::getenv("DAS_STAGED_VPR");
+    pl->vpr = (vv && std::atoi(vv) == 1) ? 1 : 2;
     *out = pl;
     return DAS_OK;
 }
@@ -170,8 +221,11 @@ das_status das_plan_get_info(const das_plan_t *plan, das_plan_info *info) {
     info->lanes_per_voxel = bi ? 16 : 1;
     info->voxels_per_group = bi ? 16 : 256;
     info->N = plan->N;
+    info->staged = plan->staged;
     return DAS_OK;
 }
+
+int32_t das_max_q_chunk(const das_plan_t *plan) { return valid_plan(plan) ? max_q_chunk(plan) : 0; }
 
 size_t das_permuted_bytes(const das_plan_t *plan, int32_t q_count) {
     if (!valid_plan(plan) || q_count < 1 || q_count > plan->p.Q)
@@ -207,13 +261,8 @@ das_status das_beamform(const das_plan_t *plan, const void *rf, const float *rx_
         return DAS_ERR_INVALID_ARGUMENT;
     if (!aligned16(rf) || !aligned16(rx_pos) || !aligned16(tau_tx) || !aligned16(w_tx) || !aligned16(out))
         return DAS_ERR_ALIGNMENT;
-    const das_problem &p = plan->p;
-    if (plan->alg == DAS_ALG_BATCH_INNER && p.layout == DAS_LAYOUT_KQMB) {
-        // 32-bit sample offsets from the first row of a 16-receiver block
-        const uint64_t chunk = (uint64_t)p.K * q_count * p.M * p.B * plan->elem_bytes;
-        if (chunk + 16ull * p.B * plan->elem_bytes > (uint64_t)UINT32_MAX)
-            return DAS_ERR_UNSUPPORTED;
-    }
+    if (q_count > max_q_chunk(plan))
+        return DAS_ERR_UNSUPPORTED;
     das_status st = check_device();
     if (st != DAS_OK)
         return st;
@@ -221,9 +270,12 @@ das_status das_beamform(const das_plan_t *plan, const void *rf, const float *rx_
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const float *rff = static_cast<const float *>(rf);
     float *o = static_cast<float *>(out);
-    hipError_t e = (plan->alg == DAS_ALG_BATCH_INNER)
-                       ? das_launch_batch_inner(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s)
-                       : das_launch_baseline(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s);
+    hipError_t e;
+    if (plan->alg == DAS_ALG_BATCH_INNER)
+        e = plan->staged ? das_launch_batch_inner_staged(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s)
+                         : das_launch_batch_inner(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s);
+    else
+        e = das_launch_baseline(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s);
     return e == hipSuccess ? DAS_OK : DAS_ERR_LAUNCH;
 }
 

@@ -27,7 +27,7 @@ __global__ __launch_bounds__(THREADS) void das_baseline_kernel(DasKParams P, con
     constexpr int C = IQ ? 2 : 1;                   // floats per sample
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int tiles_x = (P.nx + PX - 1) / PX, tiles_y = (P.ny + PY - 1) / PY;
-    int t = blockIdx.x;
+    int t = das::xcd_tile(blockIdx.x, gridDim.x);
     const int tx = t % tiles_x;
     t /= tiles_x;
     const int ty = t % tiles_y;

@@ -29,28 +29,41 @@ struct FVec {
     float v[NF];
 };
 
-// NF consecutive floats at p (p aligned to min(16, 4 NF) bytes).
-template <int NF>
-__device__ __forceinline__ FVec<NF> load_f(const char *p) {
-    FVec<NF> r;
+// NF consecutive floats at byte offset off (+ the constant IMM) of r.
+template <int NF, int IMM>
+__device__ __forceinline__ FVec<NF> buf_load(das::BufRsrc r, uint32_t off) {
+    FVec<NF> x;
     if constexpr (NF == 1) {
-        r.v[0] = *reinterpret_cast<const float *>(p);
+        x.v[0] = das::buffer_load_f32(r, (int)(off + IMM), 0, 0);
     } else if constexpr (NF == 2) {
-        const float2 t = *reinterpret_cast<const float2 *>(p);
-        r.v[0] = t.x;
-        r.v[1] = t.y;
+        const das::f32x2 t = das::buffer_load_f32x2(r, (int)(off + IMM), 0, 0);
+        x.v[0] = t.x;
+        x.v[1] = t.y;
     } else {
 #pragma unroll
         for (int i = 0; i < NF / 4; ++i) {
-            const float4 t = *reinterpret_cast<const float4 *>(p + 16 * i);
-            r.v[4 * i + 0] = t.x;
-            r.v[4 * i + 1] = t.y;
-            r.v[4 * i + 2] = t.z;
-            r.v[4 * i + 3] = t.w;
+            const das::f32x4 t = das::buffer_load_f32x4(r, (int)(off + IMM + 16 * i), 0, 0);
+            x.v[4 * i + 0] = t.x;
+            x.v[4 * i + 1] = t.y;
+            x.v[4 * i + 2] = t.z;
+            x.v[4 * i + 3] = t.w;
         }
     }
-    return r;
+    return x;
 }
+
+// Frames of one lane: FL frames starting at a per-lane base.  VEC: the FL
+// frames are adjacent (one FL-wide vector load per tap).  Otherwise they are
+// 16 frames apart (lane li owns frames li, li + 16, ...), so that each load is
+// a plain dword and the 16 lanes of a row read 64 contiguous bytes: on gfx950
+// a 64-bit vector load costs as many address cycles as a 128-bit one, so
+// 2-frame vectors would halve the rate at which rows are delivered.
+template <bool IQ, int FL>
+struct FrameMap {
+    static constexpr bool VEC = IQ || FL != 2;
+    static constexpr int TILE = ROW * FL;                 // frames per row pass
+    __device__ static int frame(int li, int f) { return VEC ? li * FL + f : li + ROW * f; }
+};
 
 template <bool IQ, int FL, int LAYOUT>
 __global__ __launch_bounds__(THREADS) void das_batch_inner_kernel(DasKParams P, const float *__restrict__ rfp,
@@ -59,6 +72,7 @@ __global__ __launch_bounds__(THREADS) void das_batch_inner_kernel(DasKParams P, 
                                                                   const float *__restrict__ w_tx,
                                                                   float *__restrict__ out,
                                                                   uint32_t tap_stride) {
+    using FM = FrameMap<IQ, FL>;
     constexpr int C = IQ ? 2 : 1;          // floats per sample
     constexpr int E = 4 * C;               // bytes per sample
     constexpr int NF = FL * C;             // floats per lane per tap
@@ -66,7 +80,7 @@ __global__ __launch_bounds__(THREADS) void das_batch_inner_kernel(DasKParams P, 
     const int vrow = lane >> 4, li = lane & (ROW - 1);
 
     const int tiles_x = (P.nx + PX - 1) / PX, tiles_y = (P.ny + PY - 1) / PY;
-    int t = blockIdx.x;
+    int t = das::xcd_tile(blockIdx.x, gridDim.x);
     const int tx = t % tiles_x;
     t /= tiles_x;
     const int ty = t % tiles_y;
@@ -77,7 +91,11 @@ __global__ __launch_bounds__(THREADS) void das_batch_inner_kernel(DasKParams P, 
     iy = min(iy, P.ny - 1);
     const int n = (iz * P.ny + iy) * P.nx + ix;
 
-    const int bl = blockIdx.y * (ROW * FL) + li * FL;      // first frame of this lane
+    // First frame of this lane.  The host guarantees that a lane's FL frames
+    // are all valid or all past B (B % FL == 0 for vector maps, B % 32 == 0
+    // for the strided map), so one flag covers them.
+    const int b0 = blockIdx.y * FM::TILE;
+    const int bl = b0 + FM::frame(li, 0);
     const bool fr_ok = bl < P.B;
     const uint32_t laneoff = (uint32_t)(fr_ok ? bl : 0) * E;
 
@@ -85,6 +103,8 @@ __global__ __launch_bounds__(THREADS) void das_batch_inner_kernel(DasKParams P, 
     // Byte distance between receivers m and m+1 of one event, and between events.
     const int64_t m_stride = (LAYOUT == DAS_LAYOUT_KQMB) ? row_bytes : row_bytes * P.K;
     const int64_t q_stride = m_stride * P.M;
+    // bytes of the permuted chunk (K x q_count x M x B samples in either layout)
+    const int64_t P_bytes = row_bytes * P.M * P.q_count * P.K;
 
     double vx, vy, vz;
     das::voxel_centre(P, ix, iy, iz, vx, vy, vz);
@@ -94,74 +114,83 @@ __global__ __launch_bounds__(THREADS) void das_batch_inner_kernel(DasKParams P, 
     for (int i = 0; i < NF; ++i) acc[i] = 0.0f;
 
     const char *rf_bytes = reinterpret_cast<const char *>(rfp);
-    for (int m0 = 0; m0 < P.M; m0 += ROW) {
-        const int mm = m0 + li;
-        const int m = min(mm, P.M - 1);
-        das::RxTerm R = das::rx_term<IQ>(P, vx, vy, vz, rx[3 * m], rx[3 * m + 1], rx[3 * m + 2]);
-        R.w = (mm < P.M) ? R.w : 0.0f;
-        // Byte offset of receiver m0 + j's row from receiver m0's, plus this
-        // lane's frames.  Past the last receiver the row of receiver M - 1 is
-        // read instead (its weights are zero), so every address stays inside.
-        uint32_t jo[ROW];
-        const int jmax = P.M - 1 - m0;
+    // Transmit events go in groups of q_group so that the frame rows in use
+    // at once across a GPU die fit its L2; the receive geometry is recomputed
+    // once per group.
+    for (int g0 = 0; g0 < P.q_count; g0 += P.q_group) {
+        const int g1 = min(g0 + P.q_group, P.q_count);
+        for (int m0 = 0; m0 < P.M; m0 += ROW) {
+            const int mm = m0 + li;
+            const int m = min(mm, P.M - 1);
+            das::RxTerm R = das::rx_term<IQ>(P, vx, vy, vz, rx[3 * m], rx[3 * m + 1], rx[3 * m + 2]);
+            R.w = (mm < P.M) ? R.w : 0.0f;
+            // Byte offset of receiver m0 + j's row from receiver m0's, plus this
+            // lane's frames.  Past the last receiver the row of receiver M - 1 is
+            // read instead (its weights are zero), so every address stays inside.
+            uint32_t jo[ROW];
+            const int jmax = P.M - 1 - m0;
 #pragma unroll
-        for (int j = 0; j < ROW; ++j) jo[j] = laneoff + (uint32_t)(min(j, jmax) * m_stride);
+            for (int j = 0; j < ROW; ++j) jo[j] = laneoff + (uint32_t)(min(j, jmax) * m_stride);
 #pragma unroll
-        for (int i = 0; i < NF; ++i) part[i] = 0.0f;
+            for (int i = 0; i < NF; ++i) part[i] = 0.0f;
 
-        for (int ql = 0; ql < P.q_count; ++ql) {
-            const int q = P.q_begin + ql;
-            const das::TxTerm T = das::tx_term<IQ>(P, tau_tx[(int64_t)q * P.N + n], w_tx[(int64_t)q * P.N + n]);
-            float pc = 1.0f, ps = 0.0f;
-            if constexpr (IQ) {
-                pc = T.pc * R.pc - T.ps * R.ps;
-                ps = T.ps * R.pc + T.pc * R.ps;
-            }
-            const das::Lerp L = das::lerp_coeffs<IQ>(T.s_tx + R.s_rx, T.w * R.w, pc, ps, P.K);
-            const uint32_t koff = L.k * tap_stride;
-            float a = L.a, b = L.b, ai = L.ai, bi = L.bi;
-            if constexpr (IQ)
-                das::settle(a, b, ai, bi);
-            else
-                das::settle(a, b);
-            // Row of (k = 0, q, m0) for both taps; wave-uniform.
-            const char *pb0 = rf_bytes + (int64_t)ql * q_stride + (int64_t)m0 * m_stride;
-            const char *pb1 = pb0 + tap_stride;
-
-            das::unroll<ROW>([&](auto J) {
-                constexpr int j = decltype(J)::value;
-                const uint32_t off = das::row_bcast<j>(koff) + jo[j];
-                const FVec<NF> x0 = load_f<NF>(pb0 + off);
-                const FVec<NF> x1 = load_f<NF>(pb1 + off);
-#pragma unroll
-                for (int f = 0; f < FL; ++f) {
-                    if constexpr (IQ) {
-                        float &re = part[2 * f], &im = part[2 * f + 1];
-                        const float x0r = x0.v[2 * f], x0i = x0.v[2 * f + 1];
-                        const float x1r = x1.v[2 * f], x1i = x1.v[2 * f + 1];
-                        das::fmac_bcast<j>(re, a, x0r);
-                        das::fnmac_bcast<j>(re, ai, x0i);
-                        das::fmac_bcast<j>(re, b, x1r);
-                        das::fnmac_bcast<j>(re, bi, x1i);
-                        das::fmac_bcast<j>(im, a, x0i);
-                        das::fmac_bcast<j>(im, ai, x0r);
-                        das::fmac_bcast<j>(im, b, x1i);
-                        das::fmac_bcast<j>(im, bi, x1r);
-                    } else {
-                        das::fmac_bcast<j>(part[f], a, x0.v[f]);
-                        das::fmac_bcast<j>(part[f], b, x1.v[f]);
-                    }
+            for (int ql = g0; ql < g1; ++ql) {
+                const int q = P.q_begin + ql;
+                const das::TxTerm T =
+                    das::tx_term<IQ>(P, tau_tx[(int64_t)q * P.N + n], w_tx[(int64_t)q * P.N + n]);
+                float pc = 1.0f, ps = 0.0f;
+                if constexpr (IQ) {
+                    pc = T.pc * R.pc - T.ps * R.ps;
+                    ps = T.ps * R.pc + T.pc * R.ps;
                 }
-            });
-        }
+                const das::Lerp L = das::lerp_coeffs<IQ>(T.s_tx + R.s_rx, T.w * R.w, pc, ps, P.K);
+                const uint32_t koff = L.k * tap_stride;
+                float a = L.a, b = L.b, ai = L.ai, bi = L.bi;
+                if constexpr (IQ)
+                    das::settle(a, b, ai, bi);
+                else
+                    das::settle(a, b);
+                // Row of (k = 0, q, m0) for both taps; wave-uniform.  The
+                // resources end at the end of the chunk.
+                const int64_t pos = (int64_t)ql * q_stride + (int64_t)m0 * m_stride;
+                const das::BufRsrc r0 = das::make_rsrc(rf_bytes + pos, (uint64_t)(P_bytes - pos));
+                const das::BufRsrc r1 =
+                    das::make_rsrc(rf_bytes + pos + tap_stride, (uint64_t)(P_bytes - pos - (int64_t)tap_stride));
+
+                das::unroll<ROW>([&](auto J) {
+                    constexpr int j = decltype(J)::value;
+                    const uint32_t off = das::row_bcast<j>(koff) + jo[j];
+                    FVec<NF> x0, x1;
+                    if constexpr (FM::VEC) {
+                        x0 = buf_load<NF, 0>(r0, off);
+                        x1 = buf_load<NF, 0>(r1, off);
+                    } else {
+                        das::unroll<FL>([&](auto F) {
+                            constexpr int f = decltype(F)::value;
+                            x0.v[f] = buf_load<1, f * ROW * E>(r0, off).v[0];
+                            x1.v[f] = buf_load<1, f * ROW * E>(r1, off).v[0];
+                        });
+                    }
+                    if constexpr (IQ) {
 #pragma unroll
-        for (int i = 0; i < NF; ++i) acc[i] += part[i];
+                        for (int f = 0; f < FL; ++f)
+                            das::cmac_bcast<j>(part[2 * f], part[2 * f + 1], a, ai, b, bi, x0.v[2 * f],
+                                               x0.v[2 * f + 1], x1.v[2 * f], x1.v[2 * f + 1]);
+                    } else {
+#pragma unroll
+                        for (int f = 0; f < FL; ++f) das::lerp_bcast<j>(part[f], a, b, x0.v[f], x1.v[f]);
+                    }
+                });
+            }
+#pragma unroll
+            for (int i = 0; i < NF; ++i) acc[i] += part[i];
+        }
     }
 
     if (vox_ok && fr_ok) {
 #pragma unroll
         for (int f = 0; f < FL; ++f) {
-            float *o = out + ((int64_t)(bl + f) * P.N + n) * C;
+            float *o = out + ((int64_t)(b0 + FM::frame(li, f)) * P.N + n) * C;
 #pragma unroll
             for (int c = 0; c < C; ++c) o[c] = P.accumulate ? o[c] + acc[f * C + c] : acc[f * C + c];
         }
@@ -174,7 +203,7 @@ hipError_t launch(const das_plan_t &plan, const DasKParams &kp, const float *rf,
     const int64_t row_bytes = (int64_t)kp.B * plan.elem_bytes;
     const int64_t tap = (LAYOUT == DAS_LAYOUT_KQMB) ? row_bytes * kp.q_count * kp.M : row_bytes;
     const int tiles = ((kp.nx + PX - 1) / PX) * ((kp.ny + PY - 1) / PY) * kp.nz;
-    const int ftiles = (kp.B + ROW * FL - 1) / (ROW * FL);
+    const int ftiles = (kp.B + FrameMap<IQ, FL>::TILE - 1) / FrameMap<IQ, FL>::TILE;
     hipLaunchKernelGGL((das_batch_inner_kernel<IQ, FL, LAYOUT>), dim3(tiles, ftiles), dim3(THREADS), 0,
                        stream, kp, rf, rx, tau, w, out, (uint32_t)tap);
     return hipGetLastError();

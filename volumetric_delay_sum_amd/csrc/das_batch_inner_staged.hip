@@ -1,0 +1,516 @@
+// LDS-staged batch-inner DAS kernel for gfx950.
+//
+// Same arithmetic as the direct batch-inner kernel ("ffdas: volumetric
+// ultrasound reconstruction at warp speed", Section 3, batch-inner tiling:
+// lanes sharing a voxel read consecutive frames of one (k, q, m) row, frames
+// being the contiguous axis after the permute), but the frame rows reach the
+// lanes through LDS instead of the vector L1.  On gfx950 a 64-lane vector load
+// costs the texture-address unit several cycles whatever its width, which caps
+// an L1-fed gather near 6 accumulations per clock per CU; LDS delivers 128-bit
+// reads at about 200 B/clk/CU even at random row offsets.  The pages note that
+// neighbouring voxels need nearly the same sample indices of each receiver
+// (Section 3, spatial locality; the tensor-core paragraphs build their dense
+// tiles on the same fact): here that locality lets a workgroup stage each
+// receiver's few distinct rows once and serve all its voxels from them.
+//
+// Mapping.  A 1024-thread workgroup owns an 8 x 8 x VPR tile of voxels; each
+// 16-lane DPP row owns the VPR voxels of one (x, y) column of the tile and
+// each lane FL consecutive frames of the frame tile.  Work goes in steps of (transmit event, block of 16
+// receivers).  Per step:
+//   1. every lane j of every row computes the sample split k and weights of
+//      receiver m0 + j for its voxel (fp64 position, as in the direct kernel);
+//   2. the window [kmin, kmax] of k over the tile's voxels with a non-zero
+//      weight is reduced per receiver (shuffles in a wave, LDS atomics across
+//      waves);
+//   3. wave w copies receiver m0 + w's rows kmin .. kmax + 1 from HBM into LDS
+//      as "pair rows": pair p holds, for every frame, samples kmin + p and
+//      kmin + p + 1 side by side, so a lane reads both interpolation taps of
+//      its frames with one ds_read_b128;
+//   4. each row walks the 16 receivers, broadcasting lane j's LDS offset and
+//      weights through DPP row_newbcast:j exactly as the direct kernel does.
+// The copy for step i + 1 is loaded into registers while step i computes and
+// written to LDS between barriers; the transmit tables are read a step ahead.
+// Two voxels per row double the arithmetic per step while the window grows by
+// about half, so the per-step barriers, window reduction and copy are spread
+// over more accumulations and the copy has longer to arrive.  A step whose window is wider than the LDS
+// window capacity falls back to direct loads from the permuted buffer, so any
+// geometry is served exactly; voxels with zero weight for a receiver do not
+// widen its window and read a row of it with zero coefficients.
+#include "das_device.h"
+
+namespace {
+
+constexpr int THREADS = 1024;
+constexpr int ROW = 16;               // lanes per voxel column (one DPP row)
+constexpr int TX = 8, TY = 8;         // lateral voxel tile of one workgroup (one column per row)
+constexpr int LDS_BUDGET = 144 * 1024;
+
+template <bool IQ, int FL>
+struct Geo {
+    static constexpr int C = IQ ? 2 : 1;                 // floats per sample
+    static constexpr int E = 4 * C;                      // bytes per sample
+    static constexpr int NF = FL * C;                    // floats per lane per tap
+    static constexpr int HALF = NF * 4;                  // bytes per lane per tap
+    static constexpr int LB = 2 * HALF;                  // bytes per lane in a pair row
+    static constexpr int PAIR = ROW * LB;                // bytes per pair row
+    static constexpr int ROWB = ROW * HALF;              // bytes of the frame tile in one sample row
+    static constexpr int WP = (LDS_BUDGET / (ROW * PAIR)) > 66 ? 66 : (LDS_BUDGET / (ROW * PAIR));
+    static constexpr int W_MAX = WP - 2;                 // pair rows per receiver (plus a guard row each end)
+    static constexpr int LPR = ROWB / 16;                // lanes per sample row in a 16-byte copy
+    static constexpr int RPR = 64 / LPR;                 // sample rows per copy round of a wave
+    static constexpr int MAXR = (W_MAX + 1 + RPR - 1) / RPR;
+    static constexpr int PAIR_BYTES = ROW * WP * PAIR;
+    static constexpr int LDS_BYTES = PAIR_BYTES + 4 * ROW * 4;
+    static_assert(ROWB % 16 == 0, "copy granularity");
+};
+
+// Per-lane state of one voxel in one step: sample index and weights.
+struct Step {
+    uint32_t k;
+    float a, b, ai, bi;
+    bool active;
+};
+
+struct Cursor {
+    int ql, m0, g0, g1;
+};
+
+struct Tx {
+    float tau, w;
+};
+
+template <bool IQ>
+__device__ __forceinline__ Step make_step(const DasKParams &P, const das::RxTerm &R, Tx tx) {
+    const das::TxTerm T = das::tx_term<IQ>(P, tx.tau, tx.w);
+    float pc = 1.0f, ps = 0.0f;
+    if constexpr (IQ) {
+        pc = T.pc * R.pc - T.ps * R.ps;
+        ps = T.ps * R.pc + T.pc * R.ps;
+    }
+    const double s = T.s_tx + R.s_rx;
+    const float w = T.w * R.w;
+    const das::Lerp L = das::lerp_coeffs<IQ>(s, w, pc, ps, P.K);
+    Step st;
+    st.k = L.k;
+    st.a = L.a;
+    st.b = L.b;
+    st.ai = L.ai;
+    st.bi = L.bi;
+    // the term counts (k in range) and carries weight
+    const double kf = __builtin_floor(s);
+    st.active = (kf >= 0.0) && (kf <= (double)(P.K - 2)) && (w != 0.0f);
+    return st;
+}
+
+template <bool IQ, int FL, int LAYOUT, int VPR>
+__global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, const float *__restrict__ rfp,
+                                                                const float *__restrict__ rx,
+                                                                const float *__restrict__ tau_tx,
+                                                                const float *__restrict__ w_tx,
+                                                                float *__restrict__ out, uint32_t tap_stride) {
+    using G = Geo<IQ, FL>;
+    constexpr int C = G::C, E = G::E, NF = G::NF;
+    __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
+    char *pairs = lds;
+    int *slots = reinterpret_cast<int *>(lds + G::PAIR_BYTES);   // [2 sets][min, max][16]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in SGPRs
+    const int li = lane & (ROW - 1);
+    const int vr = wave * 4 + (lane >> 4);           // voxel column 0..63
+
+    const int tiles_x = (P.nx + TX - 1) / TX, tiles_y = (P.ny + TY - 1) / TY;
+    int t = das::xcd_tile(blockIdx.x, gridDim.x);
+    const int tx = t % tiles_x;
+    t /= tiles_x;
+    const int ty = t % tiles_y;
+    const int tz = t / tiles_y;
+    int ix = tx * TX + (vr % TX), iy = ty * TY + (vr / TX);
+    const bool col_ok = ix < P.nx && iy < P.ny;
+    ix = min(ix, P.nx - 1);
+    iy = min(iy, P.ny - 1);
+    int n[VPR];
+    bool vox_ok[VPR];
+#pragma unroll
+    for (int v = 0; v < VPR; ++v) {
+        const int iz = tz * VPR + v;
+        vox_ok[v] = col_ok && iz < P.nz;
+        n[v] = (min(iz, P.nz - 1) * P.ny + iy) * P.nx + ix;
+    }
+
+    // frames of this lane: FL adjacent frames of the frame tile
+    const int b0 = blockIdx.y * (ROW * FL);
+    const int bl = b0 + li * FL;
+    const bool fr_ok = bl < P.B;
+    const uint32_t laneoff_g = (uint32_t)(fr_ok ? bl : 0) * E;   // byte offset in a global row
+    const uint32_t laneoff_l = (uint32_t)li * G::LB;              // byte offset in a pair row
+
+    const int64_t rowfull = (int64_t)P.B * E;                       // one (k, q, m) row, all frames
+    const int64_t m_stride = (LAYOUT == DAS_LAYOUT_KQMB) ? rowfull : rowfull * P.K;
+    const int64_t q_stride = m_stride * P.M;
+    const int64_t chunk_bytes = rowfull * P.M * P.q_count * P.K;
+    const char *rf_bytes = reinterpret_cast<const char *>(rfp);
+
+    // zero the pair rows (so a zero weight never meets a non-finite stale value) and the window slots
+    for (int i = tid * 16; i < G::PAIR_BYTES; i += THREADS * 16)
+        *reinterpret_cast<int4 *>(pairs + i) = make_int4(0, 0, 0, 0);
+    if (tid < 2 * 2 * ROW)
+        slots[tid] = ((tid / ROW) & 1) ? INT_MIN : INT_MAX;
+    __syncthreads();
+
+    // ---- step helpers ---------------------------------------------------
+    das::RxTerm R[VPR];                  // receive terms of (voxel v, m0 + li) for the current block
+    auto load_geometry = [&](int m0) {
+        const int mm = m0 + li;
+        const int m = min(mm, P.M - 1);
+        const float px = rx[3 * m], py = rx[3 * m + 1], pz = rx[3 * m + 2];
+#pragma unroll
+        for (int v = 0; v < VPR; ++v) {
+            // voxel centres are recomputed per receiver block rather than kept in registers
+            double vx, vy, vz;
+            das::voxel_centre(P, ix, iy, min(tz * VPR + v, P.nz - 1), vx, vy, vz);
+            R[v] = das::rx_term<IQ>(P, vx, vy, vz, px, py, pz);
+            R[v].w = (mm < P.M) ? R[v].w : 0.0f;
+        }
+    };
+    // Transmit tables of the voxels, read a step ahead through buffer loads
+    // (base per event, lane offset n).
+    auto load_tx = [&](const Cursor &c, Tx (&tx)[VPR]) {
+        const int64_t q = P.q_begin + c.ql;
+        const das::BufRsrc rt = das::make_rsrc(reinterpret_cast<const char *>(tau_tx + q * P.N), (uint64_t)P.N * 4);
+        const das::BufRsrc rw = das::make_rsrc(reinterpret_cast<const char *>(w_tx + q * P.N), (uint64_t)P.N * 4);
+#pragma unroll
+        for (int v = 0; v < VPR; ++v)
+            tx[v] = Tx{das::buffer_load_f32(rt, n[v] * 4, 0, 0), das::buffer_load_f32(rw, n[v] * 4, 0, 0)};
+    };
+    // Publish the lanes' k to the window of their receiver: min/max over the
+    // row's voxels and the wave's four rows (gfx950 row swaps: lanes l and
+    // l +- 32, then rows 2r and 2r + 1), then one LDS atomic per wave and receiver.
+    auto publish = [&](const Step (&s)[VPR], int set) {
+        int kmn = INT_MAX, kmx = INT_MIN;
+#pragma unroll
+        for (int v = 0; v < VPR; ++v) {
+            kmn = min(kmn, s[v].active ? (int)s[v].k : INT_MAX);
+            kmx = max(kmx, s[v].active ? (int)s[v].k : INT_MIN);
+        }
+        {
+            const auto a = __builtin_amdgcn_permlane32_swap(kmn, kmn, false, false);
+            const auto b = __builtin_amdgcn_permlane32_swap(kmx, kmx, false, false);
+            kmn = min((int)a[0], (int)a[1]);
+            kmx = max((int)b[0], (int)b[1]);
+        }
+        {
+            const auto a = __builtin_amdgcn_permlane16_swap(kmn, kmn, false, false);
+            const auto b = __builtin_amdgcn_permlane16_swap(kmx, kmx, false, false);
+            kmn = min((int)a[0], (int)a[1]);
+            kmx = max((int)b[0], (int)b[1]);
+        }
+        if (lane < ROW && kmn != INT_MAX) {
+            atomicMin(&slots[set * 2 * ROW + li], kmn);
+            atomicMax(&slots[set * 2 * ROW + ROW + li], kmx);
+        }
+    };
+    auto advance = [&](Cursor &c) -> bool {
+        if (++c.ql < c.g1)
+            return true;
+        c.ql = c.g0;
+        c.m0 += ROW;
+        if (c.m0 < P.M)
+            return true;
+        c.m0 = 0;
+        c.g0 = c.g1;
+        c.g1 = min(c.g0 + P.q_group, P.q_count);
+        c.ql = c.g0;
+        return c.g0 < P.q_count;
+    };
+
+    // Window of the step in slot set `set`: per lane and voxel the LDS byte
+    // offset of its receiver's pair row for k; the copy of this wave's receiver.
+    struct Window {
+        uint32_t loff[VPR];
+        int kmin_w, rows_w;    // wave's copy: first sample row, number of sample rows
+        bool overflow;
+    };
+    auto read_window = [&](const Step (&s)[VPR], int set) -> Window {
+        Window wdw;
+        const int kmn = slots[set * 2 * ROW + li], kmx = slots[set * 2 * ROW + ROW + li];
+        const int np = (kmn <= kmx) ? kmx - kmn + 1 : 0;           // pair rows of receiver li
+        const uint32_t base = (uint32_t)(li * G::WP + 1) * G::PAIR;
+#pragma unroll
+        for (int v = 0; v < VPR; ++v)
+            wdw.loff[v] = s[v].active ? base + (uint32_t)((int)s[v].k - kmn) * G::PAIR : base;
+        wdw.overflow = __any(np > G::W_MAX);
+        const int kmn_w = slots[set * 2 * ROW + wave], kmx_w = slots[set * 2 * ROW + ROW + wave];
+        wdw.kmin_w = kmn_w;
+        wdw.rows_w = (kmn_w <= kmx_w) ? kmx_w - kmn_w + 2 : 0;     // sample rows kmin .. kmax + 1
+        return wdw;
+    };
+
+    // Copy of one receiver's sample rows (wave w copies receiver m0 + w).  All
+    // rounds are issued back to back; rows past the window repeat its last row
+    // (loaded, never stored).  The base address is wave-uniform and the lane
+    // offsets are fixed, so the loads need little vector address arithmetic.
+    int4 pf[G::MAXR];
+    const int crow = lane / G::LPR;                  // sample row within a copy round
+    const uint32_t cbyte = (uint32_t)(lane % G::LPR) * 16;   // byte offset within the frame-tile row
+    const int64_t kstride = (LAYOUT == DAS_LAYOUT_KQMB) ? (int64_t)P.q_count * P.M * rowfull : rowfull;
+    auto copy_load = [&](const Cursor &c, const Window &wdw) {
+        if (wdw.rows_w == 0)
+            return;
+        const int m = c.m0 + wave;
+        const int64_t qm = (LAYOUT == DAS_LAYOUT_KQMB) ? ((int64_t)c.ql * P.M + m) * rowfull
+                                                       : ((int64_t)c.ql * P.M + m) * (int64_t)P.K * rowfull;
+        const int kmin = __builtin_amdgcn_readfirstlane(wdw.kmin_w);
+        const int64_t start = qm + (int64_t)b0 * E + (int64_t)kmin * kstride;
+        const das::BufRsrc rs = das::make_rsrc(rf_bytes + start, (uint64_t)(chunk_bytes - start));
+        const int last = __builtin_amdgcn_readfirstlane(wdw.rows_w) - 1;
+#pragma unroll
+        for (int r = 0; r < G::MAXR; ++r) {
+            const int rr = min(r * G::RPR + crow, last);
+            const das::f32x4 v = das::buffer_load_f32x4(rs, (int)((uint32_t)rr * (uint32_t)kstride + cbyte), 0, 0);
+            pf[r] = __builtin_bit_cast(int4, v);
+        }
+    };
+    auto copy_store = [&](const Window &wdw) {
+        char *dst = pairs + (uint32_t)(wave * G::WP) * G::PAIR;
+#pragma unroll
+        for (int r = 0; r < G::MAXR; ++r) {
+            const int rr = r * G::RPR + crow;        // sample row kmin + rr feeds pair rows rr (first) and rr - 1 (second)
+            if (r * G::RPR < wdw.rows_w && rr < wdw.rows_w) {
+                const char *v = reinterpret_cast<const char *>(&pf[r]);
+                constexpr int U = G::HALF < 16 ? G::HALF : 16;
+#pragma unroll
+                for (int u = 0; u < 16 / U; ++u) {
+                    const uint32_t o = cbyte + u * U;             // byte within the frame-tile row
+                    const uint32_t cidx = o / G::HALF, sub = o % G::HALF;
+                    char *first = dst + (uint32_t)(rr + 1) * G::PAIR + cidx * G::LB + sub;
+                    char *second = dst + (uint32_t)rr * G::PAIR + cidx * G::LB + G::HALF + sub;
+                    if constexpr (U == 4) {
+                        const int x = *reinterpret_cast<const int *>(v + u * U);
+                        *reinterpret_cast<int *>(first) = x;
+                        *reinterpret_cast<int *>(second) = x;
+                    } else if constexpr (U == 8) {
+                        const int2 x = *reinterpret_cast<const int2 *>(v + u * U);
+                        *reinterpret_cast<int2 *>(first) = x;
+                        *reinterpret_cast<int2 *>(second) = x;
+                    } else {
+                        const int4 x = *reinterpret_cast<const int4 *>(v + u * U);
+                        *reinterpret_cast<int4 *>(first) = x;
+                        *reinterpret_cast<int4 *>(second) = x;
+                    }
+                }
+            }
+        }
+    };
+
+    float acc[VPR][NF], part[VPR][NF];
+#pragma unroll
+    for (int v = 0; v < VPR; ++v)
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+            acc[v][i] = 0.0f;
+            part[v][i] = 0.0f;
+        }
+
+    // One voxel of one step from LDS.
+    auto compute_lds = [&](const Step &s, uint32_t loff, float (&pt)[NF]) {
+        float a = s.a, b = s.b, ai = s.ai, bi = s.bi;
+        if constexpr (IQ)
+            das::settle(a, b, ai, bi);
+        else
+            das::settle(a, b);
+        das::unroll<ROW>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            const uint32_t addr = das::row_bcast<j>(loff) + laneoff_l;
+            float x[2 * NF];
+#pragma unroll
+            for (int i = 0; i < 2 * NF; i += 4) {
+                const das::f32x4 v = *reinterpret_cast<const das::f32x4 *>(pairs + addr + 4 * i);
+                x[i] = v.x;
+                x[i + 1] = v.y;
+                if constexpr (2 * NF > 2) {
+                    x[i + 2] = v.z;
+                    x[i + 3] = v.w;
+                }
+            }
+            if constexpr (IQ) {
+#pragma unroll
+                for (int f = 0; f < FL; ++f)
+                    das::cmac_bcast<j>(pt[2 * f], pt[2 * f + 1], a, ai, b, bi, x[2 * f], x[2 * f + 1],
+                                       x[NF + 2 * f], x[NF + 2 * f + 1]);
+            } else {
+#pragma unroll
+                for (int f = 0; f < FL; ++f) das::lerp_bcast<j>(pt[f], a, b, x[f], x[NF + f]);
+            }
+        });
+    };
+    // One voxel of one step by direct loads from the permuted buffer (windows too wide for LDS).
+    auto compute_direct = [&](const Step &s, const Cursor &c, float (&pt)[NF]) {
+        float a = s.a, b = s.b, ai = s.ai, bi = s.bi;
+        if constexpr (IQ)
+            das::settle(a, b, ai, bi);
+        else
+            das::settle(a, b);
+        const uint32_t koff = s.k * tap_stride;
+        const int jmax = P.M - 1 - c.m0;
+        const int64_t pos = (int64_t)c.ql * q_stride + (int64_t)c.m0 * m_stride;
+        const das::BufRsrc r0 = das::make_rsrc(rf_bytes + pos, (uint64_t)(chunk_bytes - pos));
+        const das::BufRsrc r1 =
+            das::make_rsrc(rf_bytes + pos + tap_stride, (uint64_t)(chunk_bytes - pos - (int64_t)tap_stride));
+        das::unroll<ROW>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            const uint32_t jo = laneoff_g + (uint32_t)(min(j, jmax) * m_stride);
+            const uint32_t off = das::row_bcast<j>(koff) + jo;
+            float x0[NF], x1[NF];
+#pragma unroll
+            for (int i = 0; i < NF; ++i) {
+                x0[i] = das::buffer_load_f32(r0, (int)(off + 4 * i), 0, 0);
+                x1[i] = das::buffer_load_f32(r1, (int)(off + 4 * i), 0, 0);
+            }
+            if constexpr (IQ) {
+#pragma unroll
+                for (int f = 0; f < FL; ++f)
+                    das::cmac_bcast<j>(pt[2 * f], pt[2 * f + 1], a, ai, b, bi, x0[2 * f], x0[2 * f + 1],
+                                       x1[2 * f], x1[2 * f + 1]);
+            } else {
+#pragma unroll
+                for (int f = 0; f < FL; ++f) das::lerp_bcast<j>(pt[f], a, b, x0[f], x1[f]);
+            }
+        });
+    };
+
+    // ---- prologue: first step --------------------------------------------
+    Cursor cur{0, 0, 0, min(P.q_group, P.q_count)};
+    load_geometry(cur.m0);
+    Step s_cur[VPR];
+    {
+        Tx tx0[VPR];
+        load_tx(cur, tx0);
+#pragma unroll
+        for (int v = 0; v < VPR; ++v) s_cur[v] = make_step<IQ>(P, R[v], tx0[v]);
+    }
+    publish(s_cur, 0);
+    Cursor nxt = cur;
+    bool has_next = advance(nxt);
+    Tx tx_nxt[VPR];
+    if (has_next)
+        load_tx(nxt, tx_nxt);
+    __syncthreads();
+    Window w_cur = read_window(s_cur, 0);
+    if (!w_cur.overflow) {
+        copy_load(cur, w_cur);
+        copy_store(w_cur);
+    }
+    __syncthreads();
+
+    // ---- main loop ---------------------------------------------------------
+    int set = 0;
+    for (;;) {
+        Cursor nxt2 = nxt;
+        const bool has_next2 = has_next && advance(nxt2);
+        Step s_nxt[VPR];
+        Tx tx_nxt2[VPR];
+        if (has_next) {
+            if (nxt.m0 != cur.m0)
+                load_geometry(nxt.m0);
+#pragma unroll
+            for (int v = 0; v < VPR; ++v) s_nxt[v] = make_step<IQ>(P, R[v], tx_nxt[v]);
+            if (has_next2)
+                load_tx(nxt2, tx_nxt2);                      // consumed next iteration
+            publish(s_nxt, set ^ 1);
+        }
+        __syncthreads();                                   // windows of the next step are complete
+        Window w_nxt{};
+        if (has_next) {
+            w_nxt = read_window(s_nxt, set ^ 1);
+            if (!w_nxt.overflow)
+                copy_load(nxt, w_nxt);                       // in flight while this step computes
+        }
+        if (tid < 2 * ROW)                                  // the current set is read by everyone by now
+            slots[set * 2 * ROW + tid] = (tid < ROW) ? INT_MAX : INT_MIN;
+
+        if (!w_cur.overflow) {
+#pragma unroll
+            for (int v = 0; v < VPR; ++v) compute_lds(s_cur[v], w_cur.loff[v], part[v]);
+        } else {
+#pragma unroll
+            for (int v = 0; v < VPR; ++v) compute_direct(s_cur[v], cur, part[v]);
+        }
+
+        if (!has_next || nxt.m0 != cur.m0 || nxt.g0 != cur.g0) {
+#pragma unroll
+            for (int v = 0; v < VPR; ++v)
+#pragma unroll
+                for (int i = 0; i < NF; ++i) {
+                    acc[v][i] += part[v][i];
+                    part[v][i] = 0.0f;
+                }
+        }
+        if (!has_next)
+            break;
+        __syncthreads();                                   // everyone is done reading the pair rows
+        if (!w_nxt.overflow)
+            copy_store(w_nxt);
+        __syncthreads();                                   // the next step's rows are in place
+        cur = nxt;
+#pragma unroll
+        for (int v = 0; v < VPR; ++v) {
+            s_cur[v] = s_nxt[v];
+            tx_nxt[v] = tx_nxt2[v];
+        }
+        w_cur = w_nxt;
+        nxt = nxt2;
+        has_next = has_next2;
+        set ^= 1;
+    }
+
+    if (fr_ok) {
+#pragma unroll
+        for (int v = 0; v < VPR; ++v) {
+            if (!vox_ok[v])
+                continue;
+#pragma unroll
+            for (int f = 0; f < FL; ++f) {
+                float *o = out + ((int64_t)(bl + f) * P.N + n[v]) * C;
+#pragma unroll
+                for (int c = 0; c < C; ++c) o[c] = P.accumulate ? o[c] + acc[v][f * C + c] : acc[v][f * C + c];
+            }
+        }
+    }
+}
+
+template <bool IQ, int FL, int LAYOUT, int VPR>
+hipError_t launch(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
+                  const float *tau, const float *w, float *out, hipStream_t stream) {
+    const int64_t row_bytes = (int64_t)kp.B * plan.elem_bytes;
+    const int64_t tap = (LAYOUT == DAS_LAYOUT_KQMB) ? row_bytes * kp.q_count * kp.M : row_bytes;
+    const int tiles = ((kp.nx + TX - 1) / TX) * ((kp.ny + TY - 1) / TY) * ((kp.nz + VPR - 1) / VPR);
+    const int ftiles = (kp.B + ROW * FL - 1) / (ROW * FL);
+    hipLaunchKernelGGL((das_bi_staged_kernel<IQ, FL, LAYOUT, VPR>), dim3(tiles, ftiles), dim3(THREADS), 0,
+                       stream, kp, rf, rx, tau, w, out, (uint32_t)tap);
+    return hipGetLastError();
+}
+
+template <int LAYOUT>
+hipError_t launch_vpr(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
+                      const float *tau, const float *w, float *out, hipStream_t stream) {
+    if (plan.vpr == 1)
+        return launch<false, 2, LAYOUT, 1>(plan, kp, rf, rx, tau, w, out, stream);
+    return launch<false, 2, LAYOUT, 2>(plan, kp, rf, rx, tau, w, out, stream);
+}
+
+}  // namespace
+
+bool das_staged_supported(const das_plan_t &plan) {
+    // fp32 with 2 frames per lane (B a multiple of 32)
+    return plan.p.dtype == DAS_F32 && plan.fl == 2;
+}
+
+hipError_t das_launch_batch_inner_staged(const das_plan_t &plan, const DasKParams &kp, const float *rf,
+                                         const float *rx, const float *tau_tx, const float *w_tx, float *out,
+                                         hipStream_t stream) {
+    return plan.p.layout == DAS_LAYOUT_KQMB
+               ? launch_vpr<DAS_LAYOUT_KQMB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream)
+               : launch_vpr<DAS_LAYOUT_QMKB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream);
+}

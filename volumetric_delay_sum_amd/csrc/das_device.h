@@ -19,6 +19,18 @@ __device__ __forceinline__ void unroll_impl(F &&f, iseq<Is...>) { (f(ic<Is>{}), 
 template <int N, class F>
 __device__ __forceinline__ void unroll(F &&f) { unroll_impl(f, typename make_iseq<N>::type{}); }
 
+// Workgroup b runs on die (XCD) b % 8 of the MI355X's eight.  Hand each die a
+// contiguous range of tiles instead, so that the workgroups sharing a die's
+// L2 work on neighbouring voxels, which read the same sample rows.  A
+// bijection on [0, nblocks): the tail past a multiple of 8 keeps its index.
+__device__ __forceinline__ int xcd_tile(int b, int nblocks) {
+    constexpr int NXCD = 8;
+    const int full = (nblocks / NXCD) * NXCD;
+    if (b >= full)
+        return b;
+    return (b % NXCD) * (full / NXCD) + b / NXCD;
+}
+
 // Voxel centre in fp64: origin + index * pitch.
 __device__ __forceinline__ void voxel_centre(const DasKParams &P, int ix, int iy, int iz,
                                              double &x, double &y, double &z) {
@@ -141,6 +153,33 @@ __device__ __forceinline__ Lerp lerp_coeffs(double s, float w, float pc, float p
 }
 
 // ---------------------------------------------------------------------------
+// Raw buffer loads.  A buffer resource (V#) holds a 48-bit base, a record
+// count in bytes and format bits; loads past the record count return 0
+// instead of touching memory, so the count acts as a hardware bounds check.
+// Addressing is base (SGPRs) + 32-bit lane offset + 12-bit immediate, which
+// keeps 64-bit address arithmetic off the vector ALU.  The LLVM intrinsics
+// are called directly.
+// ---------------------------------------------------------------------------
+typedef int BufRsrc __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ float buffer_load_f32(BufRsrc r, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.load.f32");
+__device__ f32x2 buffer_load_f32x2(BufRsrc r, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.load.v2f32");
+__device__ f32x4 buffer_load_f32x4(BufRsrc r, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.load.v4f32");
+
+// Resource over [base, base + bytes) (bytes clamped to 2^32 - 1), stride 0.
+__device__ __forceinline__ BufRsrc make_rsrc(const char *base, uint64_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    BufRsrc r;
+    r.x = (int)(uint32_t)a;
+    r.y = (int)((uint32_t)(a >> 32) & 0xffffu);
+    r.z = (int)(bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes);
+    r.w = 0x00020000;   // gfx9 family: 32-bit data format, raw access
+    return r;
+}
+
+// ---------------------------------------------------------------------------
 // Row broadcast on wave64: DPP row_newbcast:J hands lane J of each 16-lane row
 // to every lane of that row (gfx90a and later).
 // ---------------------------------------------------------------------------
@@ -149,20 +188,34 @@ __device__ __forceinline__ uint32_t row_bcast(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x150 + J, 0xF, 0xF, true);
 }
 
-// acc += coef[lane J of the row] * x, as one v_fmac_f32_dpp.  The compiler
-// does not fold a DPP move into v_fmac (tied accumulator), so this is written
-// out.  Every coefficient read this way must have been written by a VALU op
-// at least two wait states earlier: see settle().
+// acc += a[lane J of the row] * x0 + b[lane J of the row] * x1, as two
+// v_fmac_f32_dpp with row_newbcast:J.  The compiler does not fold a DPP move
+// into v_fmac (tied accumulator), so this is written out; one asm block per
+// receiver step keeps the two FMAs together.  Every coefficient read this way
+// must have been written by a VALU op at least two wait states earlier: see
+// settle().
 template <int J>
-__device__ __forceinline__ void fmac_bcast(float &acc, float coef, float x) {
-    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-        : "+v"(acc) : "v"(coef), "v"(x), "n"(J));
+__device__ __forceinline__ void lerp_bcast(float &acc, float a, float b, float x0, float x1) {
+    asm("v_fmac_f32_dpp %0, %1, %3 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %2, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc) : "v"(a), "v"(b), "v"(x0), "v"(x1), "n"(J));
 }
-// acc -= coef[lane J of the row] * x
+
+// Complex version: (re, im) += (a + j ai)(x0r + j x0i) + (b + j bi)(x1r + j x1i),
+// coefficients from lane J of the row.
 template <int J>
-__device__ __forceinline__ void fnmac_bcast(float &acc, float coef, float x) {
-    asm("v_fmac_f32_dpp %0, -%1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-        : "+v"(acc) : "v"(coef), "v"(x), "n"(J));
+__device__ __forceinline__ void cmac_bcast(float &re, float &im, float a, float ai, float b, float bi,
+                                           float x0r, float x0i, float x1r, float x1i) {
+    asm("v_fmac_f32_dpp %0, %2, %6 row_newbcast:%10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %2, %7 row_newbcast:%10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, -%3, %7 row_newbcast:%10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %3, %6 row_newbcast:%10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, %4, %8 row_newbcast:%10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %4, %9 row_newbcast:%10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %0, -%5, %9 row_newbcast:%10 row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %5, %8 row_newbcast:%10 row_mask:0xf bank_mask:0xf"
+        : "+v"(re), "+v"(im)
+        : "v"(a), "v"(ai), "v"(b), "v"(bi), "v"(x0r), "v"(x0i), "v"(x1r), "v"(x1i), "n"(J));
 }
 
 // Two wait states after the last VALU write of the given registers, so that

@@ -21,6 +21,7 @@ struct DasKParams {
     int32_t nx, ny, nz, N;
     int32_t B, Q, M, K;
     int32_t q_begin, q_count; // transmit events of this launch (absolute q)
+    int32_t q_group;          // batch-inner: transmit events per receiver sweep
     int32_t accumulate;       // 0 overwrite, 1 add
 };
 
@@ -31,6 +32,9 @@ struct das_plan {
     int32_t elem_bytes;       // 4 or 8
     int32_t fl;               // batch-inner: frames per lane
     int32_t bt;               // baseline: frames per lane
+    int32_t q_group;          // batch-inner: transmit events per receiver sweep
+    int32_t staged;           // batch-inner: 1 = LDS-staged kernel, 0 = direct loads
+    int32_t vpr;              // staged kernel: voxels per DPP row (depth of the 8 x 8 x vpr tile)
 };
 
 // Launchers (defined next to their kernels).  They assume validated input.
@@ -39,6 +43,10 @@ hipError_t das_launch_permute(const das_plan_t &plan, const void *rf, void *out,
 hipError_t das_launch_baseline(const das_plan_t &plan, const DasKParams &kp, const float *rf,
                                const float *rx, const float *tau_tx, const float *w_tx,
                                float *out, hipStream_t stream);
+bool das_staged_supported(const das_plan_t &plan);
+hipError_t das_launch_batch_inner_staged(const das_plan_t &plan, const DasKParams &kp, const float *rf,
+                                         const float *rx, const float *tau_tx, const float *w_tx, float *out,
+                                         hipStream_t stream);
 hipError_t das_launch_batch_inner(const das_plan_t &plan, const DasKParams &kp, const float *rf,
                                   const float *rx, const float *tau_tx, const float *w_tx,
                                   float *out, hipStream_t stream);
