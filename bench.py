@@ -148,7 +148,8 @@ def main():
     perm_avg = float(np.mean(perm_ms))
     flops_per_acc = 8 if cfg.iq else 4          # 2 FMA (real) or 8 FMA (complex) per accumulation
     achieved = accs * flops_per_acc / (kern_avg * 1e-3) / 1e12
-    kernel_name = "das_batch_inner_kernel" if bi else "das_baseline_kernel"
+    kernel_name = ("das_bi_staged_kernel" if plan.info["staged"] else "das_batch_inner_kernel") if bi \
+        else "das_baseline_kernel"
     traffic = stored_traffic(kernel_name, cfg.name)
 
     cpu = None

@@ -57,16 +57,20 @@ int32_t pick_fl(int32_t B, int32_t dtype) {
     return 1;
 }
 
-// Transmit events per receiver sweep of the batch-inner kernel: enough to
-// amortize the receive geometry, few enough that the frame rows a die touches
-// at once stay in its 4 MB L2.  DAS_Q_GROUP overrides (tuning sweeps).
-int32_t pick_q_group(const das_problem &p, int32_t elem) {
+// Transmit events per receiver sweep of the batch-inner kernels.  The direct
+// kernel reads every row through L2, so it keeps the rows a die touches at
+// once within its 4 MB (a few events); the LDS-staged kernel fetches each
+// row once per tile and instead amortizes the receive geometry over all
+// events.  DAS_Q_GROUP overrides (tuning sweeps).
+int32_t pick_q_group(const das_problem &p, int32_t elem, bool staged) {
     const char *env = std::getenv("DAS_Q_GROUP");
     if (env) {
         const int v = std::atoi(env);
         if (v >= 1)
             return v;
     }
+    if (staged)
+        return p.Q;
     const int64_t row = (int64_t)p.B * elem;
     return row <= 128 ? 3 : (row <= 256 ? 2 : 1);
 }
@@ -196,12 +200,12 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
     pl->elem_bytes = elem;
     pl->fl = pick_fl(p.B, p.dtype);
     pl->bt = 8;
-    pl->q_group = pick_q_group(p, elem);
     // LDS-staged batch-inner kernel where it is built; DAS_BI_KERNEL=direct
     // selects the direct-load kernel (comparisons).
     const char *kv = std::getenv("DAS_BI_KERNEL");
     pl->staged = (pl->alg == DAS_ALG_BATCH_INNER && das_staged_supported(*pl) &&
                   !(kv && std::strcmp(kv, "direct") == 0)) ? 1 : 0;
+    pl->q_group = pick_q_group(p, elem, pl->staged != 0);
     const char *vv = std::getenv("DAS_STAGED_VPR");
     pl->vpr = (vv && std::atoi(vv) == 1) ? 1 : 2;
     *out = pl;
