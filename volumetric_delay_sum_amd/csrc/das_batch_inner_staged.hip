@@ -60,7 +60,7 @@ struct Geo {
     static constexpr int RPR = 64 / LPR;                 // sample rows per copy round of a wave
     static constexpr int MAXR = (W_MAX + 1 + RPR - 1) / RPR;
     static constexpr int PAIR_BYTES = ROW * WP * PAIR;
-    static constexpr int LDS_BYTES = PAIR_BYTES + 4 * ROW * 4;
+    static constexpr int LDS_BYTES = PAIR_BYTES + 3 * 2 * ROW * 4;
     static_assert(ROWB % 16 == 0, "copy granularity");
 };
 
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     constexpr int C = G::C, E = G::E, NF = G::NF;
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
     char *pairs = lds;
-    int *slots = reinterpret_cast<int *>(lds + G::PAIR_BYTES);   // [2 sets][min, max][16]
+    int *slots = reinterpret_cast<int *>(lds + G::PAIR_BYTES);   // [3 sets][min, max][16]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     // zero the pair rows (so a zero weight never meets a non-finite stale value) and the window slots
     for (int i = tid * 16; i < G::PAIR_BYTES; i += THREADS * 16)
         *reinterpret_cast<int4 *>(pairs + i) = make_int4(0, 0, 0, 0);
-    if (tid < 2 * 2 * ROW)
+    if (tid < 3 * 2 * ROW)
         slots[tid] = ((tid / ROW) & 1) ? INT_MIN : INT_MAX;
     __syncthreads();
 
@@ -322,6 +322,8 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             das::settle(a, b);
         das::unroll<ROW>([&](auto J) {
             constexpr int j = decltype(J)::value;
+            if constexpr (j == ROW / 2)
+                __builtin_amdgcn_sched_barrier(0);   // at most half the receivers' reads in flight
             const uint32_t addr = das::row_bcast<j>(loff) + laneoff_l;
             float x[2 * NF];
 #pragma unroll
@@ -380,22 +382,32 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         });
     };
 
-    // ---- prologue: first step --------------------------------------------
+    // ---- prologue: windows of steps 0 and 1, pair rows of step 0 ----------
+    // Slot set of step i is i % 3: the window of step i + 2 is published while
+    // step i computes, read after the barriers that end step i.
     Cursor cur{0, 0, 0, min(P.q_group, P.q_count)};
     load_geometry(cur.m0);
-    Step s_cur[VPR];
-    {
-        Tx tx0[VPR];
-        load_tx(cur, tx0);
+    Step s_cur[VPR], s_nxt[VPR];
+    Tx tx_a[VPR], tx_b[VPR];
+    load_tx(cur, tx_a);
 #pragma unroll
-        for (int v = 0; v < VPR; ++v) s_cur[v] = make_step<IQ>(P, R[v], tx0[v]);
-    }
+    for (int v = 0; v < VPR; ++v) s_cur[v] = make_step<IQ>(P, R[v], tx_a[v]);
     publish(s_cur, 0);
     Cursor nxt = cur;
     bool has_next = advance(nxt);
-    Tx tx_nxt[VPR];
-    if (has_next)
-        load_tx(nxt, tx_nxt);
+    Cursor nxt2 = nxt;
+    bool has_next2 = has_next && advance(nxt2);
+    if (has_next) {
+        if (nxt.m0 != cur.m0)
+            load_geometry(nxt.m0);
+        load_tx(nxt, tx_b);
+#pragma unroll
+        for (int v = 0; v < VPR; ++v) s_nxt[v] = make_step<IQ>(P, R[v], tx_b[v]);
+        publish(s_nxt, 1);
+    }
+    Tx tx_nxt2[VPR];                                   // tables of step i + 2, read a step ahead
+    if (has_next2)
+        load_tx(nxt2, tx_nxt2);
     __syncthreads();
     Window w_cur = read_window(s_cur, 0);
     if (!w_cur.overflow) {
@@ -405,30 +417,16 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     __syncthreads();
 
     // ---- main loop ---------------------------------------------------------
-    int set = 0;
+    int set = 0;                                       // slot set of the current step
     for (;;) {
-        Cursor nxt2 = nxt;
-        const bool has_next2 = has_next && advance(nxt2);
-        Step s_nxt[VPR];
-        Tx tx_nxt2[VPR];
-        if (has_next) {
-            if (nxt.m0 != cur.m0)
-                load_geometry(nxt.m0);
-#pragma unroll
-            for (int v = 0; v < VPR; ++v) s_nxt[v] = make_step<IQ>(P, R[v], tx_nxt[v]);
-            if (has_next2)
-                load_tx(nxt2, tx_nxt2);                      // consumed next iteration
-            publish(s_nxt, set ^ 1);
-        }
-        __syncthreads();                                   // windows of the next step are complete
+        const int set1 = (set == 2) ? 0 : set + 1, set2 = (set1 == 2) ? 0 : set1 + 1;
+        // pair rows of the next step: in flight while this step computes
         Window w_nxt{};
         if (has_next) {
-            w_nxt = read_window(s_nxt, set ^ 1);
+            w_nxt = read_window(s_nxt, set1);
             if (!w_nxt.overflow)
-                copy_load(nxt, w_nxt);                       // in flight while this step computes
+                copy_load(nxt, w_nxt);
         }
-        if (tid < 2 * ROW)                                  // the current set is read by everyone by now
-            slots[set * 2 * ROW + tid] = (tid < ROW) ? INT_MAX : INT_MIN;
 
         if (!w_cur.overflow) {
 #pragma unroll
@@ -437,6 +435,23 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
 #pragma unroll
             for (int v = 0; v < VPR; ++v) compute_direct(s_cur[v], cur, part[v]);
         }
+
+        // the step after next: geometry, sample split, window
+        Cursor nxt3 = nxt2;
+        const bool has_next3 = has_next2 && advance(nxt3);
+        Step s_nxt2[VPR];
+        Tx tx_nxt3[VPR];
+        if (has_next2) {
+            if (nxt2.m0 != nxt.m0)
+                load_geometry(nxt2.m0);
+#pragma unroll
+            for (int v = 0; v < VPR; ++v) s_nxt2[v] = make_step<IQ>(P, R[v], tx_nxt2[v]);
+            if (has_next3)
+                load_tx(nxt3, tx_nxt3);                      // consumed next iteration
+            publish(s_nxt2, set2);
+        }
+        if (tid < 2 * ROW)                                  // this step's window was read last step
+            slots[set * 2 * ROW + tid] = (tid < ROW) ? INT_MAX : INT_MIN;
 
         if (!has_next || nxt.m0 != cur.m0 || nxt.g0 != cur.g0) {
 #pragma unroll
@@ -449,20 +464,23 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         }
         if (!has_next)
             break;
-        __syncthreads();                                   // everyone is done reading the pair rows
+        __syncthreads();                                   // pair rows read; the step-after-next window published
         if (!w_nxt.overflow)
             copy_store(w_nxt);
         __syncthreads();                                   // the next step's rows are in place
         cur = nxt;
+        nxt = nxt2;
+        nxt2 = nxt3;
+        has_next = has_next2;
+        has_next2 = has_next3;
 #pragma unroll
         for (int v = 0; v < VPR; ++v) {
             s_cur[v] = s_nxt[v];
-            tx_nxt[v] = tx_nxt2[v];
+            s_nxt[v] = s_nxt2[v];
+            tx_nxt2[v] = tx_nxt3[v];
         }
         w_cur = w_nxt;
-        nxt = nxt2;
-        has_next = has_next2;
-        set ^= 1;
+        set = set1;
     }
 
     if (fr_ok) {
