@@ -79,26 +79,38 @@ struct Tx {
     float tau, w;
 };
 
+// Sample split of one (voxel, event, receiver): s = (tau_tx - t0) fs + d fs / c
+// in fp64, the receive part (already less t0 fs) from the geometry.  A term
+// counts iff 0 <= floor(s) <= K - 2; a term that does not gets weight 0 and
+// k = 0, so its reads stay inside the window.
 template <bool IQ>
 __device__ __forceinline__ Step make_step(const DasKParams &P, const das::RxTerm &R, Tx tx) {
-    const das::TxTerm T = das::tx_term<IQ>(P, tx.tau, tx.w);
-    float pc = 1.0f, ps = 0.0f;
-    if constexpr (IQ) {
-        pc = T.pc * R.pc - T.ps * R.ps;
-        ps = T.ps * R.pc + T.pc * R.ps;
-    }
-    const double s = T.s_tx + R.s_rx;
-    const float w = T.w * R.w;
-    const das::Lerp L = das::lerp_coeffs<IQ>(s, w, pc, ps, P.K);
-    Step st;
-    st.k = L.k;
-    st.a = L.a;
-    st.b = L.b;
-    st.ai = L.ai;
-    st.bi = L.bi;
-    // the term counts (k in range) and carries weight
+    const double s = __builtin_fma((double)tx.tau, P.fs, R.s_rx);
     const double kf = __builtin_floor(s);
-    st.active = (kf >= 0.0) && (kf <= (double)(P.K - 2)) && (w != 0.0f);
+    const bool valid = (kf >= 0.0) && (kf <= (double)(P.K - 2));
+    const float f = (float)(s - kf);
+    const float w = valid ? tx.w * R.w : 0.0f;
+    Step st;
+    st.k = valid ? (uint32_t)(int32_t)kf : 0u;
+    st.active = w != 0.0f;
+    const float bw = w * f, aw = w - bw;
+    if constexpr (IQ) {
+        // phase exp(+j 2 pi f0 (tau_tx + d / c)): event part times receive part
+        double cyc = (double)tx.tau * P.f0;
+        cyc -= __builtin_floor(cyc);
+        float sn, cs;
+        sincospif(2.0f * (float)cyc, &sn, &cs);
+        const float pc = cs * R.pc - sn * R.ps, ps = sn * R.pc + cs * R.ps;
+        st.a = aw * pc;
+        st.ai = aw * ps;
+        st.b = bw * pc;
+        st.bi = bw * ps;
+    } else {
+        st.a = aw;
+        st.b = bw;
+        st.ai = 0.0f;
+        st.bi = 0.0f;
+    }
     return st;
 }
 
@@ -171,18 +183,19 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             double vx, vy, vz;
             das::voxel_centre(P, ix, iy, min(tz * VPR + v, P.nz - 1), vx, vy, vz);
             R[v] = das::rx_term<IQ>(P, vx, vy, vz, px, py, pz);
+            R[v].s_rx -= P.t0fs;
             R[v].w = (mm < P.M) ? R[v].w : 0.0f;
         }
     };
     // Transmit tables of the voxels, read a step ahead through buffer loads
     // (base per event, lane offset n).
+    const das::BufRsrc rs_tau = das::make_rsrc(reinterpret_cast<const char *>(tau_tx), (uint64_t)P.Q * P.N * 4);
+    const das::BufRsrc rs_wtx = das::make_rsrc(reinterpret_cast<const char *>(w_tx), (uint64_t)P.Q * P.N * 4);
     auto load_tx = [&](const Cursor &c, Tx (&tx)[VPR]) {
-        const int64_t q = P.q_begin + c.ql;
-        const das::BufRsrc rt = das::make_rsrc(reinterpret_cast<const char *>(tau_tx + q * P.N), (uint64_t)P.N * 4);
-        const das::BufRsrc rw = das::make_rsrc(reinterpret_cast<const char *>(w_tx + q * P.N), (uint64_t)P.N * 4);
+        const uint32_t qoff = (uint32_t)(P.q_begin + c.ql) * (uint32_t)P.N * 4u;   // the launch keeps Q N 4 < 2^32
 #pragma unroll
         for (int v = 0; v < VPR; ++v)
-            tx[v] = Tx{das::buffer_load_f32(rt, n[v] * 4, 0, 0), das::buffer_load_f32(rw, n[v] * 4, 0, 0)};
+            tx[v] = Tx{das::buffer_load_f32(rs_tau, n[v] * 4, (int)qoff, 0), das::buffer_load_f32(rs_wtx, n[v] * 4, (int)qoff, 0)};
     };
     // Publish the lanes' k to the window of their receiver: min/max over the
     // row's voxels and the wave's four rows (gfx950 row swaps: lanes l and
@@ -232,74 +245,90 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         int kmin_w, rows_w;    // wave's copy: first sample row, number of sample rows
         bool overflow;
     };
-    auto read_window = [&](const Step (&s)[VPR], int set) -> Window {
+    struct Slots {
+        int kmn, kmx, kmn_w, kmx_w;
+    };
+    auto read_slots = [&](int set) -> Slots {
+        return Slots{slots[set * 2 * ROW + li], slots[set * 2 * ROW + ROW + li], slots[set * 2 * ROW + wave],
+                     slots[set * 2 * ROW + ROW + wave]};
+    };
+    auto make_window = [&](const Step (&s)[VPR], const Slots &sl) -> Window {
         Window wdw;
-        const int kmn = slots[set * 2 * ROW + li], kmx = slots[set * 2 * ROW + ROW + li];
-        const int np = (kmn <= kmx) ? kmx - kmn + 1 : 0;           // pair rows of receiver li
+        const int np = (sl.kmn <= sl.kmx) ? sl.kmx - sl.kmn + 1 : 0;     // pair rows of receiver li
         const uint32_t base = (uint32_t)(li * G::WP + 1) * G::PAIR;
 #pragma unroll
         for (int v = 0; v < VPR; ++v)
-            wdw.loff[v] = s[v].active ? base + (uint32_t)((int)s[v].k - kmn) * G::PAIR : base;
+            wdw.loff[v] = s[v].active ? base + (uint32_t)((int)s[v].k - sl.kmn) * G::PAIR : base;
         wdw.overflow = __any(np > G::W_MAX);
-        const int kmn_w = slots[set * 2 * ROW + wave], kmx_w = slots[set * 2 * ROW + ROW + wave];
-        wdw.kmin_w = kmn_w;
-        wdw.rows_w = (kmn_w <= kmx_w) ? kmx_w - kmn_w + 2 : 0;     // sample rows kmin .. kmax + 1
+        wdw.kmin_w = sl.kmn_w;
+        wdw.rows_w = (sl.kmn_w <= sl.kmx_w) ? sl.kmx_w - sl.kmn_w + 2 : 0;   // sample rows kmin .. kmax + 1
         return wdw;
     };
+    auto read_window = [&](const Step (&s)[VPR], int set) -> Window { return make_window(s, read_slots(set)); };
 
-    // Copy of one receiver's sample rows (wave w copies receiver m0 + w).  All
-    // rounds are issued back to back; rows past the window repeat its last row
-    // (loaded, never stored).  The base address is wave-uniform and the lane
-    // offsets are fixed, so the loads need little vector address arithmetic.
+    // Copy of one receiver's sample rows (wave w copies receiver m0 + w), in
+    // rounds of RPR rows: lane (rho, c) loads 16 bytes (frames 4c .. 4c + 3 of
+    // the frame tile) of sample row kmin + RPR r + rho.  The number of rounds is
+    // wave-uniform; rows past the window are loaded (inside the buffer, or zero
+    // past its end) but never stored.  The base address is wave-uniform and the
+    // lane offsets fixed, so the loads need little vector address arithmetic.
+    static_assert(G::HALF == 8 && G::LPR == 8, "copy layout assumes 2 fp32 frames per reader lane");
     int4 pf[G::MAXR];
-    const int crow = lane / G::LPR;                  // sample row within a copy round
-    const uint32_t cbyte = (uint32_t)(lane % G::LPR) * 16;   // byte offset within the frame-tile row
+    const int crow = lane / G::LPR;                  // rho: sample row within a copy round
+    const int cchunk = lane % G::LPR;                // c: 16-byte chunk of the frame-tile row
+    const uint32_t cbyte = (uint32_t)cchunk * 16;
     const int64_t kstride = (LAYOUT == DAS_LAYOUT_KQMB) ? (int64_t)P.q_count * P.M * rowfull : rowfull;
+    const uint32_t kstride32 = (uint32_t)kstride;
+    const uint32_t coff = (uint32_t)crow * kstride32 + cbyte;
+    auto copy_rounds = [&](const Window &wdw) { return __builtin_amdgcn_readfirstlane((wdw.rows_w + G::RPR - 1) / G::RPR); };
+    // The launch keeps the chunk under 4 GiB, so offsets in it are 32-bit.
+    const das::BufRsrc rs_chunk = das::make_rsrc(rf_bytes, (uint64_t)chunk_bytes);
+    const uint32_t mstride32 = (uint32_t)m_stride;
+    const uint32_t b0off = (uint32_t)b0 * E;
     auto copy_load = [&](const Cursor &c, const Window &wdw) {
-        if (wdw.rows_w == 0)
-            return;
-        const int m = c.m0 + wave;
-        const int64_t qm = (LAYOUT == DAS_LAYOUT_KQMB) ? ((int64_t)c.ql * P.M + m) * rowfull
-                                                       : ((int64_t)c.ql * P.M + m) * (int64_t)P.K * rowfull;
-        const int kmin = __builtin_amdgcn_readfirstlane(wdw.kmin_w);
-        const int64_t start = qm + (int64_t)b0 * E + (int64_t)kmin * kstride;
-        const das::BufRsrc rs = das::make_rsrc(rf_bytes + start, (uint64_t)(chunk_bytes - start));
-        const int last = __builtin_amdgcn_readfirstlane(wdw.rows_w) - 1;
+        const int nr = copy_rounds(wdw);
+        const uint32_t kmin = (uint32_t)__builtin_amdgcn_readfirstlane(wdw.kmin_w);
+        const uint32_t start = ((uint32_t)c.ql * (uint32_t)P.M + (uint32_t)(c.m0 + wave)) * mstride32 + b0off + kmin * kstride32;
 #pragma unroll
         for (int r = 0; r < G::MAXR; ++r) {
-            const int rr = min(r * G::RPR + crow, last);
-            const das::f32x4 v = das::buffer_load_f32x4(rs, (int)((uint32_t)rr * (uint32_t)kstride + cbyte), 0, 0);
-            pf[r] = __builtin_bit_cast(int4, v);
+            if (r < nr) {
+                // lane part in the vector offset, window and round in the scalar offset
+                const das::f32x4 v = das::buffer_load_f32x4(rs_chunk, (int)coff, (int)(start + (uint32_t)(r * G::RPR) * kstride32), 0);
+                pf[r] = __builtin_bit_cast(int4, v);
+            }
         }
     };
+    // Sample row kmin + rr feeds pair row rr (first tap) and pair row rr - 1
+    // (second tap); a lane's frames 4c, 4c + 1 go to reader lane 2c and frames
+    // 4c + 2, 4c + 3 to reader lane 2c + 1.  That is four 8-byte targets per
+    // lane, all within one 32-byte stretch of a 256-byte pair row, so lanes of
+    // the same c share banks.  Store instruction i sends the lane of row rho to
+    // target (i + rho) mod 4: every instruction then spreads its 64 lanes over
+    // all 64 banks (two dwords per bank, the minimum for 512 bytes).  The
+    // targets are fixed per lane; a round adds RPR pair rows as an immediate.
+    uint32_t waddr[4];
+    {
+        const uint32_t base = (uint32_t)(wave * G::WP + 1) * G::PAIR + (uint32_t)crow * G::PAIR + (uint32_t)cchunk * 2 * G::LB;
+        const uint32_t tgt[4] = {base, base + G::LB, base - G::PAIR + G::HALF, base - G::PAIR + G::LB + G::HALF};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = (i + crow) & 3;
+            waddr[i] = t == 0 ? tgt[0] : t == 1 ? tgt[1] : t == 2 ? tgt[2] : tgt[3];
+        }
+    }
+    const bool row_even = (crow & 1) == 0;
     auto copy_store = [&](const Window &wdw) {
-        char *dst = pairs + (uint32_t)(wave * G::WP) * G::PAIR;
+        const int nr = copy_rounds(wdw);
 #pragma unroll
         for (int r = 0; r < G::MAXR; ++r) {
-            const int rr = r * G::RPR + crow;        // sample row kmin + rr feeds pair rows rr (first) and rr - 1 (second)
-            if (r * G::RPR < wdw.rows_w && rr < wdw.rows_w) {
-                const char *v = reinterpret_cast<const char *>(&pf[r]);
-                constexpr int U = G::HALF < 16 ? G::HALF : 16;
-#pragma unroll
-                for (int u = 0; u < 16 / U; ++u) {
-                    const uint32_t o = cbyte + u * U;             // byte within the frame-tile row
-                    const uint32_t cidx = o / G::HALF, sub = o % G::HALF;
-                    char *first = dst + (uint32_t)(rr + 1) * G::PAIR + cidx * G::LB + sub;
-                    char *second = dst + (uint32_t)rr * G::PAIR + cidx * G::LB + G::HALF + sub;
-                    if constexpr (U == 4) {
-                        const int x = *reinterpret_cast<const int *>(v + u * U);
-                        *reinterpret_cast<int *>(first) = x;
-                        *reinterpret_cast<int *>(second) = x;
-                    } else if constexpr (U == 8) {
-                        const int2 x = *reinterpret_cast<const int2 *>(v + u * U);
-                        *reinterpret_cast<int2 *>(first) = x;
-                        *reinterpret_cast<int2 *>(second) = x;
-                    } else {
-                        const int4 x = *reinterpret_cast<const int4 *>(v + u * U);
-                        *reinterpret_cast<int4 *>(first) = x;
-                        *reinterpret_cast<int4 *>(second) = x;
-                    }
-                }
+            if (r < nr && r * G::RPR + crow < wdw.rows_w) {
+                const int2 lo = make_int2(pf[r].x, pf[r].y), hi = make_int2(pf[r].z, pf[r].w);
+                const int2 a = row_even ? lo : hi, b = row_even ? hi : lo;
+                const uint32_t RO = (uint32_t)(r * G::RPR * G::PAIR);
+                *reinterpret_cast<int2 *>(pairs + waddr[0] + RO) = a;
+                *reinterpret_cast<int2 *>(pairs + waddr[1] + RO) = b;
+                *reinterpret_cast<int2 *>(pairs + waddr[2] + RO) = a;
+                *reinterpret_cast<int2 *>(pairs + waddr[3] + RO) = b;
             }
         }
     };
@@ -313,38 +342,61 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             part[v][i] = 0.0f;
         }
 
-    // One voxel of one step from LDS.
-    auto compute_lds = [&](const Step &s, uint32_t loff, float (&pt)[NF]) {
-        float a = s.a, b = s.b, ai = s.ai, bi = s.bi;
-        if constexpr (IQ)
-            das::settle(a, b, ai, bi);
-        else
-            das::settle(a, b);
-        das::unroll<ROW>([&](auto J) {
-            constexpr int j = decltype(J)::value;
-            if constexpr (j == ROW / 2)
-                __builtin_amdgcn_sched_barrier(0);   // at most half the receivers' reads in flight
-            const uint32_t addr = das::row_bcast<j>(loff) + laneoff_l;
+    // All voxels of one step from LDS: VPR x 16 (voxel, receiver) items, each
+    // one LDS read of the pair row (2 NF floats) and 2 FL (IQ: 8 FL) FMAs with
+    // the receiver's coefficients broadcast from its lane.  The reads are issued
+    // DEPTH items ahead; the scheduling fences keep the compiler from sinking
+    // each read next to its use, which would leave one read in flight per wave.
+    constexpr int NITEM = VPR * ROW;
+    constexpr int DEPTH = (VPR == 1) ? 8 : 6;
+    constexpr int NV4 = (2 * NF) / 4;              // 16-byte reads per item
+    auto compute_lds = [&](const Step (&s)[VPR], const uint32_t (&loff)[VPR], float (&pt)[VPR][NF]) {
+        float a[VPR], b[VPR], ai[VPR], bi[VPR];
+#pragma unroll
+        for (int v = 0; v < VPR; ++v) {
+            a[v] = s[v].a;
+            b[v] = s[v].b;
+            ai[v] = s[v].ai;
+            bi[v] = s[v].bi;
+            if constexpr (IQ)
+                das::settle(a[v], b[v], ai[v], bi[v]);
+            else
+                das::settle(a[v], b[v]);
+        }
+        das::f32x4 ring[DEPTH][NV4];
+        auto issue = [&](auto T) {
+            constexpr int t = decltype(T)::value;
+            constexpr int v = t / ROW, j = t % ROW;
+            const uint32_t addr = das::row_bcast<j>(loff[v]) + laneoff_l;
+#pragma unroll
+            for (int u = 0; u < NV4; ++u)
+                ring[t % DEPTH][u] = *reinterpret_cast<const das::f32x4 *>(pairs + addr + 16 * u);
+        };
+        das::unroll<DEPTH>([&](auto T) { issue(T); });
+        __builtin_amdgcn_sched_barrier(0);
+        das::unroll<NITEM>([&](auto T) {
+            constexpr int t = decltype(T)::value;
+            constexpr int v = t / ROW, j = t % ROW;
             float x[2 * NF];
 #pragma unroll
-            for (int i = 0; i < 2 * NF; i += 4) {
-                const das::f32x4 v = *reinterpret_cast<const das::f32x4 *>(pairs + addr + 4 * i);
-                x[i] = v.x;
-                x[i + 1] = v.y;
-                if constexpr (2 * NF > 2) {
-                    x[i + 2] = v.z;
-                    x[i + 3] = v.w;
-                }
+            for (int u = 0; u < NV4; ++u) {
+                x[4 * u] = ring[t % DEPTH][u].x;
+                x[4 * u + 1] = ring[t % DEPTH][u].y;
+                x[4 * u + 2] = ring[t % DEPTH][u].z;
+                x[4 * u + 3] = ring[t % DEPTH][u].w;
             }
             if constexpr (IQ) {
 #pragma unroll
                 for (int f = 0; f < FL; ++f)
-                    das::cmac_bcast<j>(pt[2 * f], pt[2 * f + 1], a, ai, b, bi, x[2 * f], x[2 * f + 1],
-                                       x[NF + 2 * f], x[NF + 2 * f + 1]);
+                    das::cmac_bcast<j>(pt[v][2 * f], pt[v][2 * f + 1], a[v], ai[v], b[v], bi[v], x[2 * f],
+                                       x[2 * f + 1], x[NF + 2 * f], x[NF + 2 * f + 1]);
             } else {
 #pragma unroll
-                for (int f = 0; f < FL; ++f) das::lerp_bcast<j>(pt[f], a, b, x[f], x[NF + f]);
+                for (int f = 0; f < FL; ++f) das::lerp_bcast<j>(pt[v][f], a[v], b[v], x[f], x[NF + f]);
             }
+            if constexpr (t + DEPTH < NITEM)
+                issue(das::ic<t + DEPTH>{});
+            __builtin_amdgcn_sched_barrier(0);
         });
     };
     // One voxel of one step by direct loads from the permuted buffer (windows too wide for LDS).
@@ -383,8 +435,8 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     };
 
     // ---- prologue: windows of steps 0 and 1, pair rows of step 0 ----------
-    // Slot set of step i is i % 3: the window of step i + 2 is published while
-    // step i computes, read after the barriers that end step i.
+    // Slot set of step i is i % 3: the window of step i + 2 is published
+    // between the two barriers that end step i and read after them.
     Cursor cur{0, 0, 0, min(P.q_group, P.q_count)};
     load_geometry(cur.m0);
     Step s_cur[VPR], s_nxt[VPR];
@@ -428,28 +480,34 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
                 copy_load(nxt, w_nxt);
         }
 
-        if (!w_cur.overflow) {
-#pragma unroll
-            for (int v = 0; v < VPR; ++v) compute_lds(s_cur[v], w_cur.loff[v], part[v]);
-        } else {
-#pragma unroll
-            for (int v = 0; v < VPR; ++v) compute_direct(s_cur[v], cur, part[v]);
-        }
-
         // the step after next: geometry, sample split, window
         Cursor nxt3 = nxt2;
         const bool has_next3 = has_next2 && advance(nxt3);
         Step s_nxt2[VPR];
         Tx tx_nxt3[VPR];
-        if (has_next2) {
-            if (nxt2.m0 != nxt.m0)
-                load_geometry(nxt2.m0);
+        auto setup_split = [&] {
+            if (has_next2) {
+                if (nxt2.m0 != nxt.m0)
+                    load_geometry(nxt2.m0);
 #pragma unroll
-            for (int v = 0; v < VPR; ++v) s_nxt2[v] = make_step<IQ>(P, R[v], tx_nxt2[v]);
-            if (has_next3)
-                load_tx(nxt3, tx_nxt3);                      // consumed next iteration
-            publish(s_nxt2, set2);
-        }
+                for (int v = 0; v < VPR; ++v) s_nxt2[v] = make_step<IQ>(P, R[v], tx_nxt2[v]);
+                if (has_next3)
+                    load_tx(nxt3, tx_nxt3);                  // consumed next iteration
+            }
+        };
+        auto setup_publish = [&] {
+            if (has_next2)
+                publish(s_nxt2, set2);
+        };
+        auto compute = [&] {
+            if (!w_cur.overflow) {
+                compute_lds(s_cur, w_cur.loff, part);
+            } else {
+#pragma unroll
+                for (int v = 0; v < VPR; ++v) compute_direct(s_cur[v], cur, part[v]);
+            }
+        };
+        compute();
         if (tid < 2 * ROW)                                  // this step's window was read last step
             slots[set * 2 * ROW + tid] = (tid < ROW) ? INT_MAX : INT_MIN;
 
@@ -464,10 +522,14 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         }
         if (!has_next)
             break;
-        __syncthreads();                                   // pair rows read; the step-after-next window published
+        __syncthreads();                                   // pair rows of this step read
+        // The step after next is set up (ALU work) before the next step's rows
+        // are stored, which gives their loads more time to land.
+        setup_split();
         if (!w_nxt.overflow)
             copy_store(w_nxt);
-        __syncthreads();                                   // the next step's rows are in place
+        setup_publish();
+        __syncthreads();                                   // next step's rows in place, the window after it published
         cur = nxt;
         nxt = nxt2;
         nxt2 = nxt3;
