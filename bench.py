@@ -58,11 +58,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="main", help="workload: tiny, mid, main, main-c64")
+    ap.add_argument("--config", default="main", help="workload: tiny, mid, main, main-c64, large")
     ap.add_argument("--layout", default="kqmb", choices=["kqmb", "qmkb"])
     ap.add_argument("--algorithm", default="batch_inner", choices=["batch_inner", "baseline"])
     ap.add_argument("--q-chunk", type=int, default=0,
                     help="transmit events per permute/beamform pair (0: as many as the plan allows)")
+    ap.add_argument("--streamed", action="store_true",
+                    help="time das_beamform_streamed: each chunk's permute overlapped with the previous "
+                         "chunk's beamform on a second stream (the kernel times still come from the "
+                         "event-timed chunked pass)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-voxels", type=int, default=0, help="oracle sample size (0: one depth slab)")
     args = ap.parse_args()
@@ -140,6 +144,29 @@ def main():
     launch_ms = [e[1].elapsed_time(e[2]) for ev in events for e in ev]
     print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
+    streamed_desc = ""
+    if args.streamed:
+        if not bi:
+            print("bench.py: --streamed needs the batch-inner algorithm", file=sys.stderr)
+            sys.exit(2)
+        perm_b = torch.empty_like(perm)
+        s_perm, s_beam = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+
+        def streamed_step():
+            plan.beamform_streamed(rf, rx_d, tau_d, w_d, out, perm, perm_b, qc,
+                                   stream_permute=s_perm, stream_beamform=s_beam)
+
+        for _ in range(max(1, args.warmup)):
+            streamed_step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            streamed_step()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        streamed_desc = ", streamed: permute of chunk c+1 on a second stream overlaps beamform of chunk c"
+        print(f"[bench] streamed: {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
     accs = das_synth.accumulations(cfg)
     ms_step = wall * 1e3 / args.steps
     value = accs / (ms_step * 1e-3) / 1e9
@@ -159,8 +186,9 @@ def main():
         nx, ny, nz = cfg.grid
         iz = nz // 2
         vox = np.arange(iz * nx * ny, (iz + 1) * nx * ny, dtype=np.int64)
-        if args.cpu_voxels:
-            vox = vox[: args.cpu_voxels]
+        # a bounded sample: about 1.2e9 accumulations (some 25 s single-threaded) unless asked otherwise
+        cap = args.cpu_voxels or max(1, int(1.25e9 // (cfg.M * cfg.Q * cfg.B)))
+        vox = vox[:cap]
         print(f"[bench] cpu baseline: oracle on {vox.size} voxels", file=sys.stderr, flush=True)
         rf_host = rf.cpu().numpy()
         t1 = time.perf_counter()
@@ -199,7 +227,8 @@ def main():
                          f"{'plane' if cfg.tx == 'plane' else 'diverging'} waves, K={cfg.K}, B={cfg.B}, "
                          f"{'complex64 IQ' if cfg.iq else 'fp32 RF'}"),
             "step": ((f"das_permute + das_beamform (batch-inner, layout {args.layout.upper()}"
-                      f", {len(chunks)} chunk(s) of <= {qc} events)") if bi else "das_beamform (baseline)"),
+                      f", {len(chunks)} chunk(s) of <= {qc} events{streamed_desc})") if bi
+                     else "das_beamform (baseline)"),
             "accumulations_per_step": accs,
             "frames_per_lane": info["frames_per_lane"],
         },

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DAS_ABI_VERSION 1
+#define DAS_ABI_VERSION 2
 
 typedef enum das_status {
     DAS_OK = 0,
@@ -165,6 +165,30 @@ das_status das_beamform(const das_plan_t *plan, const void *rf, const float *rx_
                         const float *tau_tx, const float *w_tx, void *out,
                         int32_t q_begin, int32_t q_count, int32_t accumulate,
                         void *hip_stream);
+
+/* Streamed batch-inner pass over all Q transmit events (a volume too large
+ * to permute at once).  Events are taken in chunks of q_chunk; chunk c is
+ * permuted on stream_permute into perm_a (c even) or perm_b (c odd) while
+ * chunk c - 1 is beamformed on stream_beamform, HIP events ordering each
+ * buffer's permute after the beamform that last read it.  The result is the
+ * same as das_permute + das_beamform over [0, Q) with the chunks after the
+ * first accumulating.
+ *   rf_bqmk, rx_pos, tau_tx, w_tx, out   as for das_permute / das_beamform
+ *   perm_a, perm_b   two distinct buffers of das_permuted_bytes(plan, q_chunk)
+ *                    bytes each
+ *   q_chunk          1 .. das_max_q_chunk(plan)
+ *   accumulate       0: out is overwritten; 1: the volume is added to out
+ *   stream_permute, stream_beamform   hipStream_t (may be the same stream)
+ * On return all work is enqueued; stream_permute is made to wait for the last
+ * beamform, so synchronizing either stream waits for the whole pass.
+ * Errors: DAS_ERR_INVALID_ARGUMENT (null pointer, perm_a == perm_b, q_chunk
+ * out of range, accumulate not 0/1); DAS_ERR_UNSUPPORTED (baseline plan, or
+ * q_chunk above das_max_q_chunk); DAS_ERR_ALIGNMENT; DAS_ERR_NO_DEVICE;
+ * DAS_ERR_LAUNCH (some chunks may already be enqueued). */
+das_status das_beamform_streamed(const das_plan_t *plan, const void *rf_bqmk, const float *rx_pos,
+                                 const float *tau_tx, const float *w_tx, void *out, void *perm_a,
+                                 void *perm_b, int32_t q_chunk, int32_t accumulate,
+                                 void *stream_permute, void *stream_beamform);
 
 /* Static text for a status code (never NULL). */
 const char *das_error_string(int status);

@@ -133,10 +133,21 @@ def test_plan_info_and_sizes():
     assert pl3.permuted_shape(2) == (2, 8, 64, 4)
 
 
-@pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (24, 1), (32, 2), (48, 1), (64, 4), (96, 4), (66, 1),
-                                  (160, 4)])
+@pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (24, 1), (32, 2), (48, 1), (64, 2), (96, 2), (66, 1),
+                                  (160, 2), (68, 4)])
 def test_frames_per_lane_choice(B, fl):
-    assert das.Plan(**_problem(B=B)).info["frames_per_lane"] == fl
+    # fp32 batch-inner: the LDS-staged kernel (2 frames per lane) wherever B % 32 == 0
+    pl = das.Plan(**_problem(B=B))
+    assert pl.info["frames_per_lane"] == fl
+    assert pl.info["staged"] == (1 if B % 32 == 0 else 0)
+
+
+@pytest.mark.parametrize("B,fl", [(32, 2), (64, 4), (96, 4), (160, 4)])
+def test_frames_per_lane_choice_direct(B, fl, monkeypatch):
+    monkeypatch.setenv("DAS_BI_KERNEL", "direct")
+    pl = das.Plan(**_problem(B=B))
+    assert pl.info["frames_per_lane"] == fl
+    assert pl.info["staged"] == 0
 
 
 @pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (31, 1), (32, 2), (40, 2), (64, 2)])
@@ -186,6 +197,30 @@ def test_beamform_argument_errors(lib):
         args = [g] * 5
         args[i] = bad
         assert lib.das_beamform(h, *args, 0, 1, 0, None) == ALIGNMENT
+
+
+def test_streamed_argument_errors(lib):
+    pl = das.Plan(**_problem())
+    h = pl._h
+    g, g2, bad = _fake(0x10000), _fake(0x20000), _fake(0x10004)
+    ok = [g, g, g, g, g, g, g2]                 # rf, rx, tau, w, out, perm_a, perm_b
+    assert lib.das_beamform_streamed(None, *ok, 1, 0, None, None) == INVALID
+    for i in range(7):
+        args = list(ok)
+        args[i] = None
+        assert lib.das_beamform_streamed(h, *args, 1, 0, None, None) == INVALID
+    assert lib.das_beamform_streamed(h, g, g, g, g, g, g, g, 1, 0, None, None) == INVALID   # perm_a == perm_b
+    assert lib.das_beamform_streamed(h, *ok, 0, 0, None, None) == INVALID                 # q_chunk 0
+    assert lib.das_beamform_streamed(h, *ok, 1, 2, None, None) == INVALID                 # accumulate not 0/1
+    assert lib.das_beamform_streamed(h, *ok, 3, 0, None, None) == UNSUPPORTED             # above max_q_chunk (Q)
+    base = das.Plan(**_problem(algorithm="baseline"))
+    assert lib.das_beamform_streamed(base._h, *ok, 1, 0, None, None) == UNSUPPORTED       # nothing to permute
+    for i in range(7):
+        args = list(ok)
+        args[i] = bad
+        assert lib.das_beamform_streamed(h, *args, 1, 0, None, None) == ALIGNMENT
+    if not _gpu():
+        assert lib.das_beamform_streamed(h, *ok, 1, 0, None, None) == NO_DEVICE
 
 
 def test_batch_inner_kqmb_chunk_limit(lib):

@@ -87,6 +87,8 @@ def load_library():
     lib.das_permute.restype = ctypes.c_int
     lib.das_beamform.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
     lib.das_beamform.restype = ctypes.c_int
+    lib.das_beamform_streamed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp]
+    lib.das_beamform_streamed.restype = ctypes.c_int
     lib.das_max_q_chunk.argtypes = [vp]
     lib.das_max_q_chunk.restype = i32
     lib.das_error_string.argtypes = [ctypes.c_int]
@@ -218,6 +220,29 @@ class Plan:
                                       w_tx.data_ptr(), out.data_ptr(), q_begin, q_count,
                                       1 if accumulate else 0, _stream_handle(stream, rf.device)),
                "das_beamform")
+        return out
+
+    def beamform_streamed(self, rf, rx_pos, tau_tx, w_tx, out, perm_a, perm_b, q_chunk: int,
+                          accumulate: bool = False, stream_permute=None, stream_beamform=None):
+        """All Q events in chunks of q_chunk: permute of chunk c+1 (stream_permute) overlaps
+        the beamform of chunk c (stream_beamform); perm_a / perm_b hold das_permuted_bytes(q_chunk)."""
+        p = self.problem
+        c = 2 if self.iq else 1
+        q_chunk = int(q_chunk)
+        rf = self._tensor(rf, p.B * p.Q * p.M * p.K * c, "rf")
+        rx_pos = self._tensor(rx_pos, 3 * p.M, "rx_pos")
+        tau_tx = self._tensor(tau_tx, p.Q * self.N, "tau_tx")
+        w_tx = self._tensor(w_tx, p.Q * self.N, "w_tx")
+        out = self._tensor(out, p.B * self.N * c, "out")
+        chunk = p.K * max(q_chunk, 0) * p.M * p.B * c
+        perm_a = self._tensor(perm_a, chunk, "perm_a")
+        perm_b = self._tensor(perm_b, chunk, "perm_b")
+        _check(self._lib.das_beamform_streamed(self._h, rf.data_ptr(), rx_pos.data_ptr(), tau_tx.data_ptr(),
+                                               w_tx.data_ptr(), out.data_ptr(), perm_a.data_ptr(),
+                                               perm_b.data_ptr(), q_chunk, 1 if accumulate else 0,
+                                               _stream_handle(stream_permute, rf.device),
+                                               _stream_handle(stream_beamform, rf.device)),
+               "das_beamform_streamed")
         return out
 
     def close(self):

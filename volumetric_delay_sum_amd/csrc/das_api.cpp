@@ -1,6 +1,7 @@
 // Host side of libdas: problem validation, plans, device checks and launches.
 // Every argument is checked before anything is enqueued; no device memory is
 // allocated here.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -200,11 +201,14 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
     pl->elem_bytes = elem;
     pl->fl = pick_fl(p.B, p.dtype);
     pl->bt = 8;
-    // LDS-staged batch-inner kernel where it is built; DAS_BI_KERNEL=direct
-    // selects the direct-load kernel (comparisons).
+    // LDS-staged batch-inner kernel where it is built (fp32, B a multiple of
+    // 32, two frames per lane: larger B runs as several 32-frame tiles);
+    // DAS_BI_KERNEL=direct selects the direct-load kernel (comparisons).
     const char *kv = std::getenv("DAS_BI_KERNEL");
-    pl->staged = (pl->alg == DAS_ALG_BATCH_INNER && das_staged_supported(*pl) &&
-                  !(kv && std::strcmp(kv, "direct") == 0)) ? 1 : 0;
+    const bool want_staged = pl->alg == DAS_ALG_BATCH_INNER && !(kv && std::strcmp(kv, "direct") == 0);
+    if (want_staged && p.dtype == DAS_F32 && p.B % 32 == 0)
+        pl->fl = 2;
+    pl->staged = (want_staged && das_staged_supported(*pl)) ? 1 : 0;
     pl->q_group = pick_q_group(p, elem, pl->staged != 0);
     const char *vv = std::getenv("DAS_STAGED_VPR");
     pl->vpr = (vv && std::atoi(vv) == 1) ? 1 : 2;
@@ -287,6 +291,60 @@ das_status das_beamform(const das_plan_t *plan, const void *rf, const float *rx_
     else
         e = das_launch_baseline(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s);
     return e == hipSuccess ? DAS_OK : DAS_ERR_LAUNCH;
+}
+
+das_status das_beamform_streamed(const das_plan_t *plan, const void *rf_bqmk, const float *rx_pos,
+                                 const float *tau_tx, const float *w_tx, void *out, void *perm_a,
+                                 void *perm_b, int32_t q_chunk, int32_t accumulate, void *stream_permute,
+                                 void *stream_beamform) {
+    if (!valid_plan(plan) || !rf_bqmk || !rx_pos || !tau_tx || !w_tx || !out || !perm_a || !perm_b)
+        return DAS_ERR_INVALID_ARGUMENT;
+    if (perm_a == perm_b || q_chunk < 1 || (accumulate != 0 && accumulate != 1))
+        return DAS_ERR_INVALID_ARGUMENT;
+    if (plan->alg != DAS_ALG_BATCH_INNER || q_chunk > max_q_chunk(plan))
+        return DAS_ERR_UNSUPPORTED;
+    if (!aligned16(rf_bqmk) || !aligned16(rx_pos) || !aligned16(tau_tx) || !aligned16(w_tx) || !aligned16(out) ||
+        !aligned16(perm_a) || !aligned16(perm_b))
+        return DAS_ERR_ALIGNMENT;
+    das_status st = check_device();
+    if (st != DAS_OK)
+        return st;
+    hipStream_t sp = static_cast<hipStream_t>(stream_permute), sb = static_cast<hipStream_t>(stream_beamform);
+    // permuted[i]: buffer i holds its chunk; consumed[i]: its beamform is done
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+    for (int i = 0; i < 4; ++i)
+        if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) {
+            for (int j = 0; j < i; ++j)
+                (void)hipEventDestroy(ev[j]);
+            return DAS_ERR_LAUNCH;
+        }
+    hipEvent_t *permuted = ev, *consumed = ev + 2;
+    void *buf[2] = {perm_a, perm_b};
+    const int32_t Q = plan->p.Q;
+    int32_t last = 0;
+    st = DAS_OK;
+    for (int32_t q0 = 0, c = 0; q0 < Q && st == DAS_OK; q0 += q_chunk, ++c) {
+        const int32_t n = std::min(q_chunk, Q - q0), i = c & 1;
+        last = i;
+        if (c >= 2 && hipStreamWaitEvent(sp, consumed[i], 0) != hipSuccess) {
+            st = DAS_ERR_LAUNCH;
+            break;
+        }
+        st = das_permute(plan, rf_bqmk, buf[i], q0, n, sp);
+        if (st == DAS_OK && (hipEventRecord(permuted[i], sp) != hipSuccess ||
+                             hipStreamWaitEvent(sb, permuted[i], 0) != hipSuccess))
+            st = DAS_ERR_LAUNCH;
+        if (st == DAS_OK)
+            st = das_beamform(plan, buf[i], rx_pos, tau_tx, w_tx, out, q0, n, c > 0 ? 1 : accumulate, sb);
+        if (st == DAS_OK && hipEventRecord(consumed[i], sb) != hipSuccess)
+            st = DAS_ERR_LAUNCH;
+    }
+    if (st == DAS_OK && hipStreamWaitEvent(sp, consumed[last], 0) != hipSuccess)
+        st = DAS_ERR_LAUNCH;
+    // events still pending in a stream are released by the runtime once they complete
+    for (int i = 0; i < 4; ++i)
+        (void)hipEventDestroy(ev[i]);
+    return st;
 }
 
 }  // extern "C"
