@@ -4,7 +4,7 @@ Each source is compiled to an object with its device assembly kept, the
 objects are linked into ``volumetric_delay_sum_amd/libdas.so``, and the kept
 assembly is scanned for the one hazard the hand-written DPP arithmetic can
 expose: a VALU write of a VGPR read through DPP fewer than two wait states
-later (or an EXEC write fewer than five).  A build with such a hazard fails.
+later (or a VALU write of EXEC fewer than five).  A build with such a hazard fails.
 """
 from __future__ import annotations
 
@@ -66,32 +66,53 @@ def _regs(tok: str) -> set[int]:
     return set()
 
 
+_LABEL = re.compile(r"^\.?[\w$.]+:$")
+
+
 def scan_dpp_hazards(asm_text: str) -> list[str]:
-    """Return a description of every DPP read too close to a VALU write of its source."""
+    """Return a description of every DPP read too close to a VALU write of its source.
+
+    The scan walks backwards from each DPP instruction until five wait states
+    have passed.  At a label it continues into every predecessor (the
+    fall-through and each branch to the label), so a hazard across a branch is
+    found too; a walk that does not settle within a few predecessor hops is
+    reported.  Functions are scanned separately.
+    """
     lines = []
     for raw in asm_text.splitlines():
         s = raw.split(";")[0].strip()
-        if not s or s.startswith(".") or s.startswith("//"):
+        if not s or s.startswith("//"):
             continue
+        if s.startswith(".") and not _LABEL.match(s):
+            continue                # assembler directive
         lines.append(s)
-    problems = []
+    # branches to each label, by line index of the branch
+    branches: dict[str, list[int]] = {}
     for i, s in enumerate(lines):
-        op = s.split()[0]
-        if "_dpp" not in op:
-            continue
-        ops = s[len(op):].split(",")
-        if len(ops) < 2:
-            continue
-        src0 = _regs(ops[1].split()[0])
-        waits = 0
-        j = i - 1
+        top = s.split()[0]
+        if top.startswith("s_cbranch") or top == "s_branch":
+            parts = s.split()
+            if len(parts) > 1:
+                branches.setdefault(parts[-1], []).append(i)
+    uncond = ("s_branch", "s_setpc_b64", "s_endpgm")
+    problems = []
+
+    def walk(dpp: str, src0: set, j: int, waits: int, hops: int):
         while j >= 0 and waits < 5:
             t = lines[j]
             if t.endswith(":"):
-                if waits < 5:
-                    # control can arrive from elsewhere: require the gap inside this block
-                    problems.append(f"label within the DPP wait window before: {s}")
-                break
+                if _LABEL.match(t) and not t.startswith("."):
+                    return          # function entry: nothing runs before it
+                if hops >= 6:
+                    problems.append(f"unresolved control flow within the DPP wait window before: {dpp}")
+                    return
+                label = t[:-1]
+                prev = lines[j - 1].split()[0] if j > 0 else "s_endpgm"
+                if prev not in uncond:
+                    walk(dpp, src0, j - 1, waits, hops + 1)
+                for b in branches.get(label, []):
+                    walk(dpp, src0, b - 1, waits, hops + 1)
+                return
             top = t.split()[0]
             if top == "s_nop":
                 waits += int(t.split()[1], 0) + 1
@@ -99,11 +120,23 @@ def scan_dpp_hazards(asm_text: str) -> list[str]:
                 if top.startswith("v_") and waits < 2:
                     dst = _regs(t[len(top):].split(",")[0])
                     if dst & src0:
-                        problems.append(f"VALU write '{t}' then DPP read '{s}' after {waits} wait states")
-                if ("exec" in t.split(",")[0]) and not top.startswith("s_waitcnt"):
-                    problems.append(f"EXEC write '{t}' then DPP '{s}' after {waits} wait states")
+                        problems.append(f"VALU write '{t}' then DPP read '{dpp}' after {waits} wait states")
+                # a VALU write of EXEC (v_cmpx, or a VALU op targeting exec) needs 5 wait
+                # states before a DPP op; scalar writes of EXEC are interlocked
+                dst0 = t[len(top):].split(",")[0].strip()
+                if top.startswith("v_cmpx") or (top.startswith("v_") and dst0 in ("exec", "exec_lo", "exec_hi")):
+                    problems.append(f"VALU EXEC write '{t}' then DPP '{dpp}' after {waits} wait states")
                 waits += 1
             j -= 1
+
+    for i, s in enumerate(lines):
+        op = s.split()[0]
+        if "_dpp" not in op:
+            continue
+        ops = s[len(op):].split(",")
+        if len(ops) < 2:
+            continue
+        walk(s, _regs(ops[1].split()[0]), i - 1, 0, 0)
     return problems
 
 

@@ -5,37 +5,38 @@
 // lanes sharing a voxel read consecutive frames of one (k, q, m) row, frames
 // being the contiguous axis after the permute), but the frame rows reach the
 // lanes through LDS instead of the vector L1.  On gfx950 a 64-lane vector load
-// costs the texture-address unit several cycles whatever its width, which caps
-// an L1-fed gather near 6 accumulations per clock per CU; LDS delivers 128-bit
-// reads at about 200 B/clk/CU even at random row offsets.  The pages note that
-// neighbouring voxels need nearly the same sample indices of each receiver
-// (Section 3, spatial locality; the tensor-core paragraphs build their dense
-// tiles on the same fact): here that locality lets a workgroup stage each
+// costs the texture-address unit many cycles whatever its width, which caps an
+// L1-fed gather near 6 accumulations per clock per CU, while LDS serves
+// 64-bit reads at random row offsets at well over 200 B/clk/CU.  The pages
+// note that neighbouring voxels need nearly the same sample indices of each
+// receiver (Section 3, spatial locality; the tensor-core paragraphs build their
+// dense tiles on the same fact): here that locality lets a workgroup stage each
 // receiver's few distinct rows once and serve all its voxels from them.
 //
 // Mapping.  A 1024-thread workgroup owns an 8 x 8 x VPR tile of voxels; each
-// 16-lane DPP row owns the VPR voxels of one (x, y) column of the tile and
-// each lane FL consecutive frames of the frame tile.  Work goes in steps of (transmit event, block of 16
-// receivers).  Per step:
-//   1. every lane j of every row computes the sample split k and weights of
-//      receiver m0 + j for its voxel (fp64 position, as in the direct kernel);
+// 16-lane DPP row owns the VPR voxels of one (x, y) column of the tile and each
+// lane FL consecutive frames of the frame tile.  Work goes in steps of
+// (transmit event, block of 16 receivers).  Per step:
+//   1. lane j of every row computes the sample split k and the weights of
+//      receiver m0 + j for its voxels (fp64 sample position);
 //   2. the window [kmin, kmax] of k over the tile's voxels with a non-zero
-//      weight is reduced per receiver (shuffles in a wave, LDS atomics across
+//      weight is reduced per receiver (lane swaps in a wave, LDS atomics across
 //      waves);
-//   3. wave w copies receiver m0 + w's rows kmin .. kmax + 1 from HBM into LDS
-//      as "pair rows": pair p holds, for every frame, samples kmin + p and
-//      kmin + p + 1 side by side, so a lane reads both interpolation taps of
-//      its frames with one ds_read_b128;
+//   3. wave w copies receiver m0 + w's sample rows kmin .. kmax + 1 (the frame
+//      tile's part of each) from HBM straight into LDS with LDS-DMA buffer
+//      loads: no registers, no store instructions;
 //   4. each row walks the 16 receivers, broadcasting lane j's LDS offset and
-//      weights through DPP row_newbcast:j exactly as the direct kernel does.
-// The copy for step i + 1 is loaded into registers while step i computes and
-// written to LDS between barriers; the transmit tables are read a step ahead.
-// Two voxels per row double the arithmetic per step while the window grows by
-// about half, so the per-step barriers, window reduction and copy are spread
-// over more accumulations and the copy has longer to arrive.  A step whose window is wider than the LDS
-// window capacity falls back to direct loads from the permuted buffer, so any
-// geometry is served exactly; voxels with zero weight for a receiver do not
-// widen its window and read a row of it with zero coefficients.
+//      weights through DPP row_newbcast:j; a lane reads its frames at k and
+//      k + 1 (two 8-byte reads of consecutive rows) and does 2 FL FMAs.
+// The rows live in two buffers: step i computes from one while the rows of
+// step i + 1 stream into the other, so a step needs one barrier.  Windows are
+// reduced two steps ahead (three slot sets) so that the copy of step i + 1
+// can start as soon as step i does; the copy rounds are spread over the
+// compute loop, where the texture addresser is otherwise idle.  A step whose
+// window is wider than a receiver's LDS region falls back to direct loads from
+// the permuted buffer, so any geometry is served exactly; voxels with zero
+// weight for a receiver do not widen its window and read a row of it with
+// zero coefficients.
 #include "das_device.h"
 
 namespace {
@@ -43,25 +44,26 @@ namespace {
 constexpr int THREADS = 1024;
 constexpr int ROW = 16;               // lanes per voxel column (one DPP row)
 constexpr int TX = 8, TY = 8;         // lateral voxel tile of one workgroup (one column per row)
-constexpr int LDS_BUDGET = 144 * 1024;
+constexpr int LDS_ROW_BUDGET = 160000;   // bytes for the two row buffers
 
 template <bool IQ, int FL>
 struct Geo {
     static constexpr int C = IQ ? 2 : 1;                 // floats per sample
     static constexpr int E = 4 * C;                      // bytes per sample
     static constexpr int NF = FL * C;                    // floats per lane per tap
-    static constexpr int HALF = NF * 4;                  // bytes per lane per tap
-    static constexpr int LB = 2 * HALF;                  // bytes per lane in a pair row
-    static constexpr int PAIR = ROW * LB;                // bytes per pair row
-    static constexpr int ROWB = ROW * HALF;              // bytes of the frame tile in one sample row
-    static constexpr int WP = (LDS_BUDGET / (ROW * PAIR)) > 66 ? 66 : (LDS_BUDGET / (ROW * PAIR));
-    static constexpr int W_MAX = WP - 2;                 // pair rows per receiver (plus a guard row each end)
+    static constexpr int LANEB = NF * 4;                 // bytes per lane in a sample row
+    static constexpr int ROWB = ROW * LANEB;             // bytes of the frame tile in one sample row
+    static constexpr int RW0 = LDS_ROW_BUDGET / (2 * ROW * ROWB);
+    static constexpr int RW = RW0 > 64 ? 64 : RW0;       // sample rows per receiver region
+    static constexpr int W_MAX = RW - 1;                 // k positions per receiver window
     static constexpr int LPR = ROWB / 16;                // lanes per sample row in a 16-byte copy
     static constexpr int RPR = 64 / LPR;                 // sample rows per copy round of a wave
-    static constexpr int MAXR = (W_MAX + 1 + RPR - 1) / RPR;
-    static constexpr int PAIR_BYTES = ROW * WP * PAIR;
-    static constexpr int LDS_BYTES = PAIR_BYTES + 3 * 2 * ROW * 4;
-    static_assert(ROWB % 16 == 0, "copy granularity");
+    static constexpr int MAXR = (RW + RPR - 1) / RPR;    // copy rounds of a full region
+    static constexpr int REGION = RW * ROWB;             // bytes of one receiver's region
+    static constexpr int BUF = ROW * REGION;             // bytes of one buffer
+    static constexpr int LDS_BYTES = 2 * BUF + 3 * 2 * ROW * 4;
+    static_assert(ROWB % 16 == 0 && 64 % LPR == 0, "copy granularity");
+    static_assert(LANEB == 8 || LANEB == 16, "reader width");
 };
 
 // Per-lane state of one voxel in one step: sample index and weights.
@@ -114,6 +116,11 @@ __device__ __forceinline__ Step make_step(const DasKParams &P, const das::RxTerm
     return st;
 }
 
+template <int NF>
+struct Tap {
+    using type = float __attribute__((ext_vector_type(NF)));
+};
+
 template <bool IQ, int FL, int LAYOUT, int VPR>
 __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, const float *__restrict__ rfp,
                                                                 const float *__restrict__ rx,
@@ -122,9 +129,9 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
                                                                 float *__restrict__ out, uint32_t tap_stride) {
     using G = Geo<IQ, FL>;
     constexpr int C = G::C, E = G::E, NF = G::NF;
+    using TapV = typename Tap<NF>::type;
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
-    char *pairs = lds;
-    int *slots = reinterpret_cast<int *>(lds + G::PAIR_BYTES);   // [3 sets][min, max][16]
+    int *slots = reinterpret_cast<int *>(lds + 2 * G::BUF);   // [3 sets][min, max][16]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     const int bl = b0 + li * FL;
     const bool fr_ok = bl < P.B;
     const uint32_t laneoff_g = (uint32_t)(fr_ok ? bl : 0) * E;   // byte offset in a global row
-    const uint32_t laneoff_l = (uint32_t)li * G::LB;              // byte offset in a pair row
+    const uint32_t laneoff_l = (uint32_t)li * G::LANEB;           // byte offset in a staged row
 
     const int64_t rowfull = (int64_t)P.B * E;                       // one (k, q, m) row, all frames
     const int64_t m_stride = (LAYOUT == DAS_LAYOUT_KQMB) ? rowfull : rowfull * P.K;
@@ -164,9 +171,9 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     const int64_t chunk_bytes = rowfull * P.M * P.q_count * P.K;
     const char *rf_bytes = reinterpret_cast<const char *>(rfp);
 
-    // zero the pair rows (so a zero weight never meets a non-finite stale value) and the window slots
-    for (int i = tid * 16; i < G::PAIR_BYTES; i += THREADS * 16)
-        *reinterpret_cast<int4 *>(pairs + i) = make_int4(0, 0, 0, 0);
+    // zero both row buffers (so a zero weight never meets a non-finite stale value) and the window slots
+    for (int i = tid * 16; i < 2 * G::BUF; i += THREADS * 16)
+        *reinterpret_cast<int4 *>(lds + i) = make_int4(0, 0, 0, 0);
     if (tid < 3 * 2 * ROW)
         slots[tid] = ((tid / ROW) & 1) ? INT_MIN : INT_MAX;
     __syncthreads();
@@ -187,15 +194,16 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             R[v].w = (mm < P.M) ? R[v].w : 0.0f;
         }
     };
-    // Transmit tables of the voxels, read a step ahead through buffer loads
-    // (base per event, lane offset n).
+    // Transmit tables of the voxels, read two steps ahead through buffer loads
+    // (event offset in the scalar offset, voxel in the lane offset).
     const das::BufRsrc rs_tau = das::make_rsrc(reinterpret_cast<const char *>(tau_tx), (uint64_t)P.Q * P.N * 4);
     const das::BufRsrc rs_wtx = das::make_rsrc(reinterpret_cast<const char *>(w_tx), (uint64_t)P.Q * P.N * 4);
-    auto load_tx = [&](const Cursor &c, Tx (&tx)[VPR]) {
+    auto load_tx = [&](const Cursor &c, Tx (&txv)[VPR]) {
         const uint32_t qoff = (uint32_t)(P.q_begin + c.ql) * (uint32_t)P.N * 4u;   // the launch keeps Q N 4 < 2^32
 #pragma unroll
         for (int v = 0; v < VPR; ++v)
-            tx[v] = Tx{das::buffer_load_f32(rs_tau, n[v] * 4, (int)qoff, 0), das::buffer_load_f32(rs_wtx, n[v] * 4, (int)qoff, 0)};
+            txv[v] = Tx{das::buffer_load_f32(rs_tau, n[v] * 4, (int)qoff, 0),
+                        das::buffer_load_f32(rs_wtx, n[v] * 4, (int)qoff, 0)};
     };
     // Publish the lanes' k to the window of their receiver: min/max over the
     // row's voxels and the wave's four rows (gfx950 row swaps: lanes l and
@@ -238,98 +246,59 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         return c.g0 < P.q_count;
     };
 
-    // Window of the step in slot set `set`: per lane and voxel the LDS byte
-    // offset of its receiver's pair row for k; the copy of this wave's receiver.
+    // Window of the step in slot set `set`, staged in buffer `buf`: per lane
+    // and voxel the LDS byte offset of its receiver's row for k; the copy of
+    // this wave's receiver.
     struct Window {
         uint32_t loff[VPR];
         int kmin_w, rows_w;    // wave's copy: first sample row, number of sample rows
         bool overflow;
     };
-    struct Slots {
-        int kmn, kmx, kmn_w, kmx_w;
-    };
-    auto read_slots = [&](int set) -> Slots {
-        return Slots{slots[set * 2 * ROW + li], slots[set * 2 * ROW + ROW + li], slots[set * 2 * ROW + wave],
-                     slots[set * 2 * ROW + ROW + wave]};
-    };
-    auto make_window = [&](const Step (&s)[VPR], const Slots &sl) -> Window {
+    auto read_window = [&](const Step (&s)[VPR], int set, int buf) -> Window {
         Window wdw;
-        const int np = (sl.kmn <= sl.kmx) ? sl.kmx - sl.kmn + 1 : 0;     // pair rows of receiver li
-        const uint32_t base = (uint32_t)(li * G::WP + 1) * G::PAIR;
+        const int kmn = slots[set * 2 * ROW + li], kmx = slots[set * 2 * ROW + ROW + li];
+        const int np = (kmn <= kmx) ? kmx - kmn + 1 : 0;            // k positions of receiver li
+        const uint32_t base = (uint32_t)(buf * G::BUF + li * G::REGION);
 #pragma unroll
         for (int v = 0; v < VPR; ++v)
-            wdw.loff[v] = s[v].active ? base + (uint32_t)((int)s[v].k - sl.kmn) * G::PAIR : base;
+            wdw.loff[v] = s[v].active ? base + (uint32_t)((int)s[v].k - kmn) * G::ROWB : base;
         wdw.overflow = __any(np > G::W_MAX);
-        wdw.kmin_w = sl.kmn_w;
-        wdw.rows_w = (sl.kmn_w <= sl.kmx_w) ? sl.kmx_w - sl.kmn_w + 2 : 0;   // sample rows kmin .. kmax + 1
+        const int kmn_w = slots[set * 2 * ROW + wave], kmx_w = slots[set * 2 * ROW + ROW + wave];
+        wdw.kmin_w = kmn_w;
+        wdw.rows_w = (kmn_w <= kmx_w) ? kmx_w - kmn_w + 2 : 0;      // sample rows kmin .. kmax + 1
         return wdw;
     };
-    auto read_window = [&](const Step (&s)[VPR], int set) -> Window { return make_window(s, read_slots(set)); };
 
-    // Copy of one receiver's sample rows (wave w copies receiver m0 + w), in
-    // rounds of RPR rows: lane (rho, c) loads 16 bytes (frames 4c .. 4c + 3 of
-    // the frame tile) of sample row kmin + RPR r + rho.  The number of rounds is
-    // wave-uniform; rows past the window are loaded (inside the buffer, or zero
-    // past its end) but never stored.  The base address is wave-uniform and the
-    // lane offsets fixed, so the loads need little vector address arithmetic.
-    static_assert(G::HALF == 8 && G::LPR == 8, "copy layout assumes 2 fp32 frames per reader lane");
-    int4 pf[G::MAXR];
-    const int crow = lane / G::LPR;                  // rho: sample row within a copy round
-    const int cchunk = lane % G::LPR;                // c: 16-byte chunk of the frame-tile row
-    const uint32_t cbyte = (uint32_t)cchunk * 16;
+    // Copy of one receiver's sample rows by LDS-DMA (wave w copies receiver
+    // m0 + w into its region of the buffer).  Round r moves RPR rows: lane
+    // (rho, c) fetches 16 bytes (chunk c of the frame tile's part) of sample
+    // row kmin + RPR r + rho, and the DMA writes lane l's 16 bytes at
+    // 16 l past the round's LDS base, i.e. row rho, chunk c of the region.
+    // Lanes past the window are masked off.  The launch keeps the chunk under
+    // 4 GiB, so the offsets are 32-bit.
+    const das::BufRsrc rs_chunk = das::make_rsrc(rf_bytes, (uint64_t)chunk_bytes);
+    const int crow = lane / G::LPR;
     const int64_t kstride = (LAYOUT == DAS_LAYOUT_KQMB) ? (int64_t)P.q_count * P.M * rowfull : rowfull;
     const uint32_t kstride32 = (uint32_t)kstride;
-    const uint32_t coff = (uint32_t)crow * kstride32 + cbyte;
-    auto copy_rounds = [&](const Window &wdw) { return __builtin_amdgcn_readfirstlane((wdw.rows_w + G::RPR - 1) / G::RPR); };
-    // The launch keeps the chunk under 4 GiB, so offsets in it are 32-bit.
-    const das::BufRsrc rs_chunk = das::make_rsrc(rf_bytes, (uint64_t)chunk_bytes);
+    const uint32_t coff = (uint32_t)crow * kstride32 + (uint32_t)(lane % G::LPR) * 16 + (uint32_t)b0 * E;
     const uint32_t mstride32 = (uint32_t)m_stride;
-    const uint32_t b0off = (uint32_t)b0 * E;
-    auto copy_load = [&](const Cursor &c, const Window &wdw) {
-        const int nr = copy_rounds(wdw);
-        const uint32_t kmin = (uint32_t)__builtin_amdgcn_readfirstlane(wdw.kmin_w);
-        const uint32_t start = ((uint32_t)c.ql * (uint32_t)P.M + (uint32_t)(c.m0 + wave)) * mstride32 + b0off + kmin * kstride32;
-#pragma unroll
-        for (int r = 0; r < G::MAXR; ++r) {
-            if (r < nr) {
-                // lane part in the vector offset, window and round in the scalar offset
-                const das::f32x4 v = das::buffer_load_f32x4(rs_chunk, (int)coff, (int)(start + (uint32_t)(r * G::RPR) * kstride32), 0);
-                pf[r] = __builtin_bit_cast(int4, v);
-            }
-        }
+    struct CopyPlan {
+        int nr, rows;        // rounds and sample rows (wave-uniform)
+        uint32_t start;      // byte offset of the window's first sample row (less the frame tile)
+        uint32_t dst;        // LDS byte offset of the region
     };
-    // Sample row kmin + rr feeds pair row rr (first tap) and pair row rr - 1
-    // (second tap); a lane's frames 4c, 4c + 1 go to reader lane 2c and frames
-    // 4c + 2, 4c + 3 to reader lane 2c + 1.  That is four 8-byte targets per
-    // lane, all within one 32-byte stretch of a 256-byte pair row, so lanes of
-    // the same c share banks.  Store instruction i sends the lane of row rho to
-    // target (i + rho) mod 4: every instruction then spreads its 64 lanes over
-    // all 64 banks (two dwords per bank, the minimum for 512 bytes).  The
-    // targets are fixed per lane; a round adds RPR pair rows as an immediate.
-    uint32_t waddr[4];
-    {
-        const uint32_t base = (uint32_t)(wave * G::WP + 1) * G::PAIR + (uint32_t)crow * G::PAIR + (uint32_t)cchunk * 2 * G::LB;
-        const uint32_t tgt[4] = {base, base + G::LB, base - G::PAIR + G::HALF, base - G::PAIR + G::LB + G::HALF};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = (i + crow) & 3;
-            waddr[i] = t == 0 ? tgt[0] : t == 1 ? tgt[1] : t == 2 ? tgt[2] : tgt[3];
-        }
-    }
-    const bool row_even = (crow & 1) == 0;
-    auto copy_store = [&](const Window &wdw) {
-        const int nr = copy_rounds(wdw);
-#pragma unroll
-        for (int r = 0; r < G::MAXR; ++r) {
-            if (r < nr && r * G::RPR + crow < wdw.rows_w) {
-                const int2 lo = make_int2(pf[r].x, pf[r].y), hi = make_int2(pf[r].z, pf[r].w);
-                const int2 a = row_even ? lo : hi, b = row_even ? hi : lo;
-                const uint32_t RO = (uint32_t)(r * G::RPR * G::PAIR);
-                *reinterpret_cast<int2 *>(pairs + waddr[0] + RO) = a;
-                *reinterpret_cast<int2 *>(pairs + waddr[1] + RO) = b;
-                *reinterpret_cast<int2 *>(pairs + waddr[2] + RO) = a;
-                *reinterpret_cast<int2 *>(pairs + waddr[3] + RO) = b;
-            }
+    auto copy_prepare = [&](const Cursor &c, const Window &wdw, int buf) -> CopyPlan {
+        const int rows = __builtin_amdgcn_readfirstlane(wdw.rows_w);
+        const uint32_t kmin = (uint32_t)__builtin_amdgcn_readfirstlane(wdw.kmin_w);
+        return CopyPlan{(rows + G::RPR - 1) / G::RPR, rows,
+                        ((uint32_t)c.ql * (uint32_t)P.M + (uint32_t)(c.m0 + wave)) * mstride32 + kmin * kstride32,
+                        (uint32_t)(buf * G::BUF + wave * G::REGION)};
+    };
+    auto copy_round = [&](const CopyPlan &cp, int r) {
+        if (r < cp.nr && r * G::RPR + crow < cp.rows) {
+            const das::lds_ptr dst = (das::lds_ptr)(lds + cp.dst + (uint32_t)(r * G::RPR * G::ROWB));   // generic -> LDS address space
+            das::buffer_load_lds(rs_chunk, dst, 16, (int)coff, (int)(cp.start + (uint32_t)(r * G::RPR) * kstride32), 0,
+                                 0);
         }
     };
 
@@ -343,14 +312,14 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         }
 
     // All voxels of one step from LDS: VPR x 16 (voxel, receiver) items, each
-    // one LDS read of the pair row (2 NF floats) and 2 FL (IQ: 8 FL) FMAs with
-    // the receiver's coefficients broadcast from its lane.  The reads are issued
-    // DEPTH items ahead; the scheduling fences keep the compiler from sinking
-    // each read next to its use, which would leave one read in flight per wave.
+    // two reads (taps k and k + 1: consecutive rows) and 2 FL (IQ: 8 FL) FMAs
+    // with the receiver's coefficients broadcast from its lane.  The reads are
+    // issued DEPTH items ahead; the scheduling fences keep the compiler from
+    // sinking each read next to its use, which would leave one read in flight
+    // per wave.  `at(t)` runs after item t (the next step's copy rounds).
     constexpr int NITEM = VPR * ROW;
     constexpr int DEPTH = (VPR == 1) ? 8 : 6;
-    constexpr int NV4 = (2 * NF) / 4;              // 16-byte reads per item
-    auto compute_lds = [&](const Step (&s)[VPR], const uint32_t (&loff)[VPR], float (&pt)[VPR][NF]) {
+    auto compute_lds = [&](const Step (&s)[VPR], const uint32_t (&loff)[VPR], float (&pt)[VPR][NF], auto &&at) {
         float a[VPR], b[VPR], ai[VPR], bi[VPR];
 #pragma unroll
         for (int v = 0; v < VPR; ++v) {
@@ -363,39 +332,40 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             else
                 das::settle(a[v], b[v]);
         }
-        das::f32x4 ring[DEPTH][NV4];
+        TapV ring0[DEPTH], ring1[DEPTH];
         auto issue = [&](auto T) {
-            constexpr int t = decltype(T)::value;
-            constexpr int v = t / ROW, j = t % ROW;
+            constexpr int tt = decltype(T)::value;
+            constexpr int v = tt / ROW, j = tt % ROW;
             const uint32_t addr = das::row_bcast<j>(loff[v]) + laneoff_l;
-#pragma unroll
-            for (int u = 0; u < NV4; ++u)
-                ring[t % DEPTH][u] = *reinterpret_cast<const das::f32x4 *>(pairs + addr + 16 * u);
+            ring0[tt % DEPTH] = *reinterpret_cast<const TapV *>(lds + addr);
+            ring1[tt % DEPTH] = *reinterpret_cast<const TapV *>(lds + addr + G::ROWB);
         };
         das::unroll<DEPTH>([&](auto T) { issue(T); });
         __builtin_amdgcn_sched_barrier(0);
         das::unroll<NITEM>([&](auto T) {
-            constexpr int t = decltype(T)::value;
-            constexpr int v = t / ROW, j = t % ROW;
-            float x[2 * NF];
-#pragma unroll
-            for (int u = 0; u < NV4; ++u) {
-                x[4 * u] = ring[t % DEPTH][u].x;
-                x[4 * u + 1] = ring[t % DEPTH][u].y;
-                x[4 * u + 2] = ring[t % DEPTH][u].z;
-                x[4 * u + 3] = ring[t % DEPTH][u].w;
-            }
+            constexpr int tt = decltype(T)::value;
+            constexpr int v = tt / ROW, j = tt % ROW;
+            const TapV x0 = ring0[tt % DEPTH], x1 = ring1[tt % DEPTH];
             if constexpr (IQ) {
 #pragma unroll
                 for (int f = 0; f < FL; ++f)
-                    das::cmac_bcast<j>(pt[v][2 * f], pt[v][2 * f + 1], a[v], ai[v], b[v], bi[v], x[2 * f],
-                                       x[2 * f + 1], x[NF + 2 * f], x[NF + 2 * f + 1]);
+                    das::cmac_bcast<j>(pt[v][2 * f], pt[v][2 * f + 1], a[v], ai[v], b[v], bi[v], x0[2 * f],
+                                       x0[2 * f + 1], x1[2 * f], x1[2 * f + 1]);
             } else {
 #pragma unroll
-                for (int f = 0; f < FL; ++f) das::lerp_bcast<j>(pt[v][f], a[v], b[v], x[f], x[NF + f]);
+                for (int f = 0; f < FL; ++f) das::lerp_bcast<j>(pt[v][f], a[v], b[v], x0[f], x1[f]);
             }
-            if constexpr (t + DEPTH < NITEM)
-                issue(das::ic<t + DEPTH>{});
+            if constexpr (tt + DEPTH < NITEM)
+                issue(das::ic<tt + DEPTH>{});
+            at(T);
+            // A SIMD issues from its oldest ready wave first, so without this its
+            // four waves would finish a step one after another and the last
+            // would run its tail alone while the others wait at the barrier.  A
+            // wave lowers its own priority as it gets through the loop, which
+            // lets the waves that are behind catch up: all four reach the
+            // barrier together with their latencies hidden by each other.
+            if constexpr ((tt + 1) % (NITEM / 4) == 0 && tt + 1 < NITEM)
+                __builtin_amdgcn_s_setprio(3 - (tt + 1) / (NITEM / 4));
             __builtin_amdgcn_sched_barrier(0);
         });
     };
@@ -434,9 +404,10 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         });
     };
 
-    // ---- prologue: windows of steps 0 and 1, pair rows of step 0 ----------
-    // Slot set of step i is i % 3: the window of step i + 2 is published
-    // between the two barriers that end step i and read after them.
+    // ---- prologue: windows of steps 0 and 1, rows of step 0 ----------------
+    // Slot set of step i is i % 3 and its rows go to buffer i % 2: the window
+    // of step i + 2 is published during step i, the rows of step i + 1 are
+    // copied during step i, and one barrier ends each step.
     Cursor cur{0, 0, 0, min(P.q_group, P.q_count)};
     load_geometry(cur.m0);
     Step s_cur[VPR], s_nxt[VPR];
@@ -461,54 +432,61 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     if (has_next2)
         load_tx(nxt2, tx_nxt2);
     __syncthreads();
-    Window w_cur = read_window(s_cur, 0);
+    Window w_cur = read_window(s_cur, 0, 0);
     if (!w_cur.overflow) {
-        copy_load(cur, w_cur);
-        copy_store(w_cur);
+        const CopyPlan cp0 = copy_prepare(cur, w_cur, 0);
+#pragma unroll
+        for (int r = 0; r < G::MAXR; ++r) copy_round(cp0, r);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0): this wave's copy has landed
     __syncthreads();
 
     // ---- main loop ---------------------------------------------------------
-    int set = 0;                                       // slot set of the current step
+    int set = 0, buf = 0;                              // slot set and row buffer of the current step
     for (;;) {
+        __builtin_amdgcn_s_setprio(3);                 // every wave starts a step at the top priority
         const int set1 = (set == 2) ? 0 : set + 1, set2 = (set1 == 2) ? 0 : set1 + 1;
-        // pair rows of the next step: in flight while this step computes
-        Window w_nxt{};
-        if (has_next) {
-            w_nxt = read_window(s_nxt, set1);
-            if (!w_nxt.overflow)
-                copy_load(nxt, w_nxt);
-        }
-
-        // the step after next: geometry, sample split, window
+        // The step after next first: geometry, sample split, window.  It is
+        // latency-bound ALU work, done while all four waves of a SIMD are
+        // active; a SIMD runs its waves in age order, so the youngest finishes
+        // its compute last, alone, where only the pipelined LDS loop hides latency.
         Cursor nxt3 = nxt2;
         const bool has_next3 = has_next2 && advance(nxt3);
         Step s_nxt2[VPR];
         Tx tx_nxt3[VPR];
-        auto setup_split = [&] {
-            if (has_next2) {
-                if (nxt2.m0 != nxt.m0)
-                    load_geometry(nxt2.m0);
+        if (has_next2) {
+            if (nxt2.m0 != nxt.m0)
+                load_geometry(nxt2.m0);
 #pragma unroll
-                for (int v = 0; v < VPR; ++v) s_nxt2[v] = make_step<IQ>(P, R[v], tx_nxt2[v]);
-                if (has_next3)
-                    load_tx(nxt3, tx_nxt3);                  // consumed next iteration
-            }
-        };
-        auto setup_publish = [&] {
-            if (has_next2)
-                publish(s_nxt2, set2);
-        };
-        auto compute = [&] {
-            if (!w_cur.overflow) {
-                compute_lds(s_cur, w_cur.loff, part);
-            } else {
+            for (int v = 0; v < VPR; ++v) s_nxt2[v] = make_step<IQ>(P, R[v], tx_nxt2[v]);
+            if (has_next3)
+                load_tx(nxt3, tx_nxt3);                  // consumed next iteration
+            publish(s_nxt2, set2);
+        }
+        // the rows of the next step stream into the other buffer while this step computes
+        Window w_nxt{};
+        CopyPlan cp{0, 0, 0, 0};
+        if (has_next) {
+            w_nxt = read_window(s_nxt, set1, buf ^ 1);
+            if (!w_nxt.overflow)
+                cp = copy_prepare(nxt, w_nxt, buf ^ 1);
+        }
+        if (!w_cur.overflow) {
+            // copy round r after item r * SPREAD + SPREAD / 2
+            constexpr int SPREAD = NITEM / G::MAXR;
+            compute_lds(s_cur, w_cur.loff, part, [&](auto T) {
+                constexpr int tt = decltype(T)::value;
+                if constexpr (tt % SPREAD == SPREAD / 2 && tt / SPREAD < G::MAXR)
+                    copy_round(cp, tt / SPREAD);
+            });
+        } else {
 #pragma unroll
-                for (int v = 0; v < VPR; ++v) compute_direct(s_cur[v], cur, part[v]);
-            }
-        };
-        compute();
-        if (tid < 2 * ROW)                                  // this step's window was read last step
+            for (int r = 0; r < G::MAXR; ++r) copy_round(cp, r);
+#pragma unroll
+            for (int v = 0; v < VPR; ++v) compute_direct(s_cur[v], cur, part[v]);
+        }
+
+        if (tid < 2 * ROW)                              // this step's window was read last step
             slots[set * 2 * ROW + tid] = (tid < ROW) ? INT_MAX : INT_MIN;
 
         if (!has_next || nxt.m0 != cur.m0 || nxt.g0 != cur.g0) {
@@ -522,14 +500,9 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         }
         if (!has_next)
             break;
-        __syncthreads();                                   // pair rows of this step read
-        // The step after next is set up (ALU work) before the next step's rows
-        // are stored, which gives their loads more time to land.
-        setup_split();
-        if (!w_nxt.overflow)
-            copy_store(w_nxt);
-        setup_publish();
-        __syncthreads();                                   // next step's rows in place, the window after it published
+        __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0): this wave's copy has landed
+        __syncthreads();                               // this step's rows read, the next step's in place,
+                                                       // the window after it published
         cur = nxt;
         nxt = nxt2;
         nxt2 = nxt3;
@@ -543,6 +516,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         }
         w_cur = w_nxt;
         set = set1;
+        buf ^= 1;
     }
 
     if (fr_ok) {

@@ -168,6 +168,14 @@ __device__ float buffer_load_f32(BufRsrc r, int voff, int soff, int aux) __asm("
 __device__ f32x2 buffer_load_f32x2(BufRsrc r, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.load.v2f32");
 __device__ f32x4 buffer_load_f32x4(BufRsrc r, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.load.v4f32");
 
+// LDS-DMA: the load writes lane l's `size` bytes to LDS at lds + size * l
+// (the LDS base goes to M0, so it must be wave-uniform) instead of to VGPRs.
+// Completion is counted by vmcnt like any vector load; masked-off lanes do
+// not write.
+typedef __attribute__((address_space(3))) void *lds_ptr;
+__device__ void buffer_load_lds(BufRsrc r, lds_ptr lds, int size, int voff, int soff, int imm, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+
 // Resource over [base, base + bytes) (bytes clamped to 2^32 - 1), stride 0.
 __device__ __forceinline__ BufRsrc make_rsrc(const char *base, uint64_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
