@@ -115,7 +115,7 @@ def test_plan_info_and_sizes():
     pl = das.Plan(**_problem(B=32, dtype="c64", f_demod=5e6))
     assert pl.info["algorithm"] == das.ALG_BATCH_INNER
     assert pl.info["elem_bytes"] == 8
-    assert pl.info["frames_per_lane"] == 2
+    assert pl.info["frames_per_lane"] == 1                  # IQ, B % 16 == 0: LDS-staged, 1 frame per lane
     assert pl.info["lanes_per_voxel"] == 16
     assert pl.info["N"] == 32
     assert pl.permuted_bytes(1) == 64 * 1 * 8 * 32 * 8
@@ -125,7 +125,8 @@ def test_plan_info_and_sizes():
     assert pl.permuted_shape(1) == (64, 1, 8, 32, 2)
     pl2 = das.Plan(**_problem(algorithm="default"))
     assert pl2.info["algorithm"] == das.ALG_BASELINE       # DEFAULT dispatches to the baseline
-    assert pl.info["staged"] == 0                           # IQ: direct-load kernel
+    assert pl.info["staged"] == 1
+    assert das.Plan(**_problem(B=40, dtype="c64", f_demod=5e6)).info["staged"] == 0   # IQ, B % 16 != 0
     assert das.Plan(**_problem(B=32)).info["staged"] == 1      # fp32, B % 32 == 0: LDS-staged
     assert das.Plan(**_problem(B=16)).info["staged"] == 0
     assert das.Plan(**_problem(B=32, algorithm="baseline")).info["staged"] == 0
@@ -150,9 +151,12 @@ def test_frames_per_lane_choice_direct(B, fl, monkeypatch):
     assert pl.info["staged"] == 0
 
 
-@pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (31, 1), (32, 2), (40, 2), (64, 2)])
+@pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (31, 1), (32, 1), (40, 2), (64, 1), (34, 2)])
 def test_frames_per_lane_choice_iq(B, fl):
-    assert das.Plan(**_problem(B=B, dtype="c64", f_demod=5e6)).info["frames_per_lane"] == fl
+    # complex64 batch-inner: the LDS-staged kernel (1 frame per lane) wherever B % 16 == 0
+    pl = das.Plan(**_problem(B=B, dtype="c64", f_demod=5e6))
+    assert pl.info["frames_per_lane"] == fl
+    assert pl.info["staged"] == (1 if B % 16 == 0 else 0)
 
 
 def test_error_strings(lib):

@@ -93,30 +93,33 @@ def test_q_chunks_sum_to_the_whole(gpu, alg, layout):
     assert_parity(y, oracle_ref(inp), f"q chunks {alg}/{layout}")
 
 
+@pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])
 @pytest.mark.parametrize("layout", ["kqmb", "qmkb"])
 @pytest.mark.parametrize("voxel", [0.25e-3, 0.6e-3, 1.5e-3], ids=["fine", "mixed", "coarse"])
-def test_staged_windows_and_fallback(gpu, layout, voxel):
-    """fp32, B = 32: the LDS-staged kernel.  Coarse voxels give k-windows wider
-    than the LDS capacity, which must fall back to direct loads; fine voxels
-    stay in LDS; the mixed pitch exercises both within one launch."""
+def test_staged_windows_and_fallback(gpu, layout, voxel, iq):
+    """B = 32: the LDS-staged kernel (fp32: 2 frames per lane, one 32-frame
+    tile; complex64: 1 frame per lane, two 16-frame tiles).  Coarse voxels give
+    k-windows wider than the LDS capacity, which must fall back to direct loads;
+    fine voxels stay in LDS; the mixed pitch exercises both within one launch."""
     cfg = das_synth.custom_config("tiny", name="staged", seed=23, array=(19, 3), grid=(11, 10, 3), K=700, B=32,
                                   tx="diverging", sources=((0.0, 0.0), (2e-3, 1e-3)), voxel=voxel,
-                                  z0=3e-3, n_scatterers=0)
+                                  z0=3e-3, n_scatterers=0, iq=iq)
     inp = Inputs(cfg, w_tx="uniform")
     plan_info = __import__("volumetric_delay_sum_amd").plan_from_fields(inp.fields, "batch_inner", layout).info
     assert plan_info["staged"] == 1
-    y = to_numpy(run_gpu(inp, "batch_inner", layout), False)
-    assert_parity(y, oracle_ref(inp), f"staged {layout} voxel {voxel}")
+    y = to_numpy(run_gpu(inp, "batch_inner", layout), iq)
+    assert_parity(y, oracle_ref(inp), f"staged {layout} voxel {voxel} iq={iq}")
 
 
-def test_staged_and_direct_kernels_agree(gpu, monkeypatch):
-    cfg = _ragged(B=64 // 2, grid=(17, 9, 2))
+@pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])
+def test_staged_and_direct_kernels_agree(gpu, monkeypatch, iq):
+    cfg = _ragged(B=32, grid=(17, 9, 2), iq=iq)
     inp = Inputs(cfg, w_tx="uniform")
-    staged = to_numpy(run_gpu(inp, "batch_inner", "kqmb"), False)
+    staged = to_numpy(run_gpu(inp, "batch_inner", "kqmb"), iq)
     monkeypatch.setenv("DAS_BI_KERNEL", "direct")
     import volumetric_delay_sum_amd as das
     assert das.plan_from_fields(inp.fields, "batch_inner", "kqmb").info["staged"] == 0
-    direct = to_numpy(run_gpu(inp, "batch_inner", "kqmb"), False)
+    direct = to_numpy(run_gpu(inp, "batch_inner", "kqmb"), iq)
     ref = oracle_ref(inp)
     assert_parity(staged, ref, "staged")
     assert_parity(direct, ref, "direct")

@@ -201,13 +201,16 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
     pl->elem_bytes = elem;
     pl->fl = pick_fl(p.B, p.dtype);
     pl->bt = 8;
-    // LDS-staged batch-inner kernel where it is built (fp32, B a multiple of
-    // 32, two frames per lane: larger B runs as several 32-frame tiles);
+    // LDS-staged batch-inner kernel where it is built (fp32 with B a multiple
+    // of 32, two frames per lane, or complex64 with B a multiple of 16, one
+    // frame per lane; larger B runs as several frame tiles);
     // DAS_BI_KERNEL=direct selects the direct-load kernel (comparisons).
     const char *kv = std::getenv("DAS_BI_KERNEL");
     const bool want_staged = pl->alg == DAS_ALG_BATCH_INNER && !(kv && std::strcmp(kv, "direct") == 0);
     if (want_staged && p.dtype == DAS_F32 && p.B % 32 == 0)
         pl->fl = 2;
+    if (want_staged && p.dtype == DAS_C64 && p.B % 16 == 0)
+        pl->fl = 1;
     pl->staged = (want_staged && das_staged_supported(*pl)) ? 1 : 0;
     pl->q_group = pick_q_group(p, elem, pl->staged != 0);
     const char *vv = std::getenv("DAS_STAGED_VPR");

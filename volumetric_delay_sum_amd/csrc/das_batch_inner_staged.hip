@@ -316,9 +316,10 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     // with the receiver's coefficients broadcast from its lane.  The reads are
     // issued DEPTH items ahead; the scheduling fences keep the compiler from
     // sinking each read next to its use, which would leave one read in flight
-    // per wave.  `at(t)` runs after item t (the next step's copy rounds).
+    // per wave (three ahead measured best with two voxels per row, eight with
+    // one).  `at(t)` runs after item t (the next step's copy rounds).
     constexpr int NITEM = VPR * ROW;
-    constexpr int DEPTH = (VPR == 1) ? 8 : 6;
+    constexpr int DEPTH = (VPR == 1) ? 8 : 3;
     auto compute_lds = [&](const Step (&s)[VPR], const uint32_t (&loff)[VPR], float (&pt)[VPR][NF], auto &&at) {
         float a[VPR], b[VPR], ai[VPR], bi[VPR];
 #pragma unroll
@@ -459,9 +460,11 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
                 load_geometry(nxt2.m0);
 #pragma unroll
             for (int v = 0; v < VPR; ++v) s_nxt2[v] = make_step<IQ>(P, R[v], tx_nxt2[v]);
+            publish(s_nxt2, set2);
+            // after the window's LDS atomics: the compiler orders those behind
+            // every outstanding vector load (the row copies write LDS)
             if (has_next3)
                 load_tx(nxt3, tx_nxt3);                  // consumed next iteration
-            publish(s_nxt2, set2);
         }
         // the rows of the next step stream into the other buffer while this step computes
         Window w_nxt{};
@@ -549,6 +552,11 @@ hipError_t launch(const das_plan_t &plan, const DasKParams &kp, const float *rf,
 template <int LAYOUT>
 hipError_t launch_vpr(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
                       const float *tau, const float *w, float *out, hipStream_t stream) {
+    // fp32: 2 frames per lane; complex64: 1 frame per lane.  Either way a lane
+    // holds 8 bytes of a sample row and a staged row is 128 bytes.
+    if (plan.p.dtype == DAS_C64)
+        return plan.vpr == 1 ? launch<true, 1, LAYOUT, 1>(plan, kp, rf, rx, tau, w, out, stream)
+                             : launch<true, 1, LAYOUT, 2>(plan, kp, rf, rx, tau, w, out, stream);
     if (plan.vpr == 1)
         return launch<false, 2, LAYOUT, 1>(plan, kp, rf, rx, tau, w, out, stream);
     return launch<false, 2, LAYOUT, 2>(plan, kp, rf, rx, tau, w, out, stream);
@@ -557,8 +565,10 @@ hipError_t launch_vpr(const das_plan_t &plan, const DasKParams &kp, const float 
 }  // namespace
 
 bool das_staged_supported(const das_plan_t &plan) {
-    // fp32 with 2 frames per lane (B a multiple of 32)
-    return plan.p.dtype == DAS_F32 && plan.fl == 2;
+    // 8 bytes of frames per lane: fp32 with 2 frames (B a multiple of 32) or
+    // complex64 with 1 (B a multiple of 16)
+    return (plan.p.dtype == DAS_F32 && plan.fl == 2 && plan.p.B % 32 == 0) ||
+           (plan.p.dtype == DAS_C64 && plan.fl == 1 && plan.p.B % 16 == 0);
 }
 
 hipError_t das_launch_batch_inner_staged(const das_plan_t &plan, const DasKParams &kp, const float *rf,
