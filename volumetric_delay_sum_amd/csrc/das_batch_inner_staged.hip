@@ -443,8 +443,16 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     __syncthreads();
 
     // ---- main loop ---------------------------------------------------------
+    // The pipeline state rotates with period 3 (sample splits of this step,
+    // the next and the one after) and 2 (transmit tables, windows), so the
+    // loop is unrolled six times with the roles passed as references: every
+    // role keeps its registers and no state is copied between steps.
     int set = 0, buf = 0;                              // slot set and row buffer of the current step
-    for (;;) {
+    Step s_spare[VPR];
+    Tx tx_spare[VPR];
+    Window w_spare{};
+    auto step = [&](Step (&sc)[VPR], Step (&sn)[VPR], Step (&sn2)[VPR], Tx (&t2)[VPR], Tx (&t3)[VPR], Window &wc,
+                    Window &wn) __attribute__((always_inline)) -> bool {
         __builtin_amdgcn_s_setprio(3);                 // every wave starts a step at the top priority
         const int set1 = (set == 2) ? 0 : set + 1, set2 = (set1 == 2) ? 0 : set1 + 1;
         // The step after next first: geometry, sample split, window.  It is
@@ -453,31 +461,29 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         // its compute last, alone, where only the pipelined LDS loop hides latency.
         Cursor nxt3 = nxt2;
         const bool has_next3 = has_next2 && advance(nxt3);
-        Step s_nxt2[VPR];
-        Tx tx_nxt3[VPR];
         if (has_next2) {
             if (nxt2.m0 != nxt.m0)
                 load_geometry(nxt2.m0);
 #pragma unroll
-            for (int v = 0; v < VPR; ++v) s_nxt2[v] = make_step<IQ>(P, R[v], tx_nxt2[v]);
-            publish(s_nxt2, set2);
+            for (int v = 0; v < VPR; ++v) sn2[v] = make_step<IQ>(P, R[v], t2[v]);
+            publish(sn2, set2);
             // after the window's LDS atomics: the compiler orders those behind
             // every outstanding vector load (the row copies write LDS)
             if (has_next3)
-                load_tx(nxt3, tx_nxt3);                  // consumed next iteration
+                load_tx(nxt3, t3);                       // consumed next step
         }
         // the rows of the next step stream into the other buffer while this step computes
-        Window w_nxt{};
+        wn = Window{};
         CopyPlan cp{0, 0, 0, 0};
         if (has_next) {
-            w_nxt = read_window(s_nxt, set1, buf ^ 1);
-            if (!w_nxt.overflow)
-                cp = copy_prepare(nxt, w_nxt, buf ^ 1);
+            wn = read_window(sn, set1, buf ^ 1);
+            if (!wn.overflow)
+                cp = copy_prepare(nxt, wn, buf ^ 1);
         }
-        if (!w_cur.overflow) {
+        if (!wc.overflow) {
             // copy round r after item r * SPREAD + SPREAD / 2
             constexpr int SPREAD = NITEM / G::MAXR;
-            compute_lds(s_cur, w_cur.loff, part, [&](auto T) {
+            compute_lds(sc, wc.loff, part, [&](auto T) {
                 constexpr int tt = decltype(T)::value;
                 if constexpr (tt % SPREAD == SPREAD / 2 && tt / SPREAD < G::MAXR)
                     copy_round(cp, tt / SPREAD);
@@ -486,7 +492,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
 #pragma unroll
             for (int r = 0; r < G::MAXR; ++r) copy_round(cp, r);
 #pragma unroll
-            for (int v = 0; v < VPR; ++v) compute_direct(s_cur[v], cur, part[v]);
+            for (int v = 0; v < VPR; ++v) compute_direct(sc[v], cur, part[v]);
         }
 
         if (tid < 2 * ROW)                              // this step's window was read last step
@@ -502,7 +508,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
                 }
         }
         if (!has_next)
-            break;
+            return false;
         __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0): this wave's copy has landed
         __syncthreads();                               // this step's rows read, the next step's in place,
                                                        // the window after it published
@@ -511,15 +517,23 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         nxt2 = nxt3;
         has_next = has_next2;
         has_next2 = has_next3;
-#pragma unroll
-        for (int v = 0; v < VPR; ++v) {
-            s_cur[v] = s_nxt[v];
-            s_nxt[v] = s_nxt2[v];
-            tx_nxt2[v] = tx_nxt3[v];
-        }
-        w_cur = w_nxt;
         set = set1;
         buf ^= 1;
+        return true;
+    };
+    for (;;) {
+        if (!step(s_cur, s_nxt, s_spare, tx_nxt2, tx_spare, w_cur, w_spare))
+            break;
+        if (!step(s_nxt, s_spare, s_cur, tx_spare, tx_nxt2, w_spare, w_cur))
+            break;
+        if (!step(s_spare, s_cur, s_nxt, tx_nxt2, tx_spare, w_cur, w_spare))
+            break;
+        if (!step(s_cur, s_nxt, s_spare, tx_spare, tx_nxt2, w_spare, w_cur))
+            break;
+        if (!step(s_nxt, s_spare, s_cur, tx_nxt2, tx_spare, w_cur, w_spare))
+            break;
+        if (!step(s_spare, s_cur, s_nxt, tx_spare, tx_nxt2, w_spare, w_cur))
+            break;
     }
 
     if (fr_ok) {
