@@ -254,19 +254,27 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         int kmin_w, rows_w;    // wave's copy: first sample row, number of sample rows
         bool overflow;
     };
-    auto read_window = [&](const Step (&s)[VPR], int set, int buf) -> Window {
+    struct Slots {
+        int kmn, kmx, kmn_w, kmx_w;    // window of receiver li, and of this wave's receiver
+    };
+    auto read_slots = [&](int set) -> Slots {
+        return Slots{slots[set * 2 * ROW + li], slots[set * 2 * ROW + ROW + li], slots[set * 2 * ROW + wave],
+                     slots[set * 2 * ROW + ROW + wave]};
+    };
+    auto make_window = [&](const Step (&s)[VPR], const Slots &sl, int buf) -> Window {
         Window wdw;
-        const int kmn = slots[set * 2 * ROW + li], kmx = slots[set * 2 * ROW + ROW + li];
-        const int np = (kmn <= kmx) ? kmx - kmn + 1 : 0;            // k positions of receiver li
+        const int np = (sl.kmn <= sl.kmx) ? sl.kmx - sl.kmn + 1 : 0;   // k positions of receiver li
         const uint32_t base = (uint32_t)(buf * G::BUF + li * G::REGION);
 #pragma unroll
         for (int v = 0; v < VPR; ++v)
-            wdw.loff[v] = s[v].active ? base + (uint32_t)((int)s[v].k - kmn) * G::ROWB : base;
+            wdw.loff[v] = s[v].active ? base + (uint32_t)((int)s[v].k - sl.kmn) * G::ROWB : base;
         wdw.overflow = __any(np > G::W_MAX);
-        const int kmn_w = slots[set * 2 * ROW + wave], kmx_w = slots[set * 2 * ROW + ROW + wave];
-        wdw.kmin_w = kmn_w;
-        wdw.rows_w = (kmn_w <= kmx_w) ? kmx_w - kmn_w + 2 : 0;      // sample rows kmin .. kmax + 1
+        wdw.kmin_w = sl.kmn_w;
+        wdw.rows_w = (sl.kmn_w <= sl.kmx_w) ? sl.kmx_w - sl.kmn_w + 2 : 0;   // sample rows kmin .. kmax + 1
         return wdw;
+    };
+    auto read_window = [&](const Step (&s)[VPR], int set, int buf) -> Window {
+        return make_window(s, read_slots(set), buf);
     };
 
     // Copy of one receiver's sample rows by LDS-DMA (wave w copies receiver
@@ -459,6 +467,10 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         // latency-bound ALU work, done while all four waves of a SIMD are
         // active; a SIMD runs its waves in age order, so the youngest finishes
         // its compute last, alone, where only the pipelined LDS loop hides latency.
+        // the next step's window slots are read first: their latency hides behind the setup
+        Slots sl{0, 0, 0, 0};
+        if (has_next)
+            sl = read_slots(set1);
         Cursor nxt3 = nxt2;
         const bool has_next3 = has_next2 && advance(nxt3);
         if (has_next2) {
@@ -476,7 +488,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         wn = Window{};
         CopyPlan cp{0, 0, 0, 0};
         if (has_next) {
-            wn = read_window(sn, set1, buf ^ 1);
+            wn = make_window(sn, sl, buf ^ 1);
             if (!wn.overflow)
                 cp = copy_prepare(nxt, wn, buf ^ 1);
         }
