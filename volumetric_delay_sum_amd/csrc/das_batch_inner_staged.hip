@@ -493,8 +493,9 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
                 cp = copy_prepare(nxt, wn, buf ^ 1);
         }
         if (!wc.overflow) {
-            // copy round r after item r * SPREAD + SPREAD / 2
-            constexpr int SPREAD = NITEM / G::MAXR;
+            // copy round r after item 2 r + 1: early, so the rows have the rest
+            // of the loop to land, yet not all at once
+            constexpr int SPREAD = 2;
             compute_lds(sc, wc.loff, part, [&](auto T) {
                 constexpr int tt = decltype(T)::value;
                 if constexpr (tt % SPREAD == SPREAD / 2 && tt / SPREAD < G::MAXR)
