@@ -328,7 +328,23 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     // one).  `at(t)` runs after item t (the next step's copy rounds).
     constexpr int NITEM = VPR * ROW;
     constexpr int DEPTH = (VPR == 1) ? 8 : 3;
-    auto compute_lds = [&](const Step (&s)[VPR], const uint32_t (&loff)[VPR], float (&pt)[VPR][NF], auto &&at) {
+    // The first DEPTH items' reads are issued by prefetch(), at the top of the
+    // step, so they land while the setup runs.
+    struct Ring {
+        TapV r0[DEPTH], r1[DEPTH];
+    };
+    auto issue_item = [&](auto T, const uint32_t (&loff)[VPR], Ring &ring) {
+        constexpr int tt = decltype(T)::value;
+        constexpr int v = tt / ROW, j = tt % ROW;
+        const uint32_t addr = das::row_bcast<j>(loff[v]) + laneoff_l;
+        ring.r0[tt % DEPTH] = *reinterpret_cast<const TapV *>(lds + addr);
+        ring.r1[tt % DEPTH] = *reinterpret_cast<const TapV *>(lds + addr + G::ROWB);
+    };
+    auto prefetch = [&](const uint32_t (&loff)[VPR], Ring &ring) {
+        das::unroll<DEPTH>([&](auto T) { issue_item(T, loff, ring); });
+    };
+    auto compute_lds = [&](const Step (&s)[VPR], const uint32_t (&loff)[VPR], float (&pt)[VPR][NF], Ring &ring,
+                           auto &&at) {
         float a[VPR], b[VPR], ai[VPR], bi[VPR];
 #pragma unroll
         for (int v = 0; v < VPR; ++v) {
@@ -341,15 +357,9 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             else
                 das::settle(a[v], b[v]);
         }
-        TapV ring0[DEPTH], ring1[DEPTH];
-        auto issue = [&](auto T) {
-            constexpr int tt = decltype(T)::value;
-            constexpr int v = tt / ROW, j = tt % ROW;
-            const uint32_t addr = das::row_bcast<j>(loff[v]) + laneoff_l;
-            ring0[tt % DEPTH] = *reinterpret_cast<const TapV *>(lds + addr);
-            ring1[tt % DEPTH] = *reinterpret_cast<const TapV *>(lds + addr + G::ROWB);
-        };
-        das::unroll<DEPTH>([&](auto T) { issue(T); });
+        auto &ring0 = ring.r0;
+        auto &ring1 = ring.r1;
+        auto issue = [&](auto T) { issue_item(T, loff, ring); };
         __builtin_amdgcn_sched_barrier(0);
         das::unroll<NITEM>([&](auto T) {
             constexpr int tt = decltype(T)::value;
@@ -463,6 +473,10 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
                     Window &wn) __attribute__((always_inline)) -> bool {
         __builtin_amdgcn_s_setprio(3);                 // every wave starts a step at the top priority
         const int set1 = (set == 2) ? 0 : set + 1, set2 = (set1 == 2) ? 0 : set1 + 1;
+        Ring ring;
+        if (!wc.overflow)
+            prefetch(wc.loff, ring);
+        __builtin_amdgcn_sched_barrier(0);
         // The step after next first: geometry, sample split, window.  It is
         // latency-bound ALU work, done while all four waves of a SIMD are
         // active; a SIMD runs its waves in age order, so the youngest finishes
@@ -496,7 +510,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             // copy round r after item 2 r + 1: early, so the rows have the rest
             // of the loop to land, yet not all at once
             constexpr int SPREAD = 2;
-            compute_lds(sc, wc.loff, part, [&](auto T) {
+            compute_lds(sc, wc.loff, part, ring, [&](auto T) {
                 constexpr int tt = decltype(T)::value;
                 if constexpr (tt % SPREAD == SPREAD / 2 && tt / SPREAD < G::MAXR)
                     copy_round(cp, tt / SPREAD);
