@@ -328,8 +328,8 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     // one).  `at(t)` runs after item t (the next step's copy rounds).
     constexpr int NITEM = VPR * ROW;
     constexpr int DEPTH = (VPR == 1) ? 8 : 3;
-    // The first DEPTH items' reads are issued by prefetch(), at the top of the
-    // step, so they land while the setup runs.
+    // The first DEPTH items' reads are issued by prefetch(), for fp32 data at
+    // the top of the step, so they land while the setup runs.
     struct Ring {
         TapV r0[DEPTH], r1[DEPTH];
     };
@@ -474,9 +474,11 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         __builtin_amdgcn_s_setprio(3);                 // every wave starts a step at the top priority
         const int set1 = (set == 2) ? 0 : set + 1, set2 = (set1 == 2) ? 0 : set1 + 1;
         Ring ring;
-        if (!wc.overflow)
-            prefetch(wc.loff, ring);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!IQ) {                           // (complex data: registers are too tight)
+            if (!wc.overflow)
+                prefetch(wc.loff, ring);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         // The step after next first: geometry, sample split, window.  It is
         // latency-bound ALU work, done while all four waves of a SIMD are
         // active; a SIMD runs its waves in age order, so the youngest finishes
@@ -510,6 +512,8 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             // copy round r after item 2 r + 1: early, so the rows have the rest
             // of the loop to land, yet not all at once
             constexpr int SPREAD = 2;
+            if constexpr (IQ)
+                prefetch(wc.loff, ring);
             compute_lds(sc, wc.loff, part, ring, [&](auto T) {
                 constexpr int tt = decltype(T)::value;
                 if constexpr (tt % SPREAD == SPREAD / 2 && tt / SPREAD < G::MAXR)
