@@ -181,17 +181,26 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     // ---- step helpers ---------------------------------------------------
     das::RxTerm R[VPR];                  // receive terms of (voxel v, m0 + li) for the current block
     auto load_geometry = [&](int m0) {
+        // The grid and receive parameters are read afresh from the kernel
+        // arguments (an opaque pointer, so the loads stay here): held across
+        // the loop they would crowd the scalar registers for a use every
+        // few steps.
+        const __attribute__((address_space(4))) char *ka =
+            (const __attribute__((address_space(4))) char *)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(ka));
+        const DasKParams &Pg = *(const DasKParams *)ka;
+        const float *rxg = *(const float *const *)(ka + sizeof(DasKParams) + sizeof(void *));
         const int mm = m0 + li;
-        const int m = min(mm, P.M - 1);
-        const float px = rx[3 * m], py = rx[3 * m + 1], pz = rx[3 * m + 2];
+        const int m = min(mm, Pg.M - 1);
+        const float px = rxg[3 * m], py = rxg[3 * m + 1], pz = rxg[3 * m + 2];
 #pragma unroll
         for (int v = 0; v < VPR; ++v) {
             // voxel centres are recomputed per receiver block rather than kept in registers
             double vx, vy, vz;
-            das::voxel_centre(P, ix, iy, min(tz * VPR + v, P.nz - 1), vx, vy, vz);
-            R[v] = das::rx_term<IQ>(P, vx, vy, vz, px, py, pz);
-            R[v].s_rx -= P.t0fs;
-            R[v].w = (mm < P.M) ? R[v].w : 0.0f;
+            das::voxel_centre(Pg, ix, iy, min(tz * VPR + v, Pg.nz - 1), vx, vy, vz);
+            R[v] = das::rx_term<IQ>(Pg, vx, vy, vz, px, py, pz);
+            R[v].s_rx -= Pg.t0fs;
+            R[v].w = (mm < Pg.M) ? R[v].w : 0.0f;
         }
     };
     // Transmit tables of the voxels, read two steps ahead through buffer loads
@@ -469,8 +478,12 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     Step s_spare[VPR];
     Tx tx_spare[VPR];
     Window w_spare{};
-    auto step = [&](Step (&sc)[VPR], Step (&sn)[VPR], Step (&sn2)[VPR], Tx (&t2)[VPR], Tx (&t3)[VPR], Window &wc,
-                    Window &wn) __attribute__((always_inline)) -> bool {
+    // `Last` false: the caller guarantees a next step (has_next), so the step
+    // has no exit.
+    auto step = [&](auto Last, Step (&sc)[VPR], Step (&sn)[VPR], Step (&sn2)[VPR], Tx (&t2)[VPR], Tx (&t3)[VPR],
+                    Window &wc, Window &wn) __attribute__((always_inline)) -> bool {
+        constexpr bool can_end = decltype(Last)::value;
+        const bool hn = can_end ? has_next : true;
         __builtin_amdgcn_s_setprio(3);                 // every wave starts a step at the top priority
         const int set1 = (set == 2) ? 0 : set + 1, set2 = (set1 == 2) ? 0 : set1 + 1;
         Ring ring;
@@ -485,7 +498,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         // its compute last, alone, where only the pipelined LDS loop hides latency.
         // the next step's window slots are read first: their latency hides behind the setup
         Slots sl{0, 0, 0, 0};
-        if (has_next)
+        if (hn)
             sl = read_slots(set1);
         Cursor nxt3 = nxt2;
         const bool has_next3 = has_next2 && advance(nxt3);
@@ -503,7 +516,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         // the rows of the next step stream into the other buffer while this step computes
         wn = Window{};
         CopyPlan cp{0, 0, 0, 0};
-        if (has_next) {
+        if (hn) {
             wn = make_window(sn, sl, buf ^ 1);
             if (!wn.overflow)
                 cp = copy_prepare(nxt, wn, buf ^ 1);
@@ -529,7 +542,15 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         if (tid < 2 * ROW)                              // this step's window was read last step
             slots[set * 2 * ROW + tid] = (tid < ROW) ? INT_MAX : INT_MIN;
 
-        if (!has_next || nxt.m0 != cur.m0 || nxt.g0 != cur.g0) {
+        const bool flush = !hn || nxt.m0 != cur.m0 || nxt.g0 != cur.g0;
+        cur = nxt;
+        nxt = nxt2;
+        nxt2 = nxt3;
+        has_next = has_next2;
+        has_next2 = has_next3;
+        set = set1;
+        buf ^= 1;
+        if (flush) {
 #pragma unroll
             for (int v = 0; v < VPR; ++v)
 #pragma unroll
@@ -538,33 +559,41 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
                     part[v][i] = 0.0f;
                 }
         }
-        if (!has_next)
+        if (!hn)
             return false;
         __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0): this wave's copy has landed
         __syncthreads();                               // this step's rows read, the next step's in place,
                                                        // the window after it published
-        cur = nxt;
-        nxt = nxt2;
-        nxt2 = nxt3;
-        has_next = has_next2;
-        has_next2 = has_next3;
-        set = set1;
-        buf ^= 1;
         return true;
     };
-    for (;;) {
-        if (!step(s_cur, s_nxt, s_spare, tx_nxt2, tx_spare, w_cur, w_spare))
-            break;
-        if (!step(s_nxt, s_spare, s_cur, tx_spare, tx_nxt2, w_spare, w_cur))
-            break;
-        if (!step(s_spare, s_cur, s_nxt, tx_nxt2, tx_spare, w_cur, w_spare))
-            break;
-        if (!step(s_cur, s_nxt, s_spare, tx_spare, tx_nxt2, w_spare, w_cur))
-            break;
-        if (!step(s_nxt, s_spare, s_cur, tx_nxt2, tx_spare, w_cur, w_spare))
-            break;
-        if (!step(s_spare, s_cur, s_nxt, tx_spare, tx_nxt2, w_spare, w_cur))
-            break;
+    // Six steps with no exit while at least seven remain (an exit inside the
+    // body would make the compiler carry undefined values through a join
+    // block and copy them lane by lane every step), then the last steps one
+    // at a time with the roles copied.
+    using das::ic;
+    const int nsteps = P.q_count * ((P.M + ROW - 1) / ROW);
+    for (int left = nsteps; left >= 7; left -= 6) {
+        step(ic<0>{}, s_cur, s_nxt, s_spare, tx_nxt2, tx_spare, w_cur, w_spare);
+        step(ic<0>{}, s_nxt, s_spare, s_cur, tx_spare, tx_nxt2, w_spare, w_cur);
+        step(ic<0>{}, s_spare, s_cur, s_nxt, tx_nxt2, tx_spare, w_cur, w_spare);
+        step(ic<0>{}, s_cur, s_nxt, s_spare, tx_spare, tx_nxt2, w_spare, w_cur);
+        step(ic<0>{}, s_nxt, s_spare, s_cur, tx_nxt2, tx_spare, w_cur, w_spare);
+        step(ic<0>{}, s_spare, s_cur, s_nxt, tx_spare, tx_nxt2, w_spare, w_cur);
+    }
+    while (step(ic<1>{}, s_cur, s_nxt, s_spare, tx_nxt2, tx_spare, w_cur, w_spare)) {
+#pragma unroll
+        for (int v = 0; v < VPR; ++v) {
+            const Step st = s_cur[v];
+            s_cur[v] = s_nxt[v];
+            s_nxt[v] = s_spare[v];
+            s_spare[v] = st;
+            const Tx tt = tx_nxt2[v];
+            tx_nxt2[v] = tx_spare[v];
+            tx_spare[v] = tt;
+        }
+        const Window wt = w_cur;
+        w_cur = w_spare;
+        w_spare = wt;
     }
 
     if (fr_ok) {
