@@ -214,32 +214,17 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             txv[v] = Tx{das::buffer_load_f32(rs_tau, n[v] * 4, (int)qoff, 0),
                         das::buffer_load_f32(rs_wtx, n[v] * 4, (int)qoff, 0)};
     };
-    // Publish the lanes' k to the window of their receiver: min/max over the
-    // row's voxels and the wave's four rows (gfx950 row swaps: lanes l and
-    // l +- 32, then rows 2r and 2r + 1), then one LDS atomic per wave and receiver.
+    // Publish the lanes' k to the window of their receiver: one LDS atomic
+    // min and max per active (voxel, receiver), four rows of a wave meeting
+    // on each receiver's slot.  The LDS has room for the conflicts; reducing
+    // across rows first would cost more ALU than the atomics save.
     auto publish = [&](const Step (&s)[VPR], int set) {
-        int kmn = INT_MAX, kmx = INT_MIN;
 #pragma unroll
-        for (int v = 0; v < VPR; ++v) {
-            kmn = min(kmn, s[v].active ? (int)s[v].k : INT_MAX);
-            kmx = max(kmx, s[v].active ? (int)s[v].k : INT_MIN);
-        }
-        {
-            const auto a = __builtin_amdgcn_permlane32_swap(kmn, kmn, false, false);
-            const auto b = __builtin_amdgcn_permlane32_swap(kmx, kmx, false, false);
-            kmn = min((int)a[0], (int)a[1]);
-            kmx = max((int)b[0], (int)b[1]);
-        }
-        {
-            const auto a = __builtin_amdgcn_permlane16_swap(kmn, kmn, false, false);
-            const auto b = __builtin_amdgcn_permlane16_swap(kmx, kmx, false, false);
-            kmn = min((int)a[0], (int)a[1]);
-            kmx = max((int)b[0], (int)b[1]);
-        }
-        if (lane < ROW && kmn != INT_MAX) {
-            atomicMin(&slots[set * 2 * ROW + li], kmn);
-            atomicMax(&slots[set * 2 * ROW + ROW + li], kmx);
-        }
+        for (int v = 0; v < VPR; ++v)
+            if (s[v].active) {
+                atomicMin(&slots[set * 2 * ROW + li], (int)s[v].k);
+                atomicMax(&slots[set * 2 * ROW + ROW + li], (int)s[v].k);
+            }
     };
     auto advance = [&](Cursor &c) -> bool {
         if (++c.ql < c.g1)
