@@ -179,17 +179,26 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     __syncthreads();
 
     // ---- step helpers ---------------------------------------------------
+    // Rarely used launch parameters are read afresh from the kernel arguments
+    // where they are needed, through an opaque pointer so the loads stay
+    // there: held across the loop they would crowd the scalar registers and
+    // spill into vector lanes.  The arguments are (P, rfp, rx, tau_tx, w_tx,
+    // out, tap_stride) in that order.
+    using kptr = const __attribute__((address_space(4))) char *;
+    auto kargs = [&]() -> kptr {
+        kptr ka = (kptr)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(ka));
+        return ka;
+    };
+    auto karg_ptr = [&](kptr ka, int i) -> const char * {   // pointer argument i (0: rfp)
+        return *(const char *const *)(ka + sizeof(DasKParams) + i * sizeof(void *));
+    };
+
     das::RxTerm R[VPR];                  // receive terms of (voxel v, m0 + li) for the current block
     auto load_geometry = [&](int m0) {
-        // The grid and receive parameters are read afresh from the kernel
-        // arguments (an opaque pointer, so the loads stay here): held across
-        // the loop they would crowd the scalar registers for a use every
-        // few steps.
-        const __attribute__((address_space(4))) char *ka =
-            (const __attribute__((address_space(4))) char *)__builtin_amdgcn_kernarg_segment_ptr();
-        asm volatile("" : "+s"(ka));
+        const kptr ka = kargs();
         const DasKParams &Pg = *(const DasKParams *)ka;
-        const float *rxg = *(const float *const *)(ka + sizeof(DasKParams) + sizeof(void *));
+        const float *rxg = reinterpret_cast<const float *>(karg_ptr(ka, 1));
         const int mm = m0 + li;
         const int m = min(mm, Pg.M - 1);
         const float px = rxg[3 * m], py = rxg[3 * m + 1], pz = rxg[3 * m + 2];
@@ -204,11 +213,26 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         }
     };
     // Transmit tables of the voxels, read two steps ahead through buffer loads
-    // (event offset in the scalar offset, voxel in the lane offset).
-    const das::BufRsrc rs_tau = das::make_rsrc(reinterpret_cast<const char *>(tau_tx), (uint64_t)P.Q * P.N * 4);
-    const das::BufRsrc rs_wtx = das::make_rsrc(reinterpret_cast<const char *>(w_tx), (uint64_t)P.Q * P.N * 4);
+    // (event offset in the scalar offset, voxel in the lane offset).  Complex
+    // data rebuilds the two buffer descriptors at each call (its registers
+    // are the tighter; measured faster there), real data keeps them: the
+    // reload's scalar-load wait would also wait for the window atomics.
+    const uint64_t tbytes = (uint64_t)P.Q * P.N * 4;
+    const das::BufRsrc rs_tau0 = das::make_rsrc(reinterpret_cast<const char *>(tau_tx), tbytes);
+    const das::BufRsrc rs_wtx0 = das::make_rsrc(reinterpret_cast<const char *>(w_tx), tbytes);
     auto load_tx = [&](const Cursor &c, Tx (&txv)[VPR]) {
-        const uint32_t qoff = (uint32_t)(P.q_begin + c.ql) * (uint32_t)P.N * 4u;   // the launch keeps Q N 4 < 2^32
+        das::BufRsrc rs_tau = rs_tau0, rs_wtx = rs_wtx0;
+        uint32_t q_begin = (uint32_t)P.q_begin, nvox = (uint32_t)P.N;
+        if constexpr (IQ) {
+            const kptr ka = kargs();
+            const DasKParams &Pt = *(const DasKParams *)ka;
+            const uint64_t tb = (uint64_t)Pt.Q * Pt.N * 4;
+            rs_tau = das::make_rsrc(karg_ptr(ka, 2), tb);
+            rs_wtx = das::make_rsrc(karg_ptr(ka, 3), tb);
+            q_begin = (uint32_t)Pt.q_begin;
+            nvox = (uint32_t)Pt.N;
+        }
+        const uint32_t qoff = (q_begin + (uint32_t)c.ql) * nvox * 4u;   // the launch keeps Q N 4 < 2^32
 #pragma unroll
         for (int v = 0; v < VPR; ++v)
             txv[v] = Tx{das::buffer_load_f32(rs_tau, n[v] * 4, (int)qoff, 0),
