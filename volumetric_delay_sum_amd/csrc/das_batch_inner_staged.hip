@@ -531,9 +531,9 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
                 cp = copy_prepare(nxt, wn, buf ^ 1);
         }
         if (!wc.overflow) {
-            // copy round r after item 2 r + 1: early, so the rows have the rest
+            // copy round r after item 4 r + 2: early, so the rows have the rest
             // of the loop to land, yet not all at once
-            constexpr int SPREAD = 2;
+            constexpr int SPREAD = 4;
             if constexpr (IQ)
                 prefetch(wc.loff, ring);
             compute_lds(sc, wc.loff, part, ring, [&](auto T) {
