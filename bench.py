@@ -167,6 +167,29 @@ def main():
         streamed_desc = ", streamed: permute of chunk c+1 on a second stream overlaps beamform of chunk c"
         print(f"[bench] streamed: {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
+    # the transmit-table generator on this workload's events (not part of a
+    # step: the tables are inputs); HBM-write bound, 8 bytes per (event, voxel)
+    if cfg.tx == "plane":
+        tx_events = [(das.TX_PLANE, (0.0, 0.0, 1.0), 1.0)] * cfg.Q
+    else:
+        tx_events = [(das.TX_DIVERGING, (vx, vy, -cfg.src_depth), 1.0) for vx, vy in cfg.sources]
+    tau_g, w_g = torch.empty_like(tau_d), torch.empty_like(w_d)
+    plan.tx_tables(tx_events, tau_g, w_g, stream=stream)
+    tx_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+    for a, b in tx_ev:
+        a.record(stream)
+        plan.tx_tables(tx_events, tau_g, w_g, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    tx_ms = float(np.median([a.elapsed_time(b) for a, b in tx_ev]))
+    tx_bytes = 8 * cfg.Q * cfg.N
+    tx_tables = {"ms": tx_ms, "bytes": tx_bytes, "GB_s": tx_bytes / (tx_ms * 1e-3) / 1e9,
+                 "hbm_frac": tx_bytes / (tx_ms * 1e-3) / 1e9 / 8000.0,
+                 "launches": (cfg.Q + 15) // 16,
+                 "matches_host_tables": bool(torch.equal(w_g, w_d)) and
+                 int((tau_g.view(torch.int32) - tau_d.view(torch.int32)).abs().max().item()) <= 1}
+    del tau_g, w_g
+
     accs = das_synth.accumulations(cfg)
     ms_step = wall * 1e3 / args.steps
     value = accs / (ms_step * 1e-3) / 1e9
@@ -247,6 +270,7 @@ def main():
             "flops_per_accumulation": flops_per_acc,
         },
         "permute_ms": perm_avg if bi else None,
+        "tx_tables": tx_tables,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

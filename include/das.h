@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DAS_ABI_VERSION 2
+#define DAS_ABI_VERSION 3
 
 typedef enum das_status {
     DAS_OK = 0,
@@ -189,6 +189,39 @@ das_status das_beamform_streamed(const das_plan_t *plan, const void *rf_bqmk, co
                                  const float *tau_tx, const float *w_tx, void *out, void *perm_a,
                                  void *perm_b, int32_t q_chunk, int32_t accumulate,
                                  void *stream_permute, void *stream_beamform);
+
+/* Kinds of transmit event for das_tx_tables. */
+enum { DAS_TX_PLANE = 0, DAS_TX_DIVERGING = 1 };
+
+typedef struct das_tx_event {
+    int32_t kind;        /* DAS_TX_PLANE | DAS_TX_DIVERGING                          */
+    int32_t reserved;    /* must be 0                                                */
+    double  v[3];        /* PLANE: unit propagation direction, v[2] > 0;
+                            DIVERGING: virtual source position, metres, v[2] < 0     */
+    double  weight;      /* finite value written to w_tx for every voxel of the event */
+} das_tx_event;
+
+/* Fill rows [q_begin, q_begin + q_count) of the per-voxel transmit tables on
+ * the GPU ("ffdas: volumetric ultrasound reconstruction at warp speed",
+ * Section 3, baseline paragraph: transmit delays and weights are tables
+ * precomputed per voxel, the input das_beamform reads).  For voxel centre r_n
+ * of the plan's grid and event e = events[q - q_begin]:
+ *   PLANE      tau_tx[q,n] = (v . r_n) / c              (zero where the front
+ *                                                         crosses the origin)
+ *   DIVERGING  tau_tx[q,n] = (|r_n - v| - |v_z|) / c     (zero where the front
+ *                                                         crosses z = 0 under
+ *                                                         the source)
+ *   w_tx[q,n]  = e.weight
+ * evaluated in fp64 without fused operations (each product, sum, square root
+ * and quotient rounded once) and rounded once to float32.
+ *   events        host array of q_count entries
+ *   tau_tx, w_tx  Q x N float32 device buffers (all Q); other rows untouched
+ * Errors: DAS_ERR_INVALID_ARGUMENT (null pointer, bad q range, unknown kind,
+ * reserved != 0, non-finite values, a plane direction that is not a unit
+ * vector within 1e-9 or has v[2] <= 0, a diverging source with v[2] >= 0);
+ * DAS_ERR_ALIGNMENT; DAS_ERR_NO_DEVICE; DAS_ERR_LAUNCH. */
+das_status das_tx_tables(const das_plan_t *plan, const das_tx_event *events, int32_t q_begin,
+                         int32_t q_count, float *tau_tx, float *w_tx, void *hip_stream);
 
 /* Static text for a status code (never NULL). */
 const char *das_error_string(int status);

@@ -131,3 +131,48 @@ def permute_qmkb(x: np.ndarray) -> np.ndarray:
     """B x Q x M x K (x 2 for IQ) -> Q x M x K x B (x 2): batch moved innermost."""
     axes = (1, 2, 3, 0) + ((4,) if x.ndim == 5 else ())
     return np.ascontiguousarray(np.transpose(x, axes))
+
+
+# Transmit-event kinds (the values of the library's enum, restated).
+TX_PLANE, TX_DIVERGING = 0, 1
+
+
+def tx_tables(fields: dict, events) -> tuple:
+    """Per-voxel transmit delays and weights of plane and diverging events.
+
+    "ffdas: volumetric ultrasound reconstruction at warp speed", Section 3,
+    baseline paragraph: the transmit delays and weights are tables computed
+    ahead per voxel.  A plane event with unit propagation direction u reaches
+    voxel centre r at (u . r) / c (time zero as the front crosses the origin);
+    a diverging event from a virtual source v (v_z < 0) at (|r - v| - |v_z|) / c
+    (time zero as the front crosses z = 0 under the source).  The weight is the
+    event's constant.  Plain fp64 numpy, every operation rounded on its own in
+    the order written, then one rounding to float32.
+
+    fields: nx, ny, nz, origin, spacing, c.  events: (kind, (vx, vy, vz), weight).
+    Returns (tau, w), each len(events) x N float32.
+    """
+    nx, ny, nz = int(fields["nx"]), int(fields["ny"]), int(fields["nz"])
+    origin = [float(v) for v in fields["origin"]]
+    spacing = [float(v) for v in fields["spacing"]]
+    c = float(fields["c"])
+    n = np.arange(nx * ny * nz, dtype=np.int64)
+    ix, iy, iz = n % nx, (n // nx) % ny, n // (nx * ny)
+    x = origin[0] + ix.astype(np.float64) * spacing[0]
+    y = origin[1] + iy.astype(np.float64) * spacing[1]
+    z = origin[2] + iz.astype(np.float64) * spacing[2]
+    tau = np.empty((len(events), n.size), dtype=np.float32)
+    w = np.empty((len(events), n.size), dtype=np.float32)
+    for e, (kind, v, weight) in enumerate(events):
+        vx, vy, vz = (float(a) for a in v)
+        if kind == TX_PLANE:
+            t = (vx * x + vy * y + vz * z) / c
+        elif kind == TX_DIVERGING:
+            dx, dy, dz = x - vx, y - vy, z - vz
+            t = (np.sqrt(dx * dx + dy * dy + dz * dz) - abs(vz)) / c
+        else:
+            raise ValueError(f"unknown transmit kind {kind}")
+        tau[e] = t.astype(np.float32)
+        w[e] = np.float32(weight)
+    return tau, w
+

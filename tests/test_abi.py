@@ -57,7 +57,8 @@ def _c_layout(struct, fields, tmp_path):
     return [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
 
 
-@pytest.mark.parametrize("cls,struct", [(das._Problem, "das_problem"), (das._PlanInfo, "das_plan_info")])
+@pytest.mark.parametrize("cls,struct", [(das._Problem, "das_problem"), (das._PlanInfo, "das_plan_info"),
+                                        (das._TxEvent, "das_tx_event")])
 def test_ctypes_mirrors_match_the_header(cls, struct, tmp_path):
     fields = [f for f, _ in cls._fields_]
     got = _c_layout(struct, fields, tmp_path)
@@ -225,6 +226,45 @@ def test_streamed_argument_errors(lib):
         assert lib.das_beamform_streamed(h, *args, 1, 0, None, None) == ALIGNMENT
     if not _gpu():
         assert lib.das_beamform_streamed(h, *ok, 1, 0, None, None) == NO_DEVICE
+
+
+def _tx_events(*specs):
+    arr = (das._TxEvent * len(specs))()
+    for i, (kind, v, weight) in enumerate(specs):
+        arr[i].kind, arr[i].reserved = kind, 0
+        arr[i].v[:] = v
+        arr[i].weight = weight
+    return arr
+
+
+def test_tx_tables_argument_errors(lib):
+    pl = das.Plan(**_problem())                  # Q = 2
+    h = pl._h
+    g, bad = _fake(0x10000), _fake(0x10004)
+    plane = (das.TX_PLANE, (0.0, 0.0, 1.0), 1.0)
+    div = (das.TX_DIVERGING, (1e-3, 0.0, -1e-2), 0.5)
+    ev = _tx_events(plane, div)
+    assert lib.das_tx_tables(None, ev, 0, 2, g, g, None) == INVALID
+    assert lib.das_tx_tables(h, None, 0, 2, g, g, None) == INVALID
+    assert lib.das_tx_tables(h, ev, 0, 2, None, g, None) == INVALID
+    assert lib.das_tx_tables(h, ev, 0, 2, g, None, None) == INVALID
+    assert lib.das_tx_tables(h, ev, 0, 0, g, g, None) == INVALID          # empty
+    assert lib.das_tx_tables(h, ev, 1, 2, g, g, None) == INVALID          # past Q
+    assert lib.das_tx_tables(h, ev, -1, 1, g, g, None) == INVALID
+    for spec in [(5, (0.0, 0.0, 1.0), 1.0),                               # unknown kind
+                 (das.TX_PLANE, (0.0, 0.0, 1.1), 1.0),                    # not a unit vector
+                 (das.TX_PLANE, (1.0, 0.0, 0.0), 1.0),                    # not towards +z
+                 (das.TX_DIVERGING, (0.0, 0.0, 1e-3), 1.0),               # source not behind the array
+                 (das.TX_DIVERGING, (0.0, 0.0, -1e-2), float("nan")),     # weight
+                 (das.TX_DIVERGING, (float("inf"), 0.0, -1e-2), 1.0)]:
+        assert lib.das_tx_tables(h, _tx_events(spec), 0, 1, g, g, None) == INVALID, spec
+    r = _tx_events(plane)
+    r[0].reserved = 1
+    assert lib.das_tx_tables(h, r, 0, 1, g, g, None) == INVALID
+    assert lib.das_tx_tables(h, ev, 0, 2, bad, g, None) == ALIGNMENT
+    assert lib.das_tx_tables(h, ev, 0, 2, g, bad, None) == ALIGNMENT
+    if not _gpu():
+        assert lib.das_tx_tables(h, ev, 0, 2, g, g, None) == NO_DEVICE
 
 
 def test_batch_inner_kqmb_chunk_limit(lib):

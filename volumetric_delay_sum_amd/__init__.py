@@ -19,12 +19,13 @@ from typing import Optional, Sequence
 
 __all__ = [
     "F32", "C64", "ALG_DEFAULT", "ALG_BASELINE", "ALG_BATCH_INNER", "LAYOUT_KQMB", "LAYOUT_QMKB",
-    "DasError", "Plan", "load_library", "library_path", "plan_from_fields",
+    "TX_PLANE", "TX_DIVERGING", "DasError", "Plan", "load_library", "library_path", "plan_from_fields",
 ]
 
 F32, C64 = 0, 1
 ALG_DEFAULT, ALG_BASELINE, ALG_BATCH_INNER = 0, 1, 2
 LAYOUT_KQMB, LAYOUT_QMKB = 0, 1
+TX_PLANE, TX_DIVERGING = 0, 1
 
 _ALG = {"default": ALG_DEFAULT, "baseline": ALG_BASELINE, "batch_inner": ALG_BATCH_INNER,
         "bl": ALG_BASELINE, "bi": ALG_BATCH_INNER}
@@ -61,6 +62,11 @@ class _PlanInfo(ctypes.Structure):
     ]
 
 
+class _TxEvent(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("reserved", ctypes.c_int32), ("v", ctypes.c_double * 3),
+                ("weight", ctypes.c_double)]
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -89,6 +95,8 @@ def load_library():
     lib.das_beamform.restype = ctypes.c_int
     lib.das_beamform_streamed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp]
     lib.das_beamform_streamed.restype = ctypes.c_int
+    lib.das_tx_tables.argtypes = [vp, ctypes.POINTER(_TxEvent), i32, i32, vp, vp, vp]
+    lib.das_tx_tables.restype = ctypes.c_int
     lib.das_max_q_chunk.argtypes = [vp]
     lib.das_max_q_chunk.restype = i32
     lib.das_error_string.argtypes = [ctypes.c_int]
@@ -244,6 +252,26 @@ class Plan:
                                                _stream_handle(stream_beamform, rf.device)),
                "das_beamform_streamed")
         return out
+
+    def tx_tables(self, events, tau_tx, w_tx, q_begin: int = 0, stream=None):
+        """Fill rows [q_begin, q_begin + len(events)) of the Q x N transmit tables.
+
+        events: sequence of (kind, (vx, vy, vz), weight) with kind TX_PLANE
+        (unit propagation direction, vz > 0) or TX_DIVERGING (virtual source
+        position in metres, vz < 0)."""
+        p = self.problem
+        arr = (_TxEvent * max(len(events), 1))()
+        for i, (kind, v, weight) in enumerate(events):
+            arr[i].kind = int(kind)
+            arr[i].reserved = 0
+            arr[i].v[:] = [float(x) for x in v]
+            arr[i].weight = float(weight)
+        tau_tx = self._tensor(tau_tx, p.Q * self.N, "tau_tx")
+        w_tx = self._tensor(w_tx, p.Q * self.N, "w_tx")
+        _check(self._lib.das_tx_tables(self._h, arr, int(q_begin), len(events), tau_tx.data_ptr(),
+                                       w_tx.data_ptr(), _stream_handle(stream, tau_tx.device)),
+               "das_tx_tables")
+        return tau_tx, w_tx
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:

@@ -350,4 +350,36 @@ das_status das_beamform_streamed(const das_plan_t *plan, const void *rf_bqmk, co
     return st;
 }
 
+das_status das_tx_tables(const das_plan_t *plan, const das_tx_event *events, int32_t q_begin, int32_t q_count,
+                         float *tau_tx, float *w_tx, void *hip_stream) {
+    if (!valid_plan(plan) || !events || !tau_tx || !w_tx)
+        return DAS_ERR_INVALID_ARGUMENT;
+    if (q_begin < 0 || q_count < 1 || (int64_t)q_begin + q_count > plan->p.Q)
+        return DAS_ERR_INVALID_ARGUMENT;
+    for (int32_t e = 0; e < q_count; ++e) {
+        const das_tx_event &ev = events[e];
+        if (ev.reserved != 0 || !is_finite(ev.weight) || !is_finite(ev.v[0]) || !is_finite(ev.v[1]) ||
+            !is_finite(ev.v[2]))
+            return DAS_ERR_INVALID_ARGUMENT;
+        if (ev.kind == DAS_TX_PLANE) {
+            const double n2 = ev.v[0] * ev.v[0] + ev.v[1] * ev.v[1] + ev.v[2] * ev.v[2];
+            if (!(ev.v[2] > 0.0) || !(std::fabs(n2 - 1.0) <= 2e-9))
+                return DAS_ERR_INVALID_ARGUMENT;
+        } else if (ev.kind == DAS_TX_DIVERGING) {
+            if (!(ev.v[2] < 0.0))
+                return DAS_ERR_INVALID_ARGUMENT;
+        } else {
+            return DAS_ERR_INVALID_ARGUMENT;
+        }
+    }
+    if (!aligned16(tau_tx) || !aligned16(w_tx))
+        return DAS_ERR_ALIGNMENT;
+    das_status st = check_device();
+    if (st != DAS_OK)
+        return st;
+    const hipError_t e = das_launch_tx_tables(*plan, events, q_begin, q_count, tau_tx, w_tx,
+                                              static_cast<hipStream_t>(hip_stream));
+    return e == hipSuccess ? DAS_OK : DAS_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -47,6 +47,11 @@ bool das_staged_supported(const das_plan_t &plan);
 hipError_t das_launch_batch_inner_staged(const das_plan_t &plan, const DasKParams &kp, const float *rf,
                                          const float *rx, const float *tau_tx, const float *w_tx, float *out,
                                          hipStream_t stream);
+// Transmit events per launch of the table generator (they travel in the
+// kernel arguments).
+constexpr int DAS_TX_EVENTS_PER_LAUNCH = 16;
+hipError_t das_launch_tx_tables(const das_plan_t &plan, const das_tx_event *events, int32_t q_begin,
+                                int32_t q_count, float *tau, float *w, hipStream_t stream);
 hipError_t das_launch_batch_inner(const das_plan_t &plan, const DasKParams &kp, const float *rf,
                                   const float *rx, const float *tau_tx, const float *w_tx,
                                   float *out, hipStream_t stream);
