@@ -25,6 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP32_TFLOPS = 157.3        # MI355X vector fp32 (published)
+PEAK_FP64_TFLOPS = 78.6         # MI355X vector fp64 (published)
 PEAK_HBM_GBS = 8000.0
 
 
@@ -67,6 +68,8 @@ def main():
                     help="time das_beamform_streamed: each chunk's permute overlapped with the previous "
                          "chunk's beamform on a second stream (the kernel times still come from the "
                          "event-timed chunked pass)")
+    ap.add_argument("--wide", action="store_true",
+                    help="float64 samples (complex128 for IQ workloads): the baseline's fp64 path")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-voxels", type=int, default=0, help="oracle sample size (0: one depth slab)")
     args = ap.parse_args()
@@ -95,12 +98,17 @@ def main():
     rx = das_synth.array_positions(cfg)
     tau, w = das_synth.tx_tables(cfg)
     rf = das_synth.rf(cfg, device=dev)
+    if args.wide:
+        if args.algorithm != "baseline":
+            print("bench.py: --wide runs the baseline algorithm (--algorithm baseline)", file=sys.stderr)
+            sys.exit(2)
+        rf = rf.double()                      # the same samples, held as float64
     rx_d = torch.from_numpy(rx).to(dev)
     tau_d = torch.from_numpy(tau).to(dev)
     w_d = torch.from_numpy(w).to(dev)
 
-    plan = das.plan_from_fields(fields, algorithm=args.algorithm, layout=args.layout)
-    out = torch.empty(plan.output_shape(), dtype=torch.float32, device=dev)
+    plan = das.plan_from_fields(fields, algorithm=args.algorithm, layout=args.layout, wide=args.wide)
+    out = torch.empty(plan.output_shape(), dtype=torch.float64 if args.wide else torch.float32, device=dev)
     bi = plan.batch_inner
     # events per das_permute / das_beamform pair (all Q unless the layout's
     # 32-bit offsets need chunks); chunks after the first accumulate into out
@@ -199,7 +207,8 @@ def main():
     flops_per_acc = 8 if cfg.iq else 4          # 2 FMA (real) or 8 FMA (complex) per accumulation
     achieved = accs * flops_per_acc / (kern_avg * 1e-3) / 1e12
     kernel_name = ("das_bi_staged_kernel" if plan.info["staged"] else "das_batch_inner_kernel") if bi \
-        else "das_baseline_kernel"
+        else ("das_baseline_f64_kernel" if args.wide else "das_baseline_kernel")
+    peak = PEAK_FP64_TFLOPS if args.wide else PEAK_FP32_TFLOPS
     traffic = stored_traffic(kernel_name, cfg.name)
 
     cpu = None
@@ -242,13 +251,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "c64" if cfg.iq else "f32",
+        "dtype": ("c128" if cfg.iq else "f64") if args.wide else ("c64" if cfg.iq else "f32"),
         "data": "synthetic",
         "config": {
             "workload": (f"{cfg.name}: {cfg.grid[0]}x{cfg.grid[1]}x{cfg.grid[2]} voxels, "
                          f"{cfg.array[0]}x{cfg.array[1]} array (M={cfg.M}), Q={cfg.Q} "
                          f"{'plane' if cfg.tx == 'plane' else 'diverging'} waves, K={cfg.K}, B={cfg.B}, "
-                         f"{'complex64 IQ' if cfg.iq else 'fp32 RF'}"),
+                         + ((f"{'complex128 IQ' if cfg.iq else 'fp64 RF'}") if args.wide else
+                            (f"{'complex64 IQ' if cfg.iq else 'fp32 RF'}"))),
             "step": ((f"das_permute + das_beamform (batch-inner, layout {args.layout.upper()}"
                       f", {len(chunks)} chunk(s) of <= {qc} events{streamed_desc})") if bi
                      else "das_beamform (baseline)"),
@@ -258,9 +268,9 @@ def main():
         "roofline": {
             "bound": "alu",
             "achieved": achieved,
-            "peak": PEAK_FP32_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": achieved / PEAK_FP32_TFLOPS,
+            "frac": achieved / peak,
             "traffic": traffic,
             "kernel": kernel_name,
             "kernel_ms_per_step": kern_avg,

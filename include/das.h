@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DAS_ABI_VERSION 3
+#define DAS_ABI_VERSION 4
 
 typedef enum das_status {
     DAS_OK = 0,
@@ -57,8 +57,12 @@ typedef enum das_status {
 } das_status;
 
 /* Sample type.  DAS_F32: real float32 RF.  DAS_C64: complex64 IQ data, stored
- * as interleaved (re, im) float32 pairs; requires f_demod > 0. */
-enum { DAS_F32 = 0, DAS_C64 = 1 };
+ * as interleaved (re, im) float32 pairs; requires f_demod > 0.  DAS_F64 and
+ * DAS_C128: the same in float64 (baseline algorithm only; the docs' ALG1
+ * supports float64 and complex128): RF and output are doubles and the delay,
+ * weights, phase and sum are all evaluated in fp64.  Receiver positions and
+ * transmit tables stay float32 for every dtype. */
+enum { DAS_F32 = 0, DAS_C64 = 1, DAS_F64 = 2, DAS_C128 = 3 };
 
 /* Kernel family.
  *  DAS_ALG_BASELINE     one lane per voxel, a tile of frames per lane, reading
@@ -68,8 +72,13 @@ enum { DAS_F32 = 0, DAS_C64 = 1 };
  *                       das_permute, a group of lanes shares one voxel and
  *                       reads consecutive frames at one (k, q, m) (the paper's
  *                       batch-inner tiling, Section 3; the docs' ALG2).
- *  DAS_ALG_DEFAULT      the baseline, as the docs' DEFAULT dispatch.          */
-enum { DAS_ALG_DEFAULT = 0, DAS_ALG_BASELINE = 1, DAS_ALG_BATCH_INNER = 2 };
+ *  DAS_ALG_DEFAULT      the baseline, as the docs' DEFAULT dispatch.
+ *  DAS_ALG_AUTO         chosen from the problem (the docs' planned automatic
+ *                       selection): batch-inner for DAS_F32 / DAS_C64 with
+ *                       B >= 16 (a frame group fills a 16-lane row), else the
+ *                       baseline.  das_plan_get_info reports the choice; a
+ *                       batch-inner plan needs das_permute before das_beamform. */
+enum { DAS_ALG_DEFAULT = 0, DAS_ALG_BASELINE = 1, DAS_ALG_BATCH_INNER = 2, DAS_ALG_AUTO = 3 };
 
 /* Frames-innermost layout made by das_permute and read by the batch-inner
  * kernel, for a chunk of q_count transmit events:
@@ -81,8 +90,8 @@ enum { DAS_LAYOUT_KQMB = 0, DAS_LAYOUT_QMKB = 1 };
 typedef struct das_problem {
     int32_t B, Q, M, K;      /* frames, transmit events, receivers, samples (K >= 2)   */
     int32_t nx, ny, nz;      /* voxel grid; n = (iz*ny + iy)*nx + ix                   */
-    int32_t dtype;           /* DAS_F32 | DAS_C64                                      */
-    int32_t algorithm;       /* DAS_ALG_DEFAULT | DAS_ALG_BASELINE | DAS_ALG_BATCH_INNER */
+    int32_t dtype;           /* DAS_F32 | DAS_C64 | DAS_F64 | DAS_C128                 */
+    int32_t algorithm;       /* DAS_ALG_DEFAULT | _BASELINE | _BATCH_INNER | _AUTO      */
     int32_t layout;          /* DAS_LAYOUT_KQMB | DAS_LAYOUT_QMKB (batch-inner only)    */
     double  origin[3];       /* metres: centre of voxel (0,0,0)                         */
     double  spacing[3];      /* metres: voxel pitch along x, y, z (> 0)                 */
@@ -90,7 +99,7 @@ typedef struct das_problem {
     double  c;               /* m/s, speed of sound (> 0)                               */
     double  t0;              /* s, time of sample k = 0                                 */
     double  f_number;        /* receive Hann over angle; <= 0 gives w_rx = 1            */
-    double  f_demod;         /* Hz: 0 with DAS_F32, > 0 with DAS_C64                    */
+    double  f_demod;         /* Hz: 0 with DAS_F32 / DAS_F64, > 0 with DAS_C64 / DAS_C128 */
 } das_problem;
 
 typedef struct das_plan das_plan_t;
@@ -99,7 +108,7 @@ typedef struct das_plan das_plan_t;
 typedef struct das_plan_info {
     int32_t algorithm;          /* resolved: DAS_ALG_BASELINE or DAS_ALG_BATCH_INNER */
     int32_t layout;
-    int32_t elem_bytes;         /* 4 (f32) or 8 (c64) per sample                     */
+    int32_t elem_bytes;         /* 4 (f32), 8 (c64, f64) or 16 (c128) per sample     */
     int32_t frames_per_lane;    /* batch-inner: frames one lane loads per vector load;
                                    baseline: frames one lane accumulates             */
     int32_t lanes_per_voxel;    /* batch-inner: 16; baseline: 1                      */
@@ -115,8 +124,9 @@ typedef struct das_plan_info {
  * das_plan_destroy.
  * Errors: DAS_ERR_INVALID_ARGUMENT for null pointers, non-positive sizes,
  * K < 2, non-finite or non-positive fs / c / spacing, unknown enums;
- * DAS_ERR_UNSUPPORTED for dtype / f_demod mismatch (C64 needs f_demod > 0,
- * F32 needs f_demod == 0) or N, B*Q*M*K beyond 2^31 elements per axis. */
+ * DAS_ERR_UNSUPPORTED for dtype / f_demod mismatch (complex types need
+ * f_demod > 0, real ones f_demod == 0), DAS_F64 / DAS_C128 with
+ * DAS_ALG_BATCH_INNER, or N, B*Q*M*K beyond 2^31 elements per axis. */
 das_status das_plan(const das_problem *problem, das_plan_t **out);
 
 void das_plan_destroy(das_plan_t *plan);
@@ -143,6 +153,8 @@ int32_t das_max_q_chunk(const das_plan_t *plan);
  *             local index q - q_begin
  * Errors: DAS_ERR_INVALID_ARGUMENT (null pointer, empty or out-of-range q
  * range, rf_perm overlapping rf_bqmk is not checked: do not alias);
+ * DAS_ERR_UNSUPPORTED (DAS_F64 / DAS_C128 plans: only the baseline, which
+ * reads B x Q x M x K directly, serves them);
  * DAS_ERR_ALIGNMENT; DAS_ERR_NO_DEVICE; DAS_ERR_LAUNCH. */
 das_status das_permute(const das_plan_t *plan, const void *rf_bqmk, void *rf_perm,
                        int32_t q_begin, int32_t q_count, void *hip_stream);
@@ -154,7 +166,9 @@ das_status das_permute(const das_plan_t *plan, const void *rf_bqmk, void *rf_per
  *   rx_pos   M x 3 float32 receiver positions (x, y, z), metres
  *   tau_tx   Q x N float32 transmit delays, seconds (absolute q)
  *   w_tx     Q x N float32 transmit weights (absolute q)
- *   out      B x N float32 (DAS_C64: B x N interleaved re/im float32 pairs)
+ *   out      B x N samples of the plan's dtype: float32, interleaved re/im
+ *            float32 pairs (DAS_C64), float64 (DAS_F64) or interleaved re/im
+ *            float64 pairs (DAS_C128); rf holds samples of the same type
  *   accumulate  0: out is overwritten; 1: the chunk's sum is added to out
  *               (to sum a volume over several q chunks)
  * Errors: DAS_ERR_INVALID_ARGUMENT (null pointer, bad q range, accumulate not

@@ -30,7 +30,7 @@ class _Geometry(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int32), ("Q", ctypes.c_int32), ("M", ctypes.c_int32), ("K", ctypes.c_int32),
         ("nx", ctypes.c_int32), ("ny", ctypes.c_int32), ("nz", ctypes.c_int32),
-        ("complex_iq", ctypes.c_int32),
+        ("complex_iq", ctypes.c_int32), ("rf_f64", ctypes.c_int32),
         ("origin", ctypes.c_double * 3), ("spacing", ctypes.c_double * 3),
         ("fs", ctypes.c_double), ("c", ctypes.c_double), ("t0", ctypes.c_double),
         ("f_number", ctypes.c_double), ("f_demod", ctypes.c_double),
@@ -78,7 +78,7 @@ def das_sum(fields: dict, rf, rx_pos, tau_tx, w_tx,
 
     fields: B, Q, M, K, nx, ny, nz, origin, spacing, fs, c, t0, f_number,
             f_demod, iq (as made by ``das_synth.problem_fields``).
-    rf: float32 B x Q x M x K (IQ: B x Q x M x K x 2).  The frame axis of rf
+    rf: float32 or float64 B x Q x M x K (IQ: B x Q x M x K x 2).  The frame axis of rf
         must hold all B frames (frame indices address it directly).
     Returns float64 (n_frames, n_voxels), or complex128 for IQ.
     """
@@ -92,7 +92,10 @@ def das_sum(fields: dict, rf, rx_pos, tau_tx, w_tx,
     g.fs, g.c, g.t0 = float(fields["fs"]), float(fields["c"]), float(fields["t0"])
     g.f_number, g.f_demod = float(fields["f_number"]), float(fields.get("f_demod", 0.0))
 
-    rf = _as_f32(rf, "rf")
+    rf = np.ascontiguousarray(rf)
+    if rf.dtype not in (np.float32, np.float64):
+        raise TypeError(f"rf must be float32 or float64, got {rf.dtype}")
+    g.rf_f64 = 1 if rf.dtype == np.float64 else 0
     rx_pos = _as_f32(rx_pos, "rx_pos")
     tau_tx = _as_f32(tau_tx, "tau_tx")
     w_tx = _as_f32(w_tx, "w_tx")

@@ -61,7 +61,13 @@ static void voxel_centre(const das_oracle_geometry *g, int64_t n, double r[3])
     r[2] = g->origin[2] + (double)iz * g->spacing[2];
 }
 
-int das_oracle_sum(const das_oracle_geometry *g, const float *rf, const float *rx_pos,
+/* One RF value, widened to fp64. */
+static double sample(const das_oracle_geometry *g, const void *rf, int64_t i)
+{
+    return g->rf_f64 ? ((const double *)rf)[i] : (double)((const float *)rf)[i];
+}
+
+int das_oracle_sum(const das_oracle_geometry *g, const void *rf, const float *rx_pos,
                    const float *tau_tx, const float *w_tx,
                    const int64_t *voxels, int64_t n_voxels,
                    const int32_t *frames, int32_t n_frames, double *out)
@@ -118,14 +124,14 @@ int das_oracle_sum(const das_oracle_geometry *g, const float *rf, const float *r
                     const int64_t row = ((b * Q + q) * M + m) * K;
                     double *o = &out[(jf * n_voxels + iv) * comps];
                     if (!iq) {
-                        const double x0 = (double)rf[row + k];
-                        const double x1 = (double)rf[row + k + 1];
+                        const double x0 = sample(g, rf, row + k);
+                        const double x1 = sample(g, rf, row + k + 1);
                         o[0] += w * ((1.0 - f) * x0 + f * x1);
                     } else {
-                        const double x0r = (double)rf[2 * (row + k)];
-                        const double x0i = (double)rf[2 * (row + k) + 1];
-                        const double x1r = (double)rf[2 * (row + k + 1)];
-                        const double x1i = (double)rf[2 * (row + k + 1) + 1];
+                        const double x0r = sample(g, rf, 2 * (row + k));
+                        const double x0i = sample(g, rf, 2 * (row + k) + 1);
+                        const double x1r = sample(g, rf, 2 * (row + k + 1));
+                        const double x1i = sample(g, rf, 2 * (row + k + 1) + 1);
                         const double vr = (1.0 - f) * x0r + f * x1r;
                         const double vi = (1.0 - f) * x0i + f * x1i;
                         o[0] += w * (vr * ph_re - vi * ph_im);

@@ -16,6 +16,7 @@ typedef struct das_oracle_geometry {
     int32_t B, Q, M, K;      /* frames, transmit events, receivers, samples       */
     int32_t nx, ny, nz;      /* voxel grid, n = (iz*ny + iy)*nx + ix              */
     int32_t complex_iq;      /* 0: real RF; 1: IQ, re/im interleaved             */
+    int32_t rf_f64;          /* 0: rf holds float32 values; 1: float64 values     */
     double origin[3];        /* centre of voxel (0,0,0), metres                  */
     double spacing[3];       /* voxel pitch, metres                              */
     double fs, c, t0;        /* sampling rate Hz, speed of sound m/s, time of k=0 */
@@ -27,7 +28,7 @@ typedef struct das_oracle_geometry {
 double das_oracle_rx_weight(double rho, double dz, double f_number);
 
 /*
- * rf      B x Q x M x K float32 (IQ: x 2 interleaved)
+ * rf      B x Q x M x K float32, or float64 if rf_f64 (IQ: x 2 interleaved)
  * rx_pos  M x 3 float32
  * tau_tx, w_tx  Q x N float32
  * voxels  n_voxels linear voxel indices (NULL: 0..n_voxels-1)
@@ -35,7 +36,7 @@ double das_oracle_rx_weight(double rho, double dz, double f_number);
  * out     n_frames x n_voxels fp64 (IQ: x 2 interleaved)
  * Returns 0, or non-zero on a bad argument or index.
  */
-int das_oracle_sum(const das_oracle_geometry *g, const float *rf, const float *rx_pos,
+int das_oracle_sum(const das_oracle_geometry *g, const void *rf, const float *rx_pos,
                    const float *tau_tx, const float *w_tx,
                    const int64_t *voxels, int64_t n_voxels,
                    const int32_t *frames, int32_t n_frames, double *out);

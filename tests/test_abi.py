@@ -135,6 +135,39 @@ def test_plan_info_and_sizes():
     assert pl3.permuted_shape(2) == (2, 8, 64, 4)
 
 
+def test_float64_dtypes_are_baseline_only():
+    f64 = das.Plan(**_problem(dtype="f64", algorithm="baseline"))
+    assert f64.info["elem_bytes"] == 8 and f64.info["algorithm"] == das.ALG_BASELINE and f64.wide
+    c128 = das.Plan(**_problem(dtype="c128", f_demod=5e6, algorithm="default"))
+    assert c128.info["elem_bytes"] == 16 and c128.info["algorithm"] == das.ALG_BASELINE and c128.iq
+    assert _status(dtype="f64", algorithm="batch_inner") == UNSUPPORTED
+    assert _status(dtype="c128", f_demod=5e6, algorithm="batch_inner") == UNSUPPORTED
+    assert _status(dtype="c128", f_demod=0.0, algorithm="baseline") == UNSUPPORTED    # complex needs f_demod
+    assert _status(dtype="f64", f_demod=5e6, algorithm="baseline") == UNSUPPORTED     # real needs none
+    assert _status(dtype=7, algorithm="baseline") == INVALID
+    # one frame (no batch dimension) is a valid fp64 problem
+    assert das.Plan(**_problem(B=1, dtype="f64", algorithm="baseline")).info["frames_per_lane"] == 8
+
+
+def test_float64_plans_do_not_permute(lib):
+    pl = das.Plan(**_problem(dtype="f64", algorithm="baseline"))
+    g = _fake(0x10000)
+    assert lib.das_permute(pl._h, g, g, 0, 1, None) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype,B,alg", [("f32", 32, das.ALG_BATCH_INNER), ("f32", 16, das.ALG_BATCH_INNER),
+                                         ("f32", 8, das.ALG_BASELINE), ("f32", 1, das.ALG_BASELINE),
+                                         ("c64", 16, das.ALG_BATCH_INNER), ("c64", 4, das.ALG_BASELINE),
+                                         ("f64", 64, das.ALG_BASELINE), ("c128", 64, das.ALG_BASELINE)])
+def test_auto_selection(dtype, B, alg):
+    pl = das.Plan(**_problem(B=B, dtype=dtype, f_demod=5e6 if dtype in ("c64", "c128") else 0.0,
+                             algorithm="auto"))
+    assert pl.info["algorithm"] == alg
+    # DEFAULT stays the baseline, as the docs dispatch it
+    assert das.Plan(**_problem(B=B, dtype=dtype, f_demod=5e6 if dtype in ("c64", "c128") else 0.0,
+                               algorithm="default")).info["algorithm"] == das.ALG_BASELINE
+
+
 @pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (24, 1), (32, 2), (48, 1), (64, 2), (96, 2), (66, 1),
                                   (160, 2), (68, 4)])
 def test_frames_per_lane_choice(B, fl):

@@ -380,7 +380,24 @@ def test_rejects_bad_arguments(oracle_mod):
     with pytest.raises(ValueError):
         oracle_mod.das_sum(f, x, rx, tau, w, frames=[f["B"]])
     with pytest.raises(TypeError):
-        oracle_mod.das_sum(f, x.astype(np.float64), rx, tau, w)
+        oracle_mod.das_sum(f, x.astype(np.float16), rx, tau, w)
+
+
+def test_float64_input_reads_doubles(oracle_mod):
+    # float64 RF (the fp64 / complex128 baseline's input): values that float32
+    # holds exactly give the float32 result bit for bit; the part float32
+    # drops is summed too (linearity), so the reader sees all 53 bits
+    for iq in (False, True):
+        f, x, rx, tau, w = _random_problem(93, iq=iq)
+        y32 = oracle_mod.das_sum(f, x, rx, tau, w)
+        np.testing.assert_array_equal(oracle_mod.das_sum(f, x.astype(np.float64), rx, tau, w), y32)
+        fine = np.random.default_rng(5).standard_normal(x.shape) * 1e-9
+        x64 = x.astype(np.float64) + fine
+        assert np.any(x64.astype(np.float32).astype(np.float64) != x64)
+        y64 = oracle_mod.das_sum(f, x64, rx, tau, w)
+        y_fine = oracle_mod.das_sum(f, fine, rx, tau, w)
+        assert np.abs(y_fine).max() > 0
+        np.testing.assert_allclose(y64, y32 + y_fine, rtol=0, atol=1e-12 * np.abs(y32).max())
 
 
 def test_permute_references():

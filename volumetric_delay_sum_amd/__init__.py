@@ -18,19 +18,20 @@ import os
 from typing import Optional, Sequence
 
 __all__ = [
-    "F32", "C64", "ALG_DEFAULT", "ALG_BASELINE", "ALG_BATCH_INNER", "LAYOUT_KQMB", "LAYOUT_QMKB",
+    "F32", "C64", "F64", "C128", "ALG_DEFAULT", "ALG_BASELINE", "ALG_BATCH_INNER", "ALG_AUTO",
+    "LAYOUT_KQMB", "LAYOUT_QMKB",
     "TX_PLANE", "TX_DIVERGING", "DasError", "Plan", "load_library", "library_path", "plan_from_fields",
 ]
 
-F32, C64 = 0, 1
-ALG_DEFAULT, ALG_BASELINE, ALG_BATCH_INNER = 0, 1, 2
+F32, C64, F64, C128 = 0, 1, 2, 3
+ALG_DEFAULT, ALG_BASELINE, ALG_BATCH_INNER, ALG_AUTO = 0, 1, 2, 3
 LAYOUT_KQMB, LAYOUT_QMKB = 0, 1
 TX_PLANE, TX_DIVERGING = 0, 1
 
 _ALG = {"default": ALG_DEFAULT, "baseline": ALG_BASELINE, "batch_inner": ALG_BATCH_INNER,
-        "bl": ALG_BASELINE, "bi": ALG_BATCH_INNER}
+        "bl": ALG_BASELINE, "bi": ALG_BATCH_INNER, "auto": ALG_AUTO}
 _LAYOUT = {"kqmb": LAYOUT_KQMB, "qmkb": LAYOUT_QMKB}
-_DTYPE = {"f32": F32, "c64": C64}
+_DTYPE = {"f32": F32, "c64": C64, "f64": F64, "c128": C128}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdas.so")
@@ -159,7 +160,12 @@ class Plan:
 
     @property
     def iq(self) -> bool:
-        return self.problem.dtype == C64
+        return self.problem.dtype in (C64, C128)
+
+    @property
+    def wide(self) -> bool:
+        """Samples (RF and output) are float64."""
+        return self.problem.dtype in (F64, C128)
 
     @property
     def batch_inner(self) -> bool:
@@ -182,14 +188,16 @@ class Plan:
         return (self.problem.B, self.N) + ((2,) if self.iq else ())
 
     # -- argument checks (sizes are unknown to the C ABI) --------------------
-    def _tensor(self, t, numel: int, name: str):
+    def _tensor(self, t, numel: int, name: str, samples: bool = False):
+        """samples: RF or output, float64 for F64 / C128 plans; everything else float32."""
         import torch
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise TypeError(f"{name} must be a CUDA tensor")
-        if t.dtype == torch.complex64:
+        if t.dtype in (torch.complex64, torch.complex128):
             t = torch.view_as_real(t)
-        if t.dtype != torch.float32:
-            raise TypeError(f"{name} must be float32 (or complex64 for IQ), got {t.dtype}")
+        want = torch.float64 if (samples and self.wide) else torch.float32
+        if t.dtype != want:
+            raise TypeError(f"{name} must be {want} (or its complex type for IQ), got {t.dtype}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
         if t.numel() != numel:
@@ -206,8 +214,8 @@ class Plan:
         p = self.problem
         q_begin, q_count = self._q_range(q_begin, q_count)
         c = 2 if self.iq else 1
-        rf = self._tensor(rf, p.B * p.Q * p.M * p.K * c, "rf")
-        out = self._tensor(out, p.K * max(q_count, 0) * p.M * p.B * c, "out")
+        rf = self._tensor(rf, p.B * p.Q * p.M * p.K * c, "rf", samples=True)
+        out = self._tensor(out, p.K * max(q_count, 0) * p.M * p.B * c, "out", samples=True)
         _check(self._lib.das_permute(self._h, rf.data_ptr(), out.data_ptr(), q_begin, q_count,
                                      _stream_handle(stream, rf.device)), "das_permute")
         return out
@@ -219,11 +227,11 @@ class Plan:
         q_begin, q_count = self._q_range(q_begin, q_count)
         c = 2 if self.iq else 1
         rf_numel = (p.K * max(q_count, 0) * p.M * p.B if self.batch_inner else p.B * p.Q * p.M * p.K) * c
-        rf = self._tensor(rf, rf_numel, "rf")
+        rf = self._tensor(rf, rf_numel, "rf", samples=True)
         rx_pos = self._tensor(rx_pos, 3 * p.M, "rx_pos")
         tau_tx = self._tensor(tau_tx, p.Q * self.N, "tau_tx")
         w_tx = self._tensor(w_tx, p.Q * self.N, "w_tx")
-        out = self._tensor(out, p.B * self.N * c, "out")
+        out = self._tensor(out, p.B * self.N * c, "out", samples=True)
         _check(self._lib.das_beamform(self._h, rf.data_ptr(), rx_pos.data_ptr(), tau_tx.data_ptr(),
                                       w_tx.data_ptr(), out.data_ptr(), q_begin, q_count,
                                       1 if accumulate else 0, _stream_handle(stream, rf.device)),
@@ -237,14 +245,14 @@ class Plan:
         p = self.problem
         c = 2 if self.iq else 1
         q_chunk = int(q_chunk)
-        rf = self._tensor(rf, p.B * p.Q * p.M * p.K * c, "rf")
+        rf = self._tensor(rf, p.B * p.Q * p.M * p.K * c, "rf", samples=True)
         rx_pos = self._tensor(rx_pos, 3 * p.M, "rx_pos")
         tau_tx = self._tensor(tau_tx, p.Q * self.N, "tau_tx")
         w_tx = self._tensor(w_tx, p.Q * self.N, "w_tx")
-        out = self._tensor(out, p.B * self.N * c, "out")
+        out = self._tensor(out, p.B * self.N * c, "out", samples=True)
         chunk = p.K * max(q_chunk, 0) * p.M * p.B * c
-        perm_a = self._tensor(perm_a, chunk, "perm_a")
-        perm_b = self._tensor(perm_b, chunk, "perm_b")
+        perm_a = self._tensor(perm_a, chunk, "perm_a", samples=True)
+        perm_b = self._tensor(perm_b, chunk, "perm_b", samples=True)
         _check(self._lib.das_beamform_streamed(self._h, rf.data_ptr(), rx_pos.data_ptr(), tau_tx.data_ptr(),
                                                w_tx.data_ptr(), out.data_ptr(), perm_a.data_ptr(),
                                                perm_b.data_ptr(), q_chunk, 1 if accumulate else 0,
@@ -285,11 +293,14 @@ class Plan:
             pass
 
 
-def plan_from_fields(fields: dict, algorithm: str = "batch_inner", layout: str = "kqmb") -> Plan:
+def plan_from_fields(fields: dict, algorithm: str = "batch_inner", layout: str = "kqmb",
+                     wide: bool = False) -> Plan:
     """Plan from a plain description (B, Q, M, K, nx, ny, nz, origin, spacing, fs, c, t0,
-    f_number, f_demod, iq)."""
+    f_number, f_demod, iq); wide: float64 samples (F64 / C128)."""
+    iq = bool(fields.get("iq"))
+    dtype = ("c128" if iq else "f64") if wide else ("c64" if iq else "f32")
     return Plan(B=fields["B"], Q=fields["Q"], M=fields["M"], K=fields["K"], nx=fields["nx"],
                 ny=fields["ny"], nz=fields["nz"], origin=fields["origin"], spacing=fields["spacing"],
                 fs=fields["fs"], c=fields["c"], t0=fields.get("t0", 0.0),
                 f_number=fields.get("f_number", 1.0), f_demod=fields.get("f_demod", 0.0),
-                dtype="c64" if fields.get("iq") else "f32", algorithm=algorithm, layout=layout)
+                dtype=dtype, algorithm=algorithm, layout=layout)

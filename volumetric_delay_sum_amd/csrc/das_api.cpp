@@ -92,6 +92,9 @@ DasKParams make_params(const das_plan_t &pl, int32_t q_begin, int32_t q_count, i
     k.f0_over_c = p.f_demod / p.c;
     k.apod = p.f_number > 0.0 ? 1 : 0;
     k.inv_theta_max = k.apod ? (float)(1.0 / std::atan(1.0 / (2.0 * p.f_number))) : 0.0f;
+    k.f_number = p.f_number;
+    k.c = p.c;
+    k.t0 = p.t0;
     k.nx = p.nx;
     k.ny = p.ny;
     k.nz = p.nz;
@@ -105,6 +108,17 @@ DasKParams make_params(const das_plan_t &pl, int32_t q_begin, int32_t q_count, i
     k.q_group = pl.q_group;
     k.accumulate = accumulate;
     return k;
+}
+
+// DAS_ALG_AUTO: the batch-inner kernels need a frame group that fills a
+// 16-lane row (B >= 16) and exist for fp32 and complex64 samples; anything
+// else runs the baseline.  DEFAULT is the baseline, as the docs dispatch it.
+int32_t resolve_algorithm(const das_problem &p) {
+    if (p.algorithm == DAS_ALG_BATCH_INNER)
+        return DAS_ALG_BATCH_INNER;
+    if (p.algorithm == DAS_ALG_AUTO && (p.dtype == DAS_F32 || p.dtype == DAS_C64) && p.B >= 16)
+        return DAS_ALG_BATCH_INNER;
+    return DAS_ALG_BASELINE;
 }
 
 bool valid_plan(const das_plan_t *plan) { return plan != nullptr; }
@@ -165,9 +179,10 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
     const das_problem &p = *problem;
     if (p.B < 1 || p.Q < 1 || p.M < 1 || p.K < 2 || p.nx < 1 || p.ny < 1 || p.nz < 1)
         return DAS_ERR_INVALID_ARGUMENT;
-    if (p.dtype != DAS_F32 && p.dtype != DAS_C64)
+    if (p.dtype != DAS_F32 && p.dtype != DAS_C64 && p.dtype != DAS_F64 && p.dtype != DAS_C128)
         return DAS_ERR_INVALID_ARGUMENT;
-    if (p.algorithm != DAS_ALG_DEFAULT && p.algorithm != DAS_ALG_BASELINE && p.algorithm != DAS_ALG_BATCH_INNER)
+    if (p.algorithm != DAS_ALG_DEFAULT && p.algorithm != DAS_ALG_BASELINE && p.algorithm != DAS_ALG_BATCH_INNER &&
+        p.algorithm != DAS_ALG_AUTO)
         return DAS_ERR_INVALID_ARGUMENT;
     if (p.layout != DAS_LAYOUT_KQMB && p.layout != DAS_LAYOUT_QMKB)
         return DAS_ERR_INVALID_ARGUMENT;
@@ -177,12 +192,16 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
     if (!is_finite(p.fs) || !(p.fs > 0.0) || !is_finite(p.c) || !(p.c > 0.0) || !is_finite(p.t0) || !is_finite(p.f_number) ||
         !is_finite(p.f_demod))
         return DAS_ERR_INVALID_ARGUMENT;
-    if (p.dtype == DAS_F32 && p.f_demod != 0.0)
+    const bool cplx = p.dtype == DAS_C64 || p.dtype == DAS_C128;
+    const bool wide = p.dtype == DAS_F64 || p.dtype == DAS_C128;   // fp64 samples: baseline only
+    if (!cplx && p.f_demod != 0.0)
         return DAS_ERR_UNSUPPORTED;
-    if (p.dtype == DAS_C64 && !(p.f_demod > 0.0))
+    if (cplx && !(p.f_demod > 0.0))
+        return DAS_ERR_UNSUPPORTED;
+    if (wide && p.algorithm == DAS_ALG_BATCH_INNER)
         return DAS_ERR_UNSUPPORTED;
     const int64_t N = (int64_t)p.nx * p.ny * p.nz;
-    const int32_t elem = p.dtype == DAS_C64 ? 8 : 4;
+    const int32_t elem = (cplx ? 2 : 1) * (wide ? 8 : 4);
     if (N > INT32_MAX)
         return DAS_ERR_UNSUPPORTED;
     // batch-inner QMKB keeps a 32-bit offset across 16 (q, m) planes
@@ -197,7 +216,7 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
         return DAS_ERR_INVALID_ARGUMENT;
     pl->p = p;
     pl->N = N;
-    pl->alg = (p.algorithm == DAS_ALG_BATCH_INNER) ? DAS_ALG_BATCH_INNER : DAS_ALG_BASELINE;
+    pl->alg = resolve_algorithm(p);
     pl->elem_bytes = elem;
     pl->fl = pick_fl(p.B, p.dtype);
     pl->bt = 8;
@@ -251,6 +270,8 @@ das_status das_permute(const das_plan_t *plan, const void *rf_bqmk, void *rf_per
         return DAS_ERR_INVALID_ARGUMENT;
     if (q_begin < 0 || q_count < 1 || (int64_t)q_begin + q_count > plan->p.Q)
         return DAS_ERR_INVALID_ARGUMENT;
+    if (plan->p.dtype == DAS_F64 || plan->p.dtype == DAS_C128)
+        return DAS_ERR_UNSUPPORTED;
     if (!aligned16(rf_bqmk) || !aligned16(rf_perm))
         return DAS_ERR_ALIGNMENT;
     das_status st = check_device();
@@ -291,6 +312,9 @@ das_status das_beamform(const das_plan_t *plan, const void *rf, const float *rx_
         e = staged ? das_launch_batch_inner_staged(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s)
                    : das_launch_batch_inner(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s);
     }
+    else if (plan->p.dtype == DAS_F64 || plan->p.dtype == DAS_C128)
+        e = das_launch_baseline_f64(*plan, kp, static_cast<const double *>(rf), rx_pos, tau_tx, w_tx,
+                                    static_cast<double *>(out), s);
     else
         e = das_launch_baseline(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s);
     return e == hipSuccess ? DAS_OK : DAS_ERR_LAUNCH;

@@ -16,6 +16,8 @@ struct DasKParams {
     double fs_over_c;         // samples per metre of path
     double f0;                // IQ demodulation frequency, Hz
     double f0_over_c;         // IQ phase cycles per metre of path
+    double f_number;          // receive Hann (fp64 kernels form theta_max themselves)
+    double c, t0;             // m/s and s, as given (fp64 kernels)
     float inv_theta_max;      // 1 / theta_max (receive Hann)
     int32_t apod;             // 0: w_rx = 1
     int32_t nx, ny, nz, N;
@@ -43,6 +45,9 @@ hipError_t das_launch_permute(const das_plan_t &plan, const void *rf, void *out,
 hipError_t das_launch_baseline(const das_plan_t &plan, const DasKParams &kp, const float *rf,
                                const float *rx, const float *tau_tx, const float *w_tx,
                                float *out, hipStream_t stream);
+hipError_t das_launch_baseline_f64(const das_plan_t &plan, const DasKParams &kp, const double *rf,
+                                   const float *rx, const float *tau_tx, const float *w_tx,
+                                   double *out, hipStream_t stream);
 bool das_staged_supported(const das_plan_t &plan);
 hipError_t das_launch_batch_inner_staged(const das_plan_t &plan, const DasKParams &kp, const float *rf,
                                          const float *rx, const float *tau_tx, const float *w_tx, float *out,
