@@ -75,3 +75,27 @@ def test_large_streamed_matches_oracle_on_a_sample(gpu):
     torch.cuda.empty_cache()
     ref = oracle.das_sum(fields, rf_sub, das_synth.array_positions(cfg), *das_synth.tx_tables(cfg), voxels=vox)
     assert_parity(y, ref, "large streamed")
+
+
+def test_large_qmkb_one_chunk_past_4gib_matches_oracle(gpu):
+    """Large in one QMKB chunk of all 16 events (17 GB): the staged kernel rebases
+    its copies per (event, receiver block) plane past 4 GiB."""
+    import torch
+    import oracle
+    cfg = das_synth.get_config("large")
+    inp = Inputs(cfg)
+    import volumetric_delay_sum_amd as das
+    plan = das.plan_from_fields(inp.fields, algorithm="batch_inner", layout="qmkb")
+    assert plan.max_q_chunk() == cfg.Q and plan.info["staged"] == 1
+    assert plan.permuted_bytes(cfg.Q) > 4 * 2 ** 30
+    print("large qmkb one chunk", flush=True)
+    out = run_gpu(inp, "batch_inner", "qmkb", q_chunk=cfg.Q)
+    frames = [0, 37, 63]
+    vox = sample_voxels(cfg, 1024, seed=6)
+    y = to_numpy(out, cfg.iq)[frames][:, vox]
+    fields = dict(inp.fields, B=len(frames))
+    rf_sub = inp.rf_d[frames].cpu().numpy()
+    del inp, out
+    torch.cuda.empty_cache()
+    ref = oracle.das_sum(fields, rf_sub, das_synth.array_positions(cfg), *das_synth.tx_tables(cfg), voxels=vox)
+    assert_parity(y, ref, "large qmkb one chunk")

@@ -304,11 +304,13 @@ das_status das_beamform(const das_plan_t *plan, const void *rf, const float *rx_
     float *o = static_cast<float *>(out);
     hipError_t e;
     if (plan->alg == DAS_ALG_BATCH_INNER) {
-        // the staged kernel addresses the RF chunk and the transmit tables with
-        // 32-bit offsets; larger ones go to the direct kernel
+        // the staged kernel addresses a KQMB chunk and the transmit tables with
+        // 32-bit offsets (a QMKB chunk is rebased per step); larger ones go to
+        // the direct kernel
         const int64_t chunk = (int64_t)plan->p.B * plan->elem_bytes * plan->p.M * q_count * plan->p.K;
         const int64_t tables = (int64_t)plan->p.Q * plan->N * 4;
-        const bool staged = plan->staged && chunk < ((int64_t)1 << 32) && tables < ((int64_t)1 << 32);
+        const bool chunk_ok = plan->p.layout == DAS_LAYOUT_QMKB || chunk < ((int64_t)1 << 32);
+        const bool staged = plan->staged && chunk_ok && tables < ((int64_t)1 << 32);
         e = staged ? das_launch_batch_inner_staged(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s)
                    : das_launch_batch_inner(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s);
     }

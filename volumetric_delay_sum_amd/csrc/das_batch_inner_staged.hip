@@ -300,8 +300,11 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     // (rho, c) fetches 16 bytes (chunk c of the frame tile's part) of sample
     // row kmin + RPR r + rho, and the DMA writes lane l's 16 bytes at
     // 16 l past the round's LDS base, i.e. row rho, chunk c of the region.
-    // Lanes past the window are masked off.  The launch keeps the chunk under
-    // 4 GiB, so the offsets are 32-bit.
+    // Lanes past the window are masked off.  KQMB: the launch keeps the chunk
+    // under 4 GiB and every offset is 32-bit.  QMKB: the (event, receiver
+    // block) plane may lie past 4 GiB, so each step's copy rebases the buffer
+    // resource on its plane (64-bit scalar arithmetic) and only the offset
+    // inside the plane (receiver, sample row, frames) stays 32-bit.
     const das::BufRsrc rs_chunk = das::make_rsrc(rf_bytes, (uint64_t)chunk_bytes);
     const int crow = lane / G::LPR;
     const int64_t kstride = (LAYOUT == DAS_LAYOUT_KQMB) ? (int64_t)P.q_count * P.M * rowfull : rowfull;
@@ -310,20 +313,29 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     const uint32_t mstride32 = (uint32_t)m_stride;
     struct CopyPlan {
         int nr, rows;        // rounds and sample rows (wave-uniform)
-        uint32_t start;      // byte offset of the window's first sample row (less the frame tile)
+        uint32_t start;      // byte offset of the window's first sample row in rs (less the frame tile)
         uint32_t dst;        // LDS byte offset of the region
+        das::BufRsrc rs;     // the chunk (KQMB) or the step's (event, receiver block) plane onwards (QMKB)
     };
     auto copy_prepare = [&](const Cursor &c, const Window &wdw, int buf) -> CopyPlan {
         const int rows = __builtin_amdgcn_readfirstlane(wdw.rows_w);
         const uint32_t kmin = (uint32_t)__builtin_amdgcn_readfirstlane(wdw.kmin_w);
-        return CopyPlan{(rows + G::RPR - 1) / G::RPR, rows,
-                        ((uint32_t)c.ql * (uint32_t)P.M + (uint32_t)(c.m0 + wave)) * mstride32 + kmin * kstride32,
-                        (uint32_t)(buf * G::BUF + wave * G::REGION)};
+        const int nr = (rows + G::RPR - 1) / G::RPR;
+        const uint32_t dst = (uint32_t)(buf * G::BUF + wave * G::REGION);
+        if constexpr (LAYOUT == DAS_LAYOUT_QMKB) {
+            const int64_t plane = ((int64_t)c.ql * P.M + c.m0) * m_stride;
+            return CopyPlan{nr, rows, (uint32_t)wave * mstride32 + kmin * kstride32, dst,
+                            das::make_rsrc(rf_bytes + plane, (uint64_t)(chunk_bytes - plane))};
+        } else {
+            return CopyPlan{nr, rows,
+                            ((uint32_t)c.ql * (uint32_t)P.M + (uint32_t)(c.m0 + wave)) * mstride32 + kmin * kstride32,
+                            dst, rs_chunk};
+        }
     };
     auto copy_round = [&](const CopyPlan &cp, int r) {
         if (r < cp.nr && r * G::RPR + crow < cp.rows) {
             const das::lds_ptr dst = (das::lds_ptr)(lds + cp.dst + (uint32_t)(r * G::RPR * G::ROWB));   // generic -> LDS address space
-            das::buffer_load_lds(rs_chunk, dst, 16, (int)coff, (int)(cp.start + (uint32_t)(r * G::RPR) * kstride32), 0,
+            das::buffer_load_lds(cp.rs, dst, 16, (int)coff, (int)(cp.start + (uint32_t)(r * G::RPR) * kstride32), 0,
                                  0);
         }
     };
@@ -524,7 +536,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         }
         // the rows of the next step stream into the other buffer while this step computes
         wn = Window{};
-        CopyPlan cp{0, 0, 0, 0};
+        CopyPlan cp{0, 0, 0, 0, rs_chunk};
         if (hn) {
             wn = make_window(sn, sl, buf ^ 1);
             if (!wn.overflow)
