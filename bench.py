@@ -60,7 +60,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="main", help="workload: tiny, mid, main, main-c64, large")
-    ap.add_argument("--layout", default="kqmb", choices=["kqmb", "qmkb"])
+    ap.add_argument("--layout", default="qmkb", choices=["kqmb", "qmkb"],
+                    help="permuted layout (QMKB: whole volumes in one chunk; KQMB: chunks under 4 GiB)")
     ap.add_argument("--algorithm", default="batch_inner", choices=["batch_inner", "baseline"])
     ap.add_argument("--q-chunk", type=int, default=0,
                     help="transmit events per permute/beamform pair (0: as many as the plan allows)")
