@@ -82,18 +82,23 @@ struct Tx {
 };
 
 // Sample split of one (voxel, event, receiver): s = (tau_tx - t0) fs + d fs / c
-// in fp64, the receive part (already less t0 fs) from the geometry.  A term
-// counts iff 0 <= floor(s) <= K - 2; a term that does not gets weight 0 and
-// k = 0, so its reads stay inside the window.
+// in fp64, the receive part from the geometry, which folds in 1 - t0 fs, so
+// s1 = s + 1 here.  For s1 >= 0 its truncation is floor(s) + 1; below 0, a
+// NaN or beyond 2^32 the conversion gives 0 or saturates, so one unsigned
+// compare of k = trunc(s1) - 1 with K - 2 keeps exactly the terms with
+// 0 <= floor(s) <= K - 2.  A term that does not count gets weight 0 (its k
+// is then not meaningful; the window and the direct loads skip it).
 template <bool IQ>
 __device__ __forceinline__ Step make_step(const DasKParams &P, const das::RxTerm &R, Tx tx) {
-    const double s = __builtin_fma((double)tx.tau, P.fs, R.s_rx);
-    const double kf = __builtin_floor(s);
-    const bool valid = (kf >= 0.0) && (kf <= (double)(P.K - 2));
-    const float f = (float)(s - kf);
+    const double s1 = __builtin_fma((double)tx.tau, P.fs, R.s_rx);
+    uint32_t k1;
+    asm("v_cvt_u32_f64 %0, %1" : "=v"(k1) : "v"(s1));        // saturating, unlike a C conversion
+    const uint32_t k = k1 - 1u;
+    const bool valid = k <= (uint32_t)(P.K - 2);
+    const float f = (float)__builtin_amdgcn_fract(s1);
     const float w = valid ? tx.w * R.w : 0.0f;
     Step st;
-    st.k = valid ? (uint32_t)(int32_t)kf : 0u;
+    st.k = k;
     st.active = w != 0.0f;
     const float bw = w * f, aw = w - bw;
     if constexpr (IQ) {
@@ -166,8 +171,9 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     const uint32_t laneoff_l = (uint32_t)li * G::LANEB;           // byte offset in a staged row
 
     const int64_t rowfull = (int64_t)P.B * E;                       // one (k, q, m) row, all frames
-    const int64_t m_stride = (LAYOUT == DAS_LAYOUT_KQMB) ? rowfull : rowfull * P.K;
-    const int64_t q_stride = m_stride * P.M;
+    // receiver stride (the plan keeps 16 K B E below 2^32, so it is 32-bit);
+    // the (event, receiver) plane (q, m) starts at (q M + m) m_stride in both layouts
+    const uint32_t m_stride = (uint32_t)((LAYOUT == DAS_LAYOUT_KQMB) ? rowfull : rowfull * P.K);
     const int64_t chunk_bytes = rowfull * P.M * P.q_count * P.K;
     const char *rf_bytes = reinterpret_cast<const char *>(rfp);
 
@@ -208,7 +214,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             double vx, vy, vz;
             das::voxel_centre(Pg, ix, iy, min(tz * VPR + v, Pg.nz - 1), vx, vy, vz);
             R[v] = das::rx_term<IQ>(Pg, vx, vy, vz, px, py, pz);
-            R[v].s_rx -= Pg.t0fs;
+            R[v].s_rx += 1.0 - Pg.t0fs;                   // the sample split takes s + 1
             R[v].w = (mm < Pg.M) ? R[v].w : 0.0f;
         }
     };
@@ -310,7 +316,6 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     const int64_t kstride = (LAYOUT == DAS_LAYOUT_KQMB) ? (int64_t)P.q_count * P.M * rowfull : rowfull;
     const uint32_t kstride32 = (uint32_t)kstride;
     const uint32_t coff = (uint32_t)crow * kstride32 + (uint32_t)(lane % G::LPR) * 16 + (uint32_t)b0 * E;
-    const uint32_t mstride32 = (uint32_t)m_stride;
     struct CopyPlan {
         int nr, rows;        // rounds and sample rows (wave-uniform)
         uint32_t start;      // byte offset of the window's first sample row in rs (less the frame tile)
@@ -324,11 +329,11 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         const uint32_t dst = (uint32_t)(buf * G::BUF + wave * G::REGION);
         if constexpr (LAYOUT == DAS_LAYOUT_QMKB) {
             const int64_t plane = ((int64_t)c.ql * P.M + c.m0) * m_stride;
-            return CopyPlan{nr, rows, (uint32_t)wave * mstride32 + kmin * kstride32, dst,
+            return CopyPlan{nr, rows, (uint32_t)wave * m_stride + kmin * kstride32, dst,
                             das::make_rsrc(rf_bytes + plane, (uint64_t)(chunk_bytes - plane))};
         } else {
             return CopyPlan{nr, rows,
-                            ((uint32_t)c.ql * (uint32_t)P.M + (uint32_t)(c.m0 + wave)) * mstride32 + kmin * kstride32,
+                            ((uint32_t)c.ql * (uint32_t)P.M + (uint32_t)(c.m0 + wave)) * m_stride + kmin * kstride32,
                             dst, rs_chunk};
         }
     };
@@ -425,15 +430,15 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             das::settle(a, b, ai, bi);
         else
             das::settle(a, b);
-        const uint32_t koff = s.k * tap_stride;
+        const uint32_t koff = (s.active ? s.k : 0u) * tap_stride;   // a term that does not count reads row 0
         const int jmax = P.M - 1 - c.m0;
-        const int64_t pos = (int64_t)c.ql * q_stride + (int64_t)c.m0 * m_stride;
+        const int64_t pos = ((int64_t)c.ql * P.M + c.m0) * m_stride;
         const das::BufRsrc r0 = das::make_rsrc(rf_bytes + pos, (uint64_t)(chunk_bytes - pos));
         const das::BufRsrc r1 =
             das::make_rsrc(rf_bytes + pos + tap_stride, (uint64_t)(chunk_bytes - pos - (int64_t)tap_stride));
         das::unroll<ROW>([&](auto J) {
             constexpr int j = decltype(J)::value;
-            const uint32_t jo = laneoff_g + (uint32_t)(min(j, jmax) * m_stride);
+            const uint32_t jo = laneoff_g + (uint32_t)min(j, jmax) * m_stride;
             const uint32_t off = das::row_bcast<j>(koff) + jo;
             float x0[NF], x1[NF];
 #pragma unroll
