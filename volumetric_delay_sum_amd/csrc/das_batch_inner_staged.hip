@@ -218,31 +218,20 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             R[v].w = (mm < Pg.M) ? R[v].w : 0.0f;
         }
     };
-    // Transmit tables of the voxels, read two steps ahead through buffer loads
-    // (event offset in the scalar offset, voxel in the lane offset).  Complex
-    // data rebuilds the two buffer descriptors at each call (its registers
-    // are the tighter; measured faster there), real data keeps them: the
-    // reload's scalar-load wait would also wait for the window atomics.
-    const uint64_t tbytes = (uint64_t)P.Q * P.N * 4;
-    const das::BufRsrc rs_tau0 = das::make_rsrc(reinterpret_cast<const char *>(tau_tx), tbytes);
-    const das::BufRsrc rs_wtx0 = das::make_rsrc(reinterpret_cast<const char *>(w_tx), tbytes);
+    // Transmit tables of the voxels, read two steps ahead.  Each table is a
+    // 64-bit scalar base advanced to the event's row in scalar arithmetic,
+    // plus the voxel's 32-bit byte offset (the launch keeps Q N 4 < 2^32):
+    // two scalar registers per table where a buffer descriptor needs four.
+    const char *tau_base = reinterpret_cast<const char *>(tau_tx);
+    const char *w_base = reinterpret_cast<const char *>(w_tx);
     auto load_tx = [&](const Cursor &c, Tx (&txv)[VPR]) {
-        das::BufRsrc rs_tau = rs_tau0, rs_wtx = rs_wtx0;
-        uint32_t q_begin = (uint32_t)P.q_begin, nvox = (uint32_t)P.N;
-        if constexpr (IQ) {
-            const kptr ka = kargs();
-            const DasKParams &Pt = *(const DasKParams *)ka;
-            const uint64_t tb = (uint64_t)Pt.Q * Pt.N * 4;
-            rs_tau = das::make_rsrc(karg_ptr(ka, 2), tb);
-            rs_wtx = das::make_rsrc(karg_ptr(ka, 3), tb);
-            q_begin = (uint32_t)Pt.q_begin;
-            nvox = (uint32_t)Pt.N;
-        }
-        const uint32_t qoff = (q_begin + (uint32_t)c.ql) * nvox * 4u;   // the launch keeps Q N 4 < 2^32
+        const uint32_t qoff = (uint32_t)(P.q_begin + c.ql) * (uint32_t)P.N * 4u;
+        const char *tq = tau_base + qoff, *wq = w_base + qoff;
 #pragma unroll
-        for (int v = 0; v < VPR; ++v)
-            txv[v] = Tx{das::buffer_load_f32(rs_tau, n[v] * 4, (int)qoff, 0),
-                        das::buffer_load_f32(rs_wtx, n[v] * 4, (int)qoff, 0)};
+        for (int v = 0; v < VPR; ++v) {
+            const uint32_t o = (uint32_t)n[v] * 4u;
+            txv[v] = Tx{*reinterpret_cast<const float *>(tq + o), *reinterpret_cast<const float *>(wq + o)};
+        }
     };
     // Publish the lanes' k to the window of their receiver: one LDS atomic
     // min and max per active (voxel, receiver), four rows of a wave meeting
