@@ -367,20 +367,21 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     auto prefetch = [&](const uint32_t (&loff)[VPR], Ring &ring) {
         das::unroll<DEPTH>([&](auto T) { issue_item(T, loff, ring); });
     };
-    auto compute_lds = [&](const Step (&s)[VPR], const uint32_t (&loff)[VPR], float (&pt)[VPR][NF], Ring &ring,
+    // The step's coefficients are settled in place (they are dead after the
+    // loop), so no register copies are needed to give them their wait states.
+    auto compute_lds = [&](Step (&s)[VPR], const uint32_t (&loff)[VPR], float (&pt)[VPR][NF], Ring &ring,
                            auto &&at) {
-        float a[VPR], b[VPR], ai[VPR], bi[VPR];
 #pragma unroll
         for (int v = 0; v < VPR; ++v) {
-            a[v] = s[v].a;
-            b[v] = s[v].b;
-            ai[v] = s[v].ai;
-            bi[v] = s[v].bi;
             if constexpr (IQ)
-                das::settle(a[v], b[v], ai[v], bi[v]);
+                das::settle(s[v].a, s[v].b, s[v].ai, s[v].bi);
             else
-                das::settle(a[v], b[v]);
+                das::settle(s[v].a, s[v].b);
         }
+        auto a = [&](int v) -> float { return s[v].a; };
+        auto b = [&](int v) -> float { return s[v].b; };
+        auto ai = [&](int v) -> float { return s[v].ai; };
+        auto bi = [&](int v) -> float { return s[v].bi; };
         auto &ring0 = ring.r0;
         auto &ring1 = ring.r1;
         auto issue = [&](auto T) { issue_item(T, loff, ring); };
@@ -392,11 +393,11 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             if constexpr (IQ) {
 #pragma unroll
                 for (int f = 0; f < FL; ++f)
-                    das::cmac_bcast<j>(pt[v][2 * f], pt[v][2 * f + 1], a[v], ai[v], b[v], bi[v], x0[2 * f],
+                    das::cmac_bcast<j>(pt[v][2 * f], pt[v][2 * f + 1], a(v), ai(v), b(v), bi(v), x0[2 * f],
                                        x0[2 * f + 1], x1[2 * f], x1[2 * f + 1]);
             } else {
 #pragma unroll
-                for (int f = 0; f < FL; ++f) das::lerp_bcast<j>(pt[v][f], a[v], b[v], x0[f], x1[f]);
+                for (int f = 0; f < FL; ++f) das::lerp_bcast<j>(pt[v][f], a(v), b(v), x0[f], x1[f]);
             }
             if constexpr (tt + DEPTH < NITEM)
                 issue(das::ic<tt + DEPTH>{});
