@@ -26,7 +26,7 @@ def _ragged(iq=False, B=12, array=(37, 1), grid=(13, 7, 3), K=300, sources=None,
 
 @pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])
 @pytest.mark.parametrize("alg,layout", ALGS)
-@pytest.mark.parametrize("B", [12, 32, 40])
+@pytest.mark.parametrize("B", [12, 32, 40, 64])
 def test_ragged_full_compare(gpu, iq, alg, layout, B):
     cfg = _ragged(iq=iq, B=B)
     inp = Inputs(cfg, w_tx="uniform")
@@ -96,12 +96,14 @@ def test_q_chunks_sum_to_the_whole(gpu, alg, layout):
 @pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])
 @pytest.mark.parametrize("layout", ["kqmb", "qmkb"])
 @pytest.mark.parametrize("voxel", [0.25e-3, 0.6e-3, 1.5e-3], ids=["fine", "mixed", "coarse"])
-def test_staged_windows_and_fallback(gpu, layout, voxel, iq):
-    """B = 32: the LDS-staged kernel (fp32: 2 frames per lane, one 32-frame
-    tile; complex64: 1 frame per lane, two 16-frame tiles).  Coarse voxels give
-    k-windows wider than the LDS capacity, which must fall back to direct loads;
-    fine voxels stay in LDS; the mixed pitch exercises both within one launch."""
-    cfg = das_synth.custom_config("tiny", name="staged", seed=23, array=(19, 3), grid=(11, 10, 3), K=700, B=32,
+@pytest.mark.parametrize("B", [32, 64])
+def test_staged_windows_and_fallback(gpu, layout, voxel, iq, B):
+    """The LDS-staged kernel.  fp32 B = 32: 2 frames per lane, one 32-frame
+    tile of 16 receivers a step; fp32 B = 64 and complex64: two frame halves
+    per row (8 receivers a step, 256-byte rows).  Coarse voxels give k-windows
+    wider than the LDS capacity, which must fall back to direct loads; fine
+    voxels stay in LDS; the mixed pitch exercises both within one launch."""
+    cfg = das_synth.custom_config("tiny", name="staged", seed=23, array=(19, 3), grid=(11, 10, 3), K=700, B=B,
                                   tx="diverging", sources=((0.0, 0.0), (2e-3, 1e-3)), voxel=voxel,
                                   z0=3e-3, n_scatterers=0, iq=iq)
     inp = Inputs(cfg, w_tx="uniform")
@@ -109,6 +111,20 @@ def test_staged_windows_and_fallback(gpu, layout, voxel, iq):
     assert plan_info["staged"] == 1
     y = to_numpy(run_gpu(inp, "batch_inner", layout), iq)
     assert_parity(y, oracle_ref(inp), f"staged {layout} voxel {voxel} iq={iq}")
+
+
+@pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])
+def test_one_and_two_frame_halves_agree(gpu, monkeypatch, iq):
+    """B = 64: the staged kernel with two frame halves per row (the default
+    there) and with one (two frame tiles) both meet the bar."""
+    cfg = _ragged(B=64, grid=(17, 9, 4), iq=iq, array=(23, 2))
+    inp = Inputs(cfg, w_tx="uniform")
+    two = to_numpy(run_gpu(inp, "batch_inner", "qmkb"), iq)
+    monkeypatch.setenv("DAS_STAGED_HALVES", "1")
+    one = to_numpy(run_gpu(inp, "batch_inner", "qmkb"), iq)
+    ref = oracle_ref(inp)
+    assert_parity(two, ref, "two halves")
+    assert_parity(one, ref, "one half")
 
 
 @pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])

@@ -234,6 +234,9 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
     pl->q_group = pick_q_group(p, elem, pl->staged != 0);
     const char *vv = std::getenv("DAS_STAGED_VPR");
     pl->vpr = (vv && std::atoi(vv) == 1) ? 1 : 2;
+    // two frame halves per row where B allows (DAS_STAGED_HALVES=1 keeps one: comparisons)
+    const char *hv = std::getenv("DAS_STAGED_HALVES");
+    pl->halves = (pl->staged && pl->vpr == 2 && p.B % (2 * 16 * pl->fl) == 0 && !(hv && std::atoi(hv) == 1)) ? 2 : 1;
     *out = pl;
     return DAS_OK;
 }

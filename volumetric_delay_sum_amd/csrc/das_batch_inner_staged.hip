@@ -46,24 +46,33 @@ constexpr int ROW = 16;               // lanes per voxel column (one DPP row)
 constexpr int TX = 8, TY = 8;         // lateral voxel tile of one workgroup (one column per row)
 constexpr int LDS_ROW_BUDGET = 160000;   // bytes for the two row buffers
 
-template <bool IQ, int FL>
+// H frame halves: a 16-lane row covers H x 16 x FL frames of the frame tile,
+// each lane FL frames in each half.  With H = 2 a step takes 8 receivers, the
+// row's two voxels sit in its two lane halves (lane li holds the pair voxel
+// li / 8, receiver li % 8) and a staged sample row is twice as long, so the
+// LDS holds the same number of rows per receiver; the per-pair work (receive
+// geometry, sample split, window) is done once for twice the frames.
+template <bool IQ, int FL, int H>
 struct Geo {
     static constexpr int C = IQ ? 2 : 1;                 // floats per sample
     static constexpr int E = 4 * C;                      // bytes per sample
-    static constexpr int NF = FL * C;                    // floats per lane per tap
-    static constexpr int LANEB = NF * 4;                 // bytes per lane in a sample row
-    static constexpr int ROWB = ROW * LANEB;             // bytes of the frame tile in one sample row
-    static constexpr int RW0 = LDS_ROW_BUDGET / (2 * ROW * ROWB);
+    static constexpr int NF = FL * C;                    // floats per lane per tap and half
+    static constexpr int LANEB = NF * 4;                 // bytes per lane in a half of a sample row
+    static constexpr int HALFB = ROW * LANEB;            // bytes of one half of a staged sample row
+    static constexpr int ROWB = H * HALFB;               // bytes of the frame tile in one sample row
+    static constexpr int NRX = ROW / H;                  // receivers per step
+    static constexpr int RW0 = LDS_ROW_BUDGET / (2 * NRX * ROWB);
     static constexpr int RW = RW0 > 64 ? 64 : RW0;       // sample rows per receiver region
     static constexpr int W_MAX = RW - 1;                 // k positions per receiver window
     static constexpr int LPR = ROWB / 16;                // lanes per sample row in a 16-byte copy
     static constexpr int RPR = 64 / LPR;                 // sample rows per copy round of a wave
-    static constexpr int MAXR = (RW + RPR - 1) / RPR;    // copy rounds of a full region
+    static constexpr int MAXR = (RW + RPR * H - 1) / (RPR * H);   // copy rounds of one wave (H waves per receiver)
     static constexpr int REGION = RW * ROWB;             // bytes of one receiver's region
-    static constexpr int BUF = ROW * REGION;             // bytes of one buffer
-    static constexpr int LDS_BYTES = 2 * BUF + 3 * 2 * ROW * 4;
+    static constexpr int BUF = NRX * REGION;             // bytes of one buffer
+    static constexpr int LDS_BYTES = 2 * BUF + 3 * 2 * NRX * 4;
     static_assert(ROWB % 16 == 0 && 64 % LPR == 0, "copy granularity");
     static_assert(LANEB == 8 || LANEB == 16, "reader width");
+    static_assert(H == 1 || H == 2, "frame halves");
 };
 
 // Per-lane state of one voxel in one step: sample index and weights.
@@ -126,23 +135,29 @@ struct Tap {
     using type = float __attribute__((ext_vector_type(NF)));
 };
 
-template <bool IQ, int FL, int LAYOUT, int VPR>
+template <bool IQ, int FL, int LAYOUT, int VPR, int H>
 __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, const float *__restrict__ rfp,
                                                                 const float *__restrict__ rx,
                                                                 const float *__restrict__ tau_tx,
                                                                 const float *__restrict__ w_tx,
                                                                 float *__restrict__ out, uint32_t tap_stride) {
-    using G = Geo<IQ, FL>;
-    constexpr int C = G::C, E = G::E, NF = G::NF;
+    using G = Geo<IQ, FL, H>;
+    constexpr int C = G::C, E = G::E, NF = G::NF, NRX = G::NRX;
+    // (voxel, receiver) pairs per lane: pair p is voxel p H + li / NRX of the
+    // row and receiver m0 + li % NRX
+    constexpr int PL = VPR / H;
+    static_assert(VPR % H == 0, "each lane half needs a voxel");
     using TapV = typename Tap<NF>::type;
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
-    int *slots = reinterpret_cast<int *>(lds + 2 * G::BUF);   // [3 sets][min, max][16]
+    int *slots = reinterpret_cast<int *>(lds + 2 * G::BUF);   // [3 sets][min, max][NRX]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in SGPRs
     const int li = lane & (ROW - 1);
     const int vr = wave * 4 + (lane >> 4);           // voxel column 0..63
+    const int lrx = li % NRX;                        // receiver of this lane's pairs (m0 + lrx)
+    const int lv0 = li / NRX;                        // voxel of pair 0 (pair p: lv0 + p H)
 
     const int tiles_x = (P.nx + TX - 1) / TX, tiles_y = (P.ny + TY - 1) / TY;
     int t = das::xcd_tile(blockIdx.x, gridDim.x);
@@ -163,12 +178,22 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         n[v] = (min(iz, P.nz - 1) * P.ny + iy) * P.nx + ix;
     }
 
-    // frames of this lane: FL adjacent frames of the frame tile
-    const int b0 = blockIdx.y * (ROW * FL);
+    int n_p[PL];                                     // voxel index of each pair of this lane
+#pragma unroll
+    for (int p = 0; p < PL; ++p) {
+        n_p[p] = n[0];
+#pragma unroll
+        for (int v = 1; v < VPR; ++v)
+            n_p[p] = (lv0 + p * H == v) ? n[v] : n_p[p];
+    }
+
+    // frames of this lane: FL adjacent frames in each of the H halves of the
+    // frame tile (half h starts h 16 FL frames in)
+    const int b0 = blockIdx.y * (H * ROW * FL);
     const int bl = b0 + li * FL;
-    const bool fr_ok = bl < P.B;
-    const uint32_t laneoff_g = (uint32_t)(fr_ok ? bl : 0) * E;   // byte offset in a global row
-    const uint32_t laneoff_l = (uint32_t)li * G::LANEB;           // byte offset in a staged row
+    const bool fr_ok = bl + (H - 1) * ROW * FL < P.B;             // the plan keeps B a multiple of the tile
+    const uint32_t laneoff_g = (uint32_t)(fr_ok ? bl : 0) * E;   // byte offset in a global row (half 0)
+    const uint32_t laneoff_l = (uint32_t)li * G::LANEB;           // byte offset in a staged row (half 0)
 
     const int64_t rowfull = (int64_t)P.B * E;                       // one (k, q, m) row, all frames
     // receiver stride (the plan keeps 16 K B E below 2^32, so it is 32-bit);
@@ -180,8 +205,8 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     // zero both row buffers (so a zero weight never meets a non-finite stale value) and the window slots
     for (int i = tid * 16; i < 2 * G::BUF; i += THREADS * 16)
         *reinterpret_cast<int4 *>(lds + i) = make_int4(0, 0, 0, 0);
-    if (tid < 3 * 2 * ROW)
-        slots[tid] = ((tid / ROW) & 1) ? INT_MIN : INT_MAX;
+    if (tid < 3 * 2 * NRX)
+        slots[tid] = ((tid / NRX) & 1) ? INT_MIN : INT_MAX;
     __syncthreads();
 
     // ---- step helpers ---------------------------------------------------
@@ -200,19 +225,19 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         return *(const char *const *)(ka + sizeof(DasKParams) + i * sizeof(void *));
     };
 
-    das::RxTerm R[VPR];                  // receive terms of (voxel v, m0 + li) for the current block
+    das::RxTerm R[PL];                   // receive terms of this lane's pairs for the current block
     auto load_geometry = [&](int m0) {
         const kptr ka = kargs();
         const DasKParams &Pg = *(const DasKParams *)ka;
         const float *rxg = reinterpret_cast<const float *>(karg_ptr(ka, 1));
-        const int mm = m0 + li;
+        const int mm = m0 + lrx;
         const int m = min(mm, Pg.M - 1);
         const float px = rxg[3 * m], py = rxg[3 * m + 1], pz = rxg[3 * m + 2];
 #pragma unroll
-        for (int v = 0; v < VPR; ++v) {
+        for (int v = 0; v < PL; ++v) {
             // voxel centres are recomputed per receiver block rather than kept in registers
             double vx, vy, vz;
-            das::voxel_centre(Pg, ix, iy, min(tz * VPR + v, Pg.nz - 1), vx, vy, vz);
+            das::voxel_centre(Pg, ix, iy, min(tz * VPR + lv0 + v * H, Pg.nz - 1), vx, vy, vz);
             R[v] = das::rx_term<IQ>(Pg, vx, vy, vz, px, py, pz);
             R[v].s_rx += 1.0 - Pg.t0fs;                   // the sample split takes s + 1
             R[v].w = (mm < Pg.M) ? R[v].w : 0.0f;
@@ -224,12 +249,12 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     // two scalar registers per table where a buffer descriptor needs four.
     const char *tau_base = reinterpret_cast<const char *>(tau_tx);
     const char *w_base = reinterpret_cast<const char *>(w_tx);
-    auto load_tx = [&](const Cursor &c, Tx (&txv)[VPR]) {
+    auto load_tx = [&](const Cursor &c, Tx (&txv)[PL]) {
         const uint32_t qoff = (uint32_t)(P.q_begin + c.ql) * (uint32_t)P.N * 4u;
         const char *tq = tau_base + qoff, *wq = w_base + qoff;
 #pragma unroll
-        for (int v = 0; v < VPR; ++v) {
-            const uint32_t o = (uint32_t)n[v] * 4u;
+        for (int v = 0; v < PL; ++v) {
+            const uint32_t o = (uint32_t)n_p[v] * 4u;
             txv[v] = Tx{*reinterpret_cast<const float *>(tq + o), *reinterpret_cast<const float *>(wq + o)};
         }
     };
@@ -237,19 +262,19 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     // min and max per active (voxel, receiver), four rows of a wave meeting
     // on each receiver's slot.  The LDS has room for the conflicts; reducing
     // across rows first would cost more ALU than the atomics save.
-    auto publish = [&](const Step (&s)[VPR], int set) {
+    auto publish = [&](const Step (&s)[PL], int set) {
 #pragma unroll
-        for (int v = 0; v < VPR; ++v)
+        for (int v = 0; v < PL; ++v)
             if (s[v].active) {
-                atomicMin(&slots[set * 2 * ROW + li], (int)s[v].k);
-                atomicMax(&slots[set * 2 * ROW + ROW + li], (int)s[v].k);
+                atomicMin(&slots[set * 2 * NRX + lrx], (int)s[v].k);
+                atomicMax(&slots[set * 2 * NRX + NRX + lrx], (int)s[v].k);
             }
     };
     auto advance = [&](Cursor &c) -> bool {
         if (++c.ql < c.g1)
             return true;
         c.ql = c.g0;
-        c.m0 += ROW;
+        c.m0 += NRX;
         if (c.m0 < P.M)
             return true;
         c.m0 = 0;
@@ -260,38 +285,40 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     };
 
     // Window of the step in slot set `set`, staged in buffer `buf`: per lane
-    // and voxel the LDS byte offset of its receiver's row for k; the copy of
-    // this wave's receiver.
+    // and pair the LDS byte offset of its receiver's row for k; the copy of
+    // this wave's receiver (wave / H; H waves share one receiver's rows).
+    const int wrx = wave / H, wpart = wave % H;
     struct Window {
-        uint32_t loff[VPR];
+        uint32_t loff[PL];
         int kmin_w, rows_w;    // wave's copy: first sample row, number of sample rows
         bool overflow;
     };
     struct Slots {
-        int kmn, kmx, kmn_w, kmx_w;    // window of receiver li, and of this wave's receiver
+        int kmn, kmx, kmn_w, kmx_w;    // window of receiver lrx, and of this wave's receiver
     };
     auto read_slots = [&](int set) -> Slots {
-        return Slots{slots[set * 2 * ROW + li], slots[set * 2 * ROW + ROW + li], slots[set * 2 * ROW + wave],
-                     slots[set * 2 * ROW + ROW + wave]};
+        return Slots{slots[set * 2 * NRX + lrx], slots[set * 2 * NRX + NRX + lrx], slots[set * 2 * NRX + wrx],
+                     slots[set * 2 * NRX + NRX + wrx]};
     };
-    auto make_window = [&](const Step (&s)[VPR], const Slots &sl, int buf) -> Window {
+    auto make_window = [&](const Step (&s)[PL], const Slots &sl, int buf) -> Window {
         Window wdw;
-        const int np = (sl.kmn <= sl.kmx) ? sl.kmx - sl.kmn + 1 : 0;   // k positions of receiver li
-        const uint32_t base = (uint32_t)(buf * G::BUF + li * G::REGION);
+        const int np = (sl.kmn <= sl.kmx) ? sl.kmx - sl.kmn + 1 : 0;   // k positions of receiver lrx
+        const uint32_t base = (uint32_t)(buf * G::BUF + lrx * G::REGION);
 #pragma unroll
-        for (int v = 0; v < VPR; ++v)
+        for (int v = 0; v < PL; ++v)
             wdw.loff[v] = s[v].active ? base + (uint32_t)((int)s[v].k - sl.kmn) * G::ROWB : base;
         wdw.overflow = __any(np > G::W_MAX);
         wdw.kmin_w = sl.kmn_w;
         wdw.rows_w = (sl.kmn_w <= sl.kmx_w) ? sl.kmx_w - sl.kmn_w + 2 : 0;   // sample rows kmin .. kmax + 1
         return wdw;
     };
-    auto read_window = [&](const Step (&s)[VPR], int set, int buf) -> Window {
+    auto read_window = [&](const Step (&s)[PL], int set, int buf) -> Window {
         return make_window(s, read_slots(set), buf);
     };
 
     // Copy of one receiver's sample rows by LDS-DMA (wave w copies receiver
-    // m0 + w into its region of the buffer).  Round r moves RPR rows: lane
+    // m0 + w / H into its region of the buffer, taking every H-th round
+    // starting at w % H).  A round moves RPR rows: lane
     // (rho, c) fetches 16 bytes (chunk c of the frame tile's part) of sample
     // row kmin + RPR r + rho, and the DMA writes lane l's 16 bytes at
     // 16 l past the round's LDS base, i.e. row rho, chunk c of the region.
@@ -314,91 +341,104 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     auto copy_prepare = [&](const Cursor &c, const Window &wdw, int buf) -> CopyPlan {
         const int rows = __builtin_amdgcn_readfirstlane(wdw.rows_w);
         const uint32_t kmin = (uint32_t)__builtin_amdgcn_readfirstlane(wdw.kmin_w);
-        const int nr = (rows + G::RPR - 1) / G::RPR;
-        const uint32_t dst = (uint32_t)(buf * G::BUF + wave * G::REGION);
+        const int nr = (rows + G::RPR * H - 1) / (G::RPR * H);     // this wave's rounds (at most)
+        const uint32_t dst = (uint32_t)(buf * G::BUF + wrx * G::REGION);
         if constexpr (LAYOUT == DAS_LAYOUT_QMKB) {
             const int64_t plane = ((int64_t)c.ql * P.M + c.m0) * m_stride;
-            return CopyPlan{nr, rows, (uint32_t)wave * m_stride + kmin * kstride32, dst,
+            return CopyPlan{nr, rows, (uint32_t)wrx * m_stride + kmin * kstride32, dst,
                             das::make_rsrc(rf_bytes + plane, (uint64_t)(chunk_bytes - plane))};
         } else {
             return CopyPlan{nr, rows,
-                            ((uint32_t)c.ql * (uint32_t)P.M + (uint32_t)(c.m0 + wave)) * m_stride + kmin * kstride32,
+                            ((uint32_t)c.ql * (uint32_t)P.M + (uint32_t)(c.m0 + wrx)) * m_stride + kmin * kstride32,
                             dst, rs_chunk};
         }
     };
     auto copy_round = [&](const CopyPlan &cp, int r) {
-        if (r < cp.nr && r * G::RPR + crow < cp.rows) {
-            const das::lds_ptr dst = (das::lds_ptr)(lds + cp.dst + (uint32_t)(r * G::RPR * G::ROWB));   // generic -> LDS address space
-            das::buffer_load_lds(cp.rs, dst, 16, (int)coff, (int)(cp.start + (uint32_t)(r * G::RPR) * kstride32), 0,
+        const int rr = r * H + wpart;                               // round of the receiver's copy
+        if (r < cp.nr && rr * G::RPR + crow < cp.rows) {
+            const das::lds_ptr dst = (das::lds_ptr)(lds + cp.dst + (uint32_t)(rr * G::RPR * G::ROWB));   // generic -> LDS address space
+            das::buffer_load_lds(cp.rs, dst, 16, (int)coff, (int)(cp.start + (uint32_t)(rr * G::RPR) * kstride32), 0,
                                  0);
         }
     };
 
-    float acc[VPR][NF], part[VPR][NF];
+    constexpr int HNF = H * NF;                      // floats of one voxel per lane and tap
+    float acc[VPR][HNF], part[VPR][HNF];
 #pragma unroll
     for (int v = 0; v < VPR; ++v)
 #pragma unroll
-        for (int i = 0; i < NF; ++i) {
+        for (int i = 0; i < HNF; ++i) {
             acc[v][i] = 0.0f;
             part[v][i] = 0.0f;
         }
 
-    // All voxels of one step from LDS: VPR x 16 (voxel, receiver) items, each
-    // two reads (taps k and k + 1: consecutive rows) and 2 FL (IQ: 8 FL) FMAs
-    // with the receiver's coefficients broadcast from its lane.  The reads are
-    // issued DEPTH items ahead; the scheduling fences keep the compiler from
-    // sinking each read next to its use, which would leave one read in flight
-    // per wave (three ahead measured best with two voxels per row, eight with
-    // one).  `at(t)` runs after item t (the next step's copy rounds).
-    constexpr int NITEM = VPR * ROW;
-    constexpr int DEPTH = (VPR == 1) ? 8 : 3;
+    // All voxels of one step from LDS: VPR x NRX (voxel, receiver) items.  Item
+    // (v, j) takes its coefficients and row offset from lane (v % H) NRX + j
+    // (pair v / H); each lane reads taps k and k + 1 of its frames (rows k and
+    // k + 1 are consecutive; H halves each) and does 2 H FL (IQ: 8 H FL) FMAs.
+    // The reads are issued DEPTH items ahead; the scheduling fences keep the
+    // compiler from sinking each read next to its use, which would leave one
+    // read in flight per wave (three ahead measured best with two voxels per
+    // row, eight with one).  `at(t)` runs after item t (the next step's copy
+    // rounds).
+    constexpr int NITEM = VPR * NRX;
+    constexpr int DEPTH = (VPR == 1) ? 8 : (H == 2 ? 2 : 3);   // H = 2: two reads per item
     // The first DEPTH items' reads are issued by prefetch(), for fp32 data at
     // the top of the step, so they land while the setup runs.
     struct Ring {
-        TapV r0[DEPTH], r1[DEPTH];
+        TapV r0[DEPTH][H], r1[DEPTH][H];
     };
-    auto issue_item = [&](auto T, const uint32_t (&loff)[VPR], Ring &ring) {
+    auto issue_item = [&](auto T, const uint32_t (&loff)[PL], Ring &ring) {
         constexpr int tt = decltype(T)::value;
-        constexpr int v = tt / ROW, j = tt % ROW;
-        const uint32_t addr = das::row_bcast<j>(loff[v]) + laneoff_l;
-        ring.r0[tt % DEPTH] = *reinterpret_cast<const TapV *>(lds + addr);
-        ring.r1[tt % DEPTH] = *reinterpret_cast<const TapV *>(lds + addr + G::ROWB);
+        constexpr int v = tt / NRX, j = tt % NRX, src = (v % H) * NRX + j, pr = v / H;
+        const uint32_t addr = das::row_bcast<src>(loff[pr]) + laneoff_l;
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+            ring.r0[tt % DEPTH][h] = *reinterpret_cast<const TapV *>(lds + addr + h * G::HALFB);
+            ring.r1[tt % DEPTH][h] = *reinterpret_cast<const TapV *>(lds + addr + G::ROWB + h * G::HALFB);
+        }
     };
-    auto prefetch = [&](const uint32_t (&loff)[VPR], Ring &ring) {
+    auto prefetch = [&](const uint32_t (&loff)[PL], Ring &ring) {
         das::unroll<DEPTH>([&](auto T) { issue_item(T, loff, ring); });
+    };
+    // Interpolate-weight-accumulate of item tt from its two taps.
+    auto item_fma = [&](auto T, Step (&s)[PL], float (&pt)[VPR][HNF], const TapV (&x0)[H], const TapV (&x1)[H]) {
+        constexpr int tt = decltype(T)::value;
+        constexpr int v = tt / NRX, j = tt % NRX, src = (v % H) * NRX + j, pr = v / H;
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+            if constexpr (IQ) {
+#pragma unroll
+                for (int f = 0; f < FL; ++f)
+                    das::cmac_bcast<src>(pt[v][h * NF + 2 * f], pt[v][h * NF + 2 * f + 1], s[pr].a, s[pr].ai,
+                                         s[pr].b, s[pr].bi, x0[h][2 * f], x0[h][2 * f + 1], x1[h][2 * f],
+                                         x1[h][2 * f + 1]);
+            } else {
+#pragma unroll
+                for (int f = 0; f < FL; ++f)
+                    das::lerp_bcast<src>(pt[v][h * NF + f], s[pr].a, s[pr].b, x0[h][f], x1[h][f]);
+            }
+        }
     };
     // The step's coefficients are settled in place (they are dead after the
     // loop), so no register copies are needed to give them their wait states.
-    auto compute_lds = [&](Step (&s)[VPR], const uint32_t (&loff)[VPR], float (&pt)[VPR][NF], Ring &ring,
-                           auto &&at) {
+    auto settle_all = [&](Step (&s)[PL]) {
 #pragma unroll
-        for (int v = 0; v < VPR; ++v) {
+        for (int p = 0; p < PL; ++p) {
             if constexpr (IQ)
-                das::settle(s[v].a, s[v].b, s[v].ai, s[v].bi);
+                das::settle(s[p].a, s[p].b, s[p].ai, s[p].bi);
             else
-                das::settle(s[v].a, s[v].b);
+                das::settle(s[p].a, s[p].b);
         }
-        auto a = [&](int v) -> float { return s[v].a; };
-        auto b = [&](int v) -> float { return s[v].b; };
-        auto ai = [&](int v) -> float { return s[v].ai; };
-        auto bi = [&](int v) -> float { return s[v].bi; };
-        auto &ring0 = ring.r0;
-        auto &ring1 = ring.r1;
+    };
+    auto compute_lds = [&](Step (&s)[PL], const uint32_t (&loff)[PL], float (&pt)[VPR][HNF], Ring &ring,
+                           auto &&at) {
+        settle_all(s);
         auto issue = [&](auto T) { issue_item(T, loff, ring); };
         __builtin_amdgcn_sched_barrier(0);
         das::unroll<NITEM>([&](auto T) {
             constexpr int tt = decltype(T)::value;
-            constexpr int v = tt / ROW, j = tt % ROW;
-            const TapV x0 = ring0[tt % DEPTH], x1 = ring1[tt % DEPTH];
-            if constexpr (IQ) {
-#pragma unroll
-                for (int f = 0; f < FL; ++f)
-                    das::cmac_bcast<j>(pt[v][2 * f], pt[v][2 * f + 1], a(v), ai(v), b(v), bi(v), x0[2 * f],
-                                       x0[2 * f + 1], x1[2 * f], x1[2 * f + 1]);
-            } else {
-#pragma unroll
-                for (int f = 0; f < FL; ++f) das::lerp_bcast<j>(pt[v][f], a(v), b(v), x0[f], x1[f]);
-            }
+            item_fma(T, s, pt, ring.r0[tt % DEPTH], ring.r1[tt % DEPTH]);
             if constexpr (tt + DEPTH < NITEM)
                 issue(das::ic<tt + DEPTH>{});
             at(T);
@@ -413,37 +453,43 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             __builtin_amdgcn_sched_barrier(0);
         });
     };
-    // One voxel of one step by direct loads from the permuted buffer (windows too wide for LDS).
-    auto compute_direct = [&](const Step &s, const Cursor &c, float (&pt)[NF]) {
-        float a = s.a, b = s.b, ai = s.ai, bi = s.bi;
+    // One voxel of one step by direct loads from the permuted buffer (windows
+    // too wide for LDS).  A term that does not count reads row 0.
+    auto compute_direct = [&](auto V, Step (&s)[PL], const Cursor &c, float (&pt)[VPR][HNF]) {
+        constexpr int v = decltype(V)::value, pr = v / H;
+        float a = s[pr].a, b = s[pr].b, ai = s[pr].ai, bi = s[pr].bi;
         if constexpr (IQ)
             das::settle(a, b, ai, bi);
         else
             das::settle(a, b);
-        const uint32_t koff = (s.active ? s.k : 0u) * tap_stride;   // a term that does not count reads row 0
+        const uint32_t koff = (s[pr].active ? s[pr].k : 0u) * tap_stride;
         const int jmax = P.M - 1 - c.m0;
         const int64_t pos = ((int64_t)c.ql * P.M + c.m0) * m_stride;
         const das::BufRsrc r0 = das::make_rsrc(rf_bytes + pos, (uint64_t)(chunk_bytes - pos));
         const das::BufRsrc r1 =
             das::make_rsrc(rf_bytes + pos + tap_stride, (uint64_t)(chunk_bytes - pos - (int64_t)tap_stride));
-        das::unroll<ROW>([&](auto J) {
-            constexpr int j = decltype(J)::value;
+        das::unroll<NRX>([&](auto J) {
+            constexpr int j = decltype(J)::value, src = (v % H) * NRX + j;
             const uint32_t jo = laneoff_g + (uint32_t)min(j, jmax) * m_stride;
-            const uint32_t off = das::row_bcast<j>(koff) + jo;
-            float x0[NF], x1[NF];
+            const uint32_t off = das::row_bcast<src>(koff) + jo;
 #pragma unroll
-            for (int i = 0; i < NF; ++i) {
-                x0[i] = das::buffer_load_f32(r0, (int)(off + 4 * i), 0, 0);
-                x1[i] = das::buffer_load_f32(r1, (int)(off + 4 * i), 0, 0);
-            }
-            if constexpr (IQ) {
+            for (int h = 0; h < H; ++h) {
+                float x0[NF], x1[NF];
 #pragma unroll
-                for (int f = 0; f < FL; ++f)
-                    das::cmac_bcast<j>(pt[2 * f], pt[2 * f + 1], a, ai, b, bi, x0[2 * f], x0[2 * f + 1],
-                                       x1[2 * f], x1[2 * f + 1]);
-            } else {
+                for (int i = 0; i < NF; ++i) {
+                    const int o = (int)(off + (uint32_t)(h * ROW * FL * E) + 4 * i);
+                    x0[i] = das::buffer_load_f32(r0, o, 0, 0);
+                    x1[i] = das::buffer_load_f32(r1, o, 0, 0);
+                }
+                if constexpr (IQ) {
 #pragma unroll
-                for (int f = 0; f < FL; ++f) das::lerp_bcast<j>(pt[f], a, b, x0[f], x1[f]);
+                    for (int f = 0; f < FL; ++f)
+                        das::cmac_bcast<src>(pt[v][h * NF + 2 * f], pt[v][h * NF + 2 * f + 1], a, ai, b, bi,
+                                             x0[2 * f], x0[2 * f + 1], x1[2 * f], x1[2 * f + 1]);
+                } else {
+#pragma unroll
+                    for (int f = 0; f < FL; ++f) das::lerp_bcast<src>(pt[v][h * NF + f], a, b, x0[f], x1[f]);
+                }
             }
         });
     };
@@ -454,11 +500,11 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     // copied during step i, and one barrier ends each step.
     Cursor cur{0, 0, 0, min(P.q_group, P.q_count)};
     load_geometry(cur.m0);
-    Step s_cur[VPR], s_nxt[VPR];
-    Tx tx_a[VPR], tx_b[VPR];
+    Step s_cur[PL], s_nxt[PL];
+    Tx tx_a[PL], tx_b[PL];
     load_tx(cur, tx_a);
 #pragma unroll
-    for (int v = 0; v < VPR; ++v) s_cur[v] = make_step<IQ>(P, R[v], tx_a[v]);
+    for (int v = 0; v < PL; ++v) s_cur[v] = make_step<IQ>(P, R[v], tx_a[v]);
     publish(s_cur, 0);
     Cursor nxt = cur;
     bool has_next = advance(nxt);
@@ -469,10 +515,10 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             load_geometry(nxt.m0);
         load_tx(nxt, tx_b);
 #pragma unroll
-        for (int v = 0; v < VPR; ++v) s_nxt[v] = make_step<IQ>(P, R[v], tx_b[v]);
+        for (int v = 0; v < PL; ++v) s_nxt[v] = make_step<IQ>(P, R[v], tx_b[v]);
         publish(s_nxt, 1);
     }
-    Tx tx_nxt2[VPR];                                   // tables of step i + 2, read a step ahead
+    Tx tx_nxt2[PL];                                    // tables of step i + 2, read a step ahead
     if (has_next2)
         load_tx(nxt2, tx_nxt2);
     __syncthreads();
@@ -491,12 +537,12 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     // loop is unrolled six times with the roles passed as references: every
     // role keeps its registers and no state is copied between steps.
     int set = 0, buf = 0;                              // slot set and row buffer of the current step
-    Step s_spare[VPR];
-    Tx tx_spare[VPR];
+    Step s_spare[PL];
+    Tx tx_spare[PL];
     Window w_spare{};
     // `Last` false: the caller guarantees a next step (has_next), so the step
     // has no exit.
-    auto step = [&](auto Last, Step (&sc)[VPR], Step (&sn)[VPR], Step (&sn2)[VPR], Tx (&t2)[VPR], Tx (&t3)[VPR],
+    auto step = [&](auto Last, Step (&sc)[PL], Step (&sn)[PL], Step (&sn2)[PL], Tx (&t2)[PL], Tx (&t3)[PL],
                     Window &wc, Window &wn) __attribute__((always_inline)) -> bool {
         constexpr bool can_end = decltype(Last)::value;
         const bool hn = can_end ? has_next : true;
@@ -522,7 +568,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             if (nxt2.m0 != nxt.m0)
                 load_geometry(nxt2.m0);
 #pragma unroll
-            for (int v = 0; v < VPR; ++v) sn2[v] = make_step<IQ>(P, R[v], t2[v]);
+            for (int v = 0; v < PL; ++v) sn2[v] = make_step<IQ>(P, R[v], t2[v]);
             publish(sn2, set2);
             // after the window's LDS atomics: the compiler orders those behind
             // every outstanding vector load (the row copies write LDS)
@@ -538,9 +584,11 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
                 cp = copy_prepare(nxt, wn, buf ^ 1);
         }
         if (!wc.overflow) {
-            // copy round r after item 4 r + 2: early, so the rows have the rest
-            // of the loop to land, yet not all at once
-            constexpr int SPREAD = 4;
+            // copy round r after item SPREAD r + SPREAD / 2 (every 4th item, every
+            // 3rd with the shorter loop of two frame halves): early, so the
+            // rows have the rest of the loop to land, yet not all at once
+            constexpr int SPREAD = (NITEM >= 4 * G::MAXR) ? 4 : 3;
+            static_assert(SPREAD * (G::MAXR - 1) + SPREAD / 2 < NITEM, "every copy round is issued");
             if constexpr (IQ)
                 prefetch(wc.loff, ring);
             compute_lds(sc, wc.loff, part, ring, [&](auto T) {
@@ -551,12 +599,11 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         } else {
 #pragma unroll
             for (int r = 0; r < G::MAXR; ++r) copy_round(cp, r);
-#pragma unroll
-            for (int v = 0; v < VPR; ++v) compute_direct(sc[v], cur, part[v]);
+            das::unroll<VPR>([&](auto V) { compute_direct(V, sc, cur, part); });
         }
 
-        if (tid < 2 * ROW)                              // this step's window was read last step
-            slots[set * 2 * ROW + tid] = (tid < ROW) ? INT_MAX : INT_MIN;
+        if (tid < 2 * NRX)                              // this step's window was read last step
+            slots[set * 2 * NRX + tid] = (tid < NRX) ? INT_MAX : INT_MIN;
 
         const bool flush = !hn || nxt.m0 != cur.m0 || nxt.g0 != cur.g0;
         cur = nxt;
@@ -570,7 +617,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
 #pragma unroll
             for (int v = 0; v < VPR; ++v)
 #pragma unroll
-                for (int i = 0; i < NF; ++i) {
+                for (int i = 0; i < HNF; ++i) {
                     acc[v][i] += part[v][i];
                     part[v][i] = 0.0f;
                 }
@@ -587,7 +634,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     // block and copy them lane by lane every step), then the last steps one
     // at a time with the roles copied.
     using das::ic;
-    const int nsteps = P.q_count * ((P.M + ROW - 1) / ROW);
+    const int nsteps = P.q_count * ((P.M + NRX - 1) / NRX);
     for (int left = nsteps; left >= 7; left -= 6) {
         step(ic<0>{}, s_cur, s_nxt, s_spare, tx_nxt2, tx_spare, w_cur, w_spare);
         step(ic<0>{}, s_nxt, s_spare, s_cur, tx_spare, tx_nxt2, w_spare, w_cur);
@@ -598,7 +645,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     }
     while (step(ic<1>{}, s_cur, s_nxt, s_spare, tx_nxt2, tx_spare, w_cur, w_spare)) {
 #pragma unroll
-        for (int v = 0; v < VPR; ++v) {
+        for (int v = 0; v < PL; ++v) {
             const Step st = s_cur[v];
             s_cur[v] = s_nxt[v];
             s_nxt[v] = s_spare[v];
@@ -618,23 +665,26 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             if (!vox_ok[v])
                 continue;
 #pragma unroll
-            for (int f = 0; f < FL; ++f) {
-                float *o = out + ((int64_t)(bl + f) * P.N + n[v]) * C;
+            for (int h = 0; h < H; ++h)
 #pragma unroll
-                for (int c = 0; c < C; ++c) o[c] = P.accumulate ? o[c] + acc[v][f * C + c] : acc[v][f * C + c];
-            }
+                for (int f = 0; f < FL; ++f) {
+                    float *o = out + ((int64_t)(bl + h * ROW * FL + f) * P.N + n[v]) * C;
+                    const float *a = &acc[v][h * NF + f * C];
+#pragma unroll
+                    for (int c = 0; c < C; ++c) o[c] = P.accumulate ? o[c] + a[c] : a[c];
+                }
         }
     }
 }
 
-template <bool IQ, int FL, int LAYOUT, int VPR>
+template <bool IQ, int FL, int LAYOUT, int VPR, int H = 1>
 hipError_t launch(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
                   const float *tau, const float *w, float *out, hipStream_t stream) {
     const int64_t row_bytes = (int64_t)kp.B * plan.elem_bytes;
     const int64_t tap = (LAYOUT == DAS_LAYOUT_KQMB) ? row_bytes * kp.q_count * kp.M : row_bytes;
     const int tiles = ((kp.nx + TX - 1) / TX) * ((kp.ny + TY - 1) / TY) * ((kp.nz + VPR - 1) / VPR);
-    const int ftiles = (kp.B + ROW * FL - 1) / (ROW * FL);
-    hipLaunchKernelGGL((das_bi_staged_kernel<IQ, FL, LAYOUT, VPR>), dim3(tiles, ftiles), dim3(THREADS), 0,
+    const int ftiles = (kp.B + H * ROW * FL - 1) / (H * ROW * FL);
+    hipLaunchKernelGGL((das_bi_staged_kernel<IQ, FL, LAYOUT, VPR, H>), dim3(tiles, ftiles), dim3(THREADS), 0,
                        stream, kp, rf, rx, tau, w, out, (uint32_t)tap);
     return hipGetLastError();
 }
@@ -644,12 +694,18 @@ hipError_t launch_vpr(const das_plan_t &plan, const DasKParams &kp, const float 
                       const float *tau, const float *w, float *out, hipStream_t stream) {
     // fp32: 2 frames per lane; complex64: 1 frame per lane.  Either way a lane
     // holds 8 bytes of a sample row and a staged row is 128 bytes.
-    if (plan.p.dtype == DAS_C64)
-        return plan.vpr == 1 ? launch<true, 1, LAYOUT, 1>(plan, kp, rf, rx, tau, w, out, stream)
-                             : launch<true, 1, LAYOUT, 2>(plan, kp, rf, rx, tau, w, out, stream);
+    // With two frame halves (B a multiple of 64 fp32 / 32 complex frames) a
+    // row is 256 bytes and a step takes 8 receivers.
+    if (plan.p.dtype == DAS_C64) {
+        if (plan.vpr == 1)
+            return launch<true, 1, LAYOUT, 1>(plan, kp, rf, rx, tau, w, out, stream);
+        return plan.halves == 2 ? launch<true, 1, LAYOUT, 2, 2>(plan, kp, rf, rx, tau, w, out, stream)
+                                : launch<true, 1, LAYOUT, 2>(plan, kp, rf, rx, tau, w, out, stream);
+    }
     if (plan.vpr == 1)
         return launch<false, 2, LAYOUT, 1>(plan, kp, rf, rx, tau, w, out, stream);
-    return launch<false, 2, LAYOUT, 2>(plan, kp, rf, rx, tau, w, out, stream);
+    return plan.halves == 2 ? launch<false, 2, LAYOUT, 2, 2>(plan, kp, rf, rx, tau, w, out, stream)
+                            : launch<false, 2, LAYOUT, 2>(plan, kp, rf, rx, tau, w, out, stream);
 }
 
 }  // namespace
