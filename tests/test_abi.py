@@ -129,7 +129,8 @@ def test_plan_info_and_sizes():
     assert pl.info["staged"] == 1
     assert das.Plan(**_problem(B=40, dtype="c64", f_demod=5e6)).info["staged"] == 0   # IQ, B % 16 != 0
     assert das.Plan(**_problem(B=32)).info["staged"] == 1      # fp32, B % 32 == 0: LDS-staged
-    assert das.Plan(**_problem(B=16)).info["staged"] == 0
+    assert das.Plan(**_problem(B=16)).info["staged"] == 1      # fp32, B % 16 == 0: LDS-staged, 1 frame per lane
+    assert das.Plan(**_problem(B=24)).info["staged"] == 0
     assert das.Plan(**_problem(B=32, algorithm="baseline")).info["staged"] == 0
     pl3 = das.Plan(**_problem(layout="qmkb"))
     assert pl3.permuted_shape(2) == (2, 8, 64, 4)
@@ -171,10 +172,11 @@ def test_auto_selection(dtype, B, alg):
 @pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (24, 1), (32, 2), (48, 1), (64, 2), (96, 2), (66, 1),
                                   (160, 2), (68, 4)])
 def test_frames_per_lane_choice(B, fl):
-    # fp32 batch-inner: the LDS-staged kernel (2 frames per lane) wherever B % 32 == 0
+    # fp32 batch-inner: the LDS-staged kernel wherever B % 16 == 0 (2 frames
+    # per lane when B % 32 == 0, else 1)
     pl = das.Plan(**_problem(B=B))
     assert pl.info["frames_per_lane"] == fl
-    assert pl.info["staged"] == (1 if B % 32 == 0 else 0)
+    assert pl.info["staged"] == (1 if B % 16 == 0 else 0)
 
 
 @pytest.mark.parametrize("B,fl", [(32, 2), (64, 4), (96, 4), (160, 4)])

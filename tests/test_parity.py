@@ -26,7 +26,7 @@ def _ragged(iq=False, B=12, array=(37, 1), grid=(13, 7, 3), K=300, sources=None,
 
 @pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])
 @pytest.mark.parametrize("alg,layout", ALGS)
-@pytest.mark.parametrize("B", [12, 32, 40, 64])
+@pytest.mark.parametrize("B", [12, 16, 32, 40, 48, 64])
 def test_ragged_full_compare(gpu, iq, alg, layout, B):
     cfg = _ragged(iq=iq, B=B)
     inp = Inputs(cfg, w_tx="uniform")
@@ -96,7 +96,7 @@ def test_q_chunks_sum_to_the_whole(gpu, alg, layout):
 @pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])
 @pytest.mark.parametrize("layout", ["kqmb", "qmkb"])
 @pytest.mark.parametrize("voxel", [0.25e-3, 0.6e-3, 1.5e-3], ids=["fine", "mixed", "coarse"])
-@pytest.mark.parametrize("B", [32, 64])
+@pytest.mark.parametrize("B", [16, 32, 64])
 def test_staged_windows_and_fallback(gpu, layout, voxel, iq, B):
     """The LDS-staged kernel.  fp32 B = 32: 2 frames per lane, one 32-frame
     tile of 16 receivers a step; fp32 B = 64 and complex64: two frame halves

@@ -221,13 +221,16 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
     pl->fl = pick_fl(p.B, p.dtype);
     pl->bt = 8;
     // LDS-staged batch-inner kernel where it is built (fp32 with B a multiple
-    // of 32, two frames per lane, or complex64 with B a multiple of 16, one
-    // frame per lane; larger B runs as several frame tiles);
+    // of 32, two frames per lane, or of 16, one frame per lane; complex64 with
+    // B a multiple of 16, one frame per lane; larger B runs as several frame
+    // tiles or two frame halves per row);
     // DAS_BI_KERNEL=direct selects the direct-load kernel (comparisons).
     const char *kv = std::getenv("DAS_BI_KERNEL");
     const bool want_staged = pl->alg == DAS_ALG_BATCH_INNER && !(kv && std::strcmp(kv, "direct") == 0);
     if (want_staged && p.dtype == DAS_F32 && p.B % 32 == 0)
         pl->fl = 2;
+    else if (want_staged && p.dtype == DAS_F32 && p.B % 16 == 0)
+        pl->fl = 1;
     if (want_staged && p.dtype == DAS_C64 && p.B % 16 == 0)
         pl->fl = 1;
     pl->staged = (want_staged && das_staged_supported(*pl)) ? 1 : 0;

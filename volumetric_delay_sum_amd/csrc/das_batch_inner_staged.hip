@@ -71,7 +71,7 @@ struct Geo {
     static constexpr int BUF = NRX * REGION;             // bytes of one buffer
     static constexpr int LDS_BYTES = 2 * BUF + 3 * 2 * NRX * 4;
     static_assert(ROWB % 16 == 0 && 64 % LPR == 0, "copy granularity");
-    static_assert(LANEB == 8 || LANEB == 16, "reader width");
+    static_assert(LANEB == 4 || LANEB == 8 || LANEB == 16, "reader width");
     static_assert(H == 1 || H == 2, "frame halves");
 };
 
@@ -702,6 +702,8 @@ hipError_t launch_vpr(const das_plan_t &plan, const DasKParams &kp, const float 
         return plan.halves == 2 ? launch<true, 1, LAYOUT, 2, 2>(plan, kp, rf, rx, tau, w, out, stream)
                                 : launch<true, 1, LAYOUT, 2>(plan, kp, rf, rx, tau, w, out, stream);
     }
+    if (plan.fl == 1)                                // fp32, B a multiple of 16 but not of 32: 64-byte rows
+        return launch<false, 1, LAYOUT, 2>(plan, kp, rf, rx, tau, w, out, stream);
     if (plan.vpr == 1)
         return launch<false, 2, LAYOUT, 1>(plan, kp, rf, rx, tau, w, out, stream);
     return plan.halves == 2 ? launch<false, 2, LAYOUT, 2, 2>(plan, kp, rf, rx, tau, w, out, stream)
@@ -711,9 +713,10 @@ hipError_t launch_vpr(const das_plan_t &plan, const DasKParams &kp, const float 
 }  // namespace
 
 bool das_staged_supported(const das_plan_t &plan) {
-    // 8 bytes of frames per lane: fp32 with 2 frames (B a multiple of 32) or
-    // complex64 with 1 (B a multiple of 16)
+    // fp32 with 2 frames per lane (B a multiple of 32) or 1 (B a multiple of
+    // 16), complex64 with 1 (B a multiple of 16)
     return (plan.p.dtype == DAS_F32 && plan.fl == 2 && plan.p.B % 32 == 0) ||
+           (plan.p.dtype == DAS_F32 && plan.fl == 1 && plan.p.B % 16 == 0) ||
            (plan.p.dtype == DAS_C64 && plan.fl == 1 && plan.p.B % 16 == 0);
 }
 
