@@ -15,19 +15,19 @@
 //
 // Mapping.  A 1024-thread workgroup owns an 8 x 8 x VPR tile of voxels; each
 // 16-lane DPP row owns the VPR voxels of one (x, y) column of the tile and each
-// lane FL consecutive frames of the frame tile.  Work goes in steps of
-// (transmit event, block of 16 receivers).  Per step:
-//   1. lane j of every row computes the sample split k and the weights of
-//      receiver m0 + j for its voxels (fp64 sample position);
+// lane FL consecutive frames of the frame tile (in each of H frame halves).
+// Work goes in steps of (transmit event, block of 16 / H receivers).  Per step:
+//   1. every lane computes the sample split k and the weights of its
+//      (voxel, receiver) pairs: receiver m0 + j for the row's voxels (H = 1),
+//      or receiver m0 + j % 8 of voxel j / 8 (H = 2) (fp64 sample position);
 //   2. the window [kmin, kmax] of k over the tile's voxels with a non-zero
-//      weight is reduced per receiver (lane swaps in a wave, LDS atomics across
-//      waves);
-//   3. wave w copies receiver m0 + w's sample rows kmin .. kmax + 1 (the frame
+//      weight is gathered per receiver by LDS atomics;
+//   3. the waves copy the receivers' sample rows kmin .. kmax + 1 (the frame
 //      tile's part of each) from HBM straight into LDS with LDS-DMA buffer
 //      loads: no registers, no store instructions;
-//   4. each row walks the 16 receivers, broadcasting lane j's LDS offset and
-//      weights through DPP row_newbcast:j; a lane reads its frames at k and
-//      k + 1 (two 8-byte reads of consecutive rows) and does 2 FL FMAs.
+//   4. each row walks its (voxel, receiver) items, broadcasting the source
+//      lane's LDS offset and weights through DPP row_newbcast; a lane reads its
+//      frames at k and k + 1 (consecutive rows) and does 2 FL H FMAs.
 // The rows live in two buffers: step i computes from one while the rows of
 // step i + 1 stream into the other, so a step needs one barrier.  Windows are
 // reduced two steps ahead (three slot sets) so that the copy of step i + 1
