@@ -1,6 +1,7 @@
 """GPU permute: bit-exact against the oracle's numpy transposes
 (B x Q x M x K -> K x Q x M x B or Q x M x K x B), including q-range chunks,
-IQ data and ragged shapes."""
+IQ data and ragged shapes: both the register transpose (fp32, B a multiple of
+16, K of 4; tails of the sample tile) and the LDS one (everything else)."""
 import numpy as np
 import pytest
 
@@ -16,7 +17,8 @@ def _plan(B, Q, M, K, iq, layout):
 
 @pytest.mark.parametrize("layout", ["kqmb", "qmkb"])
 @pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])
-@pytest.mark.parametrize("shape", [(8, 1, 64, 512), (12, 3, 37, 301), (33, 2, 5, 70), (1, 1, 1, 2), (64, 2, 16, 128)])
+@pytest.mark.parametrize("shape", [(8, 1, 64, 512), (12, 3, 37, 301), (33, 2, 5, 70), (1, 1, 1, 2), (64, 2, 16, 128),
+                                   (32, 2, 7, 100), (16, 3, 5, 36), (48, 1, 3, 4), (32, 1, 3, 70)])
 def test_permute_bit_exact(gpu, layout, iq, shape):
     import torch
     import oracle

@@ -2,9 +2,10 @@
 // ("ffdas: volumetric ultrasound reconstruction at warp speed", Section 3,
 // batch-inner tiling: frames become the contiguous axis so that lanes sharing
 // a voxel read consecutive frames of one (k, q, m) row; ffdas docs "How It
-// Works", ALG2).  Per (q, m) plane this is a B x K -> K x B transpose, staged
-// through LDS so that both the HBM reads (along k) and the HBM writes (along b)
-// are contiguous.  Pure data movement, HBM-bound: 2 x elem bytes per sample.
+// Works", ALG2).  Per (q, m) plane this is a B x K -> K x B transpose in which
+// both the HBM reads (along k) and the HBM writes (along b) are contiguous:
+// through registers for fp32 with B a multiple of 16, else through LDS.  Pure
+// data movement, HBM-bound: 2 x elem bytes per sample.
 #include "das_internal.h"
 
 namespace {
@@ -68,6 +69,82 @@ __global__ __launch_bounds__(THREADS) void permute_kernel(const T *__restrict__ 
     }
 }
 
+// fp32 with B a multiple of FB (16 or 32): no LDS.  A wave owns FB frames x
+// (256 / FB) samples of one (q, m) plane; lane (g, c) loads the 4 x 4 block of
+// frames 4g..4g+3 and samples 4c..4c+3 (four 16-byte loads, each wave load
+// reading FB / 4 runs of 4 c-lanes x 16 B = whole lines of a frame row),
+// transposes it in registers and stores four 16-byte pieces: the FB / 4 lanes
+// of one sample row write its FB frames as one contiguous run.  Loads and
+// stores are non-temporal (the data streams through once).
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int FB, int LAYOUT>
+__global__ __launch_bounds__(THREADS) void permute_f32_kernel(const float *__restrict__ in, float *__restrict__ out,
+                                                              int32_t B, int32_t Q, int32_t M, int32_t K,
+                                                              int32_t q_begin, int32_t q_count, int32_t tiles_k,
+                                                              int32_t tiles_b) {
+    constexpr int G = FB / 4;                 // frame groups per wave tile
+    constexpr int CK = 64 / G;                // sample groups per wave tile
+    constexpr int WK = 4 * CK;                // samples per wave tile
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane % G, c = lane / G;
+    int64_t blk = (int64_t)blockIdx.x * (THREADS / 64) + wave;      // wave tile
+    const int32_t tk = (int32_t)(blk % tiles_k);
+    blk /= tiles_k;
+    const int32_t tb = (int32_t)(blk % tiles_b);
+    blk /= tiles_b;
+    if (blk >= (int64_t)q_count * M)
+        return;                                                     // past the last plane (whole wave)
+    const int32_t plane = (int32_t)blk;
+    const int32_t ql = plane / M, m = plane - ql * M, q = q_begin + ql;
+    const int32_t k = tk * WK + 4 * c;
+    const int32_t b = tb * FB + 4 * g;
+    if (k >= K)
+        return;
+    const int64_t fstride = (int64_t)Q * M * K;                     // floats between frames of the input
+    const float *src = in + (((int64_t)b * Q + q) * M + m) * (int64_t)K + k;
+    f32x4_t x[4];
+    if (k + 3 < K) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            x[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(src + i * fstride));
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[i][j] = (k + j < K) ? src[i * fstride + j] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (k + j >= K)
+            break;
+        const f32x4_t y = {x[0][j], x[1][j], x[2][j], x[3][j]};     // frames b..b+3 of sample k + j
+        int64_t dst;
+        if constexpr (LAYOUT == DAS_LAYOUT_KQMB)
+            dst = (((int64_t)(k + j) * q_count + ql) * M + m) * (int64_t)B + b;
+        else
+            dst = (((int64_t)ql * M + m) * (int64_t)K + (k + j)) * (int64_t)B + b;
+        __builtin_nontemporal_store(y, reinterpret_cast<f32x4_t *>(out + dst));
+    }
+}
+
+template <int FB, int LAYOUT>
+hipError_t launch_f32(const das_plan_t &plan, const void *rf, void *out, int32_t q_begin, int32_t q_count,
+                      hipStream_t stream) {
+    const das_problem &p = plan.p;
+    constexpr int WK = 4 * (64 / (FB / 4));
+    const int32_t tiles_k = (p.K + WK - 1) / WK;
+    const int32_t tiles_b = p.B / FB;
+    const int64_t waves = (int64_t)tiles_k * tiles_b * q_count * p.M;
+    const int64_t blocks = (waves + THREADS / 64 - 1) / (THREADS / 64);
+    if (blocks > 0x7fffffffLL)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((permute_f32_kernel<FB, LAYOUT>), dim3((uint32_t)blocks), dim3(THREADS), 0, stream,
+                       static_cast<const float *>(rf), static_cast<float *>(out), p.B, p.Q, p.M, p.K, q_begin,
+                       q_count, tiles_k, tiles_b);
+    return hipGetLastError();
+}
+
 template <typename T, int LAYOUT>
 hipError_t launch(const das_plan_t &plan, const void *rf, void *out, int32_t q_begin, int32_t q_count,
                   hipStream_t stream) {
@@ -92,6 +169,14 @@ hipError_t das_launch_permute(const das_plan_t &plan, const void *rf, void *out,
     if (c64)
         return kqmb ? launch<float2, DAS_LAYOUT_KQMB>(plan, rf, out, q_begin, q_count, stream)
                     : launch<float2, DAS_LAYOUT_QMKB>(plan, rf, out, q_begin, q_count, stream);
+    // the register transpose needs 16-byte aligned runs: K a multiple of 4 (input rows), B of 16 (output rows)
+    const bool vec = plan.p.K % 4 == 0;
+    if (vec && plan.p.B % 32 == 0)
+        return kqmb ? launch_f32<32, DAS_LAYOUT_KQMB>(plan, rf, out, q_begin, q_count, stream)
+                    : launch_f32<32, DAS_LAYOUT_QMKB>(plan, rf, out, q_begin, q_count, stream);
+    if (vec && plan.p.B % 16 == 0)
+        return kqmb ? launch_f32<16, DAS_LAYOUT_KQMB>(plan, rf, out, q_begin, q_count, stream)
+                    : launch_f32<16, DAS_LAYOUT_QMKB>(plan, rf, out, q_begin, q_count, stream);
     return kqmb ? launch<float, DAS_LAYOUT_KQMB>(plan, rf, out, q_begin, q_count, stream)
                 : launch<float, DAS_LAYOUT_QMKB>(plan, rf, out, q_begin, q_count, stream);
 }
