@@ -388,14 +388,26 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     struct Ring {
         TapV r0[DEPTH][H], r1[DEPTH][H];
     };
+    // With 8 bytes per lane the two taps are read by two separate
+    // instructions: on gfx950 two 64-bit reads of rows k and k + 1 are served
+    // about a third faster than the one two-address read the compiler would
+    // merge them into (same bytes); the volatile LDS pointer keeps them apart.
+    // 32-bit taps keep the merged read, which measured slightly faster.
+    using LdsTap = const volatile __attribute__((address_space(3))) TapV *;
+    auto read_tap = [&](uint32_t off) -> TapV {
+        if constexpr (G::LANEB == 8)
+            return *(LdsTap)(lds + off);
+        else
+            return *reinterpret_cast<const TapV *>(lds + off);
+    };
     auto issue_item = [&](auto T, const uint32_t (&loff)[PL], Ring &ring) {
         constexpr int tt = decltype(T)::value;
         constexpr int v = tt / NRX, j = tt % NRX, src = (v % H) * NRX + j, pr = v / H;
         const uint32_t addr = das::row_bcast<src>(loff[pr]) + laneoff_l;
 #pragma unroll
         for (int h = 0; h < H; ++h) {
-            ring.r0[tt % DEPTH][h] = *reinterpret_cast<const TapV *>(lds + addr + h * G::HALFB);
-            ring.r1[tt % DEPTH][h] = *reinterpret_cast<const TapV *>(lds + addr + G::ROWB + h * G::HALFB);
+            ring.r0[tt % DEPTH][h] = read_tap(addr + h * G::HALFB);
+            ring.r1[tt % DEPTH][h] = read_tap(addr + G::ROWB + h * G::HALFB);
         }
     };
     auto prefetch = [&](const uint32_t (&loff)[PL], Ring &ring) {
