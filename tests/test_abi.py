@@ -116,7 +116,7 @@ def test_plan_info_and_sizes():
     pl = das.Plan(**_problem(B=32, dtype="c64", f_demod=5e6))
     assert pl.info["algorithm"] == das.ALG_BATCH_INNER
     assert pl.info["elem_bytes"] == 8
-    assert pl.info["frames_per_lane"] == 1                  # IQ, B % 16 == 0: LDS-staged, 1 frame per lane
+    assert pl.info["frames_per_lane"] == 2                  # IQ, B % 32 == 0: LDS-staged split rows, 2 frames per lane
     assert pl.info["lanes_per_voxel"] == 16
     assert pl.info["N"] == 32
     assert pl.permuted_bytes(1) == 64 * 1 * 8 * 32 * 8
@@ -169,11 +169,11 @@ def test_auto_selection(dtype, B, alg):
                                algorithm="default")).info["algorithm"] == das.ALG_BASELINE
 
 
-@pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (24, 1), (32, 2), (48, 1), (64, 2), (96, 2), (66, 1),
-                                  (160, 2), (68, 4)])
+@pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (24, 1), (32, 2), (48, 1), (64, 4), (96, 2), (66, 1),
+                                  (160, 2), (192, 4), (68, 4)])
 def test_frames_per_lane_choice(B, fl):
-    # fp32 batch-inner: the LDS-staged kernel wherever B % 16 == 0 (2 frames
-    # per lane when B % 32 == 0, else 1)
+    # fp32 batch-inner: the LDS-staged kernel wherever B % 16 == 0 (4 frames
+    # per lane in split rows when B % 64 == 0, 2 when B % 32 == 0, else 1)
     pl = das.Plan(**_problem(B=B))
     assert pl.info["frames_per_lane"] == fl
     assert pl.info["staged"] == (1 if B % 16 == 0 else 0)
@@ -187,9 +187,10 @@ def test_frames_per_lane_choice_direct(B, fl, monkeypatch):
     assert pl.info["staged"] == 0
 
 
-@pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (31, 1), (32, 1), (40, 2), (64, 1), (34, 2)])
+@pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (31, 1), (32, 2), (40, 2), (48, 1), (64, 2), (34, 2)])
 def test_frames_per_lane_choice_iq(B, fl):
-    # complex64 batch-inner: the LDS-staged kernel (1 frame per lane) wherever B % 16 == 0
+    # complex64 batch-inner: the LDS-staged kernel wherever B % 16 == 0 (2
+    # frames per lane in split rows when B % 32 == 0, else 1)
     pl = das.Plan(**_problem(B=B, dtype="c64", f_demod=5e6))
     assert pl.info["frames_per_lane"] == fl
     assert pl.info["staged"] == (1 if B % 16 == 0 else 0)
@@ -342,3 +343,14 @@ def test_binding_checks_tensor_sizes_before_the_call():
     cpu = torch.zeros(10)
     with pytest.raises(TypeError):
         pl.beamform(cpu, cpu, cpu, cpu, cpu)
+
+
+@pytest.mark.parametrize("B,dtype", [(64, "f32"), (32, "c64")])
+def test_split_rows_can_be_switched_off(B, dtype, monkeypatch):
+    # DAS_STAGED_SPLIT=1 keeps whole rows (8 bytes per lane), for comparisons
+    kw = dict(B=B, dtype=dtype, f_demod=5e6 if dtype == "c64" else 0.0)
+    assert das.Plan(**_problem(**kw)).info["frames_per_lane"] == (4 if dtype == "f32" else 2)
+    monkeypatch.setenv("DAS_STAGED_SPLIT", "1")
+    pl = das.Plan(**_problem(**kw))
+    assert pl.info["staged"] == 1
+    assert pl.info["frames_per_lane"] == (2 if dtype == "f32" else 1)

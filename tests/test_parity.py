@@ -99,8 +99,9 @@ def test_q_chunks_sum_to_the_whole(gpu, alg, layout):
 @pytest.mark.parametrize("B", [16, 32, 64])
 def test_staged_windows_and_fallback(gpu, layout, voxel, iq, B):
     """The LDS-staged kernel.  fp32 B = 32: 2 frames per lane, one 32-frame
-    tile of 16 receivers a step; fp32 B = 64 and complex64: two frame halves
-    per row (8 receivers a step, 256-byte rows).  Coarse voxels give k-windows
+    tile of 16 receivers a step; fp32 B = 64 and complex64 B = 32 and 64:
+    split rows (two voxels per DPP row, 16 bytes per lane, 8 receivers a
+    step, 256-byte rows).  Coarse voxels give k-windows
     wider than the LDS capacity, which must fall back to direct loads; fine
     voxels stay in LDS; the mixed pitch exercises both within one launch."""
     cfg = das_synth.custom_config("tiny", name="staged", seed=23, array=(19, 3), grid=(11, 10, 3), K=700, B=B,
@@ -114,17 +115,17 @@ def test_staged_windows_and_fallback(gpu, layout, voxel, iq, B):
 
 
 @pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])
-def test_one_and_two_frame_halves_agree(gpu, monkeypatch, iq):
-    """B = 64: the staged kernel with two frame halves per row (the default
-    there) and with one (two frame tiles) both meet the bar."""
+def test_split_and_whole_rows_agree(gpu, monkeypatch, iq):
+    """B = 64: the staged kernel with split rows (the default there) and with
+    whole rows (two frame tiles) both meet the bar."""
     cfg = _ragged(B=64, grid=(17, 9, 4), iq=iq, array=(23, 2))
     inp = Inputs(cfg, w_tx="uniform")
-    two = to_numpy(run_gpu(inp, "batch_inner", "qmkb"), iq)
-    monkeypatch.setenv("DAS_STAGED_HALVES", "1")
-    one = to_numpy(run_gpu(inp, "batch_inner", "qmkb"), iq)
+    split = to_numpy(run_gpu(inp, "batch_inner", "qmkb"), iq)
+    monkeypatch.setenv("DAS_STAGED_SPLIT", "1")
+    whole = to_numpy(run_gpu(inp, "batch_inner", "qmkb"), iq)
     ref = oracle_ref(inp)
-    assert_parity(two, ref, "two halves")
-    assert_parity(one, ref, "one half")
+    assert_parity(split, ref, "split rows")
+    assert_parity(whole, ref, "whole rows")
 
 
 @pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])

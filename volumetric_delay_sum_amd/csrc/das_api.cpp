@@ -222,8 +222,9 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
     pl->bt = 8;
     // LDS-staged batch-inner kernel where it is built (fp32 with B a multiple
     // of 32, two frames per lane, or of 16, one frame per lane; complex64 with
-    // B a multiple of 16, one frame per lane; larger B runs as several frame
-    // tiles or two frame halves per row);
+    // B a multiple of 16, one frame per lane; B a multiple of 64 fp32 or 32
+    // complex frames runs split rows with twice the frames per lane; larger B
+    // runs as several frame tiles);
     // DAS_BI_KERNEL=direct selects the direct-load kernel (comparisons).
     const char *kv = std::getenv("DAS_BI_KERNEL");
     const bool want_staged = pl->alg == DAS_ALG_BATCH_INNER && !(kv && std::strcmp(kv, "direct") == 0);
@@ -233,13 +234,18 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
         pl->fl = 1;
     if (want_staged && p.dtype == DAS_C64 && p.B % 16 == 0)
         pl->fl = 1;
+    pl->split = 1;
     pl->staged = (want_staged && das_staged_supported(*pl)) ? 1 : 0;
     pl->q_group = pick_q_group(p, elem, pl->staged != 0);
     const char *vv = std::getenv("DAS_STAGED_VPR");
     pl->vpr = (vv && std::atoi(vv) == 1) ? 1 : 2;
-    // two frame halves per row where B allows (DAS_STAGED_HALVES=1 keeps one: comparisons)
-    const char *hv = std::getenv("DAS_STAGED_HALVES");
-    pl->halves = (pl->staged && pl->vpr == 2 && p.B % (2 * 16 * pl->fl) == 0 && !(hv && std::atoi(hv) == 1)) ? 2 : 1;
+    // split rows where B allows (DAS_STAGED_SPLIT=1 keeps whole rows: comparisons)
+    const char *sv = std::getenv("DAS_STAGED_SPLIT");
+    if (pl->staged && pl->vpr == 2 && pl->fl * (p.dtype == DAS_C64 ? 2 : 1) == 2 && p.B % (2 * 16 * pl->fl) == 0 &&
+        !(sv && std::atoi(sv) == 1)) {
+        pl->split = 2;
+        pl->fl *= 2;
+    }
     *out = pl;
     return DAS_OK;
 }

@@ -15,11 +15,11 @@
 //
 // Mapping.  A 1024-thread workgroup owns an 8 x 8 x VPR tile of voxels; each
 // 16-lane DPP row owns the VPR voxels of one (x, y) column of the tile and each
-// lane FL consecutive frames of the frame tile (in each of H frame halves).
-// Work goes in steps of (transmit event, block of 16 / H receivers).  Per step:
+// lane FL consecutive frames of the frame tile.  Work goes in steps of
+// (transmit event, block of 16 / S receivers).  Per step:
 //   1. every lane computes the sample split k and the weights of its
-//      (voxel, receiver) pairs: receiver m0 + j for the row's voxels (H = 1),
-//      or receiver m0 + j % 8 of voxel j / 8 (H = 2) (fp64 sample position);
+//      (voxel, receiver) pairs: receiver m0 + j for the row's voxels (S = 1),
+//      or receiver m0 + j % 8 of voxel j / 8 (S = 2) (fp64 sample position);
 //   2. the window [kmin, kmax] of k over the tile's voxels with a non-zero
 //      weight is gathered per receiver by LDS atomics;
 //   3. the waves copy the receivers' sample rows kmin .. kmax + 1 (the frame
@@ -27,7 +27,7 @@
 //      loads: no registers, no store instructions;
 //   4. each row walks its (voxel, receiver) items, broadcasting the source
 //      lane's LDS offset and weights through DPP row_newbcast; a lane reads its
-//      frames at k and k + 1 (consecutive rows) and does 2 FL H FMAs.
+//      frames at k and k + 1 (consecutive rows) and does 2 FL FMAs.
 // The rows live in two buffers: step i computes from one while the rows of
 // step i + 1 stream into the other, so a step needs one barrier.  Windows are
 // reduced two steps ahead (three slot sets) so that the copy of step i + 1
@@ -46,33 +46,34 @@ constexpr int ROW = 16;               // lanes per voxel column (one DPP row)
 constexpr int TX = 8, TY = 8;         // lateral voxel tile of one workgroup (one column per row)
 constexpr int LDS_ROW_BUDGET = 160000;   // bytes for the two row buffers
 
-// H frame halves: a 16-lane row covers H x 16 x FL frames of the frame tile,
-// each lane FL frames in each half.  With H = 2 a step takes 8 receivers, the
-// row's two voxels sit in its two lane halves (lane li holds the pair voxel
-// li / 8, receiver li % 8) and a staged sample row is twice as long, so the
-// LDS holds the same number of rows per receiver; the per-pair work (receive
-// geometry, sample split, window) is done once for twice the frames.
-template <bool IQ, int FL, int H>
+// Split rows (S = 2), for 16-byte lanes (4 fp32 or 2 complex frames, a staged
+// sample row of 256 bytes): a step takes 8 receivers, so the LDS holds as many
+// rows per receiver as with 128-byte rows and 16 receivers, and the row's two
+// voxels sit in its two lane halves (lane li holds the pair voxel li / 8,
+// receiver li % 8); the per-pair work (receive geometry, sample split,
+// window) serves 64 fp32 or 32 complex frames.  Each tap is then one 16-byte
+// LDS read per lane, which gfx950 serves at nearly twice the bytes per clock
+// of 8-byte reads.
+template <bool IQ, int FL, int S>
 struct Geo {
     static constexpr int C = IQ ? 2 : 1;                 // floats per sample
     static constexpr int E = 4 * C;                      // bytes per sample
-    static constexpr int NF = FL * C;                    // floats per lane per tap and half
-    static constexpr int LANEB = NF * 4;                 // bytes per lane in a half of a sample row
-    static constexpr int HALFB = ROW * LANEB;            // bytes of one half of a staged sample row
-    static constexpr int ROWB = H * HALFB;               // bytes of the frame tile in one sample row
-    static constexpr int NRX = ROW / H;                  // receivers per step
+    static constexpr int NF = FL * C;                    // floats per lane per tap
+    static constexpr int LANEB = NF * 4;                 // bytes per lane in a sample row
+    static constexpr int ROWB = ROW * LANEB;             // bytes of the frame tile in one sample row
+    static constexpr int NRX = ROW / S;                  // receivers per step
     static constexpr int RW0 = LDS_ROW_BUDGET / (2 * NRX * ROWB);
     static constexpr int RW = RW0 > 64 ? 64 : RW0;       // sample rows per receiver region
     static constexpr int W_MAX = RW - 1;                 // k positions per receiver window
     static constexpr int LPR = ROWB / 16;                // lanes per sample row in a 16-byte copy
     static constexpr int RPR = 64 / LPR;                 // sample rows per copy round of a wave
-    static constexpr int MAXR = (RW + RPR * H - 1) / (RPR * H);   // copy rounds of one wave (H waves per receiver)
+    static constexpr int MAXR = (RW + RPR * S - 1) / (RPR * S);   // copy rounds of one wave (S waves per receiver)
     static constexpr int REGION = RW * ROWB;             // bytes of one receiver's region
     static constexpr int BUF = NRX * REGION;             // bytes of one buffer
     static constexpr int LDS_BYTES = 2 * BUF + 3 * 2 * NRX * 4;
     static_assert(ROWB % 16 == 0 && 64 % LPR == 0, "copy granularity");
     static_assert(LANEB == 4 || LANEB == 8 || LANEB == 16, "reader width");
-    static_assert(H == 1 || H == 2, "frame halves");
+    static_assert(S == 1 || (S == 2 && LANEB == 16), "split rows");
 };
 
 // Per-lane state of one voxel in one step: sample index and weights.
@@ -135,18 +136,18 @@ struct Tap {
     using type = float __attribute__((ext_vector_type(NF)));
 };
 
-template <bool IQ, int FL, int LAYOUT, int VPR, int H>
+template <bool IQ, int FL, int LAYOUT, int VPR, int S>
 __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, const float *__restrict__ rfp,
                                                                 const float *__restrict__ rx,
                                                                 const float *__restrict__ tau_tx,
                                                                 const float *__restrict__ w_tx,
                                                                 float *__restrict__ out, uint32_t tap_stride) {
-    using G = Geo<IQ, FL, H>;
+    using G = Geo<IQ, FL, S>;
     constexpr int C = G::C, E = G::E, NF = G::NF, NRX = G::NRX;
-    // (voxel, receiver) pairs per lane: pair p is voxel p H + li / NRX of the
+    // (voxel, receiver) pairs per lane: pair p is voxel p S + li / NRX of the
     // row and receiver m0 + li % NRX
-    constexpr int PL = VPR / H;
-    static_assert(VPR % H == 0, "each lane half needs a voxel");
+    constexpr int PL = VPR / S;
+    static_assert(VPR % S == 0, "each lane half needs a voxel");
     using TapV = typename Tap<NF>::type;
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
     int *slots = reinterpret_cast<int *>(lds + 2 * G::BUF);   // [3 sets][min, max][NRX]
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     const int li = lane & (ROW - 1);
     const int vr = wave * 4 + (lane >> 4);           // voxel column 0..63
     const int lrx = li % NRX;                        // receiver of this lane's pairs (m0 + lrx)
-    const int lv0 = li / NRX;                        // voxel of pair 0 (pair p: lv0 + p H)
+    const int lv0 = li / NRX;                        // voxel of pair 0 (pair p: lv0 + p S)
 
     const int tiles_x = (P.nx + TX - 1) / TX, tiles_y = (P.ny + TY - 1) / TY;
     int t = das::xcd_tile(blockIdx.x, gridDim.x);
@@ -184,16 +185,15 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         n_p[p] = n[0];
 #pragma unroll
         for (int v = 1; v < VPR; ++v)
-            n_p[p] = (lv0 + p * H == v) ? n[v] : n_p[p];
+            n_p[p] = (lv0 + p * S == v) ? n[v] : n_p[p];
     }
 
-    // frames of this lane: FL adjacent frames in each of the H halves of the
-    // frame tile (half h starts h 16 FL frames in)
-    const int b0 = blockIdx.y * (H * ROW * FL);
+    // frames of this lane: FL adjacent frames of the frame tile
+    const int b0 = blockIdx.y * (ROW * FL);
     const int bl = b0 + li * FL;
-    const bool fr_ok = bl + (H - 1) * ROW * FL < P.B;             // the plan keeps B a multiple of the tile
-    const uint32_t laneoff_g = (uint32_t)(fr_ok ? bl : 0) * E;   // byte offset in a global row (half 0)
-    const uint32_t laneoff_l = (uint32_t)li * G::LANEB;           // byte offset in a staged row (half 0)
+    const bool fr_ok = bl < P.B;                                  // the plan keeps B a multiple of the tile
+    const uint32_t laneoff_g = (uint32_t)(fr_ok ? bl : 0) * E;   // byte offset in a global row
+    const uint32_t laneoff_l = (uint32_t)li * G::LANEB;           // byte offset in a staged row
 
     const int64_t rowfull = (int64_t)P.B * E;                       // one (k, q, m) row, all frames
     // receiver stride (the plan keeps 16 K B E below 2^32, so it is 32-bit);
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         for (int v = 0; v < PL; ++v) {
             // voxel centres are recomputed per receiver block rather than kept in registers
             double vx, vy, vz;
-            das::voxel_centre(Pg, ix, iy, min(tz * VPR + lv0 + v * H, Pg.nz - 1), vx, vy, vz);
+            das::voxel_centre(Pg, ix, iy, min(tz * VPR + lv0 + v * S, Pg.nz - 1), vx, vy, vz);
             R[v] = das::rx_term<IQ>(Pg, vx, vy, vz, px, py, pz);
             R[v].s_rx += 1.0 - Pg.t0fs;                   // the sample split takes s + 1
             R[v].w = (mm < Pg.M) ? R[v].w : 0.0f;
@@ -286,8 +286,8 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
 
     // Window of the step in slot set `set`, staged in buffer `buf`: per lane
     // and pair the LDS byte offset of its receiver's row for k; the copy of
-    // this wave's receiver (wave / H; H waves share one receiver's rows).
-    const int wrx = wave / H, wpart = wave % H;
+    // this wave's receiver (wave / S; S waves share one receiver's rows).
+    const int wrx = wave / S, wpart = wave % S;
     struct Window {
         uint32_t loff[PL];
         int kmin_w, rows_w;    // wave's copy: first sample row, number of sample rows
@@ -317,8 +317,8 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     };
 
     // Copy of one receiver's sample rows by LDS-DMA (wave w copies receiver
-    // m0 + w / H into its region of the buffer, taking every H-th round
-    // starting at w % H).  A round moves RPR rows: lane
+    // m0 + w / S into its region of the buffer, taking every S-th round
+    // starting at w % S).  A round moves RPR rows: lane
     // (rho, c) fetches 16 bytes (chunk c of the frame tile's part) of sample
     // row kmin + RPR r + rho, and the DMA writes lane l's 16 bytes at
     // 16 l past the round's LDS base, i.e. row rho, chunk c of the region.
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     auto copy_prepare = [&](const Cursor &c, const Window &wdw, int buf) -> CopyPlan {
         const int rows = __builtin_amdgcn_readfirstlane(wdw.rows_w);
         const uint32_t kmin = (uint32_t)__builtin_amdgcn_readfirstlane(wdw.kmin_w);
-        const int nr = (rows + G::RPR * H - 1) / (G::RPR * H);     // this wave's rounds (at most)
+        const int nr = (rows + G::RPR * S - 1) / (G::RPR * S);     // this wave's rounds (at most)
         const uint32_t dst = (uint32_t)(buf * G::BUF + wrx * G::REGION);
         if constexpr (LAYOUT == DAS_LAYOUT_QMKB) {
             const int64_t plane = ((int64_t)c.ql * P.M + c.m0) * m_stride;
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         }
     };
     auto copy_round = [&](const CopyPlan &cp, int r) {
-        const int rr = r * H + wpart;                               // round of the receiver's copy
+        const int rr = r * S + wpart;                               // round of the receiver's copy
         if (r < cp.nr && rr * G::RPR + crow < cp.rows) {
             const das::lds_ptr dst = (das::lds_ptr)(lds + cp.dst + (uint32_t)(rr * G::RPR * G::ROWB));   // generic -> LDS address space
             das::buffer_load_lds(cp.rs, dst, 16, (int)coff, (int)(cp.start + (uint32_t)(rr * G::RPR) * kstride32), 0,
@@ -362,31 +362,30 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         }
     };
 
-    constexpr int HNF = H * NF;                      // floats of one voxel per lane and tap
-    float acc[VPR][HNF], part[VPR][HNF];
+    float acc[VPR][NF], part[VPR][NF];
 #pragma unroll
     for (int v = 0; v < VPR; ++v)
 #pragma unroll
-        for (int i = 0; i < HNF; ++i) {
+        for (int i = 0; i < NF; ++i) {
             acc[v][i] = 0.0f;
             part[v][i] = 0.0f;
         }
 
     // All voxels of one step from LDS: VPR x NRX (voxel, receiver) items.  Item
-    // (v, j) takes its coefficients and row offset from lane (v % H) NRX + j
-    // (pair v / H); each lane reads taps k and k + 1 of its frames (rows k and
-    // k + 1 are consecutive; H halves each) and does 2 H FL (IQ: 8 H FL) FMAs.
+    // (v, j) takes its coefficients and row offset from lane (v % S) NRX + j
+    // (pair v / S); each lane reads taps k and k + 1 of its frames (rows k and
+    // k + 1 are consecutive) and does 2 FL (IQ: 8 FL) FMAs.
     // The reads are issued DEPTH items ahead; the scheduling fences keep the
     // compiler from sinking each read next to its use, which would leave one
     // read in flight per wave (three ahead measured best with two voxels per
     // row, eight with one).  `at(t)` runs after item t (the next step's copy
     // rounds).
     constexpr int NITEM = VPR * NRX;
-    constexpr int DEPTH = (VPR == 1) ? 8 : (H == 2 ? 2 : 3);   // H = 2: two reads per item
+    constexpr int DEPTH = (VPR == 1) ? 8 : (G::LANEB == 16 ? 2 : 3);   // 16-byte lanes: 8 registers per item
     // The first DEPTH items' reads are issued by prefetch(), for fp32 data at
     // the top of the step, so they land while the setup runs.
     struct Ring {
-        TapV r0[DEPTH][H], r1[DEPTH][H];
+        TapV r0[DEPTH], r1[DEPTH];
     };
     // With 8 bytes per lane the two taps are read by two separate
     // instructions: on gfx950 two 64-bit reads of rows k and k + 1 are served
@@ -402,34 +401,26 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     };
     auto issue_item = [&](auto T, const uint32_t (&loff)[PL], Ring &ring) {
         constexpr int tt = decltype(T)::value;
-        constexpr int v = tt / NRX, j = tt % NRX, src = (v % H) * NRX + j, pr = v / H;
+        constexpr int v = tt / NRX, j = tt % NRX, src = (v % S) * NRX + j, pr = v / S;
         const uint32_t addr = das::row_bcast<src>(loff[pr]) + laneoff_l;
-#pragma unroll
-        for (int h = 0; h < H; ++h) {
-            ring.r0[tt % DEPTH][h] = read_tap(addr + h * G::HALFB);
-            ring.r1[tt % DEPTH][h] = read_tap(addr + G::ROWB + h * G::HALFB);
-        }
+        ring.r0[tt % DEPTH] = read_tap(addr);
+        ring.r1[tt % DEPTH] = read_tap(addr + G::ROWB);
     };
     auto prefetch = [&](const uint32_t (&loff)[PL], Ring &ring) {
         das::unroll<DEPTH>([&](auto T) { issue_item(T, loff, ring); });
     };
     // Interpolate-weight-accumulate of item tt from its two taps.
-    auto item_fma = [&](auto T, Step (&s)[PL], float (&pt)[VPR][HNF], const TapV (&x0)[H], const TapV (&x1)[H]) {
+    auto item_fma = [&](auto T, Step (&s)[PL], float (&pt)[VPR][NF], const TapV &x0, const TapV &x1) {
         constexpr int tt = decltype(T)::value;
-        constexpr int v = tt / NRX, j = tt % NRX, src = (v % H) * NRX + j, pr = v / H;
+        constexpr int v = tt / NRX, j = tt % NRX, src = (v % S) * NRX + j, pr = v / S;
+        if constexpr (IQ) {
 #pragma unroll
-        for (int h = 0; h < H; ++h) {
-            if constexpr (IQ) {
+            for (int f = 0; f < FL; ++f)
+                das::cmac_bcast<src>(pt[v][2 * f], pt[v][2 * f + 1], s[pr].a, s[pr].ai, s[pr].b, s[pr].bi,
+                                     x0[2 * f], x0[2 * f + 1], x1[2 * f], x1[2 * f + 1]);
+        } else {
 #pragma unroll
-                for (int f = 0; f < FL; ++f)
-                    das::cmac_bcast<src>(pt[v][h * NF + 2 * f], pt[v][h * NF + 2 * f + 1], s[pr].a, s[pr].ai,
-                                         s[pr].b, s[pr].bi, x0[h][2 * f], x0[h][2 * f + 1], x1[h][2 * f],
-                                         x1[h][2 * f + 1]);
-            } else {
-#pragma unroll
-                for (int f = 0; f < FL; ++f)
-                    das::lerp_bcast<src>(pt[v][h * NF + f], s[pr].a, s[pr].b, x0[h][f], x1[h][f]);
-            }
+            for (int f = 0; f < FL; ++f) das::lerp_bcast<src>(pt[v][f], s[pr].a, s[pr].b, x0[f], x1[f]);
         }
     };
     // The step's coefficients are settled in place (they are dead after the
@@ -443,7 +434,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
                 das::settle(s[p].a, s[p].b);
         }
     };
-    auto compute_lds = [&](Step (&s)[PL], const uint32_t (&loff)[PL], float (&pt)[VPR][HNF], Ring &ring,
+    auto compute_lds = [&](Step (&s)[PL], const uint32_t (&loff)[PL], float (&pt)[VPR][NF], Ring &ring,
                            auto &&at) {
         settle_all(s);
         auto issue = [&](auto T) { issue_item(T, loff, ring); };
@@ -467,8 +458,8 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     };
     // One voxel of one step by direct loads from the permuted buffer (windows
     // too wide for LDS).  A term that does not count reads row 0.
-    auto compute_direct = [&](auto V, Step (&s)[PL], const Cursor &c, float (&pt)[VPR][HNF]) {
-        constexpr int v = decltype(V)::value, pr = v / H;
+    auto compute_direct = [&](auto V, Step (&s)[PL], const Cursor &c, float (&pt)[VPR][NF]) {
+        constexpr int v = decltype(V)::value, pr = v / S;
         float a = s[pr].a, b = s[pr].b, ai = s[pr].ai, bi = s[pr].bi;
         if constexpr (IQ)
             das::settle(a, b, ai, bi);
@@ -481,27 +472,24 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         const das::BufRsrc r1 =
             das::make_rsrc(rf_bytes + pos + tap_stride, (uint64_t)(chunk_bytes - pos - (int64_t)tap_stride));
         das::unroll<NRX>([&](auto J) {
-            constexpr int j = decltype(J)::value, src = (v % H) * NRX + j;
+            constexpr int j = decltype(J)::value, src = (v % S) * NRX + j;
             const uint32_t jo = laneoff_g + (uint32_t)min(j, jmax) * m_stride;
             const uint32_t off = das::row_bcast<src>(koff) + jo;
+            float x0[NF], x1[NF];
 #pragma unroll
-            for (int h = 0; h < H; ++h) {
-                float x0[NF], x1[NF];
+            for (int i = 0; i < NF; ++i) {
+                const int o = (int)(off + 4 * i);
+                x0[i] = das::buffer_load_f32(r0, o, 0, 0);
+                x1[i] = das::buffer_load_f32(r1, o, 0, 0);
+            }
+            if constexpr (IQ) {
 #pragma unroll
-                for (int i = 0; i < NF; ++i) {
-                    const int o = (int)(off + (uint32_t)(h * ROW * FL * E) + 4 * i);
-                    x0[i] = das::buffer_load_f32(r0, o, 0, 0);
-                    x1[i] = das::buffer_load_f32(r1, o, 0, 0);
-                }
-                if constexpr (IQ) {
+                for (int f = 0; f < FL; ++f)
+                    das::cmac_bcast<src>(pt[v][2 * f], pt[v][2 * f + 1], a, ai, b, bi, x0[2 * f], x0[2 * f + 1],
+                                         x1[2 * f], x1[2 * f + 1]);
+            } else {
 #pragma unroll
-                    for (int f = 0; f < FL; ++f)
-                        das::cmac_bcast<src>(pt[v][h * NF + 2 * f], pt[v][h * NF + 2 * f + 1], a, ai, b, bi,
-                                             x0[2 * f], x0[2 * f + 1], x1[2 * f], x1[2 * f + 1]);
-                } else {
-#pragma unroll
-                    for (int f = 0; f < FL; ++f) das::lerp_bcast<src>(pt[v][h * NF + f], a, b, x0[f], x1[f]);
-                }
+                for (int f = 0; f < FL; ++f) das::lerp_bcast<src>(pt[v][f], a, b, x0[f], x1[f]);
             }
         });
     };
@@ -597,8 +585,8 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         }
         if (!wc.overflow) {
             // copy round r after item SPREAD r + SPREAD / 2 (every 4th item, every
-            // 3rd with the shorter loop of two frame halves): early, so the
-            // rows have the rest of the loop to land, yet not all at once
+            // 3rd with the shorter loop of split rows): early, so the rows
+            // have the rest of the loop to land, yet not all at once
             constexpr int SPREAD = (NITEM >= 4 * G::MAXR) ? 4 : 3;
             static_assert(SPREAD * (G::MAXR - 1) + SPREAD / 2 < NITEM, "every copy round is issued");
             if constexpr (IQ)
@@ -629,7 +617,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
 #pragma unroll
             for (int v = 0; v < VPR; ++v)
 #pragma unroll
-                for (int i = 0; i < HNF; ++i) {
+                for (int i = 0; i < NF; ++i) {
                     acc[v][i] += part[v][i];
                     part[v][i] = 0.0f;
                 }
@@ -677,26 +665,24 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             if (!vox_ok[v])
                 continue;
 #pragma unroll
-            for (int h = 0; h < H; ++h)
+            for (int f = 0; f < FL; ++f) {
+                float *o = out + ((int64_t)(bl + f) * P.N + n[v]) * C;
+                const float *a = &acc[v][f * C];
 #pragma unroll
-                for (int f = 0; f < FL; ++f) {
-                    float *o = out + ((int64_t)(bl + h * ROW * FL + f) * P.N + n[v]) * C;
-                    const float *a = &acc[v][h * NF + f * C];
-#pragma unroll
-                    for (int c = 0; c < C; ++c) o[c] = P.accumulate ? o[c] + a[c] : a[c];
-                }
+                for (int c = 0; c < C; ++c) o[c] = P.accumulate ? o[c] + a[c] : a[c];
+            }
         }
     }
 }
 
-template <bool IQ, int FL, int LAYOUT, int VPR, int H = 1>
+template <bool IQ, int FL, int LAYOUT, int VPR, int S = 1>
 hipError_t launch(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
                   const float *tau, const float *w, float *out, hipStream_t stream) {
     const int64_t row_bytes = (int64_t)kp.B * plan.elem_bytes;
     const int64_t tap = (LAYOUT == DAS_LAYOUT_KQMB) ? row_bytes * kp.q_count * kp.M : row_bytes;
     const int tiles = ((kp.nx + TX - 1) / TX) * ((kp.ny + TY - 1) / TY) * ((kp.nz + VPR - 1) / VPR);
-    const int ftiles = (kp.B + H * ROW * FL - 1) / (H * ROW * FL);
-    hipLaunchKernelGGL((das_bi_staged_kernel<IQ, FL, LAYOUT, VPR, H>), dim3(tiles, ftiles), dim3(THREADS), 0,
+    const int ftiles = (kp.B + ROW * FL - 1) / (ROW * FL);
+    hipLaunchKernelGGL((das_bi_staged_kernel<IQ, FL, LAYOUT, VPR, S>), dim3(tiles, ftiles), dim3(THREADS), 0,
                        stream, kp, rf, rx, tau, w, out, (uint32_t)tap);
     return hipGetLastError();
 }
@@ -705,31 +691,35 @@ template <int LAYOUT>
 hipError_t launch_vpr(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
                       const float *tau, const float *w, float *out, hipStream_t stream) {
     // fp32: 2 frames per lane; complex64: 1 frame per lane.  Either way a lane
-    // holds 8 bytes of a sample row and a staged row is 128 bytes.
-    // With two frame halves (B a multiple of 64 fp32 / 32 complex frames) a
-    // row is 256 bytes and a step takes 8 receivers.
+    // holds 8 bytes of a sample row and a staged row is 128 bytes.  Split rows
+    // (B a multiple of 64 fp32 / 32 complex frames): 16 bytes per lane (4 fp32
+    // or 2 complex frames), 256-byte rows, 8 receivers a step.
     if (plan.p.dtype == DAS_C64) {
         if (plan.vpr == 1)
             return launch<true, 1, LAYOUT, 1>(plan, kp, rf, rx, tau, w, out, stream);
-        return plan.halves == 2 ? launch<true, 1, LAYOUT, 2, 2>(plan, kp, rf, rx, tau, w, out, stream)
-                                : launch<true, 1, LAYOUT, 2>(plan, kp, rf, rx, tau, w, out, stream);
+        return plan.split == 2 ? launch<true, 2, LAYOUT, 2, 2>(plan, kp, rf, rx, tau, w, out, stream)
+                               : launch<true, 1, LAYOUT, 2>(plan, kp, rf, rx, tau, w, out, stream);
     }
     if (plan.fl == 1)                                // fp32, B a multiple of 16 but not of 32: 64-byte rows
         return launch<false, 1, LAYOUT, 2>(plan, kp, rf, rx, tau, w, out, stream);
     if (plan.vpr == 1)
         return launch<false, 2, LAYOUT, 1>(plan, kp, rf, rx, tau, w, out, stream);
-    return plan.halves == 2 ? launch<false, 2, LAYOUT, 2, 2>(plan, kp, rf, rx, tau, w, out, stream)
-                            : launch<false, 2, LAYOUT, 2>(plan, kp, rf, rx, tau, w, out, stream);
+    return plan.split == 2 ? launch<false, 4, LAYOUT, 2, 2>(plan, kp, rf, rx, tau, w, out, stream)
+                           : launch<false, 2, LAYOUT, 2>(plan, kp, rf, rx, tau, w, out, stream);
 }
 
 }  // namespace
 
 bool das_staged_supported(const das_plan_t &plan) {
-    // fp32 with 2 frames per lane (B a multiple of 32) or 1 (B a multiple of
-    // 16), complex64 with 1 (B a multiple of 16)
-    return (plan.p.dtype == DAS_F32 && plan.fl == 2 && plan.p.B % 32 == 0) ||
-           (plan.p.dtype == DAS_F32 && plan.fl == 1 && plan.p.B % 16 == 0) ||
-           (plan.p.dtype == DAS_C64 && plan.fl == 1 && plan.p.B % 16 == 0);
+    // fp32 with 4 frames per lane (split rows, B a multiple of 64), 2 (B a
+    // multiple of 32) or 1 (B a multiple of 16); complex64 with 2 (split rows,
+    // B a multiple of 32) or 1 (B a multiple of 16)
+    const int32_t B = plan.p.B;
+    if (plan.p.dtype == DAS_F32)
+        return (plan.fl == 4 && plan.split == 2 && B % 64 == 0) || (plan.fl == 2 && plan.split == 1 && B % 32 == 0) ||
+               (plan.fl == 1 && plan.split == 1 && B % 16 == 0);
+    return plan.p.dtype == DAS_C64 &&
+           ((plan.fl == 2 && plan.split == 2 && B % 32 == 0) || (plan.fl == 1 && plan.split == 1 && B % 16 == 0));
 }
 
 hipError_t das_launch_batch_inner_staged(const das_plan_t &plan, const DasKParams &kp, const float *rf,

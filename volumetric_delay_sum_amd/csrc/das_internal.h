@@ -37,7 +37,8 @@ struct das_plan {
     int32_t q_group;          // batch-inner: transmit events per receiver sweep
     int32_t staged;           // batch-inner: 1 = LDS-staged kernel, 0 = direct loads
     int32_t vpr;              // staged kernel: voxels per DPP row (depth of the 8 x 8 x vpr tile)
-    int32_t halves;           // staged kernel: frame halves per row (2: 64 fp32 / 32 complex frames, 8 receivers a step)
+    int32_t split;            // staged kernel: 2 = each DPP row split between two voxels (16-byte lanes,
+                              // 64 fp32 / 32 complex frames, 8 receivers a step), else 1
 };
 
 // Launchers (defined next to their kernels).  They assume validated input.
