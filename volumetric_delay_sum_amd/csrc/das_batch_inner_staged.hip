@@ -76,11 +76,13 @@ struct Geo {
     static_assert(S == 1 || (S == 2 && LANEB == 16), "split rows");
 };
 
-// Per-lane state of one voxel in one step: sample index and weights.
+// Per-lane state of one voxel in one step: sample index and weights.  Every
+// field is 32-bit: a padded struct copied between the pipeline roles leaves
+// its padding bytes in private (scratch) memory, written every step.
 struct Step {
     uint32_t k;
     float a, b, ai, bi;
-    bool active;
+    uint32_t active;    // 1 if the weight is non-zero
 };
 
 struct Cursor {
@@ -109,7 +111,7 @@ __device__ __forceinline__ Step make_step(const DasKParams &P, const das::RxTerm
     const float w = valid ? tx.w * R.w : 0.0f;
     Step st;
     st.k = k;
-    st.active = w != 0.0f;
+    st.active = w != 0.0f ? 1u : 0u;
     const float bw = w * f, aw = w - bw;
     if constexpr (IQ) {
         // phase exp(+j 2 pi f0 (tau_tx + d / c)): event part times receive part
@@ -291,7 +293,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     struct Window {
         uint32_t loff[PL];
         int kmin_w, rows_w;    // wave's copy: first sample row, number of sample rows
-        bool overflow;
+        uint32_t overflow;     // 32-bit for the same reason as Step
     };
     struct Slots {
         int kmn, kmx, kmn_w, kmx_w;    // window of receiver lrx, and of this wave's receiver
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
 #pragma unroll
         for (int v = 0; v < PL; ++v)
             wdw.loff[v] = s[v].active ? base + (uint32_t)((int)s[v].k - sl.kmn) * G::ROWB : base;
-        wdw.overflow = __any(np > G::W_MAX);
+        wdw.overflow = __any(np > G::W_MAX) ? 1u : 0u;
         wdw.kmin_w = sl.kmn_w;
         wdw.rows_w = (sl.kmn_w <= sl.kmx_w) ? sl.kmx_w - sl.kmn_w + 2 : 0;   // sample rows kmin .. kmax + 1
         return wdw;
