@@ -63,6 +63,19 @@ def test_degenerate_shapes(gpu, alg, layout):
     assert np.all(ref == 0.0) and np.all(y == 0.0)
 
 
+@pytest.mark.parametrize("f_number", [0.3, 0.45, 0.7, 1.0, 3.0, 0.0])
+@pytest.mark.parametrize("alg,layout", [("baseline", "kqmb"), ("batch_inner", "qmkb")])
+def test_receive_apodization_f_numbers(gpu, f_number, alg, layout):
+    """Receive Hann at several f-numbers.  From 0.45 up the kernels evaluate
+    the plan's polynomial in sin^2(theta); 0.3 takes the atan2f / cospif
+    path; 0 switches apodization off.  A 37 x 3 array over a 13 x 7 x 3 grid
+    puts many receivers on both sides of the aperture edge."""
+    cfg = _ragged(B=32, array=(37, 3), f_number=f_number)
+    inp = Inputs(cfg, w_tx="uniform")
+    y = to_numpy(run_gpu(inp, alg, layout), False)
+    assert_parity(y, oracle_ref(inp), f"f# {f_number} {alg}/{layout}")
+
+
 @pytest.mark.parametrize("alg,layout", ALGS)
 def test_terms_off_the_record_end(gpu, alg, layout):
     # K short enough that deep voxels lose part of their (q, m) terms

@@ -76,6 +76,85 @@ int32_t pick_q_group(const das_problem &p, int32_t elem, bool staged) {
     return row <= 128 ? 3 : (row <= 256 ? 2 : 1);
 }
 
+// Receive Hann over the angle from the array normal (the oracle's
+// definition: 0.5 (1 + cos(pi theta / theta_max)) for dz > 0 and theta <
+// theta_max) written as a function of v = 1 - cos(theta), scaled to
+// y = v / vmax in [0, 1) over the aperture:
+// w(y) = cos^2(pi/2 theta(y) / theta_max), theta = 2 asin(sqrt(v / 2)).
+// w is an even function of theta, hence a power series in 1 - cos(theta)
+// whose only singularity is at v = 2 (theta = pi), at least 1 away from the
+// aperture for any f-number, so a short polynomial fits it everywhere; the
+// kernels then need a reciprocal and a few FMAs instead of atan2 and cos.
+// The fit is Chebyshev interpolation on [0, 1], taken to monomials in y and
+// accepted at the lowest degree whose fp32 Horner evaluation stays within
+// 2.5e-7 of w on a fine grid (degree 7 at most; checked for f-numbers from
+// 1e-6 to 1e9).  Returns false if no degree reaches that.
+bool fit_apodization(das_plan_t *pl) {
+    pl->apod_inv_vmax = 0.0f;
+    for (int i = 0; i < DAS_APOD_TERMS; ++i) pl->apod_c[i] = 0.0f;
+    const double F = pl->p.f_number;
+    if (!(F > 0.0))
+        return true;                                 // no apodization
+    const double pi = 3.14159265358979323846;
+    const double tm = std::atan(1.0 / (2.0 * F));
+    const double sh = std::sin(0.5 * tm);
+    const double vmax = 2.0 * sh * sh;              // 1 - cos(theta_max), without cancellation
+    auto w = [&](double y) {
+        const double v = std::min(std::max(y * vmax, 0.0), 2.0);
+        const double c = std::cos(0.5 * pi * (2.0 * std::asin(std::sqrt(0.5 * v))) / tm);
+        return c * c;
+    };
+    for (int deg = 1; deg < DAS_APOD_TERMS; ++deg) {
+        const int n = deg + 1;
+        double cheb[DAS_APOD_TERMS] = {0};
+        for (int j = 0; j < n; ++j) {
+            double s = 0.0;
+            for (int k = 0; k < n; ++k) {
+                const double th = pi * (k + 0.5) / n;
+                s += w(0.5 + 0.5 * std::cos(th)) * std::cos(j * th);
+            }
+            cheb[j] = (j == 0 ? 1.0 : 2.0) * s / n;
+        }
+        // sum_j cheb[j] T_j(z) as monomials in z (T_{j+1} = 2 z T_j - T_{j-1}) ...
+        double tprev[DAS_APOD_TERMS] = {1.0}, tcur[DAS_APOD_TERMS] = {0.0, 1.0}, pz[DAS_APOD_TERMS] = {0};
+        pz[0] = cheb[0];
+        for (int j = 1; j < n; ++j) {
+            for (int i = 0; i <= j; ++i) pz[i] += cheb[j] * tcur[i];
+            double tnext[DAS_APOD_TERMS] = {0};
+            for (int i = 0; i <= j && i + 1 < DAS_APOD_TERMS; ++i) tnext[i + 1] += 2.0 * tcur[i];
+            for (int i = 0; i < DAS_APOD_TERMS; ++i) tnext[i] -= tprev[i];
+            std::memcpy(tprev, tcur, sizeof tcur);
+            std::memcpy(tcur, tnext, sizeof tnext);
+        }
+        // ... then in y, with z = 2 y - 1 (Horner composition)
+        double py[DAS_APOD_TERMS] = {0};
+        for (int i = deg; i >= 0; --i) {
+            double nx[DAS_APOD_TERMS] = {0};
+            for (int m = 0; m < deg; ++m) {
+                nx[m + 1] += 2.0 * py[m];
+                nx[m] -= py[m];
+            }
+            nx[0] += pz[i];
+            std::memcpy(py, nx, sizeof nx);
+        }
+        float c32[DAS_APOD_TERMS] = {0};
+        for (int i = 0; i <= deg; ++i) c32[i] = (float)py[i];
+        double err = 0.0;
+        for (int g = 0; g <= 4000; ++g) {
+            const double y = g / 4000.0;
+            float acc = c32[DAS_APOD_TERMS - 1];
+            for (int i = DAS_APOD_TERMS - 2; i >= 0; --i) acc = std::fma(acc, (float)y, c32[i]);
+            err = std::max(err, std::fabs((double)acc - w(y)));
+        }
+        if (err <= 2.5e-7) {
+            pl->apod_inv_vmax = (float)(1.0 / vmax);
+            for (int i = 0; i < DAS_APOD_TERMS; ++i) pl->apod_c[i] = c32[i];
+            return true;
+        }
+    }
+    return false;
+}
+
 DasKParams make_params(const das_plan_t &pl, int32_t q_begin, int32_t q_count, int32_t accumulate) {
     const das_problem &p = pl.p;
     DasKParams k{};
@@ -91,7 +170,8 @@ DasKParams make_params(const das_plan_t &pl, int32_t q_begin, int32_t q_count, i
     k.f0 = p.f_demod;
     k.f0_over_c = p.f_demod / p.c;
     k.apod = p.f_number > 0.0 ? 1 : 0;
-    k.inv_theta_max = k.apod ? (float)(1.0 / std::atan(1.0 / (2.0 * p.f_number))) : 0.0f;
+    k.apod_inv_vmax = pl.apod_inv_vmax;
+    for (int i = 0; i < DAS_APOD_TERMS; ++i) k.apod_c[i] = pl.apod_c[i];
     k.f_number = p.f_number;
     k.c = p.c;
     k.t0 = p.t0;
@@ -235,6 +315,10 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
     if (want_staged && p.dtype == DAS_C64 && p.B % 16 == 0)
         pl->fl = 1;
     pl->split = 1;
+    if (!fit_apodization(pl)) {
+        delete pl;
+        return DAS_ERR_UNSUPPORTED;
+    }
     pl->staged = (want_staged && das_staged_supported(*pl)) ? 1 : 0;
     pl->q_group = pick_q_group(p, elem, pl->staged != 0);
     const char *vv = std::getenv("DAS_STAGED_VPR");

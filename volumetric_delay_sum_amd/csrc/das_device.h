@@ -51,14 +51,17 @@ __device__ __forceinline__ double sqrt_f64(double x) {
 }
 
 // Receive apodization: Hann over the angle from the array normal,
-// 0.5 (1 + cos(pi theta / theta_max)) = cos^2(pi/2 theta / theta_max) for
-// dz > 0 and theta < theta_max, else 0.  fp32 is enough for a weight.
-__device__ __forceinline__ float rx_weight(const DasKParams &P, float rho, float dz) {
-    float th = atan2f(rho, dz);
-    float u = th * P.inv_theta_max;
-    float c = cospif(0.5f * u);
-    float w = c * c;
-    w = (dz > 0.0f && u < 1.0f) ? w : 0.0f;
+// 0.5 (1 + cos(pi theta / theta_max)) for dz > 0 and theta < theta_max, else
+// 0, evaluated as the plan's polynomial in y = (1 - cos theta) / (1 - cos
+// theta_max), inside the aperture iff y < 1.  1 - cos theta = rho^2 / (d (d +
+// dz)) has no cancellation; fp32 is enough for a weight (about 1e-6).
+__device__ __forceinline__ float rx_weight(const DasKParams &P, double rho2, double d, double dz) {
+    const float den = (float)(d * (d + dz));
+    const float y = (float)rho2 * __builtin_amdgcn_rcpf(den) * P.apod_inv_vmax;
+    float w = P.apod_c[DAS_APOD_TERMS - 1];
+#pragma unroll
+    for (int i = DAS_APOD_TERMS - 2; i >= 0; --i) w = __builtin_fmaf(w, y, P.apod_c[i]);
+    w = (dz > 0.0 && y < 1.0f) ? w : 0.0f;
     return P.apod ? w : 1.0f;
 }
 
@@ -74,12 +77,12 @@ template <bool IQ>
 __device__ __forceinline__ RxTerm rx_term(const DasKParams &P, double vx, double vy, double vz,
                                           float px, float py, float pz) {
     const double dx = vx - (double)px, dy = vy - (double)py, dz = vz - (double)pz;
-    const double d2 = __builtin_fma(dx, dx, __builtin_fma(dy, dy, dz * dz));
+    const double rho2 = __builtin_fma(dx, dx, dy * dy);
+    const double d2 = __builtin_fma(dz, dz, rho2);
     const double d = sqrt_f64(d2);
     RxTerm t;
     t.s_rx = d * P.fs_over_c;
-    const float rho = sqrtf((float)__builtin_fma(dx, dx, dy * dy));
-    t.w = rx_weight(P, rho, (float)dz);
+    t.w = rx_weight(P, rho2, d, dz);
     t.pc = 1.0f;
     t.ps = 0.0f;
     if constexpr (IQ) {
@@ -182,7 +185,12 @@ __device__ __forceinline__ BufRsrc make_rsrc(const char *base, uint64_t bytes) {
     BufRsrc r;
     r.x = (int)(uint32_t)a;
     r.y = (int)((uint32_t)(a >> 32) & 0xffffu);
-    r.z = (int)(bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes);
+    // clamp to 32 bits by testing the high word: scalar code has no 64-bit
+    // ordered compare, and the compiler would otherwise turn the test back
+    // into one, done in vector registers (the operands are wave-uniform)
+    uint32_t hi = (uint32_t)(bytes >> 32);
+    asm("" : "+s"(hi));
+    r.z = (int)(hi != 0u ? 0xffffffffu : (uint32_t)bytes);
     r.w = 0x00020000;   // gfx9 family: 32-bit data format, raw access
     return r;
 }

@@ -7,6 +7,9 @@
 
 #include "das.h"
 
+// Terms of the receive-apodization polynomial (degree DAS_APOD_TERMS - 1).
+#define DAS_APOD_TERMS 8
+
 // Kernel-side constants of one beamform launch, passed by value.
 struct DasKParams {
     double ox, oy, oz;        // voxel (0,0,0) centre, metres
@@ -18,8 +21,11 @@ struct DasKParams {
     double f0_over_c;         // IQ phase cycles per metre of path
     double f_number;          // receive Hann (fp64 kernels form theta_max themselves)
     double c, t0;             // m/s and s, as given (fp64 kernels)
-    float inv_theta_max;      // 1 / theta_max (receive Hann)
     int32_t apod;             // 0: w_rx = 1
+    // receive Hann as a polynomial in y = (1 - cos theta) / (1 - cos theta_max):
+    // w = sum_i apod_c[i] y^i inside the aperture (y < 1, dz > 0)
+    float apod_inv_vmax;      // 1 / (1 - cos theta_max)
+    float apod_c[DAS_APOD_TERMS];
     int32_t nx, ny, nz, N;
     int32_t B, Q, M, K;
     int32_t q_begin, q_count; // transmit events of this launch (absolute q)
@@ -37,6 +43,8 @@ struct das_plan {
     int32_t q_group;          // batch-inner: transmit events per receiver sweep
     int32_t staged;           // batch-inner: 1 = LDS-staged kernel, 0 = direct loads
     int32_t vpr;              // staged kernel: voxels per DPP row (depth of the 8 x 8 x vpr tile)
+    float apod_inv_vmax;      // receive Hann polynomial (see DasKParams), fitted once per plan
+    float apod_c[DAS_APOD_TERMS];
     int32_t split;            // staged kernel: 2 = each DPP row split between two voxels (16-byte lanes,
                               // 64 fp32 / 32 complex frames, 8 receivers a step), else 1
 };
