@@ -44,7 +44,7 @@ namespace {
 constexpr int THREADS = 1024;
 constexpr int ROW = 16;               // lanes per voxel column (one DPP row)
 constexpr int TX = 8, TY = 8;         // lateral voxel tile of one workgroup (one column per row)
-constexpr int LDS_ROW_BUDGET = 160000;   // bytes for the two row buffers
+constexpr int LDS_TOTAL = 163840;          // LDS of one workgroup on gfx950 (160 KiB)
 
 // Split rows (S = 2), for 16-byte lanes (4 fp32 or 2 complex frames, a staged
 // sample row of 256 bytes): a step takes 8 receivers, so the LDS holds as many
@@ -54,7 +54,7 @@ constexpr int LDS_ROW_BUDGET = 160000;   // bytes for the two row buffers
 // window) serves 64 fp32 or 32 complex frames.  Each tap is then one 16-byte
 // LDS read per lane, which gfx950 serves at nearly twice the bytes per clock
 // of 8-byte reads.
-template <bool IQ, int FL, int S>
+template <bool IQ, int FL, int S, int VPR>
 struct Geo {
     static constexpr int C = IQ ? 2 : 1;                 // floats per sample
     static constexpr int E = 4 * C;                      // bytes per sample
@@ -62,7 +62,14 @@ struct Geo {
     static constexpr int LANEB = NF * 4;                 // bytes per lane in a sample row
     static constexpr int ROWB = ROW * LANEB;             // bytes of the frame tile in one sample row
     static constexpr int NRX = ROW / S;                  // receivers per step
-    static constexpr int RW0 = LDS_ROW_BUDGET / (2 * NRX * ROWB);
+    static constexpr int NITEM = VPR * NRX;              // (voxel, receiver) items of a DPP row per step
+    // Weights of an item come from a table in LDS for 16-byte lanes (8 or 16
+    // FMAs per item), through DPP otherwise (see the compute loop)
+    static constexpr bool WTAB = LANEB == 16;
+    static constexpr int CW = IQ ? 4 : 2;                // floats of an item's weights (a, b; IQ: a, ai, b, bi)
+    static constexpr int COEF = WTAB ? (THREADS / ROW) * NITEM * CW * 4 : 0;   // weight table: [DPP row][item][CW]
+    static constexpr int SLOTS = 3 * 2 * NRX * 4;        // window slots: [3 sets][min, max][NRX]
+    static constexpr int RW0 = (LDS_TOTAL - COEF - SLOTS) / (2 * NRX * ROWB);
     static constexpr int RW = RW0 > 64 ? 64 : RW0;       // sample rows per receiver region
     static constexpr int W_MAX = RW - 1;                 // k positions per receiver window
     static constexpr int LPR = ROWB / 16;                // lanes per sample row in a 16-byte copy
@@ -70,7 +77,8 @@ struct Geo {
     static constexpr int MAXR = (RW + RPR * S - 1) / (RPR * S);   // copy rounds of one wave (S waves per receiver)
     static constexpr int REGION = RW * ROWB;             // bytes of one receiver's region
     static constexpr int BUF = NRX * REGION;             // bytes of one buffer
-    static constexpr int LDS_BYTES = 2 * BUF + 3 * 2 * NRX * 4;
+    static constexpr int LDS_BYTES = 2 * BUF + SLOTS + COEF;
+    static_assert(LDS_BYTES <= LDS_TOTAL, "LDS budget");
     static_assert(ROWB % 16 == 0 && 64 % LPR == 0, "copy granularity");
     static_assert(LANEB == 4 || LANEB == 8 || LANEB == 16, "reader width");
     static_assert(S == 1 || (S == 2 && LANEB == 16), "split rows");
@@ -144,7 +152,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
                                                                 const float *__restrict__ tau_tx,
                                                                 const float *__restrict__ w_tx,
                                                                 float *__restrict__ out, uint32_t tap_stride) {
-    using G = Geo<IQ, FL, S>;
+    using G = Geo<IQ, FL, S, VPR>;
     constexpr int C = G::C, E = G::E, NF = G::NF, NRX = G::NRX;
     // (voxel, receiver) pairs per lane: pair p is voxel p S + li / NRX of the
     // row and receiver m0 + li % NRX
@@ -153,6 +161,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     using TapV = typename Tap<NF>::type;
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
     int *slots = reinterpret_cast<int *>(lds + 2 * G::BUF);   // [3 sets][min, max][NRX]
+    constexpr uint32_t COEF_AT = 2 * G::BUF + G::SLOTS;       // weight table
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -374,20 +383,55 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         }
 
     // All voxels of one step from LDS: VPR x NRX (voxel, receiver) items.  Item
-    // (v, j) takes its coefficients and row offset from lane (v % S) NRX + j
-    // (pair v / S); each lane reads taps k and k + 1 of its frames (rows k and
-    // k + 1 are consecutive) and does 2 FL (IQ: 8 FL) FMAs.
+    // (v, j) takes its row offset from lane (v % S) NRX + j (pair v / S)
+    // through DPP; each lane reads taps k and k + 1 of its frames (rows k and
+    // k + 1 are consecutive) and does 2 FL (IQ: 8 FL) FMAs.  gfx950 issues
+    // plain fp32 FMAs two per cycle but DPP ones one per cycle.  With 16-byte
+    // lanes (8 or 16 FMAs per item) the weights therefore come from the row's
+    // table in LDS, one read that the row's 16 lanes share, and the FMAs are
+    // plain; with 8- or 4-byte lanes that read would add half again to the
+    // LDS bytes per item, which then binds, so the FMAs take the weights from
+    // lane (v % S) NRX + j through DPP.
     // The reads are issued DEPTH items ahead; the scheduling fences keep the
     // compiler from sinking each read next to its use, which would leave one
     // read in flight per wave (three ahead measured best with two voxels per
     // row, eight with one).  `at(t)` runs after item t (the next step's copy
     // rounds).
-    constexpr int NITEM = VPR * NRX;
-    constexpr int DEPTH = (VPR == 1) ? 8 : (G::LANEB == 16 ? 2 : 3);   // 16-byte lanes: 8 registers per item
+    constexpr int NITEM = G::NITEM;
+    constexpr bool WTAB = G::WTAB;
+    constexpr int DEPTH = (VPR == 1) ? 8 : (WTAB ? 2 : 3);
     // The first DEPTH items' reads are issued by prefetch(), for fp32 data at
     // the top of the step, so they land while the setup runs.
+    using CoefV = typename Tap<G::CW>::type;
     struct Ring {
         TapV r0[DEPTH], r1[DEPTH];
+        CoefV c[WTAB ? DEPTH : 1];
+    };
+    // this DPP row's weight table: item t at t CW floats.  The base is made
+    // opaque so that item offsets are added, not OR-ed, to it and fold into
+    // the reads' immediate offsets (one base register, not one per item).
+    uint32_t coef_row = COEF_AT + (uint32_t)vr * (uint32_t)(NITEM * G::CW * 4);
+    asm volatile("" : "+v"(coef_row));
+    using LdsCoefR = const volatile __attribute__((address_space(3))) CoefV *;
+    using LdsCoefW = volatile __attribute__((address_space(3))) CoefV *;
+    // Each lane enters the weights of its pairs (item (lv0 + p S) NRX + lrx).
+    // The row's 16 lanes are one wave's, whose LDS accesses complete in
+    // order, so the reads of this step follow these writes and the writes
+    // follow the reads of the step before; volatile keeps the compiler from
+    // reordering them.
+    auto write_coef = [&](const Step (&s)[PL]) {
+        if constexpr (!WTAB)
+            return;
+#pragma unroll
+        for (int p = 0; p < PL; ++p) {
+            const int t = (lv0 + p * S) * NRX + lrx;
+            CoefV c;
+            if constexpr (IQ)
+                c = CoefV{s[p].a, s[p].ai, s[p].b, s[p].bi};
+            else
+                c = CoefV{s[p].a, s[p].b};
+            *(LdsCoefW)(lds + coef_row + (uint32_t)t * (G::CW * 4)) = c;
+        }
     };
     // With 8 bytes per lane the two taps are read by two separate
     // instructions: on gfx950 two 64-bit reads of rows k and k + 1 are served
@@ -407,26 +451,57 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         const uint32_t addr = das::row_bcast<src>(loff[pr]) + laneoff_l;
         ring.r0[tt % DEPTH] = read_tap(addr);
         ring.r1[tt % DEPTH] = read_tap(addr + G::ROWB);
+        if constexpr (WTAB)
+            ring.c[tt % DEPTH] = *(LdsCoefR)(lds + coef_row + (uint32_t)(tt * G::CW * 4));
     };
     auto prefetch = [&](const uint32_t (&loff)[PL], Ring &ring) {
         das::unroll<DEPTH>([&](auto T) { issue_item(T, loff, ring); });
     };
-    // Interpolate-weight-accumulate of item tt from its two taps.
-    auto item_fma = [&](auto T, Step (&s)[PL], float (&pt)[VPR][NF], const TapV &x0, const TapV &x1) {
+    // Interpolate-weight-accumulate of item tt from its two taps and weights
+    // (from the table, c, or by DPP from the source lane's step state, s).
+    auto item_fma = [&](auto T, Step (&s)[PL], float (&pt)[VPR][NF], const TapV &x0, const TapV &x1,
+                        const CoefV &c) {
         constexpr int tt = decltype(T)::value;
         constexpr int v = tt / NRX, j = tt % NRX, src = (v % S) * NRX + j, pr = v / S;
-        if constexpr (IQ) {
+        if constexpr (!WTAB) {
+            if constexpr (IQ) {
 #pragma unroll
-            for (int f = 0; f < FL; ++f)
-                das::cmac_bcast<src>(pt[v][2 * f], pt[v][2 * f + 1], s[pr].a, s[pr].ai, s[pr].b, s[pr].bi,
-                                     x0[2 * f], x0[2 * f + 1], x1[2 * f], x1[2 * f + 1]);
+                for (int f = 0; f < FL; ++f)
+                    das::cmac_bcast<src>(pt[v][2 * f], pt[v][2 * f + 1], s[pr].a, s[pr].ai, s[pr].b, s[pr].bi,
+                                         x0[2 * f], x0[2 * f + 1], x1[2 * f], x1[2 * f + 1]);
+            } else {
+#pragma unroll
+                for (int f = 0; f < FL; ++f) das::lerp_bcast<src>(pt[v][f], s[pr].a, s[pr].b, x0[f], x1[f]);
+            }
+            return;
+        }
+        if constexpr (IQ) {
+            // (re, im) += (a + j ai)(x0r + j x0i) + (b + j bi)(x1r + j x1i)
+#pragma unroll
+            for (int f = 0; f < FL; ++f) {
+                float &re = pt[v][2 * f], &im = pt[v][2 * f + 1];
+                re = __builtin_fmaf(c[0], x0[2 * f], re);
+                im = __builtin_fmaf(c[0], x0[2 * f + 1], im);
+                re = __builtin_fmaf(-c[1], x0[2 * f + 1], re);
+                im = __builtin_fmaf(c[1], x0[2 * f], im);
+                re = __builtin_fmaf(c[2], x1[2 * f], re);
+                im = __builtin_fmaf(c[2], x1[2 * f + 1], im);
+                re = __builtin_fmaf(-c[3], x1[2 * f + 1], re);
+                im = __builtin_fmaf(c[3], x1[2 * f], im);
+            }
         } else {
 #pragma unroll
-            for (int f = 0; f < FL; ++f) das::lerp_bcast<src>(pt[v][f], s[pr].a, s[pr].b, x0[f], x1[f]);
+            for (int f = 0; f < FL; ++f) pt[v][f] = __builtin_fmaf(c[0], x0[f], pt[v][f]);
+#pragma unroll
+            for (int f = 0; f < FL; ++f) pt[v][f] = __builtin_fmaf(c[1], x1[f], pt[v][f]);
         }
+        // Pin the item's sums here: left alone, the compiler sinks these FMAs
+        // to the end of the step and keeps every item's taps live.
+#pragma unroll
+        for (int i = 0; i < NF; ++i) asm volatile("" : "+v"(pt[v][i]));
     };
-    // The step's coefficients are settled in place (they are dead after the
-    // loop), so no register copies are needed to give them their wait states.
+    // DPP weights are settled in place (they are dead after the loop), so no
+    // register copies are needed to give them their wait states.
     auto settle_all = [&](Step (&s)[PL]) {
 #pragma unroll
         for (int p = 0; p < PL; ++p) {
@@ -438,12 +513,13 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     };
     auto compute_lds = [&](Step (&s)[PL], const uint32_t (&loff)[PL], float (&pt)[VPR][NF], Ring &ring,
                            auto &&at) {
-        settle_all(s);
+        if constexpr (!WTAB)
+            settle_all(s);
         auto issue = [&](auto T) { issue_item(T, loff, ring); };
         __builtin_amdgcn_sched_barrier(0);
         das::unroll<NITEM>([&](auto T) {
             constexpr int tt = decltype(T)::value;
-            item_fma(T, s, pt, ring.r0[tt % DEPTH], ring.r1[tt % DEPTH]);
+            item_fma(T, s, pt, ring.r0[tt % DEPTH], ring.r1[tt % DEPTH], ring.c[WTAB ? tt % DEPTH : 0]);
             if constexpr (tt + DEPTH < NITEM)
                 issue(das::ic<tt + DEPTH>{});
             at(T);
@@ -551,6 +627,8 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
         __builtin_amdgcn_s_setprio(3);                 // every wave starts a step at the top priority
         const int set1 = (set == 2) ? 0 : set + 1, set2 = (set1 == 2) ? 0 : set1 + 1;
         Ring ring;
+        if (!wc.overflow)
+            write_coef(sc);
         if constexpr (!IQ) {                           // (complex data: registers are too tight)
             if (!wc.overflow)
                 prefetch(wc.loff, ring);
