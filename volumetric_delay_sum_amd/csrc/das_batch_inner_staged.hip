@@ -26,8 +26,10 @@
 //      tile's part of each) from HBM straight into LDS with LDS-DMA buffer
 //      loads: no registers, no store instructions;
 //   4. each row walks its (voxel, receiver) items, broadcasting the source
-//      lane's LDS offset and weights through DPP row_newbcast; a lane reads its
-//      frames at k and k + 1 (consecutive rows) and does 2 FL FMAs.
+//      lane's LDS offset through DPP row_newbcast, and its weights the same
+//      way (8- and 4-byte lanes) or from a per-row table in LDS (16-byte
+//      lanes); a lane reads its frames at k and k + 1 (consecutive rows) and
+//      does 2 FL (complex: 8 FL) FMAs.
 // The rows live in two buffers: step i computes from one while the rows of
 // step i + 1 stream into the other, so a step needs one barrier.  Windows are
 // reduced two steps ahead (three slot sets) so that the copy of step i + 1
