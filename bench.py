@@ -16,6 +16,7 @@ from __future__ import annotations
 import argparse
 import glob
 import hashlib
+import re
 import json
 import os
 import sys
@@ -29,13 +30,18 @@ PEAK_FP64_TFLOPS = 78.6         # MI355X vector fp64 (published)
 PEAK_HBM_GBS = 8000.0
 
 
+_COMMENT = re.compile(r"/\*.*?\*/|//[^\n]*", re.S)
+
+
 def kernel_source_hash() -> str:
-    """Hash of the kernel sources; a stored counter reading is valid only for the same hash."""
+    """Hash of the kernel sources' code (comments and whitespace dropped); a
+    stored counter reading is valid only for the same hash."""
     h = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "volumetric_delay_sum_amd", "csrc", "*"))):
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode())
-            h.update(fh.read())
+        with open(f, encoding="utf-8", errors="replace") as fh:
+            code = " ".join(_COMMENT.sub(" ", fh.read()).split())
+        h.update(os.path.basename(f).encode())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 
