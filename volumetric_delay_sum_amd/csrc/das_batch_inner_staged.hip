@@ -69,7 +69,12 @@ struct Geo {
     // FMAs per item), through DPP otherwise (see the compute loop)
     static constexpr bool WTAB = LANEB == 16;
     static constexpr int CW = IQ ? 4 : 2;                // floats of an item's weights (a, b; IQ: a, ai, b, bi)
-    static constexpr int COEF = WTAB ? (THREADS / ROW) * NITEM * CW * 4 : 0;   // weight table: [DPP row][item][CW]
+    // weight table: [DPP row][item][CW], each row's part padded by 16 bytes so
+    // that the four rows of a wave, which read one record each per item, fall
+    // in different LDS banks (unpadded, 128- or 256-byte parts put them in the
+    // same banks, a 2- or 4-way conflict)
+    static constexpr int COEF_ROW = NITEM * CW * 4 + 16;
+    static constexpr int COEF = WTAB ? (THREADS / ROW) * COEF_ROW : 0;
     static constexpr int SLOTS = 3 * 2 * NRX * 4;        // window slots: [3 sets][min, max][NRX]
     static constexpr int RW0 = (LDS_TOTAL - COEF - SLOTS) / (2 * NRX * ROWB);
     static constexpr int RW = RW0 > 64 ? 64 : RW0;       // sample rows per receiver region
@@ -412,7 +417,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     // this DPP row's weight table: item t at t CW floats.  The base is made
     // opaque so that item offsets are added, not OR-ed, to it and fold into
     // the reads' immediate offsets (one base register, not one per item).
-    uint32_t coef_row = COEF_AT + (uint32_t)vr * (uint32_t)(NITEM * G::CW * 4);
+    uint32_t coef_row = COEF_AT + (uint32_t)vr * (uint32_t)G::COEF_ROW;
     asm volatile("" : "+v"(coef_row));
     using LdsCoefR = const volatile __attribute__((address_space(3))) CoefV *;
     using LdsCoefW = volatile __attribute__((address_space(3))) CoefV *;
