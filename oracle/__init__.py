@@ -10,6 +10,8 @@ numpy transposes: the permute is a pure relayout, so the library primitive is
 its definition ("ffdas: volumetric ultrasound reconstruction at warp speed",
 Section 3, batch-inner tiling: B x Q x M x K becomes K x Q x M x B; ffdas docs,
 "How It Works", ALG2: the batch index moves to the innermost position).
+``to_binary16`` is the rounding of the binary16 storage variant (numpy's
+float16 conversion, pinned against hand-derived bit patterns).
 """
 from __future__ import annotations
 
@@ -134,6 +136,26 @@ def permute_qmkb(x: np.ndarray) -> np.ndarray:
     """B x Q x M x K (x 2 for IQ) -> Q x M x K x B (x 2): batch moved innermost."""
     axes = (1, 2, 3, 0) + ((4,) if x.ndim == 5 else ())
     return np.ascontiguousarray(np.transpose(x, axes))
+
+
+def to_binary16(x: np.ndarray) -> np.ndarray:
+    """Samples as they are held with binary16 storage, widened back to float32.
+
+    "ffdas: volumetric ultrasound reconstruction at warp speed", Section 3, FP16
+    variant: the samples are kept in half precision and converted to fp32
+    before the interpolation; ffdas docs, mixed-precision API: half for real
+    data, half2 (a pair of halves) for complex data.  Each float32 value is
+    rounded to the nearest IEEE binary16 value, ties to even, with subnormal
+    halves kept, overflow to infinity and NaN kept NaN (numpy's float16
+    conversion); the widening back is exact.  Complex data (a trailing re/im
+    axis) is rounded per component.  The beamform of binary16 storage is then
+    ``das_sum`` of these samples.
+    """
+    x = np.asarray(x)
+    if x.dtype != np.float32:
+        raise TypeError(f"binary16 storage rounds float32 samples, got {x.dtype}")
+    with np.errstate(over="ignore"):
+        return x.astype(np.float16).astype(np.float32)
 
 
 # Transmit-event kinds (the values of the library's enum, restated).

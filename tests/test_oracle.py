@@ -409,3 +409,76 @@ def test_permute_references():
     assert z.shape == (3, 4, 5, 2) and z[2, 3, 4, 1] == x[1, 2, 3, 4]
     xi = np.arange(2 * 3 * 4 * 5 * 2, dtype=np.float32).reshape(2, 3, 4, 5, 2)
     assert oracle.permute_kqmb(xi)[4, 2, 3, 1, 1] == xi[1, 2, 3, 4, 1]
+
+
+# ---------------------------------------------------------------------------
+# Binary16 storage (the FP16 variant): the rounding, pinned bit for bit to
+# hand-derived cases, and the beamform of rounded samples.
+# ---------------------------------------------------------------------------
+
+GOLDEN16 = os.path.join(os.path.dirname(__file__), "golden", "binary16_cases.json")
+
+
+def test_binary16_hand_cases():
+    import oracle
+    cases = json.load(open(GOLDEN16))["cases"]
+    x = np.array([int(c["f32"], 16) for c in cases], dtype=np.uint32).view(np.float32)
+    got = oracle.to_binary16(x).astype(np.float16).view(np.uint16)
+    for c, g in zip(cases, got):
+        assert int(g) == int(c["f16"], 16), f"{c['f32']} -> {int(g):#06x}, expected {c['f16']} ({c['why']})"
+
+
+def test_binary16_keeps_representable_values_and_nan():
+    import oracle
+    # every finite binary16 value, as float32, comes back unchanged
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    finite = h[np.isfinite(h)].astype(np.float32)
+    np.testing.assert_array_equal(oracle.to_binary16(finite), finite)
+    assert np.isnan(oracle.to_binary16(np.array([np.nan], dtype=np.float32)))[0]
+    with pytest.raises(TypeError):
+        oracle.to_binary16(np.zeros(3, dtype=np.float64))
+
+
+def test_binary16_is_the_nearest_half():
+    import oracle
+    # brute force over random float32 values in the normal range: no finite
+    # half is closer than the rounded one, and the error is at most 2^-11 |x|
+    rng = np.random.default_rng(61)
+    x = (rng.standard_normal(4000) * np.exp2(rng.integers(-13, 15, 4000))).astype(np.float32)
+    y = oracle.to_binary16(x).astype(np.float64)
+    halves = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    grid = np.unique(halves[np.isfinite(halves)].astype(np.float64))
+    xd = x.astype(np.float64)
+    i = np.clip(np.searchsorted(grid, xd), 1, grid.size - 1)
+    best = np.minimum(np.abs(grid[i] - xd), np.abs(grid[i - 1] - xd))
+    np.testing.assert_array_equal(np.abs(y - xd), best)
+    normal = (np.abs(xd) >= np.exp2(-14)) & (np.abs(xd) <= 65504.0)
+    assert normal.sum() > 3000
+    assert np.all(np.abs(y - xd)[normal] <= np.exp2(-11) * np.abs(xd)[normal])
+
+
+def test_binary16_storage_beamform(oracle_mod):
+    import oracle
+    for iq in (False, True):
+        f, x, rx, tau, w = _random_problem(71, iq=iq)
+        # samples a half holds exactly: storage changes nothing
+        xi = np.random.default_rng(72).integers(-2048, 2049, x.shape).astype(np.float32)
+        np.testing.assert_array_equal(oracle_mod.das_sum(f, oracle.to_binary16(xi), rx, tau, w),
+                                      oracle_mod.das_sum(f, xi, rx, tau, w))
+        # general samples: the change is the beamform of the rounding error
+        # (linearity; the error is exact in float32), bounded by the weight sum
+        # times the largest error, itself at most 2^-11 max|x|
+        x16 = oracle.to_binary16(x)
+        d = (x16 - x).astype(np.float32)
+        assert np.abs(d).max() > 0
+        y32 = oracle_mod.das_sum(f, x, rx, tau, w)
+        y16 = oracle_mod.das_sum(f, x16, rx, tau, w)
+        yd = oracle_mod.das_sum(f, d, rx, tau, w)
+        np.testing.assert_allclose(y16, y32 + yd, rtol=0, atol=1e-12 * np.abs(y32).max())
+        ones = np.ones(x.shape, dtype=np.float32)
+        if iq:
+            ones[..., 1] = 0.0
+        wsum = np.abs(oracle_mod.das_sum(f, ones, rx, tau, w))     # weights are >= 0 here
+        bound = wsum * np.abs(d).max() * (2.0 if iq else 1.0)
+        assert np.all(np.abs(y16 - y32) <= bound + 1e-12)
+        assert np.abs(d).max() <= np.exp2(-11) * np.abs(x).max()
