@@ -77,6 +77,9 @@ def main():
                          "event-timed chunked pass)")
     ap.add_argument("--wide", action="store_true",
                     help="float64 samples (complex128 for IQ workloads): the baseline's fp64 path")
+    ap.add_argument("--storage", default="native", choices=["native", "f16"],
+                    help="samples in the permuted buffer: as given, or rounded to binary16 by the permute "
+                         "(batch-inner; the arithmetic stays fp32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-voxels", type=int, default=0, help="oracle sample size (0: one depth slab)")
     args = ap.parse_args()
@@ -114,7 +117,12 @@ def main():
     tau_d = torch.from_numpy(tau).to(dev)
     w_d = torch.from_numpy(w).to(dev)
 
-    plan = das.plan_from_fields(fields, algorithm=args.algorithm, layout=args.layout, wide=args.wide)
+    h16 = args.storage == "f16"
+    if h16 and (args.wide or args.algorithm != "batch_inner"):
+        print("bench.py: --storage f16 is a batch-inner option for fp32 / complex64 samples", file=sys.stderr)
+        sys.exit(2)
+    plan = das.plan_from_fields(fields, algorithm=args.algorithm, layout=args.layout, wide=args.wide,
+                                storage=args.storage)
     out = torch.empty(plan.output_shape(), dtype=torch.float64 if args.wide else torch.float32, device=dev)
     bi = plan.batch_inner
     # events per das_permute / das_beamform pair (all Q unless the layout's
@@ -123,7 +131,8 @@ def main():
     if args.q_chunk > 0:
         qc = min(qc, args.q_chunk)
     chunks = [(q0, min(qc, cfg.Q - q0)) for q0 in range(0, cfg.Q, qc)]
-    perm = torch.empty(plan.permuted_shape(qc), dtype=torch.float32, device=dev) if bi else None
+    perm = torch.empty(plan.permuted_shape(qc), dtype=torch.float16 if h16 else torch.float32,
+                       device=dev) if bi else None
     per_event = perm.numel() // qc if bi else 0
     stream = torch.cuda.current_stream(dev)
 
@@ -216,7 +225,7 @@ def main():
     kernel_name = ("das_bi_staged_kernel" if plan.info["staged"] else "das_batch_inner_kernel") if bi \
         else ("das_baseline_f64_kernel" if args.wide else "das_baseline_kernel")
     peak = PEAK_FP64_TFLOPS if args.wide else PEAK_FP32_TFLOPS
-    traffic = stored_traffic(kernel_name, cfg.name)
+    traffic = stored_traffic(kernel_name, cfg.name + ("-f16" if h16 else ""))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -230,6 +239,8 @@ def main():
         vox = vox[:cap]
         print(f"[bench] cpu baseline: oracle on {vox.size} voxels", file=sys.stderr, flush=True)
         rf_host = rf.cpu().numpy()
+        if h16:
+            rf_host = oracle.to_binary16(rf_host)      # the samples the kernel reads
         t1 = time.perf_counter()
         ref = oracle.das_sum(fields, rf_host, rx, tau, w, voxels=vox)
         cpu_s = time.perf_counter() - t1
@@ -243,7 +254,7 @@ def main():
         cpu = {"value": cpu_acc / cpu_s / 1e9, "unit": "G acc/s", "cores": 1, "kind": "oracle",
                "sample": f"{cfg.name}: depth slab iz={iz} ({vox.size} voxels) x all {cfg.Q} events x "
                          f"{cfg.M} receivers x {cfg.B} frames = {cpu_acc:.3e} accumulations in {cpu_s:.1f} s, "
-                         "single-threaded fp64 C oracle",
+                         "single-threaded fp64 C oracle" + (" of the binary16-rounded samples" if h16 else ""),
                "gpu_parity_on_sample": {"max_rel": max(p[0] for p in parity), "l2_rel": max(p[1] for p in parity)}}
 
     info = plan.info
@@ -271,6 +282,8 @@ def main():
                      else "das_beamform (baseline)"),
             "accumulations_per_step": accs,
             "frames_per_lane": info["frames_per_lane"],
+            "storage": ("binary16 samples in the permuted buffer (rounded by the permute, widened to fp32 "
+                        "in the kernel)") if h16 else "samples as given",
         },
         "roofline": {
             "bound": "alu",

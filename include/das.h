@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DAS_ABI_VERSION 4
+#define DAS_ABI_VERSION 5
 
 typedef enum das_status {
     DAS_OK = 0,
@@ -87,12 +87,29 @@ enum { DAS_ALG_DEFAULT = 0, DAS_ALG_BASELINE = 1, DAS_ALG_BATCH_INNER = 2, DAS_A
  *                   innermost, the other axes kept in order)               */
 enum { DAS_LAYOUT_KQMB = 0, DAS_LAYOUT_QMKB = 1 };
 
+/* Storage of the samples in the permuted buffer ("ffdas: volumetric
+ * ultrasound reconstruction at warp speed", FP16 variant: samples kept in
+ * half precision and widened to fp32 before the interpolation; ffdas docs,
+ * mixed-precision API: half for real data, half2 for complex).
+ *  DAS_STORE_NATIVE  the plan's dtype (float32, or float32 re/im pairs)
+ *  DAS_STORE_F16     IEEE binary16: one half per DAS_F32 sample, a (re, im)
+ *                    pair of halves per DAS_C64 sample.  das_permute rounds
+ *                    each float32 to nearest, ties to even (overflow gives
+ *                    +-inf, subnormal halves are kept, NaN stays NaN);
+ *                    das_beamform widens every half exactly to float32 and
+ *                    computes as for DAS_STORE_NATIVE.  So the result is the
+ *                    float32 beamform of the rounded samples.  Batch-inner
+ *                    DAS_F32 / DAS_C64 plans only (the conversion is part of
+ *                    the permute).                                          */
+enum { DAS_STORE_NATIVE = 0, DAS_STORE_F16 = 1 };
+
 typedef struct das_problem {
     int32_t B, Q, M, K;      /* frames, transmit events, receivers, samples (K >= 2)   */
     int32_t nx, ny, nz;      /* voxel grid; n = (iz*ny + iy)*nx + ix                   */
     int32_t dtype;           /* DAS_F32 | DAS_C64 | DAS_F64 | DAS_C128                 */
     int32_t algorithm;       /* DAS_ALG_DEFAULT | _BASELINE | _BATCH_INNER | _AUTO      */
     int32_t layout;          /* DAS_LAYOUT_KQMB | DAS_LAYOUT_QMKB (batch-inner only)    */
+    int32_t storage;         /* DAS_STORE_NATIVE | DAS_STORE_F16 (batch-inner only)     */
     double  origin[3];       /* metres: centre of voxel (0,0,0)                         */
     double  spacing[3];      /* metres: voxel pitch along x, y, z (> 0)                 */
     double  fs;              /* Hz, sampling rate (> 0)                                 */
@@ -117,6 +134,8 @@ typedef struct das_plan_info {
     int32_t staged;             /* batch-inner: 1 if frame rows are staged through LDS
                                    (8 x 8 voxel tiles per 1024-thread workgroup), 0 if
                                    every lane loads its rows from memory             */
+    int32_t store_bytes;        /* bytes per sample in the permuted buffer: elem_bytes,
+                                   or 2 (DAS_F32) / 4 (DAS_C64) with DAS_STORE_F16   */
 } das_plan_info;
 
 /* Validate a problem and build a host-side plan.  Host only: no HIP call, no
@@ -126,7 +145,9 @@ typedef struct das_plan_info {
  * K < 2, non-finite or non-positive fs / c / spacing, unknown enums;
  * DAS_ERR_UNSUPPORTED for dtype / f_demod mismatch (complex types need
  * f_demod > 0, real ones f_demod == 0), DAS_F64 / DAS_C128 with
- * DAS_ALG_BATCH_INNER, or N, B*Q*M*K beyond 2^31 elements per axis. */
+ * DAS_ALG_BATCH_INNER, DAS_STORE_F16 with a plan that does not resolve to
+ * the batch-inner algorithm or with DAS_F64 / DAS_C128, or N, B*Q*M*K beyond
+ * 2^31 elements per axis. */
 das_status das_plan(const das_problem *problem, das_plan_t **out);
 
 void das_plan_destroy(das_plan_t *plan);
@@ -134,7 +155,7 @@ void das_plan_destroy(das_plan_t *plan);
 das_status das_plan_get_info(const das_plan_t *plan, das_plan_info *info);
 
 /* Bytes of the permuted buffer that holds q_count transmit events
- * (K * q_count * M * B * elem_bytes, in either layout).  0 on a bad argument. */
+ * (K * q_count * M * B * store_bytes, in either layout).  0 on a bad argument. */
 size_t das_permuted_bytes(const das_plan_t *plan, int32_t q_count);
 
 /* Largest q_count one das_beamform call accepts with this plan: Q, except
@@ -147,7 +168,8 @@ int32_t das_max_q_chunk(const das_plan_t *plan);
 /* Permute transmit events [q_begin, q_begin + q_count) of the B x Q x M x K
  * input into the plan's frames-innermost layout ("ffdas: volumetric
  * ultrasound reconstruction at warp speed", Section 3, batch-inner tiling:
- * frames become the contiguous axis; ffdas docs, ALG2).  Bit-exact relayout.
+ * frames become the contiguous axis; ffdas docs, ALG2).  Bit-exact relayout,
+ * or with DAS_STORE_F16 the relayout of each sample rounded to binary16.
  *   rf_bqmk   B x Q x M x K samples (all Q), elem_bytes each
  *   rf_perm   das_permuted_bytes(plan, q_count) bytes; event q is stored at
  *             local index q - q_begin
@@ -162,7 +184,7 @@ das_status das_permute(const das_plan_t *plan, const void *rf_bqmk, void *rf_per
 /* Beamform transmit events [q_begin, q_begin + q_count) into out.
  *   rf       baseline: the B x Q x M x K input (all Q, indexed by absolute q);
  *            batch-inner: the permuted chunk made by das_permute with the same
- *            q_begin / q_count
+ *            q_begin / q_count (binary16 samples with DAS_STORE_F16)
  *   rx_pos   M x 3 float32 receiver positions (x, y, z), metres
  *   tau_tx   Q x N float32 transmit delays, seconds (absolute q)
  *   w_tx     Q x N float32 transmit weights (absolute q)

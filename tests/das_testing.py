@@ -57,16 +57,17 @@ class Inputs:
 
 
 def run_gpu(inp: Inputs, algorithm: str, layout: str = "kqmb", q_chunk: int | None = None,
-            out=None, accumulate_into=None):
+            out=None, accumulate_into=None, storage: str = "native"):
     """Beamform all events through the C ABI; returns the device output tensor.
 
     Batch-inner runs permute + beamform per chunk of q_chunk events (all Q at
-    once by default), accumulating chunks after the first.
+    once by default), accumulating chunks after the first.  storage "f16":
+    binary16 samples in the permuted buffer.
     """
     import torch
     import volumetric_delay_sum_amd as das
 
-    plan = das.plan_from_fields(inp.fields, algorithm=algorithm, layout=layout)
+    plan = das.plan_from_fields(inp.fields, algorithm=algorithm, layout=layout, storage=storage)
     if out is None:
         out = torch.full(plan.output_shape(), float("nan"), dtype=torch.float32, device=inp.rf_d.device)
     Q = inp.cfg.Q
@@ -74,7 +75,8 @@ def run_gpu(inp: Inputs, algorithm: str, layout: str = "kqmb", q_chunk: int | No
     if plan.batch_inner:
         qc = min(Q if q_chunk is None else q_chunk, plan.max_q_chunk())
         assert qc >= 1
-        perm = torch.empty(plan.permuted_shape(qc), dtype=torch.float32, device=inp.rf_d.device)
+        perm = torch.empty(plan.permuted_shape(qc), dtype=torch.float16 if plan.store_f16 else torch.float32,
+                           device=inp.rf_d.device)
         for q0 in range(0, Q, qc):
             n = min(qc, Q - q0)
             view = perm.view(-1)[: perm.numel() // qc * n]
@@ -94,9 +96,11 @@ def to_numpy(out, iq: bool) -> np.ndarray:
     return y[..., 0] + 1j * y[..., 1] if iq else y
 
 
-def oracle_ref(inp: Inputs, voxels=None, frames=None):
+def oracle_ref(inp: Inputs, voxels=None, frames=None, storage: str = "native"):
+    """The oracle on the same inputs; storage "f16": of the samples rounded to binary16."""
     import oracle
-    return oracle.das_sum(inp.fields, inp.rf_host, inp.rx, inp.tau, inp.w, voxels=voxels, frames=frames)
+    rf = oracle.to_binary16(inp.rf_host) if storage == "f16" else inp.rf_host
+    return oracle.das_sum(inp.fields, rf, inp.rx, inp.tau, inp.w, voxels=voxels, frames=frames)
 
 
 def sample_voxels(cfg: das_synth.Config, count: int, seed: int = 0) -> np.ndarray:

@@ -354,3 +354,54 @@ def test_split_rows_can_be_switched_off(B, dtype, monkeypatch):
     pl = das.Plan(**_problem(**kw))
     assert pl.info["staged"] == 1
     assert pl.info["frames_per_lane"] == (2 if dtype == "f32" else 1)
+
+
+# ---- binary16 storage of the permuted buffer -------------------------------
+
+def test_storage_enum_is_validated():
+    assert _status(storage=2) == INVALID
+    assert _status(storage=-1) == INVALID
+    assert _status(storage="native") == OK and _status(storage="f16") == OK
+
+
+def test_binary16_storage_needs_batch_inner():
+    assert _status(storage="f16", algorithm="baseline") == UNSUPPORTED
+    assert _status(storage="f16", algorithm="default") == UNSUPPORTED
+    assert _status(storage="f16", algorithm="auto", B=8) == UNSUPPORTED        # auto resolves to the baseline
+    assert _status(storage="f16", algorithm="auto", B=32) == OK
+    assert _status(storage="f16", dtype="f64", algorithm="baseline") == UNSUPPORTED
+    assert _status(storage="f16", dtype="c128", f_demod=5e6, algorithm="baseline") == UNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype,B,store,fl,staged", [
+    ("f32", 32, 2, 2, 1), ("f32", 64, 2, 2, 1), ("f32", 96, 2, 2, 1), ("f32", 16, 2, 2, 0),
+    ("f32", 24, 2, 2, 0), ("f32", 68, 2, 4, 0), ("f32", 7, 2, 1, 0), ("c64", 32, 4, 2, 1),
+    ("c64", 64, 4, 2, 1), ("c64", 16, 4, 1, 0), ("c64", 34, 4, 2, 0)])
+def test_binary16_plan_info(dtype, B, store, fl, staged):
+    iq = dtype == "c64"
+    pl = das.Plan(**_problem(B=B, dtype=dtype, f_demod=5e6 if iq else 0.0, storage="f16"))
+    assert pl.store_f16
+    assert pl.info["elem_bytes"] == (8 if iq else 4)
+    assert pl.info["store_bytes"] == store
+    assert pl.info["frames_per_lane"] == fl
+    assert pl.info["staged"] == staged
+    native = das.Plan(**_problem(B=B, dtype=dtype, f_demod=5e6 if iq else 0.0))
+    assert native.info["store_bytes"] == native.info["elem_bytes"]
+    assert pl.permuted_bytes(1) * 2 == native.permuted_bytes(1)
+    assert pl.permuted_shape(2) == native.permuted_shape(2)
+
+
+def test_binary16_direct_frames_per_lane(monkeypatch):
+    monkeypatch.setenv("DAS_BI_KERNEL", "direct")
+    pl = das.Plan(**_problem(B=32, storage="f16"))
+    assert pl.info["staged"] == 0 and pl.info["frames_per_lane"] == 2
+    assert das.Plan(**_problem(B=64, storage="f16")).info["frames_per_lane"] == 4
+
+
+def test_binary16_kqmb_chunk_limit_counts_half_bytes():
+    # a KQMB chunk must stay below 4 GiB: with 2-byte samples twice the events fit
+    kw = dict(B=64, Q=64, M=1024, K=4096)
+    native = das.Plan(**_problem(**kw))
+    half = das.Plan(**_problem(storage="f16", **kw))
+    assert native.max_q_chunk() == 3
+    assert half.max_q_chunk() == 7

@@ -19,19 +19,21 @@ from typing import Optional, Sequence
 
 __all__ = [
     "F32", "C64", "F64", "C128", "ALG_DEFAULT", "ALG_BASELINE", "ALG_BATCH_INNER", "ALG_AUTO",
-    "LAYOUT_KQMB", "LAYOUT_QMKB",
+    "LAYOUT_KQMB", "LAYOUT_QMKB", "STORE_NATIVE", "STORE_F16",
     "TX_PLANE", "TX_DIVERGING", "DasError", "Plan", "load_library", "library_path", "plan_from_fields",
 ]
 
 F32, C64, F64, C128 = 0, 1, 2, 3
 ALG_DEFAULT, ALG_BASELINE, ALG_BATCH_INNER, ALG_AUTO = 0, 1, 2, 3
 LAYOUT_KQMB, LAYOUT_QMKB = 0, 1
+STORE_NATIVE, STORE_F16 = 0, 1
 TX_PLANE, TX_DIVERGING = 0, 1
 
 _ALG = {"default": ALG_DEFAULT, "baseline": ALG_BASELINE, "batch_inner": ALG_BATCH_INNER,
         "bl": ALG_BASELINE, "bi": ALG_BATCH_INNER, "auto": ALG_AUTO}
 _LAYOUT = {"kqmb": LAYOUT_KQMB, "qmkb": LAYOUT_QMKB}
 _DTYPE = {"f32": F32, "c64": C64, "f64": F64, "c128": C128}
+_STORAGE = {"native": STORE_NATIVE, "f16": STORE_F16}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdas.so")
@@ -49,6 +51,7 @@ class _Problem(ctypes.Structure):
         ("B", ctypes.c_int32), ("Q", ctypes.c_int32), ("M", ctypes.c_int32), ("K", ctypes.c_int32),
         ("nx", ctypes.c_int32), ("ny", ctypes.c_int32), ("nz", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("algorithm", ctypes.c_int32), ("layout", ctypes.c_int32),
+        ("storage", ctypes.c_int32),
         ("origin", ctypes.c_double * 3), ("spacing", ctypes.c_double * 3),
         ("fs", ctypes.c_double), ("c", ctypes.c_double), ("t0", ctypes.c_double),
         ("f_number", ctypes.c_double), ("f_demod", ctypes.c_double),
@@ -60,6 +63,7 @@ class _PlanInfo(ctypes.Structure):
         ("algorithm", ctypes.c_int32), ("layout", ctypes.c_int32), ("elem_bytes", ctypes.c_int32),
         ("frames_per_lane", ctypes.c_int32), ("lanes_per_voxel", ctypes.c_int32),
         ("voxels_per_group", ctypes.c_int32), ("N", ctypes.c_int64), ("staged", ctypes.c_int32),
+        ("store_bytes", ctypes.c_int32),
     ]
 
 
@@ -132,7 +136,8 @@ class Plan:
     def __init__(self, *, B: int, Q: int, M: int, K: int, nx: int, ny: int, nz: int,
                  origin: Sequence[float], spacing: Sequence[float], fs: float, c: float,
                  t0: float = 0.0, f_number: float = 1.0, f_demod: float = 0.0,
-                 dtype: str = "f32", algorithm: str = "batch_inner", layout: str = "kqmb"):
+                 dtype: str = "f32", algorithm: str = "batch_inner", layout: str = "kqmb",
+                 storage: str = "native"):
         lib = load_library()
         p = _Problem()
         p.B, p.Q, p.M, p.K = int(B), int(Q), int(M), int(K)
@@ -140,6 +145,7 @@ class Plan:
         p.dtype = _DTYPE[dtype] if isinstance(dtype, str) else int(dtype)
         p.algorithm = _ALG[algorithm] if isinstance(algorithm, str) else int(algorithm)
         p.layout = _LAYOUT[layout] if isinstance(layout, str) else int(layout)
+        p.storage = _STORAGE[storage] if isinstance(storage, str) else int(storage)
         p.origin[:] = [float(v) for v in origin]
         p.spacing[:] = [float(v) for v in spacing]
         p.fs, p.c, p.t0 = float(fs), float(c), float(t0)
@@ -168,6 +174,11 @@ class Plan:
         return self.problem.dtype in (F64, C128)
 
     @property
+    def store_f16(self) -> bool:
+        """The permuted buffer holds binary16 samples (torch.float16 tensors)."""
+        return self.problem.storage == STORE_F16
+
+    @property
     def batch_inner(self) -> bool:
         return self.info["algorithm"] == ALG_BATCH_INNER
 
@@ -188,14 +199,18 @@ class Plan:
         return (self.problem.B, self.N) + ((2,) if self.iq else ())
 
     # -- argument checks (sizes are unknown to the C ABI) --------------------
-    def _tensor(self, t, numel: int, name: str, samples: bool = False):
-        """samples: RF or output, float64 for F64 / C128 plans; everything else float32."""
+    def _tensor(self, t, numel: int, name: str, samples: bool = False, permuted: bool = False):
+        """samples: RF or output, float64 for F64 / C128 plans; permuted: a permuted
+        buffer, float16 for STORE_F16 plans; everything else float32."""
         import torch
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise TypeError(f"{name} must be a CUDA tensor")
-        if t.dtype in (torch.complex64, torch.complex128):
+        if t.dtype in (torch.complex64, torch.complex128, torch.complex32):
             t = torch.view_as_real(t)
-        want = torch.float64 if (samples and self.wide) else torch.float32
+        if permuted and self.store_f16:
+            want = torch.float16
+        else:
+            want = torch.float64 if (samples and self.wide) else torch.float32
         if t.dtype != want:
             raise TypeError(f"{name} must be {want} (or its complex type for IQ), got {t.dtype}")
         if not t.is_contiguous():
@@ -215,7 +230,7 @@ class Plan:
         q_begin, q_count = self._q_range(q_begin, q_count)
         c = 2 if self.iq else 1
         rf = self._tensor(rf, p.B * p.Q * p.M * p.K * c, "rf", samples=True)
-        out = self._tensor(out, p.K * max(q_count, 0) * p.M * p.B * c, "out", samples=True)
+        out = self._tensor(out, p.K * max(q_count, 0) * p.M * p.B * c, "out", samples=True, permuted=True)
         _check(self._lib.das_permute(self._h, rf.data_ptr(), out.data_ptr(), q_begin, q_count,
                                      _stream_handle(stream, rf.device)), "das_permute")
         return out
@@ -227,7 +242,7 @@ class Plan:
         q_begin, q_count = self._q_range(q_begin, q_count)
         c = 2 if self.iq else 1
         rf_numel = (p.K * max(q_count, 0) * p.M * p.B if self.batch_inner else p.B * p.Q * p.M * p.K) * c
-        rf = self._tensor(rf, rf_numel, "rf", samples=True)
+        rf = self._tensor(rf, rf_numel, "rf", samples=True, permuted=self.batch_inner)
         rx_pos = self._tensor(rx_pos, 3 * p.M, "rx_pos")
         tau_tx = self._tensor(tau_tx, p.Q * self.N, "tau_tx")
         w_tx = self._tensor(w_tx, p.Q * self.N, "w_tx")
@@ -251,8 +266,8 @@ class Plan:
         w_tx = self._tensor(w_tx, p.Q * self.N, "w_tx")
         out = self._tensor(out, p.B * self.N * c, "out", samples=True)
         chunk = p.K * max(q_chunk, 0) * p.M * p.B * c
-        perm_a = self._tensor(perm_a, chunk, "perm_a", samples=True)
-        perm_b = self._tensor(perm_b, chunk, "perm_b", samples=True)
+        perm_a = self._tensor(perm_a, chunk, "perm_a", samples=True, permuted=True)
+        perm_b = self._tensor(perm_b, chunk, "perm_b", samples=True, permuted=True)
         _check(self._lib.das_beamform_streamed(self._h, rf.data_ptr(), rx_pos.data_ptr(), tau_tx.data_ptr(),
                                                w_tx.data_ptr(), out.data_ptr(), perm_a.data_ptr(),
                                                perm_b.data_ptr(), q_chunk, 1 if accumulate else 0,
@@ -294,13 +309,14 @@ class Plan:
 
 
 def plan_from_fields(fields: dict, algorithm: str = "batch_inner", layout: str = "kqmb",
-                     wide: bool = False) -> Plan:
+                     wide: bool = False, storage: str = "native") -> Plan:
     """Plan from a plain description (B, Q, M, K, nx, ny, nz, origin, spacing, fs, c, t0,
-    f_number, f_demod, iq); wide: float64 samples (F64 / C128)."""
+    f_number, f_demod, iq); wide: float64 samples (F64 / C128); storage: "native" or
+    "f16" (binary16 samples in the permuted buffer)."""
     iq = bool(fields.get("iq"))
     dtype = ("c128" if iq else "f64") if wide else ("c64" if iq else "f32")
     return Plan(B=fields["B"], Q=fields["Q"], M=fields["M"], K=fields["K"], nx=fields["nx"],
                 ny=fields["ny"], nz=fields["nz"], origin=fields["origin"], spacing=fields["spacing"],
                 fs=fields["fs"], c=fields["c"], t0=fields.get("t0", 0.0),
                 f_number=fields.get("f_number", 1.0), f_demod=fields.get("f_demod", 0.0),
-                dtype=dtype, algorithm=algorithm, layout=layout)
+                dtype=dtype, algorithm=algorithm, layout=layout, storage=storage)

@@ -47,8 +47,12 @@ das_status check_device() {
 // Frames per lane of the batch-inner kernel.  fp32: 4 adjacent frames (one
 // 128-bit load) when B is a multiple of 4 and at least 64; 2 frames 16 apart
 // (two dword loads) when B is a multiple of 32; else 1.  IQ: 2 adjacent
-// complex frames (128-bit) when B is even and at least 32; else 1.
-int32_t pick_fl(int32_t B, int32_t dtype) {
+// complex frames (128-bit) when B is even and at least 32; else 1.  binary16
+// storage: adjacent frames, 4 (B a multiple of 4, at least 64) or 2 (B even)
+// real ones, complex as above.
+int32_t pick_fl(int32_t B, int32_t dtype, bool h16) {
+    if (h16)        // binary16: frames adjacent, a lane loads at least 4 bytes (2 halves) per tap where B allows
+        return (dtype == DAS_C64) ? ((B % 2 == 0 && B >= 32) ? 2 : 1) : ((B % 4 == 0 && B >= 64) ? 4 : (B % 2 == 0 ? 2 : 1));
     if (dtype == DAS_C64)
         return (B % 2 == 0 && B >= 32) ? 2 : 1;
     if (B % 4 == 0 && B >= 64)
@@ -207,7 +211,7 @@ bool valid_plan(const das_plan_t *plan) { return plan != nullptr; }
 // the first row of a 16-receiver block.
 bool kqmb_chunk_fits(const das_plan_t *plan, int64_t q_count) {
     const das_problem &p = plan->p;
-    const uint64_t row = (uint64_t)p.B * plan->elem_bytes;
+    const uint64_t row = (uint64_t)p.B * plan->store_bytes;
     const uint64_t chunk = (uint64_t)p.K * q_count * p.M * row;
     return chunk + 16ull * row <= (uint64_t)UINT32_MAX;
 }
@@ -266,6 +270,8 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
         return DAS_ERR_INVALID_ARGUMENT;
     if (p.layout != DAS_LAYOUT_KQMB && p.layout != DAS_LAYOUT_QMKB)
         return DAS_ERR_INVALID_ARGUMENT;
+    if (p.storage != DAS_STORE_NATIVE && p.storage != DAS_STORE_F16)
+        return DAS_ERR_INVALID_ARGUMENT;
     for (int i = 0; i < 3; ++i)
         if (!is_finite(p.origin[i]) || !is_finite(p.spacing[i]))
             return DAS_ERR_INVALID_ARGUMENT;
@@ -279,6 +285,10 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
     if (cplx && !(p.f_demod > 0.0))
         return DAS_ERR_UNSUPPORTED;
     if (wide && p.algorithm == DAS_ALG_BATCH_INNER)
+        return DAS_ERR_UNSUPPORTED;
+    // binary16 storage is made by the permute, so only batch-inner plans have it
+    const bool h16 = p.storage == DAS_STORE_F16;
+    if (h16 && (wide || resolve_algorithm(p) != DAS_ALG_BATCH_INNER))
         return DAS_ERR_UNSUPPORTED;
     const int64_t N = (int64_t)p.nx * p.ny * p.nz;
     const int32_t elem = (cplx ? 2 : 1) * (wide ? 8 : 4);
@@ -298,7 +308,9 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
     pl->N = N;
     pl->alg = resolve_algorithm(p);
     pl->elem_bytes = elem;
-    pl->fl = pick_fl(p.B, p.dtype);
+    pl->h16 = h16 ? 1 : 0;
+    pl->store_bytes = h16 ? elem / 2 : elem;
+    pl->fl = pick_fl(p.B, p.dtype, h16);
     pl->bt = 8;
     // LDS-staged batch-inner kernel where it is built (fp32 with B a multiple
     // of 32, two frames per lane, or of 16, one frame per lane; complex64 with
@@ -308,11 +320,16 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
     // DAS_BI_KERNEL=direct selects the direct-load kernel (comparisons).
     const char *kv = std::getenv("DAS_BI_KERNEL");
     const bool want_staged = pl->alg == DAS_ALG_BATCH_INNER && !(kv && std::strcmp(kv, "direct") == 0);
-    if (want_staged && p.dtype == DAS_F32 && p.B % 32 == 0)
+    if (h16) {
+        // binary16 rows: 2 fp32 frames (4 bytes) per lane for B a multiple of
+        // 32, 2 complex frames (8 bytes) for B a multiple of 32
+        if (want_staged && p.B % 32 == 0)
+            pl->fl = 2;
+    } else if (want_staged && p.dtype == DAS_F32 && p.B % 32 == 0)
         pl->fl = 2;
     else if (want_staged && p.dtype == DAS_F32 && p.B % 16 == 0)
         pl->fl = 1;
-    if (want_staged && p.dtype == DAS_C64 && p.B % 16 == 0)
+    if (!h16 && want_staged && p.dtype == DAS_C64 && p.B % 16 == 0)
         pl->fl = 1;
     pl->split = 1;
     if (!fit_apodization(pl)) {
@@ -320,13 +337,13 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
         return DAS_ERR_UNSUPPORTED;
     }
     pl->staged = (want_staged && das_staged_supported(*pl)) ? 1 : 0;
-    pl->q_group = pick_q_group(p, elem, pl->staged != 0);
+    pl->q_group = pick_q_group(p, pl->store_bytes, pl->staged != 0);
     const char *vv = std::getenv("DAS_STAGED_VPR");
-    pl->vpr = (vv && std::atoi(vv) == 1) ? 1 : 2;
+    pl->vpr = (!h16 && vv && std::atoi(vv) == 1) ? 1 : 2;
     // split rows where B allows (DAS_STAGED_SPLIT=1 keeps whole rows: comparisons)
     const char *sv = std::getenv("DAS_STAGED_SPLIT");
-    if (pl->staged && pl->vpr == 2 && pl->fl * (p.dtype == DAS_C64 ? 2 : 1) == 2 && p.B % (2 * 16 * pl->fl) == 0 &&
-        !(sv && std::atoi(sv) == 1)) {
+    if (pl->staged && !h16 && pl->vpr == 2 && pl->fl * (p.dtype == DAS_C64 ? 2 : 1) == 2 &&
+        p.B % (2 * 16 * pl->fl) == 0 && !(sv && std::atoi(sv) == 1)) {
         pl->split = 2;
         pl->fl *= 2;
     }
@@ -348,6 +365,7 @@ das_status das_plan_get_info(const das_plan_t *plan, das_plan_info *info) {
     info->voxels_per_group = bi ? 16 : 256;
     info->N = plan->N;
     info->staged = plan->staged;
+    info->store_bytes = plan->store_bytes;
     return DAS_OK;
 }
 
@@ -357,7 +375,7 @@ size_t das_permuted_bytes(const das_plan_t *plan, int32_t q_count) {
     if (!valid_plan(plan) || q_count < 1 || q_count > plan->p.Q)
         return 0;
     const das_problem &p = plan->p;
-    return (size_t)p.K * (size_t)q_count * (size_t)p.M * (size_t)p.B * (size_t)plan->elem_bytes;
+    return (size_t)p.K * (size_t)q_count * (size_t)p.M * (size_t)p.B * (size_t)plan->store_bytes;
 }
 
 das_status das_permute(const das_plan_t *plan, const void *rf_bqmk, void *rf_perm, int32_t q_begin,
@@ -403,7 +421,7 @@ das_status das_beamform(const das_plan_t *plan, const void *rf, const float *rx_
         // the staged kernel addresses a KQMB chunk and the transmit tables with
         // 32-bit offsets (a QMKB chunk is rebased per step); larger ones go to
         // the direct kernel
-        const int64_t chunk = (int64_t)plan->p.B * plan->elem_bytes * plan->p.M * q_count * plan->p.K;
+        const int64_t chunk = (int64_t)plan->p.B * plan->store_bytes * plan->p.M * q_count * plan->p.K;
         const int64_t tables = (int64_t)plan->p.Q * plan->N * 4;
         const bool chunk_ok = plan->p.layout == DAS_LAYOUT_QMKB || chunk < ((int64_t)1 << 32);
         const bool staged = plan->staged && chunk_ok && tables < ((int64_t)1 << 32);

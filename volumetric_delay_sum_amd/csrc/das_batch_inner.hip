@@ -52,29 +52,62 @@ __device__ __forceinline__ FVec<NF> buf_load(das::BufRsrc r, uint32_t off) {
     return x;
 }
 
+// NF consecutive binary16 samples at byte offset off (+ IMM) of r, widened to float32.
+template <int NF, int IMM>
+__device__ __forceinline__ FVec<NF> buf_load_h(das::BufRsrc r, uint32_t off) {
+    FVec<NF> x;
+    if constexpr (NF == 1) {
+        x.v[0] = (float)das::buffer_load_f16(r, (int)(off + IMM), 0, 0);
+    } else {
+        constexpr int ND = NF / 2;               // dwords
+        uint32_t d[ND];
+        if constexpr (ND == 1) {
+            d[0] = __builtin_bit_cast(uint32_t, das::buffer_load_f32(r, (int)(off + IMM), 0, 0));
+        } else if constexpr (ND == 2) {
+            const das::f32x2 t = das::buffer_load_f32x2(r, (int)(off + IMM), 0, 0);
+            const float t0 = t.x, t1 = t.y;
+            d[0] = __builtin_bit_cast(uint32_t, t0);
+            d[1] = __builtin_bit_cast(uint32_t, t1);
+        } else {
+            static_assert(ND == 4, "up to 8 halves per lane");
+            const das::f32x4 t = das::buffer_load_f32x4(r, (int)(off + IMM), 0, 0);
+            const float t0 = t.x, t1 = t.y, t2 = t.z, t3 = t.w;
+            d[0] = __builtin_bit_cast(uint32_t, t0);
+            d[1] = __builtin_bit_cast(uint32_t, t1);
+            d[2] = __builtin_bit_cast(uint32_t, t2);
+            d[3] = __builtin_bit_cast(uint32_t, t3);
+        }
+#pragma unroll
+        for (int i = 0; i < ND; ++i) das::widen2(d[i], x.v[2 * i], x.v[2 * i + 1]);
+    }
+    return x;
+}
+
 // Frames of one lane: FL frames starting at a per-lane base.  VEC: the FL
 // frames are adjacent (one FL-wide vector load per tap).  Otherwise they are
 // 16 frames apart (lane li owns frames li, li + 16, ...), so that each load is
 // a plain dword and the 16 lanes of a row read 64 contiguous bytes: on gfx950
 // a 64-bit vector load costs as many address cycles as a 128-bit one, so
-// 2-frame vectors would halve the rate at which rows are delivered.
-template <bool IQ, int FL>
+// 2-frame vectors would halve the rate at which rows are delivered.  Binary16
+// rows (H) always take adjacent frames.
+template <bool IQ, int FL, bool H>
 struct FrameMap {
-    static constexpr bool VEC = IQ || FL != 2;
+    static constexpr bool VEC = IQ || FL != 2 || H;
     static constexpr int TILE = ROW * FL;                 // frames per row pass
     __device__ static int frame(int li, int f) { return VEC ? li * FL + f : li + ROW * f; }
 };
 
-template <bool IQ, int FL, int LAYOUT>
+// H: the permuted rows hold binary16 samples (widened on load).
+template <bool IQ, int FL, int LAYOUT, bool H>
 __global__ __launch_bounds__(THREADS) void das_batch_inner_kernel(DasKParams P, const float *__restrict__ rfp,
                                                                   const float *__restrict__ rx,
                                                                   const float *__restrict__ tau_tx,
                                                                   const float *__restrict__ w_tx,
                                                                   float *__restrict__ out,
                                                                   uint32_t tap_stride) {
-    using FM = FrameMap<IQ, FL>;
+    using FM = FrameMap<IQ, FL, H>;
     constexpr int C = IQ ? 2 : 1;          // floats per sample
-    constexpr int E = 4 * C;               // bytes per sample
+    constexpr int E = (H ? 2 : 4) * C;     // bytes per stored sample
     constexpr int NF = FL * C;             // floats per lane per tap
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int vrow = lane >> 4, li = lane & (ROW - 1);
@@ -161,7 +194,10 @@ __global__ __launch_bounds__(THREADS) void das_batch_inner_kernel(DasKParams P, 
                     constexpr int j = decltype(J)::value;
                     const uint32_t off = das::row_bcast<j>(koff) + jo[j];
                     FVec<NF> x0, x1;
-                    if constexpr (FM::VEC) {
+                    if constexpr (H) {
+                        x0 = buf_load_h<NF, 0>(r0, off);
+                        x1 = buf_load_h<NF, 0>(r1, off);
+                    } else if constexpr (FM::VEC) {
                         x0 = buf_load<NF, 0>(r0, off);
                         x1 = buf_load<NF, 0>(r1, off);
                     } else {
@@ -197,40 +233,47 @@ __global__ __launch_bounds__(THREADS) void das_batch_inner_kernel(DasKParams P, 
     }
 }
 
-template <bool IQ, int FL, int LAYOUT>
+template <bool IQ, int FL, int LAYOUT, bool H>
 hipError_t launch(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
                   const float *tau, const float *w, float *out, hipStream_t stream) {
-    const int64_t row_bytes = (int64_t)kp.B * plan.elem_bytes;
+    const int64_t row_bytes = (int64_t)kp.B * plan.store_bytes;
     const int64_t tap = (LAYOUT == DAS_LAYOUT_KQMB) ? row_bytes * kp.q_count * kp.M : row_bytes;
     const int tiles = ((kp.nx + PX - 1) / PX) * ((kp.ny + PY - 1) / PY) * kp.nz;
-    const int ftiles = (kp.B + FrameMap<IQ, FL>::TILE - 1) / FrameMap<IQ, FL>::TILE;
-    hipLaunchKernelGGL((das_batch_inner_kernel<IQ, FL, LAYOUT>), dim3(tiles, ftiles), dim3(THREADS), 0,
+    const int ftiles = (kp.B + FrameMap<IQ, FL, H>::TILE - 1) / FrameMap<IQ, FL, H>::TILE;
+    hipLaunchKernelGGL((das_batch_inner_kernel<IQ, FL, LAYOUT, H>), dim3(tiles, ftiles), dim3(THREADS), 0,
                        stream, kp, rf, rx, tau, w, out, (uint32_t)tap);
     return hipGetLastError();
 }
 
-template <bool IQ, int LAYOUT>
+template <bool IQ, int LAYOUT, bool H>
 hipError_t launch_fl(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
                      const float *tau, const float *w, float *out, hipStream_t stream) {
     switch (plan.fl) {
     case 4:
-        return launch<IQ, 4, LAYOUT>(plan, kp, rf, rx, tau, w, out, stream);
+        return launch<IQ, 4, LAYOUT, H>(plan, kp, rf, rx, tau, w, out, stream);
     case 2:
-        return launch<IQ, 2, LAYOUT>(plan, kp, rf, rx, tau, w, out, stream);
+        return launch<IQ, 2, LAYOUT, H>(plan, kp, rf, rx, tau, w, out, stream);
     default:
-        return launch<IQ, 1, LAYOUT>(plan, kp, rf, rx, tau, w, out, stream);
+        return launch<IQ, 1, LAYOUT, H>(plan, kp, rf, rx, tau, w, out, stream);
     }
+}
+
+template <bool H>
+hipError_t launch_dtype(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
+                        const float *tau_tx, const float *w_tx, float *out, hipStream_t stream) {
+    const bool iq = plan.p.dtype == DAS_C64;
+    const bool kqmb = plan.p.layout == DAS_LAYOUT_KQMB;
+    if (iq)
+        return kqmb ? launch_fl<true, DAS_LAYOUT_KQMB, H>(plan, kp, rf, rx, tau_tx, w_tx, out, stream)
+                    : launch_fl<true, DAS_LAYOUT_QMKB, H>(plan, kp, rf, rx, tau_tx, w_tx, out, stream);
+    return kqmb ? launch_fl<false, DAS_LAYOUT_KQMB, H>(plan, kp, rf, rx, tau_tx, w_tx, out, stream)
+                : launch_fl<false, DAS_LAYOUT_QMKB, H>(plan, kp, rf, rx, tau_tx, w_tx, out, stream);
 }
 
 }  // namespace
 
 hipError_t das_launch_batch_inner(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
                                   const float *tau_tx, const float *w_tx, float *out, hipStream_t stream) {
-    const bool iq = plan.p.dtype == DAS_C64;
-    const bool kqmb = plan.p.layout == DAS_LAYOUT_KQMB;
-    if (iq)
-        return kqmb ? launch_fl<true, DAS_LAYOUT_KQMB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream)
-                    : launch_fl<true, DAS_LAYOUT_QMKB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream);
-    return kqmb ? launch_fl<false, DAS_LAYOUT_KQMB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream)
-                : launch_fl<false, DAS_LAYOUT_QMKB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream);
+    return plan.h16 ? launch_dtype<true>(plan, kp, rf, rx, tau_tx, w_tx, out, stream)
+                    : launch_dtype<false>(plan, kp, rf, rx, tau_tx, w_tx, out, stream);
 }

@@ -41,6 +41,8 @@
 // zero coefficients.
 #include "das_device.h"
 
+#include <type_traits>
+
 namespace {
 
 constexpr int THREADS = 1024;
@@ -56,18 +58,20 @@ constexpr int LDS_TOTAL = 163840;          // LDS of one workgroup on gfx950 (16
 // window) serves 64 fp32 or 32 complex frames.  Each tap is then one 16-byte
 // LDS read per lane, which gfx950 serves at nearly twice the bytes per clock
 // of 8-byte reads.
-template <bool IQ, int FL, int S, int VPR>
+// H: the rows hold binary16 samples, widened to float32 in the compute loop.
+template <bool IQ, int FL, int S, int VPR, bool H>
 struct Geo {
     static constexpr int C = IQ ? 2 : 1;                 // floats per sample
-    static constexpr int E = 4 * C;                      // bytes per sample
+    static constexpr int E = (H ? 2 : 4) * C;            // bytes per stored sample
     static constexpr int NF = FL * C;                    // floats per lane per tap
-    static constexpr int LANEB = NF * 4;                 // bytes per lane in a sample row
+    static constexpr int LANEB = FL * E;                 // bytes per lane in a sample row
     static constexpr int ROWB = ROW * LANEB;             // bytes of the frame tile in one sample row
     static constexpr int NRX = ROW / S;                  // receivers per step
     static constexpr int NITEM = VPR * NRX;              // (voxel, receiver) items of a DPP row per step
-    // Weights of an item come from a table in LDS for 16-byte lanes (8 or 16
-    // FMAs per item), through DPP otherwise (see the compute loop)
-    static constexpr bool WTAB = LANEB == 16;
+    // Weights of an item come from a table in LDS for 8 or 16 FMAs per item
+    // (16-byte lanes) and for binary16 rows, through DPP otherwise (see the
+    // compute loop)
+    static constexpr bool WTAB = NF >= 4 || H;
     static constexpr int CW = IQ ? 4 : 2;                // floats of an item's weights (a, b; IQ: a, ai, b, bi)
     // weight table: [DPP row][item][CW], each row's part padded by 16 bytes so
     // that the four rows of a wave, which read one record each per item, fall
@@ -152,20 +156,59 @@ template <int NF>
 struct Tap {
     using type = float __attribute__((ext_vector_type(NF)));
 };
+// a lane's binary16 tap as loaded: ND dwords of two halves each
+template <int ND>
+struct RawTap {
+    using type = uint32_t __attribute__((ext_vector_type(ND)));
+};
+template <>
+struct RawTap<1> {
+    using type = uint32_t;
+};
 
-template <bool IQ, int FL, int LAYOUT, int VPR, int S>
+// Dword I of a binary16 tap (one dword: the tap itself).
+template <int I, typename TV>
+__device__ __forceinline__ uint32_t das_dword(const TV &x) {
+    if constexpr (sizeof(TV) == 4)
+        return x;
+    else
+        return x[I];
+}
+
+// Tap as float32 values y[NF]: a float32 tap as it is, a binary16 one widened.
+// The compiler folds each widening into the FMA that uses it (v_fma_mix_f32).
+// That issues one per cycle where a plain FMA issues two, but measured faster
+// on complex data than separate conversions feeding plain FMAs (33.1 against
+// 29.2 ms on the Main complex workload), which need more registers.
+template <bool H, int NF, typename TV>
+__device__ __forceinline__ void widen_tap(const TV &x, float (&y)[NF]) {
+    if constexpr (!H) {
+#pragma unroll
+        for (int i = 0; i < NF; ++i) y[i] = x[i];
+    } else if constexpr (NF == 2) {
+        das::widen2(x, y[0], y[1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < NF / 2; ++i) {
+            const uint32_t d = x[i];
+            das::widen2(d, y[2 * i], y[2 * i + 1]);
+        }
+    }
+}
+
+template <bool IQ, int FL, int LAYOUT, int VPR, int S, bool H>
 __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, const float *__restrict__ rfp,
                                                                 const float *__restrict__ rx,
                                                                 const float *__restrict__ tau_tx,
                                                                 const float *__restrict__ w_tx,
                                                                 float *__restrict__ out, uint32_t tap_stride) {
-    using G = Geo<IQ, FL, S, VPR>;
+    using G = Geo<IQ, FL, S, VPR, H>;
     constexpr int C = G::C, E = G::E, NF = G::NF, NRX = G::NRX;
     // (voxel, receiver) pairs per lane: pair p is voxel p S + li / NRX of the
     // row and receiver m0 + li % NRX
     constexpr int PL = VPR / S;
     static_assert(VPR % S == 0, "each lane half needs a voxel");
-    using TapV = typename Tap<NF>::type;
+    using TapV = typename std::conditional<H, typename RawTap<G::LANEB / 4>::type, typename Tap<NF>::type>::type;
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
     int *slots = reinterpret_cast<int *>(lds + 2 * G::BUF);   // [3 sets][min, max][NRX]
     constexpr uint32_t COEF_AT = 2 * G::BUF + G::SLOTS;       // weight table
@@ -398,7 +441,9 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     // table in LDS, one read that the row's 16 lanes share, and the FMAs are
     // plain; with 8- or 4-byte lanes that read would add half again to the
     // LDS bytes per item, which then binds, so the FMAs take the weights from
-    // lane (v % S) NRX + j through DPP.
+    // lane (v % S) NRX + j through DPP.  Binary16 rows take the table too:
+    // their FMAs read the halves directly (v_fma_mix_f32), which has no DPP
+    // form, and their taps carry half the bytes, which leaves the LDS room.
     // The reads are issued DEPTH items ahead; the scheduling fences keep the
     // compiler from sinking each read next to its use, which would leave one
     // read in flight per wave (three ahead measured best with two voxels per
@@ -466,10 +511,13 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     };
     // Interpolate-weight-accumulate of item tt from its two taps and weights
     // (from the table, c, or by DPP from the source lane's step state, s).
-    auto item_fma = [&](auto T, Step (&s)[PL], float (&pt)[VPR][NF], const TapV &x0, const TapV &x1,
+    auto item_fma = [&](auto T, Step (&s)[PL], float (&pt)[VPR][NF], const TapV &t0, const TapV &t1,
                         const CoefV &c) {
         constexpr int tt = decltype(T)::value;
         constexpr int v = tt / NRX, j = tt % NRX, src = (v % S) * NRX + j, pr = v / S;
+        float x0[NF], x1[NF];
+        widen_tap<H, NF>(t0, x0);
+        widen_tap<H, NF>(t1, x1);
         if constexpr (!WTAB) {
             if constexpr (IQ) {
 #pragma unroll
@@ -496,6 +544,16 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
                 re = __builtin_fmaf(-c[3], x1[2 * f + 1], re);
                 im = __builtin_fmaf(c[3], x1[2 * f], im);
             }
+        } else if constexpr (H) {
+            // binary16 frames straight from the tap dwords (frame f in half f % 2 of dword f / 2)
+            das::unroll<FL>([&](auto F) {
+                constexpr int f = decltype(F)::value;
+                das::fma_half<f % 2>(pt[v][f], c[0], das_dword<f / 2>(t0));
+            });
+            das::unroll<FL>([&](auto F) {
+                constexpr int f = decltype(F)::value;
+                das::fma_half<f % 2>(pt[v][f], c[1], das_dword<f / 2>(t1));
+            });
         } else {
 #pragma unroll
             for (int f = 0; f < FL; ++f) pt[v][f] = __builtin_fmaf(c[0], x0[f], pt[v][f]);
@@ -561,11 +619,21 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             const uint32_t jo = laneoff_g + (uint32_t)min(j, jmax) * m_stride;
             const uint32_t off = das::row_bcast<src>(koff) + jo;
             float x0[NF], x1[NF];
+            if constexpr (H) {
 #pragma unroll
-            for (int i = 0; i < NF; ++i) {
-                const int o = (int)(off + 4 * i);
-                x0[i] = das::buffer_load_f32(r0, o, 0, 0);
-                x1[i] = das::buffer_load_f32(r1, o, 0, 0);
+                for (int i = 0; i < NF / 2; ++i) {
+                    const int o = (int)(off + 4 * i);
+                    const float d0 = das::buffer_load_f32(r0, o, 0, 0), d1 = das::buffer_load_f32(r1, o, 0, 0);
+                    das::widen2(__builtin_bit_cast(uint32_t, d0), x0[2 * i], x0[2 * i + 1]);
+                    das::widen2(__builtin_bit_cast(uint32_t, d1), x1[2 * i], x1[2 * i + 1]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NF; ++i) {
+                    const int o = (int)(off + 4 * i);
+                    x0[i] = das::buffer_load_f32(r0, o, 0, 0);
+                    x1[i] = das::buffer_load_f32(r1, o, 0, 0);
+                }
             }
             if constexpr (IQ) {
 #pragma unroll
@@ -762,14 +830,14 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     }
 }
 
-template <bool IQ, int FL, int LAYOUT, int VPR, int S = 1>
+template <bool IQ, int FL, int LAYOUT, int VPR, int S = 1, bool H = false>
 hipError_t launch(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
                   const float *tau, const float *w, float *out, hipStream_t stream) {
-    const int64_t row_bytes = (int64_t)kp.B * plan.elem_bytes;
+    const int64_t row_bytes = (int64_t)kp.B * plan.store_bytes;
     const int64_t tap = (LAYOUT == DAS_LAYOUT_KQMB) ? row_bytes * kp.q_count * kp.M : row_bytes;
     const int tiles = ((kp.nx + TX - 1) / TX) * ((kp.ny + TY - 1) / TY) * ((kp.nz + VPR - 1) / VPR);
     const int ftiles = (kp.B + ROW * FL - 1) / (ROW * FL);
-    hipLaunchKernelGGL((das_bi_staged_kernel<IQ, FL, LAYOUT, VPR, S>), dim3(tiles, ftiles), dim3(THREADS), 0,
+    hipLaunchKernelGGL((das_bi_staged_kernel<IQ, FL, LAYOUT, VPR, S, H>), dim3(tiles, ftiles), dim3(THREADS), 0,
                        stream, kp, rf, rx, tau, w, out, (uint32_t)tap);
     return hipGetLastError();
 }
@@ -780,7 +848,11 @@ hipError_t launch_vpr(const das_plan_t &plan, const DasKParams &kp, const float 
     // fp32: 2 frames per lane; complex64: 1 frame per lane.  Either way a lane
     // holds 8 bytes of a sample row and a staged row is 128 bytes.  Split rows
     // (B a multiple of 64 fp32 / 32 complex frames): 16 bytes per lane (4 fp32
-    // or 2 complex frames), 256-byte rows, 8 receivers a step.
+    // or 2 complex frames), 256-byte rows, 8 receivers a step.  Binary16
+    // rows: 2 frames per lane (4 bytes fp32, 8 bytes complex).
+    if (plan.h16)
+        return plan.p.dtype == DAS_C64 ? launch<true, 2, LAYOUT, 2, 1, true>(plan, kp, rf, rx, tau, w, out, stream)
+                                       : launch<false, 2, LAYOUT, 2, 1, true>(plan, kp, rf, rx, tau, w, out, stream);
     if (plan.p.dtype == DAS_C64) {
         if (plan.vpr == 1)
             return launch<true, 1, LAYOUT, 1>(plan, kp, rf, rx, tau, w, out, stream);
@@ -802,6 +874,8 @@ bool das_staged_supported(const das_plan_t &plan) {
     // multiple of 32) or 1 (B a multiple of 16); complex64 with 2 (split rows,
     // B a multiple of 32) or 1 (B a multiple of 16)
     const int32_t B = plan.p.B;
+    if (plan.h16)                                    // binary16: 2 frames per lane, B a multiple of 32
+        return plan.fl == 2 && plan.split == 1 && B % 32 == 0;
     if (plan.p.dtype == DAS_F32)
         return (plan.fl == 4 && plan.split == 2 && B % 64 == 0) || (plan.fl == 2 && plan.split == 1 && B % 32 == 0) ||
                (plan.fl == 1 && plan.split == 1 && B % 16 == 0);

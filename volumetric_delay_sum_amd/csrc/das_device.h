@@ -170,6 +170,26 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ float buffer_load_f32(BufRsrc r, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.load.f32");
 __device__ f32x2 buffer_load_f32x2(BufRsrc r, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.load.v2f32");
 __device__ f32x4 buffer_load_f32x4(BufRsrc r, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.load.v4f32");
+__device__ _Float16 buffer_load_f16(BufRsrc r, int voff, int soff, int aux) __asm("llvm.amdgcn.raw.buffer.load.f16");
+
+// Binary16 samples widened to float32 (exact: every half is a float).  A
+// dword holds two halves, the lower address in the low 16 bits.
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void widen2(uint32_t bits, float &lo, float &hi) {
+    const h2_t h = __builtin_bit_cast(h2_t, bits);
+    lo = (float)h.x;
+    hi = (float)h.y;
+}
+
+// acc += c * (the low (HI = 0) or high half of bits, widened): one
+// v_fma_mix_f32, the same single rounding as a conversion and an FMA.
+template <int HI>
+__device__ __forceinline__ void fma_half(float &acc, float c, uint32_t bits) {
+    if constexpr (HI)
+        asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(acc) : "v"(c), "v"(bits));
+    else
+        asm("v_fma_mix_f32 %0, %1, %2, %0 op_sel_hi:[0,1,0]" : "+v"(acc) : "v"(c), "v"(bits));
+}
 
 // LDS-DMA: the load writes lane l's `size` bytes to LDS at lds + size * l
 // (the LDS base goes to M0, so it must be wave-uniform) instead of to VGPRs.

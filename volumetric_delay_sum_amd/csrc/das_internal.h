@@ -47,6 +47,8 @@ struct das_plan {
     float apod_c[DAS_APOD_TERMS];
     int32_t split;            // staged kernel: 2 = each DPP row split between two voxels (16-byte lanes,
                               // 64 fp32 / 32 complex frames, 8 receivers a step), else 1
+    int32_t h16;              // batch-inner: the permuted buffer holds binary16 samples (DAS_STORE_F16)
+    int32_t store_bytes;      // bytes per sample in the permuted buffer (elem_bytes, or half that with h16)
 };
 
 // Launchers (defined next to their kernels).  They assume validated input.

@@ -5,17 +5,42 @@
 // Works", ALG2).  Per (q, m) plane this is a B x K -> K x B transpose in which
 // both the HBM reads (along k) and the HBM writes (along b) are contiguous:
 // through registers for fp32 with B a multiple of 16, else through LDS.  Pure
-// data movement, HBM-bound: 2 x elem bytes per sample.
+// data movement, HBM-bound: elem bytes read and elem (binary16: elem / 2)
+// bytes written per sample.
+//
+// Binary16 storage (the paper's FP16 variant, Section 3; ffdas docs,
+// mixed-precision API): the permute rounds each float32 to the nearest half,
+// ties to even (v_cvt_f16_f32 in the default rounding mode; halves below the
+// normal range are kept as subnormals, overflow gives infinity), so the
+// conversion costs no pass of its own.
 #include "das_internal.h"
 
+#include <type_traits>
+
 namespace {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+
+// A sample as stored: unchanged, or rounded to binary16 (per component).
+template <typename To>
+__device__ __forceinline__ To stored(float x) {
+    return (To)x;
+}
+template <typename To>
+__device__ __forceinline__ To stored(float2 x) {
+    if constexpr (sizeof(To) == sizeof(float2))
+        return x;
+    else
+        return To{(_Float16)x.x, (_Float16)x.y};
+}
 
 constexpr int TK = 64;          // samples per tile
 constexpr int TB = 32;          // frames per tile
 constexpr int THREADS = 256;
 
-template <typename T, int LAYOUT>
-__global__ __launch_bounds__(THREADS) void permute_kernel(const T *__restrict__ in, T *__restrict__ out,
+template <typename T, typename TO, int LAYOUT>
+__global__ __launch_bounds__(THREADS) void permute_kernel(const T *__restrict__ in, TO *__restrict__ out,
                                                           int32_t B, int32_t Q, int32_t M, int32_t K,
                                                           int32_t q_begin, int32_t q_count,
                                                           int32_t tiles_k, int32_t tiles_b) {
@@ -63,7 +88,7 @@ __global__ __launch_bounds__(THREADS) void permute_kernel(const T *__restrict__ 
                     dst = (((int64_t)k * q_count + ql) * M + m) * (int64_t)B + b;
                 else
                     dst = (((int64_t)ql * M + m) * (int64_t)K + k) * (int64_t)B + b;
-                out[dst] = tile[bb][kk];
+                out[dst] = stored<TO>(tile[bb][kk]);
             }
         }
     }
@@ -75,11 +100,12 @@ __global__ __launch_bounds__(THREADS) void permute_kernel(const T *__restrict__ 
 // reading FB / 4 runs of 4 c-lanes x 16 B = whole lines of a frame row),
 // transposes it in registers and stores four 16-byte pieces: the FB / 4 lanes
 // of one sample row write its FB frames as one contiguous run.  Loads and
-// stores are non-temporal (the data streams through once).
+// stores are non-temporal (the data streams through once).  With binary16
+// storage (H) each piece is 8 bytes of four halves.
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-template <int FB, int LAYOUT>
-__global__ __launch_bounds__(THREADS) void permute_f32_kernel(const float *__restrict__ in, float *__restrict__ out,
+template <int FB, int LAYOUT, bool H>
+__global__ __launch_bounds__(THREADS) void permute_f32_kernel(const float *__restrict__ in, void *__restrict__ out,
                                                               int32_t B, int32_t Q, int32_t M, int32_t K,
                                                               int32_t q_begin, int32_t q_count, int32_t tiles_k,
                                                               int32_t tiles_b) {
@@ -124,11 +150,16 @@ __global__ __launch_bounds__(THREADS) void permute_f32_kernel(const float *__res
             dst = (((int64_t)(k + j) * q_count + ql) * M + m) * (int64_t)B + b;
         else
             dst = (((int64_t)ql * M + m) * (int64_t)K + (k + j)) * (int64_t)B + b;
-        __builtin_nontemporal_store(y, reinterpret_cast<f32x4_t *>(out + dst));
+        if constexpr (H) {
+            const h4_t yh = {(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
+            __builtin_nontemporal_store(yh, reinterpret_cast<h4_t *>(out) + dst / 4);
+        } else {
+            __builtin_nontemporal_store(y, reinterpret_cast<f32x4_t *>(static_cast<float *>(out) + dst));
+        }
     }
 }
 
-template <int FB, int LAYOUT>
+template <int FB, int LAYOUT, bool H>
 hipError_t launch_f32(const das_plan_t &plan, const void *rf, void *out, int32_t q_begin, int32_t q_count,
                       hipStream_t stream) {
     const das_problem &p = plan.p;
@@ -139,13 +170,13 @@ hipError_t launch_f32(const das_plan_t &plan, const void *rf, void *out, int32_t
     const int64_t blocks = (waves + THREADS / 64 - 1) / (THREADS / 64);
     if (blocks > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((permute_f32_kernel<FB, LAYOUT>), dim3((uint32_t)blocks), dim3(THREADS), 0, stream,
-                       static_cast<const float *>(rf), static_cast<float *>(out), p.B, p.Q, p.M, p.K, q_begin,
+    hipLaunchKernelGGL((permute_f32_kernel<FB, LAYOUT, H>), dim3((uint32_t)blocks), dim3(THREADS), 0, stream,
+                       static_cast<const float *>(rf), out, p.B, p.Q, p.M, p.K, q_begin,
                        q_count, tiles_k, tiles_b);
     return hipGetLastError();
 }
 
-template <typename T, int LAYOUT>
+template <typename T, typename TO, int LAYOUT>
 hipError_t launch(const das_plan_t &plan, const void *rf, void *out, int32_t q_begin, int32_t q_count,
                   hipStream_t stream) {
     const das_problem &p = plan.p;
@@ -154,29 +185,37 @@ hipError_t launch(const das_plan_t &plan, const void *rf, void *out, int32_t q_b
     const int64_t blocks = (int64_t)tiles_k * tiles_b * q_count * p.M;
     if (blocks > 0x7fffffffLL)
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((permute_kernel<T, LAYOUT>), dim3((uint32_t)blocks), dim3(THREADS), 0, stream,
-                       static_cast<const T *>(rf), static_cast<T *>(out), p.B, p.Q, p.M, p.K, q_begin,
+    hipLaunchKernelGGL((permute_kernel<T, TO, LAYOUT>), dim3((uint32_t)blocks), dim3(THREADS), 0, stream,
+                       static_cast<const T *>(rf), static_cast<TO *>(out), p.B, p.Q, p.M, p.K, q_begin,
                        q_count, tiles_k, tiles_b);
     return hipGetLastError();
+}
+
+template <bool H>
+hipError_t launch_dtype(const das_plan_t &plan, const void *rf, void *out, int32_t q_begin, int32_t q_count,
+                        hipStream_t stream) {
+    using TO1 = typename std::conditional<H, _Float16, float>::type;
+    using TO2 = typename std::conditional<H, h2_t, float2>::type;
+    const bool kqmb = plan.p.layout == DAS_LAYOUT_KQMB;
+    if (plan.p.dtype == DAS_C64)
+        return kqmb ? launch<float2, TO2, DAS_LAYOUT_KQMB>(plan, rf, out, q_begin, q_count, stream)
+                    : launch<float2, TO2, DAS_LAYOUT_QMKB>(plan, rf, out, q_begin, q_count, stream);
+    // the register transpose needs 16-byte aligned runs: K a multiple of 4 (input rows), B of 16 (output rows)
+    const bool vec = plan.p.K % 4 == 0;
+    if (vec && plan.p.B % 32 == 0)
+        return kqmb ? launch_f32<32, DAS_LAYOUT_KQMB, H>(plan, rf, out, q_begin, q_count, stream)
+                    : launch_f32<32, DAS_LAYOUT_QMKB, H>(plan, rf, out, q_begin, q_count, stream);
+    if (vec && plan.p.B % 16 == 0)
+        return kqmb ? launch_f32<16, DAS_LAYOUT_KQMB, H>(plan, rf, out, q_begin, q_count, stream)
+                    : launch_f32<16, DAS_LAYOUT_QMKB, H>(plan, rf, out, q_begin, q_count, stream);
+    return kqmb ? launch<float, TO1, DAS_LAYOUT_KQMB>(plan, rf, out, q_begin, q_count, stream)
+                : launch<float, TO1, DAS_LAYOUT_QMKB>(plan, rf, out, q_begin, q_count, stream);
 }
 
 }  // namespace
 
 hipError_t das_launch_permute(const das_plan_t &plan, const void *rf, void *out, int32_t q_begin,
                               int32_t q_count, hipStream_t stream) {
-    const bool c64 = plan.p.dtype == DAS_C64;
-    const bool kqmb = plan.p.layout == DAS_LAYOUT_KQMB;
-    if (c64)
-        return kqmb ? launch<float2, DAS_LAYOUT_KQMB>(plan, rf, out, q_begin, q_count, stream)
-                    : launch<float2, DAS_LAYOUT_QMKB>(plan, rf, out, q_begin, q_count, stream);
-    // the register transpose needs 16-byte aligned runs: K a multiple of 4 (input rows), B of 16 (output rows)
-    const bool vec = plan.p.K % 4 == 0;
-    if (vec && plan.p.B % 32 == 0)
-        return kqmb ? launch_f32<32, DAS_LAYOUT_KQMB>(plan, rf, out, q_begin, q_count, stream)
-                    : launch_f32<32, DAS_LAYOUT_QMKB>(plan, rf, out, q_begin, q_count, stream);
-    if (vec && plan.p.B % 16 == 0)
-        return kqmb ? launch_f32<16, DAS_LAYOUT_KQMB>(plan, rf, out, q_begin, q_count, stream)
-                    : launch_f32<16, DAS_LAYOUT_QMKB>(plan, rf, out, q_begin, q_count, stream);
-    return kqmb ? launch<float, DAS_LAYOUT_KQMB>(plan, rf, out, q_begin, q_count, stream)
-                : launch<float, DAS_LAYOUT_QMKB>(plan, rf, out, q_begin, q_count, stream);
+    return plan.h16 ? launch_dtype<true>(plan, rf, out, q_begin, q_count, stream)
+                    : launch_dtype<false>(plan, rf, out, q_begin, q_count, stream);
 }
