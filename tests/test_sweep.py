@@ -1,8 +1,8 @@
 """GPU parity over seeded random shapes: frame counts that select every kernel
 variant (baseline, direct loads, LDS-staged with 1, 2 or 4 frames per lane,
 split rows, fallback to direct loads), both layouts, fp32 and complex64,
-several f-numbers, plane and diverging transmits, events in one call or one
-at a time.  Each case is compared element by element with the fp64 oracle
+binary16 or native sample storage, several f-numbers, plane and diverging
+transmits, events in one call or one at a time.  Each case is compared element by element with the fp64 oracle
 to the same bar as the other parity tests."""
 import numpy as np
 import pytest
@@ -33,18 +33,19 @@ def _case(i):
     r = rng.random()
     alg, layout = ("baseline", "kqmb") if r < 0.2 else ("batch_inner", "kqmb" if r < 0.6 else "qmkb")
     q_chunk = 1 if rng.random() < 0.3 else None
-    return cfg, alg, layout, q_chunk
+    storage = "f16" if alg == "batch_inner" and rng.random() < 0.3 else "native"
+    return cfg, alg, layout, q_chunk, storage
 
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_shapes(gpu, i):
-    cfg, alg, layout, q_chunk = _case(i)
+    cfg, alg, layout, q_chunk, storage = _case(i)
     what = (f"case {i}: B={cfg.B} iq={cfg.iq} M={cfg.M} grid={cfg.grid} K={cfg.K} Q={cfg.Q} "
-            f"voxel={cfg.voxel} f#={cfg.f_number} {cfg.tx} {alg}/{layout} q_chunk={q_chunk}")
+            f"voxel={cfg.voxel} f#={cfg.f_number} {cfg.tx} {alg}/{layout} q_chunk={q_chunk} storage={storage}")
     print(what, flush=True)
     inp = Inputs(cfg, w_tx="uniform")
-    y = to_numpy(run_gpu(inp, alg, layout, q_chunk=q_chunk), cfg.iq)
-    ref = oracle_ref(inp)
+    y = to_numpy(run_gpu(inp, alg, layout, q_chunk=q_chunk, storage=storage), cfg.iq)
+    ref = oracle_ref(inp, storage=storage)
     if np.abs(ref).max() == 0.0:            # every term out of range: exact zeros
         assert np.all(np.asarray(y) == 0.0), what
     else:
