@@ -92,7 +92,7 @@ struct Geo {
     static_assert(LDS_BYTES <= LDS_TOTAL, "LDS budget");
     static_assert(ROWB % 16 == 0 && 64 % LPR == 0, "copy granularity");
     static_assert(LANEB == 4 || LANEB == 8 || LANEB == 16, "reader width");
-    static_assert(S == 1 || (S == 2 && LANEB == 16), "split rows");
+    static_assert(S == 1 || (S == 2 && (LANEB == 16 || H)), "split rows");
 };
 
 // Per-lane state of one voxel in one step: sample index and weights.  Every
@@ -849,9 +849,12 @@ hipError_t launch_vpr(const das_plan_t &plan, const DasKParams &kp, const float 
     // holds 8 bytes of a sample row and a staged row is 128 bytes.  Split rows
     // (B a multiple of 64 fp32 / 32 complex frames): 16 bytes per lane (4 fp32
     // or 2 complex frames), 256-byte rows, 8 receivers a step.  Binary16
-    // rows: 2 frames per lane (4 bytes fp32, 8 bytes complex).
+    // rows: 2 frames per lane (4 bytes fp32, 8 bytes complex); complex ones
+    // split between two voxels as above (8 receivers a step), which halves the
+    // per-lane step state: with whole rows the kernel spilled registers
+    // (Main complex workload 29.3 ms, split 24.5 ms).
     if (plan.h16)
-        return plan.p.dtype == DAS_C64 ? launch<true, 2, LAYOUT, 2, 1, true>(plan, kp, rf, rx, tau, w, out, stream)
+        return plan.p.dtype == DAS_C64 ? launch<true, 2, LAYOUT, 2, 2, true>(plan, kp, rf, rx, tau, w, out, stream)
                                        : launch<false, 2, LAYOUT, 2, 1, true>(plan, kp, rf, rx, tau, w, out, stream);
     if (plan.p.dtype == DAS_C64) {
         if (plan.vpr == 1)
