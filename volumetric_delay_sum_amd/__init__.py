@@ -10,6 +10,11 @@ The operation ("ffdas: volumetric ultrasound reconstruction at warp speed",
 Section 3; ffdas docs "How It Works"): for each voxel n and frame b, sum over
 transmit events q and receivers m of w_tx[q,n] * w_rx[m,n] times the RF sample
 linearly interpolated at the delay tau_tx[q,n] + |r_n - p_m| / c.
+
+``Plan(..., storage="f16")`` keeps the permuted samples in binary16 (the
+paper's FP16 variant; the docs' ``half`` / ``half2``): permuted buffers are then
+torch.float16 tensors, rounded by ``permute`` and widened to fp32 by
+``beamform``.
 """
 from __future__ import annotations
 

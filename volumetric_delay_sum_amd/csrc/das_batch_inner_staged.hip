@@ -39,6 +39,10 @@
 // the permuted buffer, so any geometry is served exactly; voxels with zero
 // weight for a receiver do not widen its window and read a row of it with
 // zero coefficients.
+//
+// Binary16 storage (the paper's FP16 variant, Section 3): the staged rows hold
+// halves, 2 frames per lane, and the FMAs widen them as they read them
+// (v_fma_mix_f32), with every item's weights from the row's LDS table.
 #include "das_device.h"
 
 #include <type_traits>
