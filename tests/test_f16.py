@@ -151,3 +151,23 @@ def test_binary16_streamed(gpu):
     sp.synchronize()
     torch.cuda.synchronize()
     assert_parity(to_numpy(out, False), oracle_ref(inp, storage="f16"), "f16 streamed")
+
+
+def test_binary16_plan_takes_half_buffers_only(gpu):
+    import torch
+    import volumetric_delay_sum_amd as das
+    plan = das.Plan(B=32, Q=2, M=4, K=64, nx=2, ny=2, nz=2, origin=(0, 0, 5e-3), spacing=(2e-4,) * 3,
+                    fs=20e6, c=1540.0, storage="f16")
+    rf = torch.zeros((32, 2, 4, 64), dtype=torch.float32, device="cuda")
+    with pytest.raises(TypeError):
+        plan.permute(rf, torch.empty(plan.permuted_shape(), dtype=torch.float32, device="cuda"))
+    perm = torch.empty(plan.permuted_shape(), dtype=torch.float16, device="cuda")
+    plan.permute(rf, perm)
+    out = torch.empty(plan.output_shape(), dtype=torch.float32, device="cuda")
+    with pytest.raises(TypeError):
+        plan.beamform(perm.float(), torch.zeros((4, 3), device="cuda"), torch.zeros((2, 8), device="cuda"),
+                      torch.zeros((2, 8), device="cuda"), out)
+    plan.beamform(perm, torch.zeros((4, 3), device="cuda"), torch.zeros((2, 8), device="cuda"),
+                  torch.ones((2, 8), device="cuda"), out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
