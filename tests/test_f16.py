@@ -171,3 +171,24 @@ def test_binary16_plan_takes_half_buffers_only(gpu):
                   torch.ones((2, 8), device="cuda"), out)
     torch.cuda.synchronize()
     assert torch.all(out == 0)
+
+
+def test_binary16_large_sampled(gpu):
+    """Large (128 x 128 x 96 voxels, 64 frames, 16 events of 1024 x 4096
+    samples) with binary16 storage in one QMKB chunk, as the benchmark runs it;
+    three frames on a seeded voxel sample against the oracle of the rounded
+    samples."""
+    import torch
+    import oracle
+    cfg = das_synth.get_config("large")
+    inp = Inputs(cfg)
+    out = run_gpu(inp, "batch_inner", "qmkb", storage="f16")
+    frames = [0, 31, 63]
+    vox = sample_voxels(cfg, 768, seed=7)
+    y = to_numpy(out, cfg.iq)[frames][:, vox]
+    fields = dict(inp.fields, B=len(frames))
+    rf_sub = oracle.to_binary16(inp.rf_d[frames].cpu().numpy())
+    del inp, out
+    torch.cuda.empty_cache()
+    ref = oracle.das_sum(fields, rf_sub, das_synth.array_positions(cfg), *das_synth.tx_tables(cfg), voxels=vox)
+    assert_parity(y, ref, "large f16")
