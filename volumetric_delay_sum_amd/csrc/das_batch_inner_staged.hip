@@ -95,7 +95,7 @@ struct Geo {
     static constexpr int LDS_BYTES = 2 * BUF + SLOTS + COEF;
     static_assert(LDS_BYTES <= LDS_TOTAL, "LDS budget");
     static_assert(ROWB % 16 == 0 && 64 % LPR == 0, "copy granularity");
-    static_assert(LANEB == 4 || LANEB == 8 || LANEB == 16, "reader width");
+    static_assert(LANEB == 4 || LANEB == 8 || LANEB == 16 || (H && LANEB == 2), "reader width");
     static_assert(S == 1 || (S == 2 && (LANEB == 16 || H)), "split rows");
 };
 
@@ -160,20 +160,26 @@ template <int NF>
 struct Tap {
     using type = float __attribute__((ext_vector_type(NF)));
 };
-// a lane's binary16 tap as loaded: ND dwords of two halves each
-template <int ND>
+// a lane's binary16 tap as loaded, LB bytes: one half, one dword of two
+// halves, or LB / 4 dwords
+template <int LB>
 struct RawTap {
-    using type = uint32_t __attribute__((ext_vector_type(ND)));
+    using type = uint32_t __attribute__((ext_vector_type(LB / 4)));
 };
 template <>
-struct RawTap<1> {
+struct RawTap<4> {
     using type = uint32_t;
 };
+template <>
+struct RawTap<2> {
+    using type = uint16_t;
+};
 
-// Dword I of a binary16 tap (one dword: the tap itself).
+// Dword I of a binary16 tap (one half or one dword: the tap itself, the half
+// in the low 16 bits).
 template <int I, typename TV>
 __device__ __forceinline__ uint32_t das_dword(const TV &x) {
-    if constexpr (sizeof(TV) == 4)
+    if constexpr (sizeof(TV) <= 4)
         return x;
     else
         return x[I];
@@ -189,6 +195,8 @@ __device__ __forceinline__ void widen_tap(const TV &x, float (&y)[NF]) {
     if constexpr (!H) {
 #pragma unroll
         for (int i = 0; i < NF; ++i) y[i] = x[i];
+    } else if constexpr (NF == 1) {
+        y[0] = (float)__builtin_bit_cast(_Float16, x);
     } else if constexpr (NF == 2) {
         das::widen2(x, y[0], y[1]);
     } else {
@@ -212,7 +220,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     // row and receiver m0 + li % NRX
     constexpr int PL = VPR / S;
     static_assert(VPR % S == 0, "each lane half needs a voxel");
-    using TapV = typename std::conditional<H, typename RawTap<G::LANEB / 4>::type, typename Tap<NF>::type>::type;
+    using TapV = typename std::conditional<H, typename RawTap<G::LANEB>::type, typename Tap<NF>::type>::type;
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
     int *slots = reinterpret_cast<int *>(lds + 2 * G::BUF);   // [3 sets][min, max][NRX]
     constexpr uint32_t COEF_AT = 2 * G::BUF + G::SLOTS;       // weight table
@@ -623,7 +631,10 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
             const uint32_t jo = laneoff_g + (uint32_t)min(j, jmax) * m_stride;
             const uint32_t off = das::row_bcast<src>(koff) + jo;
             float x0[NF], x1[NF];
-            if constexpr (H) {
+            if constexpr (H && NF == 1) {
+                x0[0] = (float)das::buffer_load_f16(r0, (int)off, 0, 0);
+                x1[0] = (float)das::buffer_load_f16(r1, (int)off, 0, 0);
+            } else if constexpr (H) {
 #pragma unroll
                 for (int i = 0; i < NF / 2; ++i) {
                     const int o = (int)(off + 4 * i);
@@ -853,10 +864,13 @@ hipError_t launch_vpr(const das_plan_t &plan, const DasKParams &kp, const float 
     // holds 8 bytes of a sample row and a staged row is 128 bytes.  Split rows
     // (B a multiple of 64 fp32 / 32 complex frames): 16 bytes per lane (4 fp32
     // or 2 complex frames), 256-byte rows, 8 receivers a step.  Binary16
-    // rows: 2 frames per lane (4 bytes fp32, 8 bytes complex); complex ones
+    // rows: 2 frames per lane (4 bytes fp32, 8 bytes complex; fp32 with B a
+    // multiple of 16 only: 1 frame, 2 bytes); complex ones
     // split between two voxels as above (8 receivers a step), which halves the
     // per-lane step state: with whole rows the kernel spilled registers
     // (Main complex workload 29.3 ms, split 24.5 ms).
+    if (plan.h16 && plan.p.dtype == DAS_F32 && plan.fl == 1)
+        return launch<false, 1, LAYOUT, 2, 1, true>(plan, kp, rf, rx, tau, w, out, stream);
     if (plan.h16)
         return plan.p.dtype == DAS_C64 ? launch<true, 2, LAYOUT, 2, 2, true>(plan, kp, rf, rx, tau, w, out, stream)
                                        : launch<false, 2, LAYOUT, 2, 1, true>(plan, kp, rf, rx, tau, w, out, stream);
@@ -881,8 +895,9 @@ bool das_staged_supported(const das_plan_t &plan) {
     // multiple of 32) or 1 (B a multiple of 16); complex64 with 2 (split rows,
     // B a multiple of 32) or 1 (B a multiple of 16)
     const int32_t B = plan.p.B;
-    if (plan.h16)                                    // binary16: 2 frames per lane, B a multiple of 32
-        return plan.fl == 2 && plan.split == 1 && B % 32 == 0;
+    if (plan.h16)                                    // binary16: 2 frames per lane (B a multiple of 32),
+        return plan.split == 1 &&                    // or 1 fp32 frame (B a multiple of 16)
+               ((plan.fl == 2 && B % 32 == 0) || (plan.fl == 1 && plan.p.dtype == DAS_F32 && B % 16 == 0));
     if (plan.p.dtype == DAS_F32)
         return (plan.fl == 4 && plan.split == 2 && B % 64 == 0) || (plan.fl == 2 && plan.split == 1 && B % 32 == 0) ||
                (plan.fl == 1 && plan.split == 1 && B % 16 == 0);
