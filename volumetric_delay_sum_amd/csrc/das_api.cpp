@@ -323,7 +323,9 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
     if (h16) {
         // binary16 rows: 2 fp32 frames (4 bytes) per lane for B a multiple of
         // 32, 2 complex frames (8 bytes) for B a multiple of 32
-        if (want_staged && p.B % 32 == 0)
+        if (want_staged && p.dtype == DAS_F32 && p.B % 64 == 0)
+            pl->fl = 4;                          // split rows, 8 bytes per lane
+        else if (want_staged && p.B % 32 == 0)
             pl->fl = 2;
         else if (want_staged && p.dtype == DAS_F32 && p.B % 16 == 0)
             pl->fl = 1;                          // one fp32 frame (2 bytes) per lane
