@@ -377,7 +377,7 @@ def test_binary16_storage_needs_batch_inner():
     ("f32", 32, 2, 2, 1), ("f32", 64, 2, 4, 1), ("f32", 128, 2, 4, 1), ("f32", 96, 2, 2, 1), ("f32", 16, 2, 1, 1),
     ("f32", 48, 2, 1, 1),
     ("f32", 24, 2, 2, 0), ("f32", 68, 2, 4, 0), ("f32", 7, 2, 1, 0), ("c64", 32, 4, 2, 1),
-    ("c64", 64, 4, 2, 1), ("c64", 16, 4, 1, 0), ("c64", 34, 4, 2, 0)])
+    ("c64", 64, 4, 2, 1), ("c64", 16, 4, 1, 1), ("c64", 48, 4, 1, 1), ("c64", 34, 4, 2, 0)])
 def test_binary16_plan_info(dtype, B, store, fl, staged):
     iq = dtype == "c64"
     pl = das.Plan(**_problem(B=B, dtype=dtype, f_demod=5e6 if iq else 0.0, storage="f16"))

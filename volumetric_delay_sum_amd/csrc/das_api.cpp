@@ -327,8 +327,8 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
             pl->fl = 4;                          // split rows, 8 bytes per lane
         else if (want_staged && p.B % 32 == 0)
             pl->fl = 2;
-        else if (want_staged && p.dtype == DAS_F32 && p.B % 16 == 0)
-            pl->fl = 1;                          // one fp32 frame (2 bytes) per lane
+        else if (want_staged && p.B % 16 == 0)
+            pl->fl = 1;                          // one frame (2 bytes fp32, 4 bytes complex) per lane
     } else if (want_staged && p.dtype == DAS_F32 && p.B % 32 == 0)
         pl->fl = 2;
     else if (want_staged && p.dtype == DAS_F32 && p.B % 16 == 0)

@@ -866,12 +866,14 @@ hipError_t launch_vpr(const das_plan_t &plan, const DasKParams &kp, const float 
     // or 2 complex frames), 256-byte rows, 8 receivers a step.  Binary16
     // rows: 2 frames per lane (4 bytes fp32, 8 bytes complex; fp32 with B a
     // multiple of 64: 4 frames in split rows, one frame tile for Large's 64;
-    // fp32 with B a multiple of 16 only: 1 frame, 2 bytes); complex ones
+    // B a multiple of 16 only: 1 frame, 2 bytes fp32, 4 bytes complex); complex ones
     // split between two voxels as above (8 receivers a step), which halves the
     // per-lane step state: with whole rows the kernel spilled registers
     // (Main complex workload 29.3 ms, split 24.5 ms).
     if (plan.h16 && plan.p.dtype == DAS_F32 && plan.fl == 1)
         return launch<false, 1, LAYOUT, 2, 1, true>(plan, kp, rf, rx, tau, w, out, stream);
+    if (plan.h16 && plan.fl == 1)                                   // complex, B a multiple of 16: 4 bytes a lane
+        return launch<true, 1, LAYOUT, 2, 2, true>(plan, kp, rf, rx, tau, w, out, stream);
     if (plan.h16 && plan.p.dtype == DAS_F32 && plan.fl == 4)      // B a multiple of 64: split rows, 8 bytes a lane
         return launch<false, 4, LAYOUT, 2, 2, true>(plan, kp, rf, rx, tau, w, out, stream);
     if (plan.h16)
@@ -901,7 +903,7 @@ bool das_staged_supported(const das_plan_t &plan) {
     if (plan.h16) {                                  // binary16: 2 frames per lane (B a multiple of 32),
         const bool real = plan.p.dtype == DAS_F32;   // or 4 fp32 frames (of 64), or 1 (of 16)
         return plan.split == 1 && ((plan.fl == 2 && B % 32 == 0) || (plan.fl == 4 && real && B % 64 == 0) ||
-                                   (plan.fl == 1 && real && B % 16 == 0));
+                                   (plan.fl == 1 && B % 16 == 0));
     }
     if (plan.p.dtype == DAS_F32)
         return (plan.fl == 4 && plan.split == 2 && B % 64 == 0) || (plan.fl == 2 && plan.split == 1 && B % 32 == 0) ||
