@@ -33,6 +33,14 @@ def assert_parity(y, ref, what=""):
         assert mx <= MAX_REL and l2 <= L2_REL, f"{what} component {i}: max {mx:.3e}, L2 {l2:.3e}"
 
 
+def assert_all_written(out, what=""):
+    """Every element of a NaN-filled device output was written (and is finite):
+    the whole volume, not only the voxels a sampled comparison looks at."""
+    import torch
+    bad = int((~torch.isfinite(out)).sum().item())
+    assert bad == 0, f"{what}: {bad} of {out.numel()} output values unwritten or non-finite"
+
+
 class Inputs:
     """Seeded inputs of one configuration, on the GPU and as host copies."""
 

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import das_synth
-from das_testing import Inputs, assert_parity, oracle_ref, run_gpu, sample_voxels, to_numpy
+from das_testing import Inputs, assert_all_written, assert_parity, oracle_ref, run_gpu, sample_voxels, to_numpy
 
 pytestmark = pytest.mark.gpu
 
@@ -81,16 +81,26 @@ def test_binary16_direct_kernel(gpu, monkeypatch, iq):
     assert_parity(y, oracle_ref(inp, storage="f16"), f"f16 direct iq={iq}")
 
 
+# frames per lane of the binary16 staged instances: B a multiple of 32 takes
+# two (complex: one pair of halves per frame, two frames), a multiple of 16
+# only takes one, and fp32 data with B a multiple of 64 takes four
+FPL16 = {(False, 16): 1, (False, 32): 2, (False, 48): 1, (False, 64): 4,
+         (True, 16): 1, (True, 32): 2, (True, 48): 1, (True, 64): 2}
+
+
 @pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])
 @pytest.mark.parametrize("voxel", [0.2e-3, 1.2e-3])
-def test_binary16_staged_windows_and_fallback(gpu, iq, voxel):
+@pytest.mark.parametrize("B", [16, 32, 48, 64])
+def test_binary16_staged_windows_and_fallback(gpu, iq, voxel, B):
     # coarse voxels make windows too wide for LDS: the direct-load fallback inside the staged kernel
     import volumetric_delay_sum_amd as das
-    cfg = das_synth.custom_config("tiny", name="win16", seed=29, array=(19, 3), grid=(11, 10, 3), K=700, B=32,
+    cfg = das_synth.custom_config("tiny", name="win16", seed=29, array=(19, 3), grid=(11, 10, 3), K=700, B=B,
                                   tx="diverging", sources=((0.0, 0.0), (2e-3, 1e-3)), iq=iq, n_scatterers=0,
                                   voxel=voxel, z0=3e-3)
     inp = Inputs(cfg, w_tx="uniform")
-    assert das.plan_from_fields(inp.fields, "batch_inner", "qmkb", storage="f16").info["staged"] == 1
+    info = das.plan_from_fields(inp.fields, "batch_inner", "qmkb", storage="f16").info
+    assert info["staged"] == 1
+    assert info["frames_per_lane"] == FPL16[(iq, B)], info
     y = to_numpy(run_gpu(inp, "batch_inner", "qmkb", storage="f16", q_chunk=1), iq)
     assert_parity(y, oracle_ref(inp, storage="f16"), f"f16 windows voxel={voxel} iq={iq}")
 
@@ -121,7 +131,9 @@ def test_binary16_main_sampled(main_inputs, layout):
     binary16 storage, in the launch configuration the benchmark times."""
     inp = main_inputs
     vox = sample_voxels(inp.cfg, 192)
-    y = to_numpy(run_gpu(inp, "batch_inner", layout, storage="f16"), False)[:, vox]
+    out = run_gpu(inp, "batch_inner", layout, storage="f16")
+    assert_all_written(out, f"main f16 {layout}")
+    y = to_numpy(out, False)[:, vox]
     assert_parity(y, oracle_ref(inp, voxels=vox, storage="f16"), f"main f16 {layout}")
 
 
@@ -129,7 +141,9 @@ def test_binary16_main_c64_sampled(gpu):
     cfg = das_synth.get_config("main-c64")
     inp = Inputs(cfg)
     vox = sample_voxels(cfg, 96)
-    y = to_numpy(run_gpu(inp, "batch_inner", "qmkb", storage="f16"), True)[:, vox]
+    out = run_gpu(inp, "batch_inner", "qmkb", storage="f16")
+    assert_all_written(out, "main-c64 f16")
+    y = to_numpy(out, True)[:, vox]
     assert_parity(y, oracle_ref(inp, voxels=vox, storage="f16"), "main-c64 f16")
 
 
@@ -183,6 +197,7 @@ def test_binary16_large_sampled(gpu):
     cfg = das_synth.get_config("large")
     inp = Inputs(cfg)
     out = run_gpu(inp, "batch_inner", "qmkb", storage="f16")
+    assert_all_written(out, "large f16")
     frames = [0, 31, 63]
     vox = sample_voxels(cfg, 768, seed=7)
     y = to_numpy(out, cfg.iq)[frames][:, vox]

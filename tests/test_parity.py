@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import das_synth
-from das_testing import Inputs, assert_parity, oracle_ref, run_gpu, sample_voxels, to_numpy
+from das_testing import Inputs, assert_all_written, assert_parity, oracle_ref, run_gpu, sample_voxels, to_numpy
 
 pytestmark = pytest.mark.gpu
 
@@ -66,9 +66,10 @@ def test_degenerate_shapes(gpu, alg, layout):
 @pytest.mark.parametrize("f_number", [0.3, 0.45, 0.7, 1.0, 3.0, 0.0])
 @pytest.mark.parametrize("alg,layout", [("baseline", "kqmb"), ("batch_inner", "qmkb")])
 def test_receive_apodization_f_numbers(gpu, f_number, alg, layout):
-    """Receive Hann at several f-numbers.  From 0.45 up the kernels evaluate
-    the plan's polynomial in sin^2(theta); 0.3 takes the atan2f / cospif
-    path; 0 switches apodization off.  A 37 x 3 array over a 13 x 7 x 3 grid
+    """Receive Hann at several f-numbers.  The kernels evaluate it as the plan's
+    polynomial in (1 - cos theta) / (1 - cos theta_max), fitted once per plan;
+    the oracle keeps the definition (fp64 atan2 and cos).  0 switches
+    apodization off.  A 37 x 3 array over a 13 x 7 x 3 grid
     puts many receivers on both sides of the aperture edge."""
     cfg = _ragged(B=32, array=(37, 3), f_number=f_number)
     inp = Inputs(cfg, w_tx="uniform")
@@ -179,7 +180,9 @@ def mid_inputs(gpu):
 def test_mid_sampled(mid_inputs, alg, layout):
     inp = mid_inputs
     vox = sample_voxels(inp.cfg, 400)
-    y = to_numpy(run_gpu(inp, alg, layout), False)[:, vox]
+    out = run_gpu(inp, alg, layout)
+    assert_all_written(out, f"mid {alg}/{layout}")
+    y = to_numpy(out, False)[:, vox]
     assert_parity(y, oracle_ref(inp, voxels=vox), f"mid {alg}/{layout}")
 
 
@@ -192,7 +195,9 @@ def main_inputs(gpu):
 def test_main_sampled(main_inputs, alg, layout):
     inp = main_inputs
     vox = sample_voxels(inp.cfg, 192)
-    y = to_numpy(run_gpu(inp, alg, layout), False)[:, vox]
+    out = run_gpu(inp, alg, layout)
+    assert_all_written(out, f"main {alg}/{layout}")
+    y = to_numpy(out, False)[:, vox]
     assert_parity(y, oracle_ref(inp, voxels=vox), f"main {alg}/{layout}")
 
 
@@ -221,7 +226,9 @@ def test_main_noise_only(gpu):
     """Worst case for relative error: no scatterer energy to dilute it."""
     inp = Inputs(das_synth.get_config("main"), scatterers=False)
     vox = sample_voxels(inp.cfg, 128, seed=3)
-    y = to_numpy(run_gpu(inp, "batch_inner", "kqmb"), False)[:, vox]
+    out = run_gpu(inp, "batch_inner", "kqmb")
+    assert_all_written(out, "main noise-only")
+    y = to_numpy(out, False)[:, vox]
     assert_parity(y, oracle_ref(inp, voxels=vox), "main noise-only")
 
 
@@ -229,5 +236,7 @@ def test_main_noise_only(gpu):
 def test_main_c64_sampled(gpu, alg, layout):
     inp = Inputs(das_synth.get_config("main-c64"))
     vox = sample_voxels(inp.cfg, 128)
-    y = to_numpy(run_gpu(inp, alg, layout), True)[:, vox]
+    out = run_gpu(inp, alg, layout)
+    assert_all_written(out, f"main-c64 {alg}/{layout}")
+    y = to_numpy(out, True)[:, vox]
     assert_parity(y, oracle_ref(inp, voxels=vox), f"main-c64 {alg}/{layout}")

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import das_synth
-from das_testing import Inputs, assert_parity, run_gpu, sample_voxels, to_numpy
+from das_testing import Inputs, assert_all_written, assert_parity, run_gpu, sample_voxels, to_numpy
 
 pytestmark = pytest.mark.gpu
 
@@ -66,6 +66,7 @@ def test_large_streamed_matches_oracle_on_a_sample(gpu):
     qc = plan.max_q_chunk()
     assert qc == 3 and plan.info["staged"] == 1
     out = _streamed(inp, qc)
+    assert_all_written(out, "large streamed")
     frames = [0, 31, 63]
     vox = sample_voxels(cfg, 1024, seed=5)
     y = to_numpy(out, cfg.iq)[frames][:, vox]
@@ -90,6 +91,7 @@ def test_large_qmkb_one_chunk_past_4gib_matches_oracle(gpu):
     assert plan.permuted_bytes(cfg.Q) > 4 * 2 ** 30
     print("large qmkb one chunk", flush=True)
     out = run_gpu(inp, "batch_inner", "qmkb", q_chunk=cfg.Q)
+    assert_all_written(out, "large qmkb one chunk")
     frames = [0, 37, 63]
     vox = sample_voxels(cfg, 1024, seed=6)
     y = to_numpy(out, cfg.iq)[frames][:, vox]

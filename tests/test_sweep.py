@@ -1,8 +1,8 @@
 """GPU parity over seeded random shapes: frame counts that select every kernel
 variant (baseline, direct loads, LDS-staged with 1, 2 or 4 frames per lane,
 split rows, fallback to direct loads), both layouts, fp32 and complex64,
-binary16 or native sample storage, several f-numbers, plane and diverging
-transmits, events in one call or one at a time.  Each case is compared element by element with the fp64 oracle
+binary16 or native sample storage, several f-numbers and start times, plane
+and diverging transmits, events in one call or one at a time.  Each case is compared element by element with the fp64 oracle
 to the same bar as the other parity tests."""
 import numpy as np
 import pytest
@@ -29,7 +29,10 @@ def _case(i):
         tx="plane" if rng.random() < 0.25 else "diverging", sources=sources,
         voxel=float(rng.choice([0.15e-3, 0.25e-3, 0.5e-3, 1.2e-3])),
         z0=float(rng.uniform(1e-3, 6e-3)),
-        f_number=float(rng.choice([0.0, 0.5, 1.0, 2.0])))
+        f_number=float(rng.choice([0.0, 0.5, 1.0, 2.0])),
+        # start time from a generator of its own, so the other draws stay as they were:
+        # zero, a whole number of sample periods, or any fraction of a microsecond
+        t0=float(np.random.default_rng([2025, i]).choice([0.0, 2.0 / 20e6, 0.37e-6, -0.61e-6])))
     r = rng.random()
     alg, layout = ("baseline", "kqmb") if r < 0.2 else ("batch_inner", "kqmb" if r < 0.6 else "qmkb")
     q_chunk = 1 if rng.random() < 0.3 else None
@@ -41,7 +44,8 @@ def _case(i):
 def test_random_shapes(gpu, i):
     cfg, alg, layout, q_chunk, storage = _case(i)
     what = (f"case {i}: B={cfg.B} iq={cfg.iq} M={cfg.M} grid={cfg.grid} K={cfg.K} Q={cfg.Q} "
-            f"voxel={cfg.voxel} f#={cfg.f_number} {cfg.tx} {alg}/{layout} q_chunk={q_chunk} storage={storage}")
+            f"voxel={cfg.voxel} f#={cfg.f_number} t0={cfg.t0} {cfg.tx} {alg}/{layout} q_chunk={q_chunk} "
+            f"storage={storage}")
     print(what, flush=True)
     inp = Inputs(cfg, w_tx="uniform")
     y = to_numpy(run_gpu(inp, alg, layout, q_chunk=q_chunk, storage=storage), cfg.iq)
