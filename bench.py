@@ -68,7 +68,7 @@ def main():
     ap.add_argument("--config", default="main", help="workload: tiny, mid, main, main-c64, large")
     ap.add_argument("--layout", default="qmkb", choices=["kqmb", "qmkb"],
                     help="permuted layout (QMKB: whole volumes in one chunk; KQMB: chunks under 4 GiB)")
-    ap.add_argument("--algorithm", default="batch_inner", choices=["batch_inner", "baseline"])
+    ap.add_argument("--algorithm", default="batch_inner", choices=["batch_inner", "baseline", "repack"])
     ap.add_argument("--q-chunk", type=int, default=0,
                     help="transmit events per permute/beamform pair (0: as many as the plan allows)")
     ap.add_argument("--streamed", action="store_true",
@@ -118,21 +118,21 @@ def main():
     w_d = torch.from_numpy(w).to(dev)
 
     h16 = args.storage == "f16"
-    if h16 and (args.wide or args.algorithm != "batch_inner"):
-        print("bench.py: --storage f16 is a batch-inner option for fp32 / complex64 samples", file=sys.stderr)
+    if h16 and (args.wide or args.algorithm == "baseline"):
+        print("bench.py: --storage f16 is a batch-inner / repack option for fp32 / complex64 samples",
+              file=sys.stderr)
         sys.exit(2)
     plan = das.plan_from_fields(fields, algorithm=args.algorithm, layout=args.layout, wide=args.wide,
                                 storage=args.storage)
     out = torch.empty(plan.output_shape(), dtype=torch.float64 if args.wide else torch.float32, device=dev)
-    bi = plan.batch_inner
+    bi = plan.permuted_input
     # events per das_permute / das_beamform pair (all Q unless the layout's
     # 32-bit offsets need chunks); chunks after the first accumulate into out
     qc = plan.max_q_chunk() if bi else cfg.Q
     if args.q_chunk > 0:
         qc = min(qc, args.q_chunk)
     chunks = [(q0, min(qc, cfg.Q - q0)) for q0 in range(0, cfg.Q, qc)]
-    perm = torch.empty(plan.permuted_shape(qc), dtype=torch.float16 if h16 else torch.float32,
-                       device=dev) if bi else None
+    perm = torch.empty(plan.permuted_shape(qc), dtype=plan.permuted_dtype(), device=dev) if bi else None
     per_event = perm.numel() // qc if bi else 0
     stream = torch.cuda.current_stream(dev)
 
@@ -222,8 +222,12 @@ def main():
     perm_avg = float(np.mean(perm_ms))
     flops_per_acc = 8 if cfg.iq else 4          # 2 FMA (real) or 8 FMA (complex) per accumulation
     achieved = accs * flops_per_acc / (kern_avg * 1e-3) / 1e12
-    kernel_name = ("das_bi_staged_kernel" if plan.info["staged"] else "das_batch_inner_kernel") if bi \
-        else ("das_baseline_f64_kernel" if args.wide else "das_baseline_kernel")
+    if plan.repack:
+        kernel_name = "das_repack_kernel"
+    elif bi:
+        kernel_name = "das_bi_staged_kernel" if plan.info["staged"] else "das_batch_inner_kernel"
+    else:
+        kernel_name = "das_baseline_f64_kernel" if args.wide else "das_baseline_kernel"
     peak = PEAK_FP64_TFLOPS if args.wide else PEAK_FP32_TFLOPS
     traffic = stored_traffic(kernel_name, cfg.name + ("-f16" if h16 else ""))
 

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DAS_ABI_VERSION 5
+#define DAS_ABI_VERSION 6
 
 typedef enum das_status {
     DAS_OK = 0,
@@ -78,14 +78,37 @@ enum { DAS_F32 = 0, DAS_C64 = 1, DAS_F64 = 2, DAS_C128 = 3 };
  *                       B >= 16 (a frame group fills a 16-lane row), else the
  *                       baseline.  das_plan_get_info reports the choice; a
  *                       batch-inner plan needs das_permute before das_beamform. */
-enum { DAS_ALG_DEFAULT = 0, DAS_ALG_BASELINE = 1, DAS_ALG_BATCH_INNER = 2, DAS_ALG_AUTO = 3 };
+/*  DAS_ALG_REPACK       the sparse interpolation repackaged into dense tile
+ *                       products on the matrix cores (the paper's tensor-core
+ *                       variant, Section 3 and Algorithm 3; the docs' ALG4):
+ *                       per group of 32 neighbouring voxels, transmit event
+ *                       and receiver, the 32 frames x 16 sample positions of
+ *                       the group's window times the 16 x 32 interpolation
+ *                       weights, one v_mfma_f32_32x32x16_f16 per 16
+ *                       positions.  Operands are binary16 halves: float32
+ *                       samples and all weights are split into hi + lo halves
+ *                       (three products, or two with DAS_STORE_F16 samples),
+ *                       so the result meets the float32 bar of the other
+ *                       kernels (relative error about 2^-21 per term), for
+ *                       |x| and |w_tx w_rx| below 65504 (the binary16 range).
+ *                       DAS_F32 with B a multiple of 32 and K <= 65535; reads
+ *                       the DAS_LAYOUT_QMBK buffer that das_permute makes for
+ *                       it (the problem's layout field is ignored).          */
+enum { DAS_ALG_DEFAULT = 0, DAS_ALG_BASELINE = 1, DAS_ALG_BATCH_INNER = 2, DAS_ALG_AUTO = 3, DAS_ALG_REPACK = 4 };
 
 /* Frames-innermost layout made by das_permute and read by the batch-inner
  * kernel, for a chunk of q_count transmit events:
  *  DAS_LAYOUT_KQMB  K x q_count x M x B  (the paper, Section 3 batch-inner)
  *  DAS_LAYOUT_QMKB  q_count x M x K x B  (the docs' ALG2 ordering: batch moved
  *                   innermost, the other axes kept in order)               */
-enum { DAS_LAYOUT_KQMB = 0, DAS_LAYOUT_QMKB = 1 };
+/*  DAS_LAYOUT_QMBK  q_count x M x B rows of ceil(K / 4) chunks of 4 sample
+ *                   positions (the repack algorithm's layout, chosen by the
+ *                   plan): per chunk, 4 halves hi then 4 halves lo of the
+ *                   float32 samples (16 bytes; hi = x rounded to the nearest
+ *                   half, ties to even, lo = x - hi rounded the same way), or
+ *                   with DAS_STORE_F16 the 4 samples rounded to halves (8
+ *                   bytes).  Positions past K hold zeros.                 */
+enum { DAS_LAYOUT_KQMB = 0, DAS_LAYOUT_QMKB = 1, DAS_LAYOUT_QMBK = 2 };
 
 /* Storage of the samples in the permuted buffer ("ffdas: volumetric
  * ultrasound reconstruction at warp speed", FP16 variant: samples kept in
@@ -99,8 +122,8 @@ enum { DAS_LAYOUT_KQMB = 0, DAS_LAYOUT_QMKB = 1 };
  *                    das_beamform widens every half exactly to float32 and
  *                    computes as for DAS_STORE_NATIVE.  So the result is the
  *                    float32 beamform of the rounded samples.  Batch-inner
- *                    DAS_F32 / DAS_C64 plans only (the conversion is part of
- *                    the permute).                                          */
+ *                    DAS_F32 / DAS_C64 and repack plans only (the conversion
+ *                    is part of the permute).                               */
 enum { DAS_STORE_NATIVE = 0, DAS_STORE_F16 = 1 };
 
 typedef struct das_problem {
@@ -127,8 +150,9 @@ typedef struct das_plan_info {
     int32_t layout;
     int32_t elem_bytes;         /* 4 (f32), 8 (c64, f64) or 16 (c128) per sample     */
     int32_t frames_per_lane;    /* batch-inner: frames one lane loads per vector load;
-                                   baseline: frames one lane accumulates             */
-    int32_t lanes_per_voxel;    /* batch-inner: 16; baseline: 1                      */
+                                   baseline: frames one lane accumulates;
+                                   repack: output frames one lane holds             */
+    int32_t lanes_per_voxel;    /* batch-inner: 16; baseline: 1; repack: 2           */
     int32_t voxels_per_group;   /* voxels one workgroup covers                       */
     int64_t N;                  /* nx * ny * nz                                      */
     int32_t staged;             /* batch-inner: 1 if frame rows are staged through LDS
@@ -147,7 +171,8 @@ typedef struct das_plan_info {
  * f_demod > 0, real ones f_demod == 0), DAS_F64 / DAS_C128 with
  * DAS_ALG_BATCH_INNER, DAS_STORE_F16 with a plan that does not resolve to
  * the batch-inner algorithm or with DAS_F64 / DAS_C128, or N, B*Q*M*K beyond
- * 2^31 elements per axis. */
+ * 2^31 elements per axis; DAS_ALG_REPACK with another dtype than DAS_F32, B
+ * not a multiple of 32, K above 65535 or Q N at or above 2^32. */
 das_status das_plan(const das_problem *problem, das_plan_t **out);
 
 void das_plan_destroy(das_plan_t *plan);
@@ -155,7 +180,9 @@ void das_plan_destroy(das_plan_t *plan);
 das_status das_plan_get_info(const das_plan_t *plan, das_plan_info *info);
 
 /* Bytes of the permuted buffer that holds q_count transmit events
- * (K * q_count * M * B * store_bytes, in either layout).  0 on a bad argument. */
+ * (K * q_count * M * B * store_bytes, in either batch-inner layout;
+ * q_count * M * B * ceil(K / 4) * 16, or * 8 with DAS_STORE_F16, for the
+ * repack layout).  0 on a bad argument. */
 size_t das_permuted_bytes(const das_plan_t *plan, int32_t q_count);
 
 /* Largest q_count one das_beamform call accepts with this plan: Q, except
@@ -183,8 +210,9 @@ das_status das_permute(const das_plan_t *plan, const void *rf_bqmk, void *rf_per
 
 /* Beamform transmit events [q_begin, q_begin + q_count) into out.
  *   rf       baseline: the B x Q x M x K input (all Q, indexed by absolute q);
- *            batch-inner: the permuted chunk made by das_permute with the same
- *            q_begin / q_count (binary16 samples with DAS_STORE_F16)
+ *            batch-inner and repack: the permuted chunk made by das_permute
+ *            with the same q_begin / q_count (binary16 samples with
+ *            DAS_STORE_F16)
  *   rx_pos   M x 3 float32 receiver positions (x, y, z), metres
  *   tau_tx   Q x N float32 transmit delays, seconds (absolute q)
  *   w_tx     Q x N float32 transmit weights (absolute q)

@@ -11,7 +11,8 @@ its definition ("ffdas: volumetric ultrasound reconstruction at warp speed",
 Section 3, batch-inner tiling: B x Q x M x K becomes K x Q x M x B; ffdas docs,
 "How It Works", ALG2: the batch index moves to the innermost position).
 ``to_binary16`` is the rounding of the binary16 storage variant (numpy's
-float16 conversion, pinned against hand-derived bit patterns).
+float16 conversion, pinned against hand-derived bit patterns);
+``split_binary16`` writes a float32 sample as a sum of two such halves.
 """
 from __future__ import annotations
 
@@ -156,6 +157,27 @@ def to_binary16(x: np.ndarray) -> np.ndarray:
         raise TypeError(f"binary16 storage rounds float32 samples, got {x.dtype}")
     with np.errstate(over="ignore"):
         return x.astype(np.float16).astype(np.float32)
+
+
+def split_binary16(x: np.ndarray) -> tuple:
+    """A float32 sample as the sum of two binary16 values, hi + lo.
+
+    The matrix-core (repack) variant multiplies binary16 operands ("ffdas:
+    volumetric ultrasound reconstruction at warp speed", Section 3,
+    tensor-core paragraphs: the products run on mixed-precision matrix
+    units), so float32 samples are held as a pair: hi is the sample rounded
+    to the nearest binary16 value (ties to even, ``to_binary16``), lo the
+    remainder x - hi (exact in float32) rounded the same way.  For samples in
+    the binary16 normal range, x - hi - lo is at most 2^-22 |x|.  Returns the
+    two arrays as float32 values.
+    """
+    x = np.asarray(x)
+    if x.dtype != np.float32:
+        raise TypeError(f"the split takes float32 samples, got {x.dtype}")
+    hi = to_binary16(x)
+    with np.errstate(invalid="ignore"):
+        rest = (x.astype(np.float64) - hi.astype(np.float64)).astype(np.float32)
+    return hi, to_binary16(rest)
 
 
 # Transmit-event kinds (the values of the library's enum, restated).

@@ -80,11 +80,10 @@ def run_gpu(inp: Inputs, algorithm: str, layout: str = "kqmb", q_chunk: int | No
         out = torch.full(plan.output_shape(), float("nan"), dtype=torch.float32, device=inp.rf_d.device)
     Q = inp.cfg.Q
     first_acc = accumulate_into is not None
-    if plan.batch_inner:
+    if plan.permuted_input:
         qc = min(Q if q_chunk is None else q_chunk, plan.max_q_chunk())
         assert qc >= 1
-        perm = torch.empty(plan.permuted_shape(qc), dtype=torch.float16 if plan.store_f16 else torch.float32,
-                           device=inp.rf_d.device)
+        perm = torch.empty(plan.permuted_shape(qc), dtype=plan.permuted_dtype(), device=inp.rf_d.device)
         for q0 in range(0, Q, qc):
             n = min(qc, Q - q0)
             view = perm.view(-1)[: perm.numel() // qc * n]

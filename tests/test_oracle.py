@@ -482,3 +482,62 @@ def test_binary16_storage_beamform(oracle_mod):
         bound = wsum * np.abs(d).max() * (2.0 if iq else 1.0)
         assert np.all(np.abs(y16 - y32) <= bound + 1e-12)
         assert np.abs(d).max() <= np.exp2(-11) * np.abs(x).max()
+
+
+# --------------------------------------------------------------------------
+# The binary16 pair of the matrix-core variant: x = hi + lo
+# --------------------------------------------------------------------------
+
+def _f32(v):
+    return np.array(v, dtype=np.float32)
+
+
+def test_split_binary16_hand_cases():
+    import oracle
+    # 1 + 2^-11 + 2^-20 lies just above the tie between 1 and 1 + 2^-10, so hi
+    # rounds up; the remainder -2^-11 + 2^-20 needs 10 significant bits: exact
+    x = _f32([1 + 2.0 ** -11 + 2.0 ** -20])
+    hi, lo = oracle.split_binary16(x)
+    assert hi[0] == 1 + 2.0 ** -10 and lo[0] == -2.0 ** -11 + 2.0 ** -20
+    # exactly on the tie: ties to even keeps 1, the remainder 2^-11 is a half
+    hi, lo = oracle.split_binary16(_f32([1 + 2.0 ** -11]))
+    assert hi[0] == 1.0 and lo[0] == 2.0 ** -11
+    # a half needs no remainder; zero stays zero; the sign is kept
+    hi, lo = oracle.split_binary16(_f32([0.5, -3.75, 0.0, 65504.0]))
+    np.testing.assert_array_equal(hi, _f32([0.5, -3.75, 0.0, 65504.0]))
+    np.testing.assert_array_equal(lo, _f32([0.0, 0.0, 0.0, 0.0]))
+    # 0.1: hi = 0x2e66 = 0.0999755859375, remainder 2.4414e-5 rounds to a half
+    hi, lo = oracle.split_binary16(_f32([0.1]))
+    assert hi[0] == np.float32(np.float16(0.1)) == 0.0999755859375
+    assert lo[0] == np.float32(np.float16(np.float32(0.1) - np.float32(0.0999755859375)))
+    # a remainder below the normal range is a subnormal half (absolute step 2^-24)
+    hi, lo = oracle.split_binary16(_f32([2.0 ** -4 + 2.0 ** -20]))
+    assert hi[0] == 2.0 ** -4 and lo[0] == 2.0 ** -20
+
+
+def test_split_binary16_error_bound_and_halves():
+    import oracle
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal(20000) * np.exp2(rng.uniform(-2, 14, 20000))).astype(np.float32)
+    x = x[np.abs(x) < 65000]
+    hi, lo = oracle.split_binary16(x)
+    # both parts are binary16 values
+    np.testing.assert_array_equal(hi.astype(np.float16).astype(np.float32), hi)
+    np.testing.assert_array_equal(lo.astype(np.float16).astype(np.float32), lo)
+    # hi is the nearest half; the pair is within 2^-22 |x| in the normal range
+    err = np.abs(x.astype(np.float64) - hi - lo)
+    assert np.all(err <= 2.0 ** -22 * np.abs(x.astype(np.float64)) + 2.0 ** -25)
+    assert np.all(np.abs(x.astype(np.float64) - hi) <= 2.0 ** -11 * np.abs(x.astype(np.float64)))
+    # values of at most 22 significant bits split exactly while the remainder's
+    # lowest bit is still a binary16 step (|x| >= 2^-3)
+    m = rng.integers(2 ** 21, 2 ** 22, 5000)
+    e = rng.integers(-3, 5, 5000)
+    y = (m.astype(np.float64) * np.exp2(e - 21)).astype(np.float32)
+    hy, ly = oracle.split_binary16(y)
+    np.testing.assert_array_equal(hy.astype(np.float64) + ly.astype(np.float64), y.astype(np.float64))
+
+
+def test_split_binary16_takes_float32_only():
+    import oracle
+    with pytest.raises(TypeError):
+        oracle.split_binary16(np.zeros(3, dtype=np.float64))

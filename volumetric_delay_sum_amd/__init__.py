@@ -15,6 +15,11 @@ linearly interpolated at the delay tau_tx[q,n] + |r_n - p_m| / c.
 paper's FP16 variant; the docs' ``half`` / ``half2``): permuted buffers are then
 torch.float16 tensors, rounded by ``permute`` and widened to fp32 by
 ``beamform``.
+
+``Plan(..., algorithm="repack")`` runs the matrix-core variant (the paper's
+tensor-core repackaging; the docs' ALG4).  Its permuted buffer is a
+torch.float16 tensor of shape (q, M, B, ceil(K / 4), 8) (hi and lo halves of
+float32 samples) or (q, M, B, ceil(K / 4), 4) with ``storage="f16"``.
 """
 from __future__ import annotations
 
@@ -23,20 +28,20 @@ import os
 from typing import Optional, Sequence
 
 __all__ = [
-    "F32", "C64", "F64", "C128", "ALG_DEFAULT", "ALG_BASELINE", "ALG_BATCH_INNER", "ALG_AUTO",
-    "LAYOUT_KQMB", "LAYOUT_QMKB", "STORE_NATIVE", "STORE_F16",
+    "F32", "C64", "F64", "C128", "ALG_DEFAULT", "ALG_BASELINE", "ALG_BATCH_INNER", "ALG_AUTO", "ALG_REPACK",
+    "LAYOUT_KQMB", "LAYOUT_QMKB", "LAYOUT_QMBK", "STORE_NATIVE", "STORE_F16",
     "TX_PLANE", "TX_DIVERGING", "DasError", "Plan", "load_library", "library_path", "plan_from_fields",
 ]
 
 F32, C64, F64, C128 = 0, 1, 2, 3
-ALG_DEFAULT, ALG_BASELINE, ALG_BATCH_INNER, ALG_AUTO = 0, 1, 2, 3
-LAYOUT_KQMB, LAYOUT_QMKB = 0, 1
+ALG_DEFAULT, ALG_BASELINE, ALG_BATCH_INNER, ALG_AUTO, ALG_REPACK = 0, 1, 2, 3, 4
+LAYOUT_KQMB, LAYOUT_QMKB, LAYOUT_QMBK = 0, 1, 2
 STORE_NATIVE, STORE_F16 = 0, 1
 TX_PLANE, TX_DIVERGING = 0, 1
 
 _ALG = {"default": ALG_DEFAULT, "baseline": ALG_BASELINE, "batch_inner": ALG_BATCH_INNER,
-        "bl": ALG_BASELINE, "bi": ALG_BATCH_INNER, "auto": ALG_AUTO}
-_LAYOUT = {"kqmb": LAYOUT_KQMB, "qmkb": LAYOUT_QMKB}
+        "bl": ALG_BASELINE, "bi": ALG_BATCH_INNER, "auto": ALG_AUTO, "repack": ALG_REPACK, "tc": ALG_REPACK}
+_LAYOUT = {"kqmb": LAYOUT_KQMB, "qmkb": LAYOUT_QMKB, "qmbk": LAYOUT_QMBK}
 _DTYPE = {"f32": F32, "c64": C64, "f64": F64, "c128": C128}
 _STORAGE = {"native": STORE_NATIVE, "f16": STORE_F16}
 
@@ -187,6 +192,20 @@ class Plan:
     def batch_inner(self) -> bool:
         return self.info["algorithm"] == ALG_BATCH_INNER
 
+    @property
+    def repack(self) -> bool:
+        return self.info["algorithm"] == ALG_REPACK
+
+    @property
+    def permuted_input(self) -> bool:
+        """beamform reads the buffer made by permute (batch-inner and repack)."""
+        return self.batch_inner or self.repack
+
+    def permuted_dtype(self):
+        """torch dtype of the permuted buffer."""
+        import torch
+        return torch.float16 if (self.store_f16 or self.repack) else torch.float32
+
     def permuted_bytes(self, q_count: Optional[int] = None) -> int:
         return int(self._lib.das_permuted_bytes(self._h, self.problem.Q if q_count is None else int(q_count)))
 
@@ -197,8 +216,17 @@ class Plan:
     def permuted_shape(self, q_count: Optional[int] = None) -> tuple:
         p = self.problem
         qc = p.Q if q_count is None else int(q_count)
+        if self.repack:
+            return (qc, p.M, p.B, (p.K + 3) // 4, 4 if self.store_f16 else 8)
         shape = (p.K, qc, p.M, p.B) if p.layout == LAYOUT_KQMB else (qc, p.M, p.K, p.B)
         return shape + ((2,) if self.iq else ())
+
+    def _permuted_numel(self, q_count: int) -> int:
+        """Elements of the permuted tensor of q_count events (halves for repack)."""
+        n = 1
+        for d in self.permuted_shape(max(q_count, 1)):
+            n *= d
+        return n if q_count >= 1 else 0
 
     def output_shape(self) -> tuple:
         return (self.problem.B, self.N) + ((2,) if self.iq else ())
@@ -212,7 +240,7 @@ class Plan:
             raise TypeError(f"{name} must be a CUDA tensor")
         if t.dtype in (torch.complex64, torch.complex128, torch.complex32):
             t = torch.view_as_real(t)
-        if permuted and self.store_f16:
+        if permuted and (self.store_f16 or self.repack):
             want = torch.float16
         else:
             want = torch.float64 if (samples and self.wide) else torch.float32
@@ -235,7 +263,7 @@ class Plan:
         q_begin, q_count = self._q_range(q_begin, q_count)
         c = 2 if self.iq else 1
         rf = self._tensor(rf, p.B * p.Q * p.M * p.K * c, "rf", samples=True)
-        out = self._tensor(out, p.K * max(q_count, 0) * p.M * p.B * c, "out", samples=True, permuted=True)
+        out = self._tensor(out, self._permuted_numel(q_count), "out", samples=True, permuted=True)
         _check(self._lib.das_permute(self._h, rf.data_ptr(), out.data_ptr(), q_begin, q_count,
                                      _stream_handle(stream, rf.device)), "das_permute")
         return out
@@ -246,8 +274,8 @@ class Plan:
         p = self.problem
         q_begin, q_count = self._q_range(q_begin, q_count)
         c = 2 if self.iq else 1
-        rf_numel = (p.K * max(q_count, 0) * p.M * p.B if self.batch_inner else p.B * p.Q * p.M * p.K) * c
-        rf = self._tensor(rf, rf_numel, "rf", samples=True, permuted=self.batch_inner)
+        rf_numel = self._permuted_numel(q_count) if self.permuted_input else p.B * p.Q * p.M * p.K * c
+        rf = self._tensor(rf, rf_numel, "rf", samples=True, permuted=self.permuted_input)
         rx_pos = self._tensor(rx_pos, 3 * p.M, "rx_pos")
         tau_tx = self._tensor(tau_tx, p.Q * self.N, "tau_tx")
         w_tx = self._tensor(w_tx, p.Q * self.N, "w_tx")
@@ -270,7 +298,7 @@ class Plan:
         tau_tx = self._tensor(tau_tx, p.Q * self.N, "tau_tx")
         w_tx = self._tensor(w_tx, p.Q * self.N, "w_tx")
         out = self._tensor(out, p.B * self.N * c, "out", samples=True)
-        chunk = p.K * max(q_chunk, 0) * p.M * p.B * c
+        chunk = self._permuted_numel(q_chunk)
         perm_a = self._tensor(perm_a, chunk, "perm_a", samples=True, permuted=True)
         perm_b = self._tensor(perm_b, chunk, "perm_b", samples=True, permuted=True)
         _check(self._lib.das_beamform_streamed(self._h, rf.data_ptr(), rx_pos.data_ptr(), tau_tx.data_ptr(),

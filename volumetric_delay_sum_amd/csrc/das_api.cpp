@@ -198,8 +198,8 @@ DasKParams make_params(const das_plan_t &pl, int32_t q_begin, int32_t q_count, i
 // 16-lane row (B >= 16) and exist for fp32 and complex64 samples; anything
 // else runs the baseline.  DEFAULT is the baseline, as the docs dispatch it.
 int32_t resolve_algorithm(const das_problem &p) {
-    if (p.algorithm == DAS_ALG_BATCH_INNER)
-        return DAS_ALG_BATCH_INNER;
+    if (p.algorithm == DAS_ALG_BATCH_INNER || p.algorithm == DAS_ALG_REPACK)
+        return p.algorithm;
     if (p.algorithm == DAS_ALG_AUTO && (p.dtype == DAS_F32 || p.dtype == DAS_C64) && p.B >= 16)
         return DAS_ALG_BATCH_INNER;
     return DAS_ALG_BASELINE;
@@ -214,6 +214,11 @@ bool kqmb_chunk_fits(const das_plan_t *plan, int64_t q_count) {
     const uint64_t row = (uint64_t)p.B * plan->store_bytes;
     const uint64_t chunk = (uint64_t)p.K * q_count * p.M * row;
     return chunk + 16ull * row <= (uint64_t)UINT32_MAX;
+}
+
+// Algorithms that read a permuted buffer made by das_permute.
+bool permuted_alg(const das_plan_t *plan) {
+    return plan->alg == DAS_ALG_BATCH_INNER || plan->alg == DAS_ALG_REPACK;
 }
 
 int32_t max_q_chunk(const das_plan_t *plan) {
@@ -266,9 +271,9 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
     if (p.dtype != DAS_F32 && p.dtype != DAS_C64 && p.dtype != DAS_F64 && p.dtype != DAS_C128)
         return DAS_ERR_INVALID_ARGUMENT;
     if (p.algorithm != DAS_ALG_DEFAULT && p.algorithm != DAS_ALG_BASELINE && p.algorithm != DAS_ALG_BATCH_INNER &&
-        p.algorithm != DAS_ALG_AUTO)
+        p.algorithm != DAS_ALG_AUTO && p.algorithm != DAS_ALG_REPACK)
         return DAS_ERR_INVALID_ARGUMENT;
-    if (p.layout != DAS_LAYOUT_KQMB && p.layout != DAS_LAYOUT_QMKB)
+    if (p.layout != DAS_LAYOUT_KQMB && p.layout != DAS_LAYOUT_QMKB && p.layout != DAS_LAYOUT_QMBK)
         return DAS_ERR_INVALID_ARGUMENT;
     if (p.storage != DAS_STORE_NATIVE && p.storage != DAS_STORE_F16)
         return DAS_ERR_INVALID_ARGUMENT;
@@ -286,11 +291,21 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
         return DAS_ERR_UNSUPPORTED;
     if (wide && p.algorithm == DAS_ALG_BATCH_INNER)
         return DAS_ERR_UNSUPPORTED;
-    // binary16 storage is made by the permute, so only batch-inner plans have it
+    // binary16 storage is made by the permute, so only plans with a permute have it
     const bool h16 = p.storage == DAS_STORE_F16;
-    if (h16 && (wide || resolve_algorithm(p) != DAS_ALG_BATCH_INNER))
+    const int32_t alg = resolve_algorithm(p);
+    if (h16 && (wide || (alg != DAS_ALG_BATCH_INNER && alg != DAS_ALG_REPACK)))
         return DAS_ERR_UNSUPPORTED;
     const int64_t N = (int64_t)p.nx * p.ny * p.nz;
+    // repack: 32-frame tiles, 16-bit sample indices in the window reduction,
+    // 32-bit element offsets into the transmit tables and one (event,
+    // receiver) plane of rows
+    if (alg == DAS_ALG_REPACK &&
+        (p.dtype != DAS_F32 || p.B % 32 != 0 || p.K > 65535 || (int64_t)p.Q * N >= ((int64_t)1 << 32) ||
+         (int64_t)p.B * ((p.K + 3) / 4) * 16 >= ((int64_t)1 << 31)))
+        return DAS_ERR_UNSUPPORTED;
+    if (p.layout == DAS_LAYOUT_QMBK && alg != DAS_ALG_REPACK)
+        return DAS_ERR_INVALID_ARGUMENT;
     const int32_t elem = (cplx ? 2 : 1) * (wide ? 8 : 4);
     if (N > INT32_MAX)
         return DAS_ERR_UNSUPPORTED;
@@ -305,8 +320,10 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
     if (!pl)
         return DAS_ERR_INVALID_ARGUMENT;
     pl->p = p;
+    if (alg == DAS_ALG_REPACK)
+        pl->p.layout = DAS_LAYOUT_QMBK;
     pl->N = N;
-    pl->alg = resolve_algorithm(p);
+    pl->alg = alg;
     pl->elem_bytes = elem;
     pl->h16 = h16 ? 1 : 0;
     pl->store_bytes = h16 ? elem / 2 : elem;
@@ -364,11 +381,12 @@ das_status das_plan_get_info(const das_plan_t *plan, das_plan_info *info) {
     info->layout = plan->p.layout;
     info->elem_bytes = plan->elem_bytes;
     const bool bi = plan->alg == DAS_ALG_BATCH_INNER;
-    info->frames_per_lane = bi ? plan->fl : plan->bt;
-    info->lanes_per_voxel = bi ? 16 : 1;
-    info->voxels_per_group = bi ? 16 : 256;
+    const bool rp = plan->alg == DAS_ALG_REPACK;
+    info->frames_per_lane = rp ? (plan->p.B % 64 == 0 ? 32 : 16) : (bi ? plan->fl : plan->bt);
+    info->lanes_per_voxel = rp ? 2 : (bi ? 16 : 1);
+    info->voxels_per_group = rp ? 256 : (bi ? 16 : 256);
     info->N = plan->N;
-    info->staged = plan->staged;
+    info->staged = rp ? 1 : plan->staged;
     info->store_bytes = plan->store_bytes;
     return DAS_OK;
 }
@@ -379,6 +397,8 @@ size_t das_permuted_bytes(const das_plan_t *plan, int32_t q_count) {
     if (!valid_plan(plan) || q_count < 1 || q_count > plan->p.Q)
         return 0;
     const das_problem &p = plan->p;
+    if (plan->alg == DAS_ALG_REPACK)
+        return (size_t)q_count * (size_t)p.M * (size_t)p.B * (size_t)das_repack_row_bytes(*plan);
     return (size_t)p.K * (size_t)q_count * (size_t)p.M * (size_t)p.B * (size_t)plan->store_bytes;
 }
 
@@ -395,8 +415,11 @@ das_status das_permute(const das_plan_t *plan, const void *rf_bqmk, void *rf_per
     das_status st = check_device();
     if (st != DAS_OK)
         return st;
-    hipError_t e = das_launch_permute(*plan, rf_bqmk, rf_perm, q_begin, q_count,
-                                      static_cast<hipStream_t>(hip_stream));
+    hipError_t e = plan->alg == DAS_ALG_REPACK
+                       ? das_launch_permute_repack(*plan, rf_bqmk, rf_perm, q_begin, q_count,
+                                                   static_cast<hipStream_t>(hip_stream))
+                       : das_launch_permute(*plan, rf_bqmk, rf_perm, q_begin, q_count,
+                                            static_cast<hipStream_t>(hip_stream));
     return e == hipSuccess ? DAS_OK : DAS_ERR_LAUNCH;
 }
 
@@ -421,7 +444,9 @@ das_status das_beamform(const das_plan_t *plan, const void *rf, const float *rx_
     const float *rff = static_cast<const float *>(rf);
     float *o = static_cast<float *>(out);
     hipError_t e;
-    if (plan->alg == DAS_ALG_BATCH_INNER) {
+    if (plan->alg == DAS_ALG_REPACK)
+        e = das_launch_repack(*plan, kp, rf, rx_pos, tau_tx, w_tx, o, s);
+    else if (plan->alg == DAS_ALG_BATCH_INNER) {
         // the staged kernel addresses a KQMB chunk and the transmit tables with
         // 32-bit offsets (a QMKB chunk is rebased per step); larger ones go to
         // the direct kernel
@@ -448,7 +473,7 @@ das_status das_beamform_streamed(const das_plan_t *plan, const void *rf_bqmk, co
         return DAS_ERR_INVALID_ARGUMENT;
     if (perm_a == perm_b || q_chunk < 1 || (accumulate != 0 && accumulate != 1))
         return DAS_ERR_INVALID_ARGUMENT;
-    if (plan->alg != DAS_ALG_BATCH_INNER || q_chunk > max_q_chunk(plan))
+    if (!permuted_alg(plan) || q_chunk > max_q_chunk(plan))
         return DAS_ERR_UNSUPPORTED;
     if (!aligned16(rf_bqmk) || !aligned16(rx_pos) || !aligned16(tau_tx) || !aligned16(w_tx) || !aligned16(out) ||
         !aligned16(perm_a) || !aligned16(perm_b))
