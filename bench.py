@@ -2,14 +2,16 @@
 """Throughput of volumetric delay-and-sum on one MI355X.
 
 One step is one pass of the whole hot path over one volume of the workload:
-das_permute (B x Q x M x K -> frames-innermost layout) followed by
-das_beamform with the batch-inner kernel, inputs already resident in HBM.
+das_permute (B x Q x M x K -> the kernel's permuted layout) followed by
+das_beamform, inputs already resident in HBM.
 
 Prints ONE JSON line.  `value` is accumulations (voxels x receivers x
-transmit events x frames) per second of whole steps; the roofline object
-describes the beamform kernel, timed with HIP events on the stream it runs on;
-cpu_baseline times the fp64 oracle on one depth slab of the same volume on the
-host.
+transmit events x frames) per second of whole steps (permute + beamform);
+`kernel_value` is the same count per second of beamform kernel time alone.
+The roofline object describes the beamform kernel, timed with HIP events on
+the stream it runs on, against its arithmetic roofline, with the on-chip
+delivery ceiling beside it; cpu_baseline times the fp64 oracle on bounded
+slabs of the same volume on the host, single-threaded and on P threads.
 """
 from __future__ import annotations
 
@@ -27,7 +29,17 @@ sys.path.insert(0, ROOT)
 
 PEAK_FP32_TFLOPS = 157.3        # MI355X vector fp32 (published)
 PEAK_FP64_TFLOPS = 78.6         # MI355X vector fp64 (published)
+PEAK_F16_MFMA_TFLOPS = 2500.0   # MI355X dense fp16 matrix (published)
 PEAK_HBM_GBS = 8000.0
+CUS, SCLK_HZ = 256, 2.4e9
+
+# LDS bytes per clock per CU that gfx950 serves for the read pattern of each
+# staged kernel instance, measured on the box with a microbenchmark (one
+# 1024-thread workgroup per CU on all CUs, random rows, wall-clock time)
+LDS_BCLK = {
+    "two ds_read_b64 (8-byte lanes)": 160.0,
+    "two ds_read_b128 (16-byte lanes, split rows)": 219.0,
+}
 
 
 _COMMENT = re.compile(r"/\*.*?\*/|//[^\n]*", re.S)
@@ -60,6 +72,65 @@ def stored_traffic(kernel: str, workload: str):
     return None
 
 
+def delivery_ceiling(plan, iq: bool, h16: bool):
+    """On-chip delivery roofline of the LDS-staged batch-inner kernel: every
+    accumulation (voxel, receiver, event, frame) needs its two samples in
+    registers, so the LDS's bytes per clock bound the accumulation rate at
+    CUS * sclk * (B/clk/CU) / (bytes per accumulation)."""
+    if not plan.batch_inner or not plan.info["staged"]:
+        return None
+    sample = (8 if iq else 4) // (2 if h16 else 1)        # bytes of one stored sample
+    lane = sample * plan.info["frames_per_lane"]           # bytes of one lane's tap
+    pattern = ("two ds_read_b128 (16-byte lanes, split rows)" if lane == 16
+               else "two ds_read_b64 (8-byte lanes)" if lane == 8 else None)
+    if pattern is None:
+        return {"bytes_per_accumulation": 2 * sample, "lane_tap_bytes": lane, "lds_B_per_clk_per_cu": None,
+                "ceiling_gacc_s": None}
+    bclk = LDS_BCLK[pattern]
+    return {"bytes_per_accumulation": 2 * sample, "lane_tap_bytes": lane, "read_pattern": pattern,
+            "lds_B_per_clk_per_cu": bclk, "ceiling_gacc_s": CUS * SCLK_HZ * bclk / (2 * sample) / 1e9}
+
+
+def stored_counter(kernel: str, workload: str, name: str):
+    """A per-launch counter value from the committed summary, if it matches these sources."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{kernel}:{workload}")
+        if rec and rec.get("source_hash") == kernel_source_hash():
+            return rec.get(name)
+    except Exception:
+        return None
+    return None
+
+
+def oracle_rates(oracle, fields, cfg, rf_host, rx, tau, w, cap: int, threads: int):
+    """The unmodified single-threaded oracle timed on the host: one depth slab
+    prefix (1 thread), then `threads` threads on disjoint slabs of the same
+    volume at once (the oracle releases the interpreter while it runs).
+    Returns (voxels of the one-thread sample, its result, seconds, P-thread
+    accumulations, P-thread seconds)."""
+    import concurrent.futures as cf
+    import numpy as np
+    nx, ny, nz = cfg.grid
+    per_vox = cfg.M * cfg.Q * cfg.B
+    iz = nz // 2
+    vox = np.arange(iz * nx * ny, (iz + 1) * nx * ny, dtype=np.int64)[:cap]
+    t1 = time.perf_counter()
+    ref = oracle.das_sum(fields, rf_host, rx, tau, w, voxels=vox)
+    one_s = time.perf_counter() - t1
+    # P threads, each a sample half as large, on other depth slabs
+    share = max(1, cap // 2)
+    slabs = [(iz + 1 + t) % nz for t in range(threads)]
+    chunks = [np.arange(z * nx * ny, (z + 1) * nx * ny, dtype=np.int64)[:share] for z in slabs]
+    t1 = time.perf_counter()
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(lambda v: oracle.das_sum(fields, rf_host, rx, tau, w, voxels=v), chunks))
+    multi_s = time.perf_counter() - t1
+    return vox, ref, one_s, sum(c.size for c in chunks) * per_vox, multi_s
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,6 +153,9 @@ def main():
                          "(batch-inner; the arithmetic stays fp32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-voxels", type=int, default=0, help="oracle sample size (0: one depth slab)")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the multi-core oracle rate (0: the host's cores available to this process, "
+                         "at most 16)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -220,7 +294,7 @@ def main():
     kern_avg = float(np.mean(kern_ms))              # beamform time per step (all chunks)
     launch_avg = float(np.mean(launch_ms))          # per beamform launch
     perm_avg = float(np.mean(perm_ms))
-    flops_per_acc = 8 if cfg.iq else 4          # 2 FMA (real) or 8 FMA (complex) per accumulation
+    flops_per_acc = 16 if cfg.iq else 4         # 2 FMA (real) or 8 FMA (complex) per accumulation
     achieved = accs * flops_per_acc / (kern_avg * 1e-3) / 1e12
     if plan.repack:
         kernel_name = "das_repack_kernel"
@@ -230,24 +304,39 @@ def main():
         kernel_name = "das_baseline_f64_kernel" if args.wide else "das_baseline_kernel"
     peak = PEAK_FP64_TFLOPS if args.wide else PEAK_FP32_TFLOPS
     traffic = stored_traffic(kernel_name, cfg.name + ("-f16" if h16 else ""))
+    # which roof binds: the algorithmic bytes of one launch (its samples, its
+    # events' tables, the output read and written) at 8 TB/s against its flops
+    # at the vector peak; then the same with the HBM bytes the counters saw
+    q_l = chunks[0][1]
+    in_bytes = (perm.numel() * perm.element_size() * q_l // qc) if bi else rf.numel() * rf.element_size() * q_l // cfg.Q
+    out_bytes = out.numel() * out.element_size()
+    alg_bytes = in_bytes + 8 * q_l * cfg.N + 2 * out_bytes
+    launch_flops = accs * flops_per_acc * q_l / cfg.Q
+    t_hbm, t_alu = alg_bytes / (PEAK_HBM_GBS * 1e9), launch_flops / (peak * 1e12)
+    hbm_frac_measured = traffic / (launch_avg * 1e-3) / (PEAK_HBM_GBS * 1e9) if traffic else None
+    bound = "hbm" if (t_hbm > t_alu or (hbm_frac_measured or 0.0) > achieved / peak) else "alu"
+    bound_basis = {"algorithmic_bytes_per_launch": alg_bytes, "hbm_time_ms_at_peak": t_hbm * 1e3,
+                   "alu_time_ms_at_peak": t_alu * 1e3,
+                   "hbm_frac_from_counters": hbm_frac_measured,
+                   "rule": "hbm if the launch's algorithmic bytes at 8 TB/s take longer than its flops at the "
+                           "vector peak, or if the counted HBM bytes per launch time exceed the ALU fraction; "
+                           "else alu"}
 
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         oracle.build(force=False)
         nx, ny, nz = cfg.grid
-        iz = nz // 2
-        vox = np.arange(iz * nx * ny, (iz + 1) * nx * ny, dtype=np.int64)
-        # a bounded sample: about 1.2e9 accumulations (some 25 s single-threaded) unless asked otherwise
-        cap = args.cpu_voxels or max(1, int(1.25e9 // (cfg.M * cfg.Q * cfg.B)))
-        vox = vox[:cap]
-        print(f"[bench] cpu baseline: oracle on {vox.size} voxels", file=sys.stderr, flush=True)
+        # bounded samples: about 8e8 accumulations single-threaded (some 17 s on the host), then half
+        # that on each of P threads, unless asked otherwise
+        cap = args.cpu_voxels or max(1, int(8e8 // (cfg.M * cfg.Q * cfg.B)))
+        threads = args.cpu_threads or min(16, len(os.sched_getaffinity(0)))
+        print(f"[bench] cpu baseline: oracle on {min(cap, nx * ny)} voxels, then {threads} threads",
+              file=sys.stderr, flush=True)
         rf_host = rf.cpu().numpy()
         if h16:
             rf_host = oracle.to_binary16(rf_host)      # the samples the kernel reads
-        t1 = time.perf_counter()
-        ref = oracle.das_sum(fields, rf_host, rx, tau, w, voxels=vox)
-        cpu_s = time.perf_counter() - t1
+        vox, ref, cpu_s, multi_acc, multi_s = oracle_rates(oracle, fields, cfg, rf_host, rx, tau, w, cap, threads)
         cpu_acc = vox.size * cfg.M * cfg.Q * cfg.B
         y = out.cpu().numpy().astype(np.float64)
         y = (y[..., 0] + 1j * y[..., 1]) if cfg.iq else y
@@ -255,13 +344,24 @@ def main():
         comps = [(y.real, ref.real), (y.imag, ref.imag)] if cfg.iq else [(y, ref)]
         parity = [(float(np.abs(g - r).max() / np.abs(r).max()), float(np.linalg.norm(g - r) / np.linalg.norm(r)))
                   for g, r in comps]
-        cpu = {"value": cpu_acc / cpu_s / 1e9, "unit": "G acc/s", "cores": 1, "kind": "oracle",
-               "sample": f"{cfg.name}: depth slab iz={iz} ({vox.size} voxels) x all {cfg.Q} events x "
-                         f"{cfg.M} receivers x {cfg.B} frames = {cpu_acc:.3e} accumulations in {cpu_s:.1f} s, "
-                         "single-threaded fp64 C oracle" + (" of the binary16-rounded samples" if h16 else ""),
+        iz = nz // 2
+        cpu = {"value": multi_acc / multi_s / 1e9, "unit": "G acc/s", "cores": threads, "kind": "oracle",
+               "sample": f"{cfg.name}: {threads} threads, each the single-threaded fp64 C oracle on its own depth "
+                         f"slab ({max(1, cap // 2)} voxels x all {cfg.Q} events x {cfg.M} receivers x {cfg.B} "
+                         f"frames), {multi_acc:.3e} accumulations in {multi_s:.1f} s"
+                         + (" of the binary16-rounded samples" if h16 else ""),
+               "one_core": {"value": cpu_acc / cpu_s / 1e9, "cores": 1,
+                            "sample": f"depth slab iz={iz} ({vox.size} voxels), {cpu_acc:.3e} accumulations "
+                                      f"in {cpu_s:.1f} s"},
                "gpu_parity_on_sample": {"max_rel": max(p[0] for p in parity), "l2_rel": max(p[1] for p in parity)}}
 
     info = plan.info
+    delivery = delivery_ceiling(plan, cfg.iq, h16) if not args.wide else None
+    if delivery and delivery.get("ceiling_gacc_s"):
+        kg = accs / (kern_avg * 1e-3) / 1e9
+        delivery["achieved_gacc_s"] = kg
+        delivery["frac"] = kg / delivery["ceiling_gacc_s"]
+        delivery["alu_ceiling_gacc_s"] = peak * 1e12 / flops_per_acc / 1e9
     rec = {
         "metric": "G voxel·receiver·transmit·frame accumulations/s (fp32), % of bounding roofline",
         "value": value,
@@ -289,8 +389,10 @@ def main():
             "storage": ("binary16 samples in the permuted buffer (rounded by the permute, widened to fp32 "
                         "in the kernel)") if h16 else "samples as given",
         },
+        "value_basis": "whole steps (permute + beamform) per second of wall time, inputs resident in HBM",
+        "kernel_value": accs / (kern_avg * 1e-3) / 1e9,
         "roofline": {
-            "bound": "alu",
+            "bound": bound,
             "achieved": achieved,
             "peak": peak,
             "unit": "TFLOP/s",
@@ -302,6 +404,8 @@ def main():
             "launches_per_step": len(chunks),
             "kernel_gacc_s": accs / (kern_avg * 1e-3) / 1e9,
             "flops_per_accumulation": flops_per_acc,
+            "bound_basis": bound_basis,
+            "delivery": delivery,
         },
         "permute_ms": perm_avg if bi else None,
         "tx_tables": tx_tables,

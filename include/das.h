@@ -92,7 +92,7 @@ enum { DAS_F32 = 0, DAS_C64 = 1, DAS_F64 = 2, DAS_C128 = 3 };
  *                       kernels (relative error about 2^-21 per term), for
  *                       |x| and |w_tx w_rx| below 65504 (the binary16 range).
  *                       DAS_F32 with B a multiple of 32 and K <= 65535; reads
- *                       the DAS_LAYOUT_QMBK buffer that das_permute makes for
+ *                       the DAS_LAYOUT_QMPB buffer that das_permute makes for
  *                       it (the problem's layout field is ignored).          */
 enum { DAS_ALG_DEFAULT = 0, DAS_ALG_BASELINE = 1, DAS_ALG_BATCH_INNER = 2, DAS_ALG_AUTO = 3, DAS_ALG_REPACK = 4 };
 
@@ -101,14 +101,15 @@ enum { DAS_ALG_DEFAULT = 0, DAS_ALG_BASELINE = 1, DAS_ALG_BATCH_INNER = 2, DAS_A
  *  DAS_LAYOUT_KQMB  K x q_count x M x B  (the paper, Section 3 batch-inner)
  *  DAS_LAYOUT_QMKB  q_count x M x K x B  (the docs' ALG2 ordering: batch moved
  *                   innermost, the other axes kept in order)               */
-/*  DAS_LAYOUT_QMBK  q_count x M x B rows of ceil(K / 4) chunks of 4 sample
- *                   positions (the repack algorithm's layout, chosen by the
- *                   plan): per chunk, 4 halves hi then 4 halves lo of the
- *                   float32 samples (16 bytes; hi = x rounded to the nearest
- *                   half, ties to even, lo = x - hi rounded the same way), or
- *                   with DAS_STORE_F16 the 4 samples rounded to halves (8
- *                   bytes).  Positions past K hold zeros.                 */
-enum { DAS_LAYOUT_KQMB = 0, DAS_LAYOUT_QMKB = 1, DAS_LAYOUT_QMBK = 2 };
+/*  DAS_LAYOUT_QMPB  q_count x M x planes x P x B x 8 halves (the repack
+ *                   algorithm's layout, chosen by the plan): per (event,
+ *                   receiver) a plane of halves hi and, for float32 samples,
+ *                   a plane lo; a plane holds P = ceil(K / 8) pieces of 8
+ *                   sample positions, a piece the B frames' 8 halves side by
+ *                   side.  hi = x rounded to the nearest half (ties to even),
+ *                   lo = x - hi rounded the same way; with DAS_STORE_F16 the
+ *                   plane hi alone.  Positions past K hold zeros.          */
+enum { DAS_LAYOUT_KQMB = 0, DAS_LAYOUT_QMKB = 1, DAS_LAYOUT_QMPB = 2 };
 
 /* Storage of the samples in the permuted buffer ("ffdas: volumetric
  * ultrasound reconstruction at warp speed", FP16 variant: samples kept in
@@ -181,8 +182,8 @@ das_status das_plan_get_info(const das_plan_t *plan, das_plan_info *info);
 
 /* Bytes of the permuted buffer that holds q_count transmit events
  * (K * q_count * M * B * store_bytes, in either batch-inner layout;
- * q_count * M * B * ceil(K / 4) * 16, or * 8 with DAS_STORE_F16, for the
- * repack layout).  0 on a bad argument. */
+ * q_count * M * ceil(K / 8) * B * 32, or * 16 with DAS_STORE_F16, for
+ * the repack layout).  0 on a bad argument. */
 size_t das_permuted_bytes(const das_plan_t *plan, int32_t q_count);
 
 /* Largest q_count one das_beamform call accepts with this plan: Q, except

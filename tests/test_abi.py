@@ -423,24 +423,24 @@ def test_repack_plan_limits():
     assert _status(algorithm="repack", B=32, K=65536) == UNSUPPORTED          # 16-bit window indices
     assert _status(algorithm="repack", B=32, Q=2, nx=2048, ny=1024, nz=1024) == UNSUPPORTED   # Q N >= 2^32
     # its layout belongs to it alone
-    assert _status(algorithm="batch_inner", B=32, layout="qmbk") == INVALID
-    assert _status(algorithm="repack", B=32, layout="qmkb") == OK             # ignored: the plan picks QMBK
+    assert _status(algorithm="batch_inner", B=32, layout="qmpb") == INVALID
+    assert _status(algorithm="repack", B=32, layout="qmkb") == OK             # ignored: the plan picks QMPB
 
 
-@pytest.mark.parametrize("storage,B,K,chunk", [("native", 32, 64, 16), ("native", 64, 66, 16),
-                                               ("f16", 32, 64, 8), ("f16", 96, 70, 8)])
-def test_repack_plan_info_and_sizes(storage, B, K, chunk):
+@pytest.mark.parametrize("storage,B,K,planes", [("native", 32, 64, 2), ("native", 64, 66, 2),
+                                                ("f16", 32, 64, 1), ("f16", 96, 70, 1)])
+def test_repack_plan_info_and_sizes(storage, B, K, planes):
     pl = das.Plan(**_problem(algorithm="repack", B=B, K=K, storage=storage))
     assert pl.repack and pl.permuted_input and not pl.batch_inner
     assert pl.info["algorithm"] == das.ALG_REPACK
-    assert pl.info["layout"] == das.LAYOUT_QMBK
+    assert pl.info["layout"] == das.LAYOUT_QMPB
     assert pl.info["lanes_per_voxel"] == 2
     assert pl.info["frames_per_lane"] == (32 if B % 64 == 0 else 16)
     assert pl.info["staged"] == 1
-    k4 = (K + 3) // 4
-    assert pl.permuted_bytes(1) == 8 * B * k4 * chunk                       # M = 8
+    npc = (K + 7) // 8
+    assert pl.permuted_bytes(1) == 8 * planes * npc * B * 16                 # M = 8
     assert pl.permuted_bytes(2) == 2 * pl.permuted_bytes(1)
-    assert pl.permuted_shape(2) == (2, 8, B, k4, chunk // 2)
+    assert pl.permuted_shape(2) == ((2, 8, npc, B, 8) if storage == "f16" else (2, 8, 2, npc, B, 8))
     assert pl.max_q_chunk() == 2
     import torch
     assert pl.permuted_dtype() == torch.float16

@@ -22,24 +22,24 @@ pytestmark = pytest.mark.gpu
 
 
 def _repack_layout(rf, q_begin, q_count, storage):
-    """The permuted buffer as the oracle defines it: (q, M, B, ceil(K/4), 8) halves,
-    hi then lo of each chunk of 4 positions (binary16: (..., 4) rounded samples)."""
+    """The permuted buffer as the oracle defines it: (q, M, 2, P, B, 8) halves,
+    the hi then the lo parts of the samples in pieces of 8 positions (P =
+    ceil(K/8), positions past K zero), each piece the B frames side by side
+    (binary16 storage: (q, M, P, B, 8) rounded samples)."""
     import oracle
     B, Q, M, K = rf.shape
-    x = np.ascontiguousarray(rf[:, q_begin:q_begin + q_count].transpose(1, 2, 0, 3))     # q, M, B, K
-    k4 = (K + 3) // 4
-    pad = np.zeros(x.shape[:3] + (4 * k4,), dtype=np.float32)
-    pad[..., :K] = x
+    npc = (K + 7) // 8
+    pad = np.zeros((B, q_count, M, 8 * npc), dtype=np.float32)
+    pad[..., :K] = rf[:, q_begin:q_begin + q_count]
+    pieces = lambda a: np.ascontiguousarray(a.reshape(B, q_count, M, npc, 8).transpose(1, 2, 3, 0, 4))
     if storage == "f16":
-        return oracle.to_binary16(pad).astype(np.float16).reshape(x.shape[:3] + (k4, 4))
+        return pieces(oracle.to_binary16(pad)).astype(np.float16)
     hi, lo = oracle.split_binary16(pad)
-    hi = hi.astype(np.float16).reshape(x.shape[:3] + (k4, 4))
-    lo = lo.astype(np.float16).reshape(x.shape[:3] + (k4, 4))
-    return np.concatenate([hi, lo], axis=-1)
+    return np.stack([pieces(hi).astype(np.float16), pieces(lo).astype(np.float16)], axis=2)
 
 
 @pytest.mark.parametrize("storage", ["native", "f16"])
-@pytest.mark.parametrize("B,K,q_begin,q_count", [(32, 64, 0, 3), (32, 67, 1, 2), (64, 130, 2, 1), (96, 5, 0, 3)])
+@pytest.mark.parametrize("B,K,q_begin,q_count", [(32, 64, 0, 3), (32, 67, 1, 2), (64, 130, 2, 1), (96, 5, 0, 3), (64, 333, 0, 3), (32, 16, 1, 1)])
 def test_permute_writes_the_split_bit_for_bit(gpu, storage, B, K, q_begin, q_count):
     import torch
     import volumetric_delay_sum_amd as das
@@ -107,6 +107,39 @@ def test_windows_staged_and_direct(gpu, storage, voxel):
     inp = Inputs(cfg, w_tx="uniform")
     y = to_numpy(run_gpu(inp, "repack", storage=storage), False)
     assert_parity(y, oracle_ref(inp, storage=storage), f"repack voxel={voxel} {storage}")
+
+
+def _max_group_window(cfg):
+    """Widest sample window (positions, k over the group plus one) of any
+    8 x 4 voxel group and (event, receiver) of the configuration, all voxels
+    counted (no apodization)."""
+    rx = das_synth.array_positions(cfg).astype(np.float64)
+    tau, _ = das_synth.tx_tables(cfg)
+    nx, ny, nz = cfg.grid
+    widest = 0
+    for iz in range(nz):
+        for gy in range(0, ny, 4):
+            for gx in range(0, nx, 8):
+                vox = np.array([(iz * ny + y) * nx + x for y in range(gy, min(gy + 4, ny))
+                                for x in range(gx, min(gx + 8, nx))])
+                pos = das_synth.voxel_positions(cfg, vox)
+                d = np.linalg.norm(pos[None] - rx[:, None], axis=-1) / cfg.c
+                k = np.floor((tau[:, vox][:, None, :] + d[None] - cfg.t0) * cfg.fs)
+                widest = max(widest, int((k.max(-1) - k.min(-1)).max()) + 2)
+    return widest
+
+
+@pytest.mark.parametrize("storage", ["native", "f16"])
+def test_windows_wider_than_the_staged_rows(gpu, storage):
+    """No apodization and 1.5 mm voxels: group windows span more positions than
+    a staged row holds (72), so those groups read their sample tiles straight
+    from the permuted buffer, several 16-position blocks each."""
+    cfg = _ragged(B=32, K=1200, voxel=1.5e-3, z0=3e-3, grid=(19, 10, 2), array=(19, 3), f_number=0.0,
+                  sources=((0.0, 0.0), (2e-3, 1e-3)))
+    assert _max_group_window(cfg) > 72
+    inp = Inputs(cfg, w_tx="uniform")
+    y = to_numpy(run_gpu(inp, "repack", storage=storage), False)
+    assert_parity(y, oracle_ref(inp, storage=storage), f"repack wide windows {storage}")
 
 
 def test_one_event_per_call_and_accumulate(gpu):

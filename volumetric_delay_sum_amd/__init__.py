@@ -18,8 +18,9 @@ torch.float16 tensors, rounded by ``permute`` and widened to fp32 by
 
 ``Plan(..., algorithm="repack")`` runs the matrix-core variant (the paper's
 tensor-core repackaging; the docs' ALG4).  Its permuted buffer is a
-torch.float16 tensor of shape (q, M, B, ceil(K / 4), 8) (hi and lo halves of
-float32 samples) or (q, M, B, ceil(K / 4), 4) with ``storage="f16"``.
+torch.float16 tensor of shape (q, M, 2, P, B, 8): the hi and lo halves of the
+float32 samples in pieces of 8 positions, P = ceil(K / 8), each piece the B
+frames side by side; (q, M, P, B, 8) with ``storage="f16"``.
 """
 from __future__ import annotations
 
@@ -29,19 +30,19 @@ from typing import Optional, Sequence
 
 __all__ = [
     "F32", "C64", "F64", "C128", "ALG_DEFAULT", "ALG_BASELINE", "ALG_BATCH_INNER", "ALG_AUTO", "ALG_REPACK",
-    "LAYOUT_KQMB", "LAYOUT_QMKB", "LAYOUT_QMBK", "STORE_NATIVE", "STORE_F16",
+    "LAYOUT_KQMB", "LAYOUT_QMKB", "LAYOUT_QMPB", "STORE_NATIVE", "STORE_F16",
     "TX_PLANE", "TX_DIVERGING", "DasError", "Plan", "load_library", "library_path", "plan_from_fields",
 ]
 
 F32, C64, F64, C128 = 0, 1, 2, 3
 ALG_DEFAULT, ALG_BASELINE, ALG_BATCH_INNER, ALG_AUTO, ALG_REPACK = 0, 1, 2, 3, 4
-LAYOUT_KQMB, LAYOUT_QMKB, LAYOUT_QMBK = 0, 1, 2
+LAYOUT_KQMB, LAYOUT_QMKB, LAYOUT_QMPB = 0, 1, 2
 STORE_NATIVE, STORE_F16 = 0, 1
 TX_PLANE, TX_DIVERGING = 0, 1
 
 _ALG = {"default": ALG_DEFAULT, "baseline": ALG_BASELINE, "batch_inner": ALG_BATCH_INNER,
         "bl": ALG_BASELINE, "bi": ALG_BATCH_INNER, "auto": ALG_AUTO, "repack": ALG_REPACK, "tc": ALG_REPACK}
-_LAYOUT = {"kqmb": LAYOUT_KQMB, "qmkb": LAYOUT_QMKB, "qmbk": LAYOUT_QMBK}
+_LAYOUT = {"kqmb": LAYOUT_KQMB, "qmkb": LAYOUT_QMKB, "qmpb": LAYOUT_QMPB}
 _DTYPE = {"f32": F32, "c64": C64, "f64": F64, "c128": C128}
 _STORAGE = {"native": STORE_NATIVE, "f16": STORE_F16}
 
@@ -217,7 +218,8 @@ class Plan:
         p = self.problem
         qc = p.Q if q_count is None else int(q_count)
         if self.repack:
-            return (qc, p.M, p.B, (p.K + 3) // 4, 4 if self.store_f16 else 8)
+            npc = (p.K + 7) // 8
+            return (qc, p.M, npc, p.B, 8) if self.store_f16 else (qc, p.M, 2, npc, p.B, 8)
         shape = (p.K, qc, p.M, p.B) if p.layout == LAYOUT_KQMB else (qc, p.M, p.K, p.B)
         return shape + ((2,) if self.iq else ())
 

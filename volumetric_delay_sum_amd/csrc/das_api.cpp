@@ -273,7 +273,7 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
     if (p.algorithm != DAS_ALG_DEFAULT && p.algorithm != DAS_ALG_BASELINE && p.algorithm != DAS_ALG_BATCH_INNER &&
         p.algorithm != DAS_ALG_AUTO && p.algorithm != DAS_ALG_REPACK)
         return DAS_ERR_INVALID_ARGUMENT;
-    if (p.layout != DAS_LAYOUT_KQMB && p.layout != DAS_LAYOUT_QMKB && p.layout != DAS_LAYOUT_QMBK)
+    if (p.layout != DAS_LAYOUT_KQMB && p.layout != DAS_LAYOUT_QMKB && p.layout != DAS_LAYOUT_QMPB)
         return DAS_ERR_INVALID_ARGUMENT;
     if (p.storage != DAS_STORE_NATIVE && p.storage != DAS_STORE_F16)
         return DAS_ERR_INVALID_ARGUMENT;
@@ -302,9 +302,9 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
     // receiver) plane of rows
     if (alg == DAS_ALG_REPACK &&
         (p.dtype != DAS_F32 || p.B % 32 != 0 || p.K > 65535 || (int64_t)p.Q * N >= ((int64_t)1 << 32) ||
-         (int64_t)p.B * ((p.K + 3) / 4) * 16 >= ((int64_t)1 << 31)))
+         (int64_t)p.B * ((p.K + 7) / 8) * 32 >= ((int64_t)1 << 31)))
         return DAS_ERR_UNSUPPORTED;
-    if (p.layout == DAS_LAYOUT_QMBK && alg != DAS_ALG_REPACK)
+    if (p.layout == DAS_LAYOUT_QMPB && alg != DAS_ALG_REPACK)
         return DAS_ERR_INVALID_ARGUMENT;
     const int32_t elem = (cplx ? 2 : 1) * (wide ? 8 : 4);
     if (N > INT32_MAX)
@@ -321,7 +321,7 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
         return DAS_ERR_INVALID_ARGUMENT;
     pl->p = p;
     if (alg == DAS_ALG_REPACK)
-        pl->p.layout = DAS_LAYOUT_QMBK;
+        pl->p.layout = DAS_LAYOUT_QMPB;
     pl->N = N;
     pl->alg = alg;
     pl->elem_bytes = elem;
@@ -398,7 +398,7 @@ size_t das_permuted_bytes(const das_plan_t *plan, int32_t q_count) {
         return 0;
     const das_problem &p = plan->p;
     if (plan->alg == DAS_ALG_REPACK)
-        return (size_t)q_count * (size_t)p.M * (size_t)p.B * (size_t)das_repack_row_bytes(*plan);
+        return (size_t)q_count * (size_t)p.M * (size_t)das_repack_qm_bytes(*plan);
     return (size_t)p.K * (size_t)q_count * (size_t)p.M * (size_t)p.B * (size_t)plan->store_bytes;
 }
 

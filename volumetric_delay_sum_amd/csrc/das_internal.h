@@ -72,9 +72,9 @@ hipError_t das_launch_tx_tables(const das_plan_t &plan, const das_tx_event *even
 hipError_t das_launch_batch_inner(const das_plan_t &plan, const DasKParams &kp, const float *rf,
                                   const float *rx, const float *tau_tx, const float *w_tx,
                                   float *out, hipStream_t stream);
-// Repack (matrix-core) path: bytes of one (event, receiver, frame) row of the
-// permuted buffer, its permute, and its beamform.
-int64_t das_repack_row_bytes(const das_plan_t &plan);
+// Repack (matrix-core) path: bytes of one (event, receiver) of the permuted
+// buffer, its permute, and its beamform.
+int64_t das_repack_qm_bytes(const das_plan_t &plan);
 hipError_t das_launch_permute_repack(const das_plan_t &plan, const void *rf, void *out, int32_t q_begin,
                                      int32_t q_count, hipStream_t stream);
 hipError_t das_launch_repack(const das_plan_t &plan, const DasKParams &kp, const void *perm, const float *rx,
