@@ -39,6 +39,7 @@ CUS, SCLK_HZ = 256, 2.4e9
 LDS_BCLK = {
     "two ds_read_b64 (8-byte lanes)": 160.0,
     "two ds_read_b128 (16-byte lanes, split rows)": 219.0,
+    "16 ds_read_b128 per lane, two whole 128-B rows, bank-group order": 238.0,
 }
 
 
@@ -73,7 +74,7 @@ def stored_traffic(kernel: str, workload: str):
 
 
 def delivery_ceiling(plan, iq: bool, h16: bool):
-    """On-chip delivery roofline of the LDS-staged batch-inner kernel: every
+    """On-chip delivery roofline of the LDS-staged batch-inner kernels: every
     accumulation (voxel, receiver, event, frame) needs its two samples in
     registers, so the LDS's bytes per clock bound the accumulation rate at
     CUS * sclk * (B/clk/CU) / (bytes per accumulation)."""
@@ -81,8 +82,11 @@ def delivery_ceiling(plan, iq: bool, h16: bool):
         return None
     sample = (8 if iq else 4) // (2 if h16 else 1)        # bytes of one stored sample
     lane = sample * plan.info["frames_per_lane"]           # bytes of one lane's tap
-    pattern = ("two ds_read_b128 (16-byte lanes, split rows)" if lane == 16
-               else "two ds_read_b64 (8-byte lanes)" if lane == 8 else None)
+    if plan.info["whole_rows"]:
+        pattern = "16 ds_read_b128 per lane, two whole 128-B rows, bank-group order"
+    else:
+        pattern = ("two ds_read_b128 (16-byte lanes, split rows)" if lane == 16
+                   else "two ds_read_b64 (8-byte lanes)" if lane == 8 else None)
     if pattern is None:
         return {"bytes_per_accumulation": 2 * sample, "lane_tap_bytes": lane, "lds_B_per_clk_per_cu": None,
                 "ceiling_gacc_s": None}
@@ -299,7 +303,8 @@ def main():
     if plan.repack:
         kernel_name = "das_repack_kernel"
     elif bi:
-        kernel_name = "das_bi_staged_kernel" if plan.info["staged"] else "das_batch_inner_kernel"
+        kernel_name = ("das_bi_rows_kernel" if plan.info["whole_rows"] else "das_bi_staged_kernel") \
+            if plan.info["staged"] else "das_batch_inner_kernel"
     else:
         kernel_name = "das_baseline_f64_kernel" if args.wide else "das_baseline_kernel"
     peak = PEAK_FP64_TFLOPS if args.wide else PEAK_FP32_TFLOPS

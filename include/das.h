@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define DAS_ABI_VERSION 6
+#define DAS_ABI_VERSION 7
 
 typedef enum das_status {
     DAS_OK = 0,
@@ -150,10 +150,12 @@ typedef struct das_plan_info {
     int32_t algorithm;          /* resolved: DAS_ALG_BASELINE or DAS_ALG_BATCH_INNER */
     int32_t layout;
     int32_t elem_bytes;         /* 4 (f32), 8 (c64, f64) or 16 (c128) per sample     */
-    int32_t frames_per_lane;    /* batch-inner: frames one lane loads per vector load;
+    int32_t frames_per_lane;    /* batch-inner: frames one lane loads per vector load
+                                   (whole-row lanes: frames one lane holds);
                                    baseline: frames one lane accumulates;
                                    repack: output frames one lane holds             */
-    int32_t lanes_per_voxel;    /* batch-inner: 16; baseline: 1; repack: 2           */
+    int32_t lanes_per_voxel;    /* batch-inner: 16 (whole-row lanes: 8); baseline: 1;
+                                   repack: 2                                         */
     int32_t voxels_per_group;   /* voxels one workgroup covers                       */
     int64_t N;                  /* nx * ny * nz                                      */
     int32_t staged;             /* batch-inner: 1 if frame rows are staged through LDS
@@ -161,6 +163,12 @@ typedef struct das_plan_info {
                                    every lane loads its rows from memory             */
     int32_t store_bytes;        /* bytes per sample in the permuted buffer: elem_bytes,
                                    or 2 (DAS_F32) / 4 (DAS_C64) with DAS_STORE_F16   */
+    int32_t whole_rows;         /* staged batch-inner: 1 if each lane reads whole
+                                   128-byte sample rows (all frames of its frame tile)
+                                   for (voxel, receiver) items of its own, 0 if the 16
+                                   lanes of a DPP row share each voxel's frames      */
+    int32_t receivers_per_step; /* staged batch-inner and repack: receivers a
+                                   workgroup stages per step; 0 otherwise            */
 } das_plan_info;
 
 /* Validate a problem and build a host-side plan.  Host only: no HIP call, no

@@ -116,8 +116,9 @@ def test_plan_info_and_sizes():
     pl = das.Plan(**_problem(B=32, dtype="c64", f_demod=5e6))
     assert pl.info["algorithm"] == das.ALG_BATCH_INNER
     assert pl.info["elem_bytes"] == 8
-    assert pl.info["frames_per_lane"] == 2                  # IQ, B % 32 == 0: LDS-staged split rows, 2 frames per lane
+    assert pl.info["frames_per_lane"] == 2                  # IQ, B % 32 == 0: LDS-staged DPP rows, split, 2 frames a lane
     assert pl.info["lanes_per_voxel"] == 16
+    assert pl.info["whole_rows"] == 0 and pl.info["receivers_per_step"] == 8
     assert pl.info["N"] == 32
     assert pl.permuted_bytes(1) == 64 * 1 * 8 * 32 * 8
     assert pl.permuted_bytes(2) == 2 * pl.permuted_bytes(1)
@@ -169,14 +170,42 @@ def test_auto_selection(dtype, B, alg):
                                algorithm="default")).info["algorithm"] == das.ALG_BASELINE
 
 
-@pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (24, 1), (32, 2), (48, 1), (64, 4), (96, 2), (66, 1),
-                                  (160, 2), (192, 4), (68, 4)])
+@pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (24, 1), (32, 32), (48, 1), (64, 32), (96, 32), (66, 1),
+                                  (160, 32), (192, 32), (68, 4)])
 def test_frames_per_lane_choice(B, fl):
-    # fp32 batch-inner: the LDS-staged kernel wherever B % 16 == 0 (4 frames
-    # per lane in split rows when B % 64 == 0, 2 when B % 32 == 0, else 1)
+    # fp32 batch-inner: the LDS-staged kernel wherever B % 16 == 0, with
+    # whole-row lanes (all 32 frames of a frame tile per lane) when B % 32 == 0
+    # and one frame per lane of a DPP row otherwise
     pl = das.Plan(**_problem(B=B))
     assert pl.info["frames_per_lane"] == fl
     assert pl.info["staged"] == (1 if B % 16 == 0 else 0)
+    assert pl.info["whole_rows"] == (1 if B % 32 == 0 else 0)
+    assert pl.info["receivers_per_step"] == (16 if B % 16 == 0 else 0)
+
+
+@pytest.mark.parametrize("B,fl", [(32, 2), (64, 4), (96, 2), (160, 2), (192, 4)])
+def test_frames_per_lane_choice_dpp_rows(B, fl, monkeypatch):
+    # DAS_STAGED_ROWS=0 keeps the DPP-row staged kernel (4 frames per lane in
+    # split rows when B % 64 == 0, else 2), for comparisons
+    monkeypatch.setenv("DAS_STAGED_ROWS", "0")
+    pl = das.Plan(**_problem(B=B))
+    assert pl.info["frames_per_lane"] == fl and pl.info["whole_rows"] == 0 and pl.info["staged"] == 1
+    assert pl.info["receivers_per_step"] == (8 if B % 64 == 0 else 16)
+
+
+@pytest.mark.parametrize("rows,iq,per_step", [("1", False, 8), ("2", False, 16), ("1", True, 8), ("2", True, 8)])
+def test_whole_row_receivers_per_step(rows, iq, per_step, monkeypatch):
+    # DAS_STAGED_ROWS picks 8 or 16 receivers a step; complex items keep 8
+    monkeypatch.setenv("DAS_STAGED_ROWS", rows)
+    pl = das.Plan(**_problem(B=32, dtype="c64" if iq else "f32", f_demod=5e6 if iq else 0.0))
+    assert pl.info["whole_rows"] == 1 and pl.info["receivers_per_step"] == per_step
+    assert pl.info["lanes_per_voxel"] == 8 and pl.info["frames_per_lane"] == (16 if iq else 32)
+
+
+def test_whole_rows_need_native_samples_and_short_records():
+    assert das.Plan(**_problem(B=32, storage="f16")).info["whole_rows"] == 0
+    assert das.Plan(**_problem(B=32, K=65535)).info["whole_rows"] == 1
+    assert das.Plan(**_problem(B=32, K=65536)).info["whole_rows"] == 0
 
 
 @pytest.mark.parametrize("B,fl", [(32, 2), (64, 4), (96, 4), (160, 4)])
@@ -189,11 +218,12 @@ def test_frames_per_lane_choice_direct(B, fl, monkeypatch):
 
 @pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (31, 1), (32, 2), (40, 2), (48, 1), (64, 2), (34, 2)])
 def test_frames_per_lane_choice_iq(B, fl):
-    # complex64 batch-inner: the LDS-staged kernel wherever B % 16 == 0 (2
-    # frames per lane in split rows when B % 32 == 0, else 1)
+    # complex64 batch-inner: the LDS-staged DPP-row kernel wherever B % 16 ==
+    # 0 (2 frames per lane in split rows when B % 32 == 0, else 1)
     pl = das.Plan(**_problem(B=B, dtype="c64", f_demod=5e6))
     assert pl.info["frames_per_lane"] == fl
     assert pl.info["staged"] == (1 if B % 16 == 0 else 0)
+    assert pl.info["whole_rows"] == 0
 
 
 def test_error_strings(lib):
@@ -347,7 +377,8 @@ def test_binding_checks_tensor_sizes_before_the_call():
 
 @pytest.mark.parametrize("B,dtype", [(64, "f32"), (32, "c64")])
 def test_split_rows_can_be_switched_off(B, dtype, monkeypatch):
-    # DAS_STAGED_SPLIT=1 keeps whole rows (8 bytes per lane), for comparisons
+    # DPP-row kernel: DAS_STAGED_SPLIT=1 keeps whole rows (8 bytes per lane), for comparisons
+    monkeypatch.setenv("DAS_STAGED_ROWS", "0")
     kw = dict(B=B, dtype=dtype, f_demod=5e6 if dtype == "c64" else 0.0)
     assert das.Plan(**_problem(**kw)).info["frames_per_lane"] == (4 if dtype == "f32" else 2)
     monkeypatch.setenv("DAS_STAGED_SPLIT", "1")

@@ -107,17 +107,23 @@ def test_q_chunks_sum_to_the_whole(gpu, alg, layout):
     assert_parity(y, oracle_ref(inp), f"q chunks {alg}/{layout}")
 
 
+@pytest.mark.parametrize("kernel", ["default", "dpp_rows"])
 @pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])
 @pytest.mark.parametrize("layout", ["kqmb", "qmkb"])
 @pytest.mark.parametrize("voxel", [0.25e-3, 0.6e-3, 1.5e-3], ids=["fine", "mixed", "coarse"])
 @pytest.mark.parametrize("B", [16, 32, 64])
-def test_staged_windows_and_fallback(gpu, layout, voxel, iq, B):
-    """The LDS-staged kernel.  fp32 B = 32: 2 frames per lane, one 32-frame
-    tile of 16 receivers a step; fp32 B = 64 and complex64 B = 32 and 64:
-    split rows (two voxels per DPP row, 16 bytes per lane, 8 receivers a
-    step, 256-byte rows).  Coarse voxels give k-windows
-    wider than the LDS capacity, which must fall back to direct loads; fine
-    voxels stay in LDS; the mixed pitch exercises both within one launch."""
+def test_staged_windows_and_fallback(gpu, monkeypatch, layout, voxel, iq, B, kernel):
+    """The LDS-staged kernels.  Default: fp32 with B a multiple of 32 runs
+    whole-row lanes (all 32 frames of a frame tile per lane, 16 receivers a
+    step), other shapes the DPP-row kernel; "dpp_rows" forces the DPP-row
+    kernel: fp32 B = 32, 2 frames per lane, one 32-frame tile of 16 receivers
+    a step; fp32 B = 64 and complex64 B = 32 and 64: split rows (two voxels
+    per DPP row, 16 bytes per lane, 8 receivers a step, 256-byte rows).
+    Coarse voxels give k-windows wider than the LDS capacity, which must fall
+    back to direct loads; fine voxels stay in LDS; the mixed pitch exercises
+    both within one launch."""
+    if kernel == "dpp_rows":
+        monkeypatch.setenv("DAS_STAGED_ROWS", "0")
     cfg = das_synth.custom_config("tiny", name="staged", seed=23, array=(19, 3), grid=(11, 10, 3), K=700, B=B,
                                   tx="diverging", sources=((0.0, 0.0), (2e-3, 1e-3)), voxel=voxel,
                                   z0=3e-3, n_scatterers=0, iq=iq)
@@ -130,10 +136,11 @@ def test_staged_windows_and_fallback(gpu, layout, voxel, iq, B):
 
 @pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])
 def test_split_and_whole_rows_agree(gpu, monkeypatch, iq):
-    """B = 64: the staged kernel with split rows (the default there) and with
-    whole rows (two frame tiles) both meet the bar."""
+    """B = 64: the DPP-row staged kernel with split rows (its default there)
+    and with whole rows (two frame tiles) both meet the bar."""
     cfg = _ragged(B=64, grid=(17, 9, 4), iq=iq, array=(23, 2))
     inp = Inputs(cfg, w_tx="uniform")
+    monkeypatch.setenv("DAS_STAGED_ROWS", "0")              # the DPP-row kernel
     split = to_numpy(run_gpu(inp, "batch_inner", "qmkb"), iq)
     monkeypatch.setenv("DAS_STAGED_SPLIT", "1")
     whole = to_numpy(run_gpu(inp, "batch_inner", "qmkb"), iq)

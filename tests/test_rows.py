@@ -1,0 +1,97 @@
+"""GPU: the LDS-staged batch-inner kernel with whole-row lanes ("ffdas:
+volumetric ultrasound reconstruction at warp speed", Section 3, batch-inner
+tiling and spatial locality), in the variants the default plan does not
+pick: 8 receivers a step (fp32) and complex64 samples.  The default (fp32,
+16 receivers a step) runs in every fp32 parity test with B a multiple of 32.
+
+Each case meets the same bar as every other kernel against the fp64 oracle
+(max|err| <= 1e-4 max|oracle|, relative L2 <= 1e-5): ragged grids and
+receiver counts, 32, 64 and 96 frames (several frame tiles), start times of
+both signs, coarse voxels whose windows exceed the staged rows (direct
+loads), one event per call with accumulation, both layouts, and the Main
+workload sampled at full size.
+"""
+import numpy as np
+import pytest
+
+import das_synth
+from das_testing import Inputs, assert_all_written, assert_parity, oracle_ref, run_gpu, sample_voxels, to_numpy
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = [("1", False), ("2", False), ("1", True)]
+IDS = ["f32-8rx", "f32-16rx", "c64-8rx"]
+
+
+def _use(monkeypatch, rows):
+    monkeypatch.setenv("DAS_STAGED_ROWS", rows)
+
+
+def _ragged(iq, B=32, K=300, **kw):
+    base = dict(name="rows", seed=61, array=(37, 2), grid=(19, 13, 5), K=K, B=B, tx="diverging",
+                sources=((0.0, 0.0), (1.5e-3, -0.5e-3), (-1e-3, 1e-3)), n_scatterers=0, iq=iq)
+    base.update(kw)
+    return das_synth.custom_config("tiny", **base)
+
+
+def _info(inp):
+    import volumetric_delay_sum_amd as das
+    return das.plan_from_fields(inp.fields, "batch_inner", "qmkb").info
+
+
+@pytest.mark.parametrize("layout", ["kqmb", "qmkb"])
+@pytest.mark.parametrize("B", [32, 64, 96])
+@pytest.mark.parametrize("rows,iq", VARIANTS, ids=IDS)
+def test_ragged(gpu, monkeypatch, rows, iq, B, layout):
+    _use(monkeypatch, rows)
+    inp = Inputs(_ragged(iq, B=B), w_tx="uniform")
+    info = _info(inp)
+    assert info["whole_rows"] == 1 and info["receivers_per_step"] == 8 * int(rows)
+    y = to_numpy(run_gpu(inp, "batch_inner", layout), iq)
+    assert_parity(y, oracle_ref(inp), f"rows={rows} iq={iq} B={B} {layout}")
+
+
+@pytest.mark.parametrize("t0", [3.0 / 20e6, 1.37e-6, -0.83e-6], ids=["3_periods", "plus_1.37us", "minus_0.83us"])
+@pytest.mark.parametrize("rows,iq", VARIANTS, ids=IDS)
+def test_start_time(gpu, monkeypatch, rows, iq, t0):
+    _use(monkeypatch, rows)
+    inp = Inputs(_ragged(iq, t0=t0, K=320), w_tx="uniform")
+    y = to_numpy(run_gpu(inp, "batch_inner", "qmkb"), iq)
+    assert_parity(y, oracle_ref(inp), f"rows={rows} iq={iq} t0={t0}")
+
+
+@pytest.mark.parametrize("voxel", [0.6e-3, 1.5e-3], ids=["mixed", "coarse"])
+@pytest.mark.parametrize("rows,iq", VARIANTS, ids=IDS)
+def test_windows_wider_than_the_regions(gpu, monkeypatch, rows, iq, voxel):
+    """Coarse voxels: some steps' windows exceed a region (38 positions with
+    16 receivers a step, 78 with 8), and those steps read the permuted buffer."""
+    _use(monkeypatch, rows)
+    cfg = _ragged(iq, K=900, voxel=voxel, z0=3e-3, grid=(19, 10, 3), array=(19, 3), f_number=0.0,
+                  sources=((0.0, 0.0), (2e-3, 1e-3)))
+    inp = Inputs(cfg, w_tx="uniform")
+    y = to_numpy(run_gpu(inp, "batch_inner", "kqmb"), iq)
+    assert_parity(y, oracle_ref(inp), f"rows={rows} iq={iq} voxel={voxel}")
+
+
+@pytest.mark.parametrize("rows,iq", VARIANTS, ids=IDS)
+def test_one_event_per_call_and_accumulate(gpu, monkeypatch, rows, iq):
+    import torch
+    _use(monkeypatch, rows)
+    inp = Inputs(_ragged(iq, B=64), w_tx="uniform")
+    ref = oracle_ref(inp)
+    assert_parity(to_numpy(run_gpu(inp, "batch_inner", "qmkb", q_chunk=1), iq), ref, f"rows={rows} q chunks")
+    shape = (inp.cfg.B, inp.cfg.N, 2) if iq else (inp.cfg.B, inp.cfg.N)
+    start = torch.linspace(-3.0, 3.0, int(np.prod(shape)), device="cuda").reshape(shape)
+    out = run_gpu(inp, "batch_inner", "kqmb", out=start.clone(), accumulate_into=True)
+    got = to_numpy(out, iq) - to_numpy(start, iq)
+    assert_parity(got, ref, f"rows={rows} accumulate")
+
+
+@pytest.mark.parametrize("rows,iq", [("1", False), ("1", True)], ids=["f32-8rx", "c64-8rx"])
+def test_main_sampled(gpu, monkeypatch, rows, iq):
+    _use(monkeypatch, rows)
+    inp = Inputs(das_synth.get_config("main-c64" if iq else "main"))
+    vox = sample_voxels(inp.cfg, 128, seed=5)
+    out = run_gpu(inp, "batch_inner", "qmkb")
+    assert_all_written(out, f"main rows={rows} iq={iq}")
+    assert_parity(to_numpy(out, iq)[:, vox], oracle_ref(inp, voxels=vox), f"main rows={rows} iq={iq}")

@@ -74,7 +74,7 @@ class _PlanInfo(ctypes.Structure):
         ("algorithm", ctypes.c_int32), ("layout", ctypes.c_int32), ("elem_bytes", ctypes.c_int32),
         ("frames_per_lane", ctypes.c_int32), ("lanes_per_voxel", ctypes.c_int32),
         ("voxels_per_group", ctypes.c_int32), ("N", ctypes.c_int64), ("staged", ctypes.c_int32),
-        ("store_bytes", ctypes.c_int32),
+        ("store_bytes", ctypes.c_int32), ("whole_rows", ctypes.c_int32), ("receivers_per_step", ctypes.c_int32),
     ]
 
 

@@ -368,6 +368,19 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
         pl->split = 2;
         pl->fl *= 2;
     }
+    // Whole-row lanes where they are built, for fp32 samples: 16 receivers a
+    // step (Main 8.2 ms against 9.2 with DPP rows).  Complex samples keep the
+    // DPP-row kernel (Main complex 21.8 ms against 28.9).  DAS_STAGED_ROWS
+    // selects explicitly: 1 or 2 receiver groups of 8 a step (complex: 1),
+    // 0 the DPP-row kernel.
+    pl->rows = 0;
+    if (pl->staged && das_rows_supported(*pl)) {
+        const char *rv = std::getenv("DAS_STAGED_ROWS");
+        const int g = rv ? std::atoi(rv) : (p.dtype == DAS_C64 ? 0 : 2);
+        pl->rows = (g == 1 || g == 2) ? g : 0;
+        if (p.dtype == DAS_C64 && pl->rows == 2)
+            pl->rows = 1;                            // complex items hold twice the weights: 8 receivers a step
+    }
     *out = pl;
     return DAS_OK;
 }
@@ -382,12 +395,17 @@ das_status das_plan_get_info(const das_plan_t *plan, das_plan_info *info) {
     info->elem_bytes = plan->elem_bytes;
     const bool bi = plan->alg == DAS_ALG_BATCH_INNER;
     const bool rp = plan->alg == DAS_ALG_REPACK;
-    info->frames_per_lane = rp ? (plan->p.B % 64 == 0 ? 32 : 16) : (bi ? plan->fl : plan->bt);
-    info->lanes_per_voxel = rp ? 2 : (bi ? 16 : 1);
-    info->voxels_per_group = rp ? 256 : (bi ? 16 : 256);
+    const bool wr = bi && plan->rows != 0;
+    const int32_t wr_frames = plan->p.dtype == DAS_C64 ? 16 : 32;
+    info->frames_per_lane = rp ? (plan->p.B % 64 == 0 ? 32 : 16) : (wr ? wr_frames : (bi ? plan->fl : plan->bt));
+    info->lanes_per_voxel = rp ? 2 : (wr ? 8 : (bi ? 16 : 1));
+    info->voxels_per_group = rp ? 256 : (wr ? 128 : (bi ? 16 : 256));
     info->N = plan->N;
     info->staged = rp ? 1 : plan->staged;
     info->store_bytes = plan->store_bytes;
+    info->whole_rows = wr ? 1 : 0;
+    info->receivers_per_step = rp ? (plan->p.B % 64 == 0 ? 4 : 8)
+                                  : (wr ? 8 * plan->rows : (bi && plan->staged ? 16 / plan->split : 0));
     return DAS_OK;
 }
 
@@ -454,8 +472,11 @@ das_status das_beamform(const das_plan_t *plan, const void *rf, const float *rx_
         const int64_t tables = (int64_t)plan->p.Q * plan->N * 4;
         const bool chunk_ok = plan->p.layout == DAS_LAYOUT_QMKB || chunk < ((int64_t)1 << 32);
         const bool staged = plan->staged && chunk_ok && tables < ((int64_t)1 << 32);
-        e = staged ? das_launch_batch_inner_staged(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s)
-                   : das_launch_batch_inner(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s);
+        if (staged && plan->rows)
+            e = das_launch_bi_rows(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s);
+        else
+            e = staged ? das_launch_batch_inner_staged(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s)
+                       : das_launch_batch_inner(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s);
     }
     else if (plan->p.dtype == DAS_F64 || plan->p.dtype == DAS_C128)
         e = das_launch_baseline_f64(*plan, kp, static_cast<const double *>(rf), rx_pos, tau_tx, w_tx,

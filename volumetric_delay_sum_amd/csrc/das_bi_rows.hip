@@ -1,0 +1,621 @@
+// LDS-staged batch-inner DAS kernel with whole-row lanes, for gfx950.
+//
+// Same method and staging as the staged batch-inner kernel ("ffdas:
+// volumetric ultrasound reconstruction at warp speed", Section 3: batch-inner
+// tiling, frames innermost after the permute; spatial locality: the voxels of
+// a small tile need a few neighbouring sample rows of each receiver, which a
+// workgroup copies once into LDS by LDS-DMA and serves to all of them).  What
+// differs is the lane mapping:
+//
+//   - A lane owns one voxel of the 8 x 8 x 2 tile, ALL frames of the frame
+//     tile (128 bytes of a sample row: 32 fp32 or 16 complex frames) and, in
+//     each step, one receiver of every group of 8.  Each (voxel, receiver)
+//     item is the lane's own: it computes the item's sample split and weights
+//     and applies them itself, so the item's 64 (complex: 128) FMAs take
+//     register weights (plain FMAs, nothing crosses lanes in the inner loop),
+//     and the per-item work is shared by 32 (16) frames.
+//   - The lane reads its item's two sample rows whole: 16 reads of 16 bytes,
+//     the LDS's widest access, from two base registers with immediate offsets.
+//   - Bank conflicts.  The 16 lanes of one read are 8 receivers x 2 voxels.
+//     Receiver regions are padded by 16 bytes, so the 8 regions of a group
+//     start in 8 different 16-byte bank groups modulo 8; and a lane reads
+//     first the one of its two rows whose parity is its voxel's parity, so the
+//     two voxels of a receiver are 128 bytes (8 bank groups) apart.  Every
+//     read instruction then touches 16 distinct 16-byte bank groups whatever
+//     rows the lanes need (the LDS serves it in one pass); in plain order the
+//     same reads conflict up to 8 ways.
+//
+// Per step (transmit event, 8 NIT receivers): the window [kmin, kmax] of k
+// over the tile's voxels with a non-zero weight is reduced per receiver (in
+// the wave by DPP and lane swaps on packed 16-bit minima, across waves by LDS
+// atomics) two steps ahead; the receivers' rows kmin .. kmax + 1 are copied
+// by LDS-DMA into the other of two buffers during the step before; one
+// barrier ends a step.  A lane's sums cover its receivers; the 8 lanes of a
+// voxel add them up once at the end (DPP).  A step whose window exceeds a
+// region reads its rows straight from the permuted buffer.
+#include "das_device.h"
+
+namespace {
+
+constexpr int WR_THREADS = 1024;
+constexpr int WR_TX = 8, WR_TY = 8, WR_TZ = 2;   // voxel tile of a workgroup
+constexpr int WR_ROWB = 128;                     // bytes of one staged sample row (the frame tile's part)
+constexpr int WR_LDS_TOTAL = 163840;             // LDS of one workgroup on gfx950 (160 KiB)
+
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+
+// Sizes of one instance: NIT items (receiver groups of 8) per lane and step.
+template <int NIT>
+struct RowsGeo {
+    static constexpr int NRX = 8 * NIT;                                      // receivers per step
+    static constexpr int SLOTS = 4 * 2 * NRX * 4;                            // window slots [4 sets][min, max][NRX]
+    static constexpr int RW = ((WR_LDS_TOTAL - SLOTS) / (2 * NRX) - 16) / WR_ROWB;   // sample rows per region
+    static constexpr int REGION = RW * WR_ROWB + 16;                         // one receiver's rows, padded
+    static constexpr int BUF = NRX * REGION;                                 // one row buffer
+    static constexpr int LDS_BYTES = 2 * BUF + SLOTS;
+    static constexpr int W_MAX = RW - 1;                                     // k positions of a window
+    static constexpr int S = 16 / NRX;                                       // waves sharing one receiver's copy
+    static constexpr int MAXR = (RW + 8 * S - 1) / (8 * S);                  // copy rounds of one wave
+    static_assert(LDS_BYTES <= WR_LDS_TOTAL, "LDS budget");
+    // an odd number of 16-byte units per region puts the regions of any 8
+    // consecutive receivers in 8 different bank groups modulo 8
+    static_assert((REGION / 16) % 2 == 1, "region bank offsets");
+};
+
+// One (voxel, receiver) item of one step: k = all ones when its weight is 0.
+// 32-bit fields only (a padded struct copied between pipeline roles would
+// keep its padding in scratch memory).
+struct RowsStep {
+    uint32_t k;
+    float a, b, ai, bi;
+};
+
+struct RowsCursor {
+    int ql, m0, g0, g1;
+};
+
+struct RowsTx {
+    float tau, w;
+};
+
+// Per item: LDS byte address of the row read first (be) and second (bo) and
+// their weights (complex: real and imaginary parts), zero when the step
+// takes its terms from direct loads.
+template <int NIT>
+struct RowsWin {
+    uint32_t be[NIT], bo[NIT];
+    float we[NIT], wo[NIT], wei[NIT], woi[NIT];
+    uint32_t overflow;
+};
+
+struct RowsCopy {
+    int nr, rows;        // copy rounds and sample rows of this wave's receiver (wave-uniform)
+    uint32_t start;      // byte offset of the window's first row in rs (less the frame tile)
+    uint32_t dst;        // LDS byte offset of the receiver's region
+    das::BufRsrc rs;
+};
+
+template <bool IQ, int LAYOUT, int NIT>
+__global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, const float *__restrict__ rfp,
+                                                                 const float *__restrict__ rx,
+                                                                 const float *__restrict__ tau_tx,
+                                                                 const float *__restrict__ w_tx,
+                                                                 float *__restrict__ out) {
+    using G = RowsGeo<NIT>;
+    constexpr int NRX = G::NRX;
+    constexpr int C = IQ ? 2 : 1;
+    constexpr int E = 4 * C;                     // bytes per sample
+    constexpr int FR = WR_ROWB / E;              // frames of a frame tile
+    constexpr int DEPTH = 3;                     // units whose reads are in flight
+    __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
+    int *slots = reinterpret_cast<int *>(lds + 2 * G::BUF);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 7;                      // receiver of each group: item i is receiver m0 + 8 i + r
+    const int v = lane >> 3;                     // voxel in the wave's row of 8
+    const uint32_t vpar = (uint32_t)v & 1u;
+
+    const int tiles_x = (P.nx + WR_TX - 1) / WR_TX, tiles_y = (P.ny + WR_TY - 1) / WR_TY;
+    int t = das::xcd_tile(blockIdx.x, gridDim.x);
+    const int tx = t % tiles_x;
+    t /= tiles_x;
+    const int ty = t % tiles_y;
+    const int tz = t / tiles_y;
+    const int ix = tx * WR_TX + v, iy = ty * WR_TY + (wave & 7), iz = tz * WR_TZ + (wave >> 3);
+    const bool vox_ok = ix < P.nx && iy < P.ny && iz < P.nz;
+    const int ixc = min(ix, P.nx - 1), iyc = min(iy, P.ny - 1), izc = min(iz, P.nz - 1);
+    const int n = (izc * P.ny + iyc) * P.nx + ixc;
+    const int b0 = blockIdx.y * FR;              // first frame of the frame tile
+
+    const int64_t rowfull = (int64_t)P.B * E;    // one (k, q, m) row, all frames
+    // receiver stride (the plan keeps 16 K B E below 2^32); the (event,
+    // receiver) plane (q, m) starts at (q M + m) m_stride in both layouts
+    const uint32_t m_stride = (uint32_t)((LAYOUT == DAS_LAYOUT_KQMB) ? rowfull : rowfull * P.K);
+    const int64_t kstride = (LAYOUT == DAS_LAYOUT_KQMB) ? (int64_t)P.q_count * P.M * rowfull : rowfull;
+    const uint32_t kstride32 = (uint32_t)kstride;
+    const int64_t chunk_bytes = rowfull * P.M * P.q_count * P.K;
+    const char *rf_bytes = reinterpret_cast<const char *>(rfp);
+
+    // zero both row buffers (a zero weight never meets a non-finite stale
+    // value) and set every window slot empty
+    for (int i = tid * 16; i < 2 * G::BUF; i += WR_THREADS * 16)
+        *reinterpret_cast<int4 *>(lds + i) = make_int4(0, 0, 0, 0);
+    if (tid < 4 * 2 * NRX)
+        slots[tid] = ((tid / NRX) & 1) ? INT_MIN : INT_MAX;
+    __syncthreads();
+
+    // ---- per-step work ---------------------------------------------------
+    // Launch constants used once per receiver block are read afresh from the
+    // kernel arguments (P, rfp, rx, tau_tx, w_tx, out) through an opaque
+    // pointer: held across the loop they would crowd the scalar registers.
+    using kptr = const __attribute__((address_space(4))) char *;
+    auto kargs = [&]() -> kptr {
+        kptr ka = (kptr)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(ka));
+        return ka;
+    };
+    das::RxTerm R[NIT];                          // receive terms of this lane's items, current block
+    auto load_geometry = [&](int m0) {
+        const kptr ka = kargs();
+        const DasKParams &Pg = *(const DasKParams *)ka;
+        const float *rxg = *(const float *const *)(ka + sizeof(DasKParams) + sizeof(void *));
+        double vx, vy, vz;
+        das::voxel_centre(Pg, ixc, iyc, izc, vx, vy, vz);
+#pragma unroll
+        for (int i = 0; i < NIT; ++i) {
+            const int mm = m0 + 8 * i + r;
+            const int m = min(mm, Pg.M - 1);
+            R[i] = das::rx_term<IQ>(Pg, vx, vy, vz, rxg[3 * m], rxg[3 * m + 1], rxg[3 * m + 2]);
+            R[i].s_rx += 1.0 - Pg.t0fs;          // the sample split takes s + 1
+            R[i].w = (mm < Pg.M && vox_ok) ? R[i].w : 0.0f;
+        }
+    };
+    // transmit tables of the lane's voxel (the launch keeps Q N 4 < 2^32)
+    const char *tau_base = reinterpret_cast<const char *>(tau_tx);
+    const char *w_base = reinterpret_cast<const char *>(w_tx);
+    auto load_tx = [&](const RowsCursor &c) -> RowsTx {
+        const uint32_t o = ((uint32_t)(P.q_begin + c.ql) * (uint32_t)P.N + (uint32_t)n) * 4u;
+        return RowsTx{*reinterpret_cast<const float *>(tau_base + o), *reinterpret_cast<const float *>(w_base + o)};
+    };
+    // Sample split of the lane's items for one event: s = (tau_tx - t0) fs +
+    // d fs / c in fp64; the receive part folds in 1 - t0 fs, so s1 = s + 1.
+    // For s1 >= 0 its truncation is floor(s) + 1; below 0, a NaN or beyond
+    // 2^32 the conversion gives 0 or saturates, so one unsigned compare of
+    // k = trunc(s1) - 1 with K - 2 keeps exactly the terms with
+    // 0 <= floor(s) <= K - 2.  IQ: the phase exp(+j 2 pi f0 (tau_tx + d / c))
+    // on the absolute delay, event part times receive part.
+    auto make_steps = [&](RowsTx tx, RowsStep (&st)[NIT]) {
+        float epc = 1.0f, eps = 0.0f;
+        if constexpr (IQ) {
+            double cyc = (double)tx.tau * P.f0;
+            cyc -= __builtin_floor(cyc);
+            sincospif(2.0f * (float)cyc, &eps, &epc);
+        }
+#pragma unroll
+        for (int i = 0; i < NIT; ++i) {
+            const double s1 = __builtin_fma((double)tx.tau, P.fs, R[i].s_rx);
+            uint32_t k1;
+            asm("v_cvt_u32_f64 %0, %1" : "=v"(k1) : "v"(s1));    // saturating, unlike a C conversion
+            const uint32_t k = k1 - 1u;
+            const bool valid = k <= (uint32_t)(P.K - 2);
+            const float f = (float)__builtin_amdgcn_fract(s1);
+            const float w = valid ? tx.w * R[i].w : 0.0f;
+            const float bw = w * f, aw = w - bw;
+            st[i].k = (w != 0.0f) ? k : 0xffffffffu;
+            if constexpr (IQ) {
+                const float pc = epc * R[i].pc - eps * R[i].ps, ps = eps * R[i].pc + epc * R[i].ps;
+                st[i].a = aw * pc;
+                st[i].ai = aw * ps;
+                st[i].b = bw * pc;
+                st[i].bi = bw * ps;
+            } else {
+                st[i].a = aw;
+                st[i].b = bw;
+                st[i].ai = 0.0f;
+                st[i].bi = 0.0f;
+            }
+        }
+    };
+    // Window of a receiver over the wave's 8 voxels: the packed key
+    // kmin | (0xffff - kmax) << 16 reduced by 16-bit minima over lanes r,
+    // r + 8, ..., r + 56 (row rotation by 8, then row and half swaps).  Lane
+    // r of the wave then adds it to the tile's slots by LDS atomics.
+    auto wave_min8 = [&](uint32_t x) -> uint32_t {
+        x = das::pk_min_u16(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false));   // row_ror:8
+        const u2_t s = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        x = das::pk_min_u16(s.x, s.y);
+        const u2_t h = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return das::pk_min_u16(h.x, h.y);
+    };
+    auto publish = [&](const RowsStep (&st)[NIT], int set) {
+#pragma unroll
+        for (int i = 0; i < NIT; ++i) {
+            const uint32_t k = st[i].k;
+            const uint32_t key = (k != 0xffffffffu) ? (k | ((0xffffu - k) << 16)) : 0xffffffffu;
+            const uint32_t red = wave_min8(key);
+            const uint32_t kmin = red & 0xffffu;
+            if (v == 0 && kmin != 0xffffu) {
+                atomicMin(&slots[set * 2 * NRX + 8 * i + r], (int)kmin);
+                atomicMax(&slots[set * 2 * NRX + NRX + 8 * i + r], (int)(0xffffu - (red >> 16)));
+            }
+        }
+    };
+    auto advance = [&](RowsCursor &c) -> bool {
+        if (++c.ql < c.g1)
+            return true;
+        c.ql = c.g0;
+        c.m0 += NRX;
+        if (c.m0 < P.M)
+            return true;
+        c.m0 = 0;
+        c.g0 = c.g1;
+        c.g1 = min(c.g0 + P.q_group, P.q_count);
+        c.ql = c.g0;
+        return c.g0 < P.q_count;
+    };
+
+    // Window of a step whose slots are in set `set` and rows in buffer `buf`:
+    // per item the LDS addresses of its two rows, the row whose parity is the
+    // voxel's parity first, and the weights in that order.  An item with
+    // weight 0 reads the region's first two rows (finite; zero weights), in
+    // the same parity order, and so does every item of a step whose window
+    // exceeds a region (`overflow`: its terms come from direct loads).
+    auto make_window = [&](const RowsStep (&st)[NIT], int set, int buf) -> RowsWin<NIT> {
+        RowsWin<NIT> wdw;
+        int kmn[NIT];
+        bool over = false;
+#pragma unroll
+        for (int i = 0; i < NIT; ++i) {
+            kmn[i] = slots[set * 2 * NRX + 8 * i + r];
+            const int kmx = slots[set * 2 * NRX + NRX + 8 * i + r];
+            const int np = (kmn[i] <= kmx) ? kmx - kmn[i] + 1 : 0;
+            over = over || np > G::W_MAX;
+        }
+        // every wave covers all receivers of the step, so the vote agrees across the workgroup
+        wdw.overflow = __any(over) ? 1u : 0u;
+#pragma unroll
+        for (int i = 0; i < NIT; ++i) {
+            const bool on = st[i].k != 0xffffffffu && !wdw.overflow;
+            const uint32_t rel = on ? (uint32_t)((int)st[i].k - kmn[i]) : 0u;
+            const uint32_t first = (rel + vpar) & 1u;       // 1: row k + 1 first
+            const uint32_t base = (uint32_t)(buf * G::BUF + (8 * i + r) * G::REGION);
+            wdw.be[i] = base + (rel + first) * WR_ROWB;
+            wdw.bo[i] = base + (rel + 1u - first) * WR_ROWB;
+            wdw.we[i] = on ? (first ? st[i].b : st[i].a) : 0.0f;
+            wdw.wo[i] = on ? (first ? st[i].a : st[i].b) : 0.0f;
+            wdw.wei[i] = on ? (first ? st[i].bi : st[i].ai) : 0.0f;
+            wdw.woi[i] = on ? (first ? st[i].ai : st[i].bi) : 0.0f;
+        }
+        return wdw;
+    };
+
+    // Copy of one receiver's rows by LDS-DMA: waves S w' .. S w' + S - 1
+    // copy receiver m0 + w', taking every S-th round.  A round moves 8 rows:
+    // lane (rho, c) fetches 16 bytes (chunk c of the frame tile's part) of row
+    // kmin + 8 round + rho, which the DMA writes at 16 lane past the round's
+    // LDS base, i.e. row rho, chunk c of the region.  KQMB: every offset is
+    // 32-bit (the launch keeps the chunk under 4 GiB).  QMKB: the resource is
+    // rebased per step on the (event, receiver block) plane, in 64-bit scalar
+    // arithmetic.  A receiver whose window exceeds its region is not copied
+    // (the step then reads the permuted buffer).
+    const das::BufRsrc rs_chunk = das::make_rsrc(rf_bytes, (uint64_t)chunk_bytes);
+    const int wrx = wave / G::S, wpart = wave % G::S;
+    const int crow = lane >> 3;
+    const uint32_t coff = (uint32_t)crow * kstride32 + (uint32_t)(lane & 7) * 16u + (uint32_t)b0 * E;
+    auto copy_prepare = [&](const RowsCursor &c, int set, int buf) -> RowsCopy {
+        const int kmn = __builtin_amdgcn_readfirstlane(slots[set * 2 * NRX + wrx]);
+        const int kmx = __builtin_amdgcn_readfirstlane(slots[set * 2 * NRX + NRX + wrx]);
+        const int np = (kmn <= kmx) ? kmx - kmn + 1 : 0;
+        const int rows = (np > 0 && np <= G::W_MAX) ? np + 1 : 0;         // rows kmin .. kmax + 1
+        const int nr = (rows + 7) / 8;
+        const uint32_t dst = (uint32_t)(buf * G::BUF + wrx * G::REGION);
+        const uint32_t kmin = (uint32_t)(rows ? kmn : 0);
+        if constexpr (LAYOUT == DAS_LAYOUT_QMKB) {
+            const int64_t plane = ((int64_t)c.ql * P.M + c.m0) * m_stride;
+            return RowsCopy{nr, rows, (uint32_t)wrx * m_stride + kmin * kstride32, dst,
+                            das::make_rsrc(rf_bytes + plane, (uint64_t)(chunk_bytes - plane))};
+        } else {
+            return RowsCopy{nr, rows,
+                            ((uint32_t)c.ql * (uint32_t)P.M + (uint32_t)(c.m0 + wrx)) * m_stride + kmin * kstride32,
+                            dst, rs_chunk};
+        }
+    };
+    auto copy_round = [&](const RowsCopy &cp, int j) {
+        const int rr = j * G::S + wpart;                       // round of the receiver's copy
+        if (rr < cp.nr && rr * 8 + crow < cp.rows) {
+            const das::lds_ptr dst = (das::lds_ptr)(lds + cp.dst + (uint32_t)(rr * 8 * WR_ROWB));
+            das::buffer_load_lds(cp.rs, dst, 16, (int)coff, (int)(cp.start + (uint32_t)(rr * 8) * kstride32), 0, 0);
+        }
+    };
+
+    // ---- interpolate-weight-accumulate ------------------------------------
+    // acc[4 s + j]: fp32 frame 4 s + j of the frame tile; complex: (re, im)
+    // of frames 2 s and 2 s + 1.  Unit u = 8 i + s of a step is chunk s (16
+    // bytes) of item i's two rows: two reads, 8 (complex: 16) FMAs.
+    float acc[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
+    using LdsF4 = const volatile __attribute__((address_space(3))) f4_t *;
+    struct Ring {
+        f4_t e[DEPTH], o[DEPTH];
+    };
+    auto issue_unit = [&](auto U, const RowsWin<NIT> &wd, Ring &ring) {
+        constexpr int u = decltype(U)::value, i = u / 8, s = u % 8;
+        ring.e[u % DEPTH] = *(LdsF4)(lds + wd.be[i] + 16 * s);
+        ring.o[u % DEPTH] = *(LdsF4)(lds + wd.bo[i] + 16 * s);
+    };
+    auto fma_chunk = [&](int s, float we, float wei, float wo, float woi, const f4_t &xe, const f4_t &xo) {
+        if constexpr (IQ) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float &re = acc[4 * s + 2 * j], &im = acc[4 * s + 2 * j + 1];
+                re = __builtin_fmaf(we, xe[2 * j], re);
+                im = __builtin_fmaf(we, xe[2 * j + 1], im);
+                re = __builtin_fmaf(-wei, xe[2 * j + 1], re);
+                im = __builtin_fmaf(wei, xe[2 * j], im);
+                re = __builtin_fmaf(wo, xo[2 * j], re);
+                im = __builtin_fmaf(wo, xo[2 * j + 1], im);
+                re = __builtin_fmaf(-woi, xo[2 * j + 1], re);
+                im = __builtin_fmaf(woi, xo[2 * j], im);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[4 * s + j] = __builtin_fmaf(we, xe[j], acc[4 * s + j]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[4 * s + j] = __builtin_fmaf(wo, xo[j], acc[4 * s + j]);
+        }
+    };
+    auto fma_unit = [&](auto U, const RowsWin<NIT> &wd, const f4_t &xe, const f4_t &xo) {
+        constexpr int u = decltype(U)::value, i = u / 8, s = u % 8;
+        float (&ac)[32] = acc;                   // (a non-dependent use, so the generic lambda captures it)
+        fma_chunk(s, wd.we[i], wd.wei[i], wd.wo[i], wd.woi[i], xe, xo);
+        // pin the chunk's sums here: left alone the compiler sinks the FMAs
+        // to the end of the step and keeps every unit's rows live
+#pragma unroll
+        for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(ac[4 * s + j]));
+    };
+    // Units U0 .. U1 - 1 in one pipeline, the reads running DEPTH units ahead
+    // of their FMAs (the scheduling fences keep the compiler from sinking
+    // each read next to its use), the next step's copy rounds spread over it.
+    // A SIMD issues from its oldest ready wave first; each wave lowers its
+    // own priority as it gets through the loop, so that the waves behind
+    // catch up and all reach the barrier together.
+    auto pipeline = [&](auto U0, auto U1, const RowsWin<NIT> &wd, const RowsCopy &cp) {
+        constexpr int u0 = decltype(U0)::value, nu = decltype(U1)::value - u0;
+        constexpr int spread = (nu / G::MAXR) > 3 ? 3 : (nu / G::MAXR);
+        static_assert(spread >= 1 && spread * (G::MAXR - 1) + spread / 2 < nu, "every copy round is issued");
+        Ring ring;
+        das::unroll<DEPTH>([&](auto U) { issue_unit(das::ic<u0 + decltype(U)::value>{}, wd, ring); });
+        __builtin_amdgcn_sched_barrier(0);
+        das::unroll<nu>([&](auto L) {
+            constexpr int l = decltype(L)::value, u = u0 + l;
+            fma_unit(das::ic<u>{}, wd, ring.e[u % DEPTH], ring.o[u % DEPTH]);
+            if constexpr (l + DEPTH < nu)
+                issue_unit(das::ic<u + DEPTH>{}, wd, ring);
+            if constexpr (l % spread == spread / 2 && l / spread < G::MAXR)
+                copy_round(cp, l / spread);
+            if constexpr ((l + 1) % (nu / 4) == 0 && l + 1 < nu)
+                __builtin_amdgcn_s_setprio(3 - (l + 1) / (nu / 4));
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    // The step's items in one pipeline.
+    // Separate ifs without elses (each updates the sums in place; an if /
+    // else chain would carry a copy of them per branch to the join).
+    // (A wave could skip the items none of its lanes has with a non-zero
+    // weight, but a pipeline inside a branch makes the compiler keep a second
+    // copy of the sums: they spill.)
+    auto compute_lds = [&](const RowsWin<NIT> &wd, const RowsCopy &cp) {
+        using das::ic;
+        pipeline(ic<0>{}, ic<8 * NIT>{}, wd, cp);
+    };
+    // A step by direct loads from the permuted buffer (a window too wide for
+    // the regions): each item with a non-zero weight reads its two rows.
+    auto compute_direct = [&](const RowsStep (&st)[NIT], const RowsCursor &c) {
+        const int64_t pos = ((int64_t)c.ql * P.M + c.m0) * m_stride;
+        const das::BufRsrc rd = das::make_rsrc(rf_bytes + pos, (uint64_t)(chunk_bytes - pos));
+#pragma unroll
+        for (int i = 0; i < NIT; ++i) {
+            if (st[i].k == 0xffffffffu)
+                continue;
+            const uint32_t o0 = (uint32_t)(8 * i + r) * m_stride + st[i].k * kstride32 + (uint32_t)b0 * E;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const f4_t x0 = das::buffer_load_f32x4(rd, (int)(o0 + 16u * s), 0, 0);
+                const f4_t x1 = das::buffer_load_f32x4(rd, (int)(o0 + kstride32 + 16u * s), 0, 0);
+                fma_chunk(s, st[i].a, st[i].ai, st[i].b, st[i].bi, x0, x1);
+            }
+        }
+    };
+
+    // ---- prologue: windows of steps 0 and 1, rows of step 0 ----------------
+    // Step i: rows in buffer i % 2, window slots in set i % 4.  During step i
+    // the rows of step i + 1 are copied (its slots read), the window of step
+    // i + 2 is published, after its products the lanes read the window of
+    // step i + 1, and the set of step i - 1 is cleared: its last reads were
+    // in step i - 1 and its next publication is in step i + 1, each on the
+    // other side of a barrier.
+    RowsCursor cur{0, 0, 0, min(P.q_group, P.q_count)};
+    load_geometry(cur.m0);
+    RowsStep s_cur[NIT], s_nxt[NIT], s_spare[NIT];
+    make_steps(load_tx(cur), s_cur);
+    publish(s_cur, 0);
+    RowsCursor nxt = cur;
+    bool has_next = advance(nxt);
+    RowsCursor nxt2 = nxt;
+    bool has_next2 = has_next && advance(nxt2);
+    if (has_next) {
+        if (nxt.m0 != cur.m0)
+            load_geometry(nxt.m0);
+        make_steps(load_tx(nxt), s_nxt);
+        publish(s_nxt, 1);
+    }
+    // transmit tables of step i + 2, read a step ahead
+    RowsTx tx_a{0.0f, 0.0f}, tx_b{0.0f, 0.0f};
+    if (has_next2)
+        tx_a = load_tx(nxt2);
+    __syncthreads();
+    RowsWin<NIT> w_cur = make_window(s_cur, 0, 0);
+    {
+        const RowsCopy cp0 = copy_prepare(cur, 0, 0);
+#pragma unroll
+        for (int j = 0; j < G::MAXR; ++j) copy_round(cp0, j);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);                  // vmcnt(0): this wave's copy has landed
+    __syncthreads();
+
+    // ---- main loop -----------------------------------------------------------
+    // The item states rotate with period 3 and the transmit tables with
+    // period 2, so the loop body is six steps with the roles passed as
+    // references and no state copied between steps (a three-step body with a
+    // third table role measured 7% slower on the Main workload).
+    int set = 0, buf = 0;
+    auto step = [&](auto Last, RowsStep (&sc)[NIT], RowsStep (&sn)[NIT], RowsStep (&sn2)[NIT], RowsTx &t2,
+                    RowsTx &t3) __attribute__((always_inline)) -> bool {
+        constexpr bool can_end = decltype(Last)::value;
+        const bool hn = can_end ? has_next : true;
+        __builtin_amdgcn_s_setprio(3);                   // every wave starts a step at the top priority
+        const int set1 = (set + 1) & 3, set2 = (set + 2) & 3, set3 = (set + 3) & 3;
+        // the next step's copy (its window was published during the last step)
+        RowsCopy cp{0, 0, 0, 0, rs_chunk};
+        if (hn)
+            cp = copy_prepare(nxt, set1, buf ^ 1);
+        // The step after next: geometry (a new receiver block), sample split,
+        // window publication.  Latency-bound fp64 work, done while all waves
+        // of a SIMD are busy with it.
+        RowsCursor nxt3 = nxt2;
+        const bool has_next3 = has_next2 && advance(nxt3);
+        if (has_next2) {
+            if (nxt2.m0 != nxt.m0)
+                load_geometry(nxt2.m0);
+            make_steps(t2, sn2);
+            publish(sn2, set2);
+            if (has_next3)
+                t3 = load_tx(nxt3);                       // consumed two steps on
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        compute_lds(w_cur, cp);
+        // A step whose window exceeds a region takes its terms from direct
+        // loads (its LDS loop ran with zero weights).  One if without an else,
+        // so the sums are updated in place (an if / else that updated them on
+        // both sides would carry a second copy of them to the join).
+        if (w_cur.overflow)
+            compute_direct(sc, cur);
+        if (hn)
+            w_cur = make_window(sn, set1, buf ^ 1);
+        if (tid < 2 * NRX)                               // the previous step's slots
+            slots[set3 * 2 * NRX + tid] = (tid < NRX) ? INT_MAX : INT_MIN;
+        cur = nxt;
+        nxt = nxt2;
+        nxt2 = nxt3;
+        has_next = has_next2;
+        has_next2 = has_next3;
+        set = set1;
+        buf ^= 1;
+        if (!hn)
+            return false;
+        __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0): this wave's copy has landed
+        __syncthreads();                                 // rows read, the next step's in place
+        return true;
+    };
+    using das::ic;
+    const int nsteps = P.q_count * ((P.M + NRX - 1) / NRX);
+    for (int left = nsteps; left >= 7; left -= 6) {
+        step(ic<0>{}, s_cur, s_nxt, s_spare, tx_a, tx_b);
+        step(ic<0>{}, s_nxt, s_spare, s_cur, tx_b, tx_a);
+        step(ic<0>{}, s_spare, s_cur, s_nxt, tx_a, tx_b);
+        step(ic<0>{}, s_cur, s_nxt, s_spare, tx_b, tx_a);
+        step(ic<0>{}, s_nxt, s_spare, s_cur, tx_a, tx_b);
+        step(ic<0>{}, s_spare, s_cur, s_nxt, tx_b, tx_a);
+    }
+    while (step(ic<1>{}, s_cur, s_nxt, s_spare, tx_a, tx_b)) {
+#pragma unroll
+        for (int i = 0; i < NIT; ++i) {
+            const RowsStep sv = s_cur[i];
+            s_cur[i] = s_nxt[i];
+            s_nxt[i] = s_spare[i];
+            s_spare[i] = sv;
+        }
+        const RowsTx tt = tx_a;
+        tx_a = tx_b;
+        tx_b = tt;
+    }
+
+    // ---- output ----------------------------------------------------------------
+    // The 8 lanes of a voxel (r = 0..7) hold sums over different receivers:
+    // add them (pair, quad and half-row DPP), then lane r writes chunk r.
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        float x = acc[j];
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+        acc[j] = x;
+    }
+    if (!vox_ok)
+        return;
+    float val[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        val[j] = acc[j];
+#pragma unroll
+        for (int s = 1; s < 8; ++s) val[j] = (r == s) ? acc[4 * s + j] : val[j];
+    }
+    if constexpr (IQ) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            float *o = out + ((int64_t)(b0 + 2 * r + j) * P.N + n) * 2;
+            o[0] = P.accumulate ? o[0] + val[2 * j] : val[2 * j];
+            o[1] = P.accumulate ? o[1] + val[2 * j + 1] : val[2 * j + 1];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float *o = out + (int64_t)(b0 + 4 * r + j) * P.N + n;
+            *o = P.accumulate ? *o + val[j] : val[j];
+        }
+    }
+}
+
+template <bool IQ, int LAYOUT, int NIT>
+hipError_t launch_rows(const DasKParams &kp, const float *rf, const float *rx, const float *tau, const float *w,
+                       float *out, hipStream_t stream) {
+    constexpr int FR = WR_ROWB / (IQ ? 8 : 4);
+    const int tiles = ((kp.nx + WR_TX - 1) / WR_TX) * ((kp.ny + WR_TY - 1) / WR_TY) * ((kp.nz + WR_TZ - 1) / WR_TZ);
+    hipLaunchKernelGGL((das_bi_rows_kernel<IQ, LAYOUT, NIT>), dim3(tiles, kp.B / FR), dim3(WR_THREADS), 0, stream, kp,
+                       rf, rx, tau, w, out);
+    return hipGetLastError();
+}
+
+template <bool IQ, int LAYOUT>
+hipError_t launch_rows_nit(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
+                           const float *tau, const float *w, float *out, hipStream_t stream) {
+    if constexpr (IQ)                                    // complex plans take 8 receivers a step
+        return launch_rows<IQ, LAYOUT, 1>(kp, rf, rx, tau, w, out, stream);
+    else
+        return plan.rows == 2 ? launch_rows<IQ, LAYOUT, 2>(kp, rf, rx, tau, w, out, stream)
+                              : launch_rows<IQ, LAYOUT, 1>(kp, rf, rx, tau, w, out, stream);
+}
+
+}  // namespace
+
+bool das_rows_supported(const das_plan_t &plan) {
+    // native samples, 128-byte frame tiles (fp32: B a multiple of 32;
+    // complex64: of 16), sample indices below 2^16 in the window keys
+    if (plan.h16 || plan.p.K > 65535)
+        return false;
+    return (plan.p.dtype == DAS_F32 && plan.p.B % 32 == 0) || (plan.p.dtype == DAS_C64 && plan.p.B % 16 == 0);
+}
+
+hipError_t das_launch_bi_rows(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
+                              const float *tau_tx, const float *w_tx, float *out, hipStream_t stream) {
+    const bool iq = plan.p.dtype == DAS_C64;
+    if (plan.p.layout == DAS_LAYOUT_KQMB)
+        return iq ? launch_rows_nit<true, DAS_LAYOUT_KQMB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream)
+                  : launch_rows_nit<false, DAS_LAYOUT_KQMB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream);
+    return iq ? launch_rows_nit<true, DAS_LAYOUT_QMKB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream)
+              : launch_rows_nit<false, DAS_LAYOUT_QMKB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream);
+}

@@ -49,6 +49,8 @@ struct das_plan {
                               // 64 fp32 / 32 complex frames, 8 receivers a step), else 1
     int32_t h16;              // batch-inner: the permuted buffer holds binary16 samples (DAS_STORE_F16)
     int32_t store_bytes;      // bytes per sample in the permuted buffer (elem_bytes, or half that with h16)
+    int32_t rows;             // staged kernel: 0 = DPP-row lanes; 1 or 2 = whole-row lanes with 8 or 16
+                              // receivers a step
 };
 
 // Launchers (defined next to their kernels).  They assume validated input.
@@ -61,6 +63,11 @@ hipError_t das_launch_baseline_f64(const das_plan_t &plan, const DasKParams &kp,
                                    const float *rx, const float *tau_tx, const float *w_tx,
                                    double *out, hipStream_t stream);
 bool das_staged_supported(const das_plan_t &plan);
+// Whole-row lanes (das_bi_rows.hip): native fp32 with B a multiple of 32 or
+// complex64 with B a multiple of 16, K below 2^16.
+bool das_rows_supported(const das_plan_t &plan);
+hipError_t das_launch_bi_rows(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
+                              const float *tau_tx, const float *w_tx, float *out, hipStream_t stream);
 hipError_t das_launch_batch_inner_staged(const das_plan_t &plan, const DasKParams &kp, const float *rf,
                                          const float *rx, const float *tau_tx, const float *w_tx, float *out,
                                          hipStream_t stream);
