@@ -46,14 +46,30 @@ LDS_BCLK = {
 _COMMENT = re.compile(r"/\*.*?\*/|//[^\n]*", re.S)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the kernel sources' code (comments and whitespace dropped); a
-    stored counter reading is valid only for the same hash."""
+# the source file of each kernel; a stored reading depends on it, on the
+# shared device headers and on the host code that picks and launches it
+KERNEL_SOURCES = {
+    "das_bi_rows_kernel": "das_bi_rows.hip",
+    "das_bi_staged_kernel": "das_batch_inner_staged.hip",
+    "das_batch_inner_kernel": "das_batch_inner.hip",
+    "das_baseline_kernel": "das_baseline.hip",
+    "das_baseline_f64_kernel": "das_baseline_f64.hip",
+    "das_repack_kernel": "das_repack.hip",
+    "permute_f32_kernel": "das_permute.hip",
+    "tx_tables_kernel": "das_tx.hip",
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the code (comments and whitespace dropped) of a kernel's source
+    file, the shared headers and the host API; a stored counter reading is
+    valid only for the same hash."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "volumetric_delay_sum_amd", "csrc", "*"))):
-        with open(f, encoding="utf-8", errors="replace") as fh:
+    csrc = os.path.join(ROOT, "volumetric_delay_sum_amd", "csrc")
+    for name in sorted({KERNEL_SOURCES[kernel], "das_device.h", "das_internal.h", "das_api.cpp"}):
+        with open(os.path.join(csrc, name), encoding="utf-8", errors="replace") as fh:
             code = " ".join(_COMMENT.sub(" ", fh.read()).split())
-        h.update(os.path.basename(f).encode())
+        h.update(name.encode())
         h.update(code.encode())
     return h.hexdigest()[:16]
 
@@ -66,7 +82,7 @@ def stored_traffic(kernel: str, workload: str):
     try:
         data = json.load(open(path))
         rec = data.get(f"{kernel}:{workload}")
-        if rec and rec.get("source_hash") == kernel_source_hash():
+        if rec and rec.get("source_hash") == kernel_source_hash(kernel):
             return rec.get("hbm_bytes_per_launch")
     except Exception:
         return None
@@ -93,20 +109,6 @@ def delivery_ceiling(plan, iq: bool, h16: bool):
     bclk = LDS_BCLK[pattern]
     return {"bytes_per_accumulation": 2 * sample, "lane_tap_bytes": lane, "read_pattern": pattern,
             "lds_B_per_clk_per_cu": bclk, "ceiling_gacc_s": CUS * SCLK_HZ * bclk / (2 * sample) / 1e9}
-
-
-def stored_counter(kernel: str, workload: str, name: str):
-    """A per-launch counter value from the committed summary, if it matches these sources."""
-    path = os.path.join(ROOT, "profiles", "counters.json")
-    if not os.path.exists(path):
-        return None
-    try:
-        rec = json.load(open(path)).get(f"{kernel}:{workload}")
-        if rec and rec.get("source_hash") == kernel_source_hash():
-            return rec.get(name)
-    except Exception:
-        return None
-    return None
 
 
 def oracle_rates(oracle, fields, cfg, rf_host, rx, tau, w, cap: int, threads: int):
@@ -160,7 +162,19 @@ def main():
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="threads of the multi-core oracle rate (0: the host's cores available to this process, "
                          "at most 16)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of 1 GiB, three times (a kernel of known HBM bytes for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings), and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        a = torch.randn(1 << 28, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"copy calibration: 3 copies of {a.numel() * 4} bytes", file=sys.stderr)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "

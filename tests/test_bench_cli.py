@@ -24,8 +24,11 @@ def test_source_hash_ignores_comments_and_layout():
     strip = lambda t: " ".join(bench._COMMENT.sub(" ", t).split())
     assert strip(a) == strip(b)
     assert strip("return x + 2;") != strip("return x + 1;")
-    h = bench.kernel_source_hash()
-    assert len(h) == 16 and h == bench.kernel_source_hash()
+    h = bench.kernel_source_hash("das_bi_rows_kernel")
+    assert len(h) == 16 and h == bench.kernel_source_hash("das_bi_rows_kernel")
+    # each kernel's readings depend on its own source: the hashes differ
+    hashes = {bench.kernel_source_hash(k) for k in bench.KERNEL_SOURCES}
+    assert len(hashes) == len(bench.KERNEL_SOURCES)
 
 
 def test_stored_traffic_is_none_for_an_unmeasured_workload():
