@@ -7,8 +7,9 @@
  * tables, receive delays and weights are computed in the kernel from the
  * receiver geometry; tensor-core paragraphs: each voxel uses the two samples
  * k and k+1 of each receiver with an interpolation weight per sample; ffdas
- * docs, "How It Works", The computational challenge: interpolate and sum the
- * aligned samples of every receiver and transmit event for each voxel):
+ * docs, "How It Works", The computational challenge: a voxel's value sums,
+ * over all transmit events and receivers, the samples interpolated at that
+ * voxel's delays):
  *
  *   y[b,n] = sum_q sum_m  w_tx[q,n] * w_rx[m,n] * v(b,q,m,n)
  *   tau    = tau_tx[q,n] + |r_n - p_m| / c

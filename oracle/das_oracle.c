@@ -11,8 +11,9 @@
  * weights are per-voxel tables while receive delays and weights come from the
  * receiver geometry; the tensor-core paragraphs say each voxel needs only the
  * two samples k and k+1 of each receiver, with an interpolation weight per
- * sample; "How It Works" on the ffdas docs: DAS interpolates and sums the
- * aligned samples from every receiver and transmit event for each voxel):
+ * sample; "How It Works" on the ffdas docs, The computational challenge:
+ * a voxel's value is the sum, over all transmit events and receivers, of
+ * the interpolated samples taken at that voxel's delays):
  *
  *   y[b,n] = sum_q sum_m  w_tx[q,n] * w_rx[m,n] * v(b,q,m,n)
  *   tau    = tau_tx[q,n] + |r_n - p_m| / c
