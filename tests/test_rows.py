@@ -95,3 +95,29 @@ def test_main_sampled(gpu, monkeypatch, rows, iq):
     out = run_gpu(inp, "batch_inner", "qmkb")
     assert_all_written(out, f"main rows={rows} iq={iq}")
     assert_parity(to_numpy(out, iq)[:, vox], oracle_ref(inp, voxels=vox), f"main rows={rows} iq={iq}")
+
+
+@pytest.mark.parametrize("rows,iq", VARIANTS, ids=IDS)
+def test_tiles_outside_every_aperture(gpu, monkeypatch, rows, iq):
+    """A volume much wider than the array: the outer tiles (8 voxels wide
+    along x) see no receiver inside their cones and skip every receiver
+    block, the next ones keep a few blocks, the central ones all.  Every voxel whose receive weights
+    are all zero comes out exactly 0 (and exactly unchanged when accumulating),
+    the rest meet the usual bar."""
+    import torch
+    _use(monkeypatch, rows)
+    cfg = _ragged(iq, B=32, K=400, array=(16, 4), grid=(40, 9, 4), voxel=0.5e-3, z0=2e-3, f_number=2.0,
+                  sources=((0.0, 0.0), (1e-3, 0.0)))
+    inp = Inputs(cfg, w_tx="uniform")
+    ref = oracle_ref(inp)
+    y = to_numpy(run_gpu(inp, "batch_inner", "qmkb"), iq)
+    zero = ref == 0.0
+    assert 0.5 < zero.mean() < 0.99, zero.mean()
+    assert np.array_equal(y == 0.0, zero)
+    assert_parity(y, ref, f"rows={rows} iq={iq} apertures")
+    shape = (cfg.B, cfg.N, 2) if iq else (cfg.B, cfg.N)
+    start = torch.linspace(-3.0, 3.0, int(np.prod(shape)), device="cuda").reshape(shape)
+    out = run_gpu(inp, "batch_inner", "qmkb", out=start.clone(), accumulate_into=True)
+    got, base = to_numpy(out, iq), to_numpy(start, iq)
+    assert np.array_equal(got[zero], base[zero])
+    assert_parity(got - base, ref, f"rows={rows} iq={iq} apertures accumulate")

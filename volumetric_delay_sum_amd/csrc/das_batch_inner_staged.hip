@@ -463,7 +463,7 @@ __global__ __launch_bounds__(THREADS) void das_bi_staged_kernel(DasKParams P, co
     // rounds).
     constexpr int NITEM = G::NITEM;
     constexpr bool WTAB = G::WTAB;
-    constexpr int DEPTH = (VPR == 1) ? 8 : (WTAB ? 2 : 3);
+    constexpr int DEPTH = (VPR == 1) ? 8 : ((WTAB || IQ) ? 2 : 3);
     // The first DEPTH items' reads are issued by prefetch(), for fp32 data at
     // the top of the step, so they land while the setup runs.
     using CoefV = typename Tap<G::CW>::type;

@@ -9,7 +9,7 @@
 //
 //   - A lane owns one voxel of the 8 x 8 x 2 tile, ALL frames of the frame
 //     tile (128 bytes of a sample row: 32 fp32 or 16 complex frames) and, in
-//     each step, one receiver of every group of 8.  Each (voxel, receiver)
+//     each step, one receiver of every block of 8 the step takes.  Each (voxel, receiver)
 //     item is the lane's own: it computes the item's sample split and weights
 //     and applies them itself, so the item's 64 (complex: 128) FMAs take
 //     register weights (plain FMAs, nothing crosses lanes in the inner loop),
@@ -25,14 +25,22 @@
 //     rows the lanes need (the LDS serves it in one pass); in plain order the
 //     same reads conflict up to 8 ways.
 //
-// Per step (transmit event, 8 NIT receivers): the window [kmin, kmax] of k
-// over the tile's voxels with a non-zero weight is reduced per receiver (in
-// the wave by DPP and lane swaps on packed 16-bit minima, across waves by LDS
-// atomics) two steps ahead; the receivers' rows kmin .. kmax + 1 are copied
-// by LDS-DMA into the other of two buffers during the step before; one
-// barrier ends a step.  A lane's sums cover its receivers; the 8 lanes of a
-// voxel add them up once at the end (DPP).  A step whose window exceeds a
-// region reads its rows straight from the permuted buffer.
+// Receive aperture.  The receive weight is zero outside the f-number cone of
+// a receiver, and for a tile near the surface most of the array's receivers
+// see none of its voxels.  At its start a workgroup marks the blocks of 8
+// receivers that have a non-zero weight for some voxel of the tile (a test
+// with a margin, so no block with a non-zero weight is left out); its sweep
+// then takes only those blocks, NIT a step.  Skipped terms are exact zeros,
+// so the sums are those of the full sweep up to the order of addition.
+//
+// Per step (transmit event, NIT blocks of 8 receivers): the window [kmin,
+// kmax] of k over the tile's voxels with a non-zero weight is reduced per
+// receiver (over voxel pairs by DPP, across the tile by LDS atomics) two
+// steps ahead; the receivers' rows kmin .. kmax + 1 are copied by LDS-DMA
+// into the other of two buffers during the step before; one barrier ends a
+// step.  A lane's sums cover its receivers; the 8 lanes of a voxel add them
+// up once at the end (DPP).  A step whose window exceeds a region reads its
+// rows straight from the permuted buffer.
 #include "das_device.h"
 
 namespace {
@@ -41,19 +49,20 @@ constexpr int WR_THREADS = 1024;
 constexpr int WR_TX = 8, WR_TY = 8, WR_TZ = 2;   // voxel tile of a workgroup
 constexpr int WR_ROWB = 128;                     // bytes of one staged sample row (the frame tile's part)
 constexpr int WR_LDS_TOTAL = 163840;             // LDS of one workgroup on gfx950 (160 KiB)
+constexpr int WR_LIVE_BLOCKS = 512;              // 8-receiver blocks a launch may have (M <= 4096)
 
 typedef float f4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
 
 // Sizes of one instance: NIT items (receiver groups of 8) per lane and step.
 template <int NIT>
 struct RowsGeo {
     static constexpr int NRX = 8 * NIT;                                      // receivers per step
     static constexpr int SLOTS = 4 * 2 * NRX * 4;                            // window slots [4 sets][min, max][NRX]
-    static constexpr int RW = ((WR_LDS_TOTAL - SLOTS) / (2 * NRX) - 16) / WR_ROWB;   // sample rows per region
+    static constexpr int LIVE_WORDS = WR_LIVE_BLOCKS / 32;                   // receiver-block mask
+    static constexpr int RW = ((WR_LDS_TOTAL - SLOTS - 4 * LIVE_WORDS) / (2 * NRX) - 16) / WR_ROWB;   // sample rows per region
     static constexpr int REGION = RW * WR_ROWB + 16;                         // one receiver's rows, padded
     static constexpr int BUF = NRX * REGION;                                 // one row buffer
-    static constexpr int LDS_BYTES = 2 * BUF + SLOTS;
+    static constexpr int LDS_BYTES = 2 * BUF + SLOTS + 4 * LIVE_WORDS;
     static constexpr int W_MAX = RW - 1;                                     // k positions of a window
     static constexpr int S = 16 / NRX;                                       // waves sharing one receiver's copy
     static constexpr int MAXR = (RW + 8 * S - 1) / (8 * S);                  // copy rounds of one wave
@@ -71,8 +80,12 @@ struct RowsStep {
     float a, b, ai, bi;
 };
 
+// Position in the sweep: event ql of the group [g0, g1), and the live
+// 8-receiver blocks of the step (blk[i] >= the block count: none).
+template <int NIT>
 struct RowsCursor {
-    int ql, m0, g0, g1;
+    int ql, g0, g1;
+    int blk[NIT];
 };
 
 struct RowsTx {
@@ -109,21 +122,34 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     constexpr int FR = WR_ROWB / E;              // frames of a frame tile
     constexpr int DEPTH = 3;                     // units whose reads are in flight
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
-    int *slots = reinterpret_cast<int *>(lds + 2 * G::BUF);
+    uint32_t *slots = reinterpret_cast<uint32_t *>(lds + 2 * G::BUF);
+    uint32_t *live = reinterpret_cast<uint32_t *>(lds + 2 * G::BUF + G::SLOTS);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int r = lane & 7;                      // receiver of each group: item i is receiver m0 + 8 i + r
+    const int r = lane & 7;                      // receiver of each block: item i is receiver 8 blk[i] + r
     const int v = lane >> 3;                     // voxel in the wave's row of 8
     const uint32_t vpar = (uint32_t)v & 1u;
 
     const int tiles_x = (P.nx + WR_TX - 1) / WR_TX, tiles_y = (P.ny + WR_TY - 1) / WR_TY;
-    int t = das::xcd_tile(blockIdx.x, gridDim.x);
-    const int tx = t % tiles_x;
-    t /= tiles_x;
-    const int ty = t % tiles_y;
-    const int tz = t / tiles_y;
+    const int tiles_z = (P.nz + WR_TZ - 1) / WR_TZ;
+    const int lat = tiles_x * tiles_y;
+    // Workgroup b runs on die b % 8 (of the MI355X's eight, each with its
+    // own L2).  Tiles go deepest first (with the receive aperture a tile's
+    // work grows with depth).  Within a depth, die x takes a chunk of
+    // lat / 8 neighbouring tiles (a row of tiles when the rows are 8 long),
+    // the chunk rotating with depth so that every die gets as much edge and
+    // centre of the volume as the others, and so about the same work.
+    const int bd = (int)blockIdx.x / lat, bw = (int)blockIdx.x % lat;
+    int bj = bw;
+    if (lat % 8 == 0) {
+        const int per = lat / 8, x = bw % 8, k = bw / 8;
+        bj = ((x + bd) % 8) * per + (k + bd) % per;
+    }
+    const int tz = tiles_z - 1 - bd;
+    const int ty = bj / tiles_x;
+    const int tx = bj % tiles_x;
     const int ix = tx * WR_TX + v, iy = ty * WR_TY + (wave & 7), iz = tz * WR_TZ + (wave >> 3);
     const bool vox_ok = ix < P.nx && iy < P.ny && iz < P.nz;
     const int ixc = min(ix, P.nx - 1), iyc = min(iy, P.ny - 1), izc = min(iz, P.nz - 1);
@@ -144,8 +170,74 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     for (int i = tid * 16; i < 2 * G::BUF; i += WR_THREADS * 16)
         *reinterpret_cast<int4 *>(lds + i) = make_int4(0, 0, 0, 0);
     if (tid < 4 * 2 * NRX)
-        slots[tid] = ((tid / NRX) & 1) ? INT_MIN : INT_MAX;
+        slots[tid] = ((tid / NRX) & 1) ? 0u : 0xffffffffu;
+    const int nblk = (P.M + 7) / 8;
+    for (int i = tid; i < G::LIVE_WORDS; i += WR_THREADS)
+        live[i] = P.apod ? 0u : 0xffffffffu;
     __syncthreads();
+
+    // ---- receive aperture of the tile ------------------------------------------
+    // A block of 8 receivers whose receive weight is zero for every voxel of
+    // the tile adds nothing: the sweep skips it, and a step takes the next NIT
+    // live blocks.  A pair counts as
+    // zero only when it is clearly outside the aperture or behind the array,
+    // by a margin far above the rounding of this fp32 test and of the
+    // weight's own: cos^2 theta <= cos^2 theta_max / (1 + 1e-3 (1 - cos^2
+    // theta_max)), i.e. dz^2 (1 - c^2)(1 + 1e-3) <= c^2 rho^2 with dz > 0, or
+    // dz below zero by more than its rounding.  Lane (v, r) tests receiver
+    // r of each block against its voxel; a wave's vote goes to the mask by
+    // one atomic per block.
+    if (P.apod) {
+        const float ctm = 1.0f - 1.0f / P.apod_inv_vmax;                 // cos theta_max
+        const float ca = (1.0f - ctm * ctm) * 1.001f, cb = ctm * ctm;
+        const float fvx = (float)(P.ox + (double)ixc * P.sx), fvy = (float)(P.oy + (double)iyc * P.sy);
+        const float fvz = (float)(P.oz + (double)izc * P.sz);
+        constexpr int UNR = 4;
+        for (int b0 = 0; b0 < nblk; b0 += UNR) {
+            bool any[UNR];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                any[u] = false;
+                const int m = (b0 + u) * 8 + r;
+                const int mc = min(m, P.M - 1);
+                const float dx = fvx - rx[3 * mc], dy = fvy - rx[3 * mc + 1], dz = fvz - rx[3 * mc + 2];
+                const float rho2 = __builtin_fmaf(dx, dx, dy * dy), dz2 = dz * dz;
+                const float ez = 1e-5f * (fabsf(fvz) + fabsf(rx[3 * mc + 2])) + 1e-30f;
+                const bool zero = (dz < -ez) || (dz > ez && dz2 * ca <= rho2 * cb);
+                any[u] = m < P.M && vox_ok && !zero;
+            }
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) {
+                const int b = b0 + u;
+                if (b < nblk && __any(any[u]) && lane == 0)
+                    atomicOr(&live[b >> 5], 1u << (b & 31));
+            }
+        }
+        __syncthreads();
+    }
+    // first live block at or after block b, or the block count if none
+    auto next_live = [&](int b) -> int {
+        while (b < nblk) {
+            const uint32_t wd = (uint32_t)__builtin_amdgcn_readfirstlane(live[b >> 5]) >> (b & 31);
+            if (wd)
+                return b + __builtin_ctz(wd);
+            b = (b | 31) + 1;
+        }
+        return nblk;
+    };
+    // the step's blocks: the NIT live blocks from block b on
+    auto take_blocks = [&](RowsCursor<NIT> &c, int b) {
+#pragma unroll
+        for (int i = 0; i < NIT; ++i) {
+            c.blk[i] = next_live(b);
+            b = c.blk[i] + 1;
+        }
+    };
+    int nlive = 0;
+    for (int w = 0; w < (nblk + 31) / 32; ++w) {
+        const uint32_t wd = (uint32_t)__builtin_amdgcn_readfirstlane(live[w]);
+        nlive += __builtin_popcount(w == nblk / 32 ? wd & ((1u << (nblk & 31)) - 1u) : wd);
+    }
 
     // ---- per-step work ---------------------------------------------------
     // Launch constants used once per receiver block are read afresh from the
@@ -158,15 +250,19 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
         return ka;
     };
     das::RxTerm R[NIT];                          // receive terms of this lane's items, current block
-    auto load_geometry = [&](int m0) {
+    auto load_geometry = [&](const RowsCursor<NIT> &c) {
         const kptr ka = kargs();
         const DasKParams &Pg = *(const DasKParams *)ka;
         const float *rxg = *(const float *const *)(ka + sizeof(DasKParams) + sizeof(void *));
+        // the voxel indices converted afresh at each use: held as doubles
+        // across the loop they would take four registers
+        int ixv = ixc, iyv = iyc;
+        asm volatile("" : "+v"(ixv), "+v"(iyv));
         double vx, vy, vz;
-        das::voxel_centre(Pg, ixc, iyc, izc, vx, vy, vz);
+        das::voxel_centre(Pg, ixv, iyv, izc, vx, vy, vz);
 #pragma unroll
         for (int i = 0; i < NIT; ++i) {
-            const int mm = m0 + 8 * i + r;
+            const int mm = 8 * c.blk[i] + r;
             const int m = min(mm, Pg.M - 1);
             R[i] = das::rx_term<IQ>(Pg, vx, vy, vz, rxg[3 * m], rxg[3 * m + 1], rxg[3 * m + 2]);
             R[i].s_rx += 1.0 - Pg.t0fs;          // the sample split takes s + 1
@@ -176,7 +272,7 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     // transmit tables of the lane's voxel (the launch keeps Q N 4 < 2^32)
     const char *tau_base = reinterpret_cast<const char *>(tau_tx);
     const char *w_base = reinterpret_cast<const char *>(w_tx);
-    auto load_tx = [&](const RowsCursor &c) -> RowsTx {
+    auto load_tx = [&](const RowsCursor<NIT> &c) -> RowsTx {
         const uint32_t o = ((uint32_t)(P.q_begin + c.ql) * (uint32_t)P.N + (uint32_t)n) * 4u;
         return RowsTx{*reinterpret_cast<const float *>(tau_base + o), *reinterpret_cast<const float *>(w_base + o)};
     };
@@ -219,38 +315,35 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
             }
         }
     };
-    // Window of a receiver over the wave's 8 voxels: the packed key
-    // kmin | (0xffff - kmax) << 16 reduced by 16-bit minima over lanes r,
-    // r + 8, ..., r + 56 (row rotation by 8, then row and half swaps).  Lane
-    // r of the wave then adds it to the tile's slots by LDS atomics.
-    auto wave_min8 = [&](uint32_t x) -> uint32_t {
-        x = das::pk_min_u16(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false));   // row_ror:8
-        const u2_t s = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-        x = das::pk_min_u16(s.x, s.y);
-        const u2_t h = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-        return das::pk_min_u16(h.x, h.y);
-    };
+    // Window of a receiver over the tile's voxels: the minimum and maximum k
+    // of its items with a non-zero weight, taken over voxel pairs (lanes r
+    // and r + 8 of a row) by DPP and then into the step's slots by LDS atomics
+    // from the even voxels (four lanes of a wave per slot; a reduction over all
+    // 8 voxels of the wave took more instructions than the atomics it saved,
+    // and atomics from all lanes, 8 per slot, queued in the LDS).  A weight-0
+    // item has k = all ones, which neither minimum nor maximum takes.
     auto publish = [&](const RowsStep (&st)[NIT], int set) {
 #pragma unroll
         for (int i = 0; i < NIT; ++i) {
+            // pairs of voxels first (lanes r and r + 8 of a row), by DPP
             const uint32_t k = st[i].k;
-            const uint32_t key = (k != 0xffffffffu) ? (k | ((0xffffu - k) << 16)) : 0xffffffffu;
-            const uint32_t red = wave_min8(key);
-            const uint32_t kmin = red & 0xffffu;
-            if (v == 0 && kmin != 0xffffu) {
-                atomicMin(&slots[set * 2 * NRX + 8 * i + r], (int)kmin);
-                atomicMax(&slots[set * 2 * NRX + NRX + 8 * i + r], (int)(0xffffu - (red >> 16)));
+            const uint32_t kx = (k != 0xffffffffu) ? k : 0u;
+            const uint32_t kn2 = min(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x128, 0xF, 0xF, false));
+            const uint32_t kx2 = max(kx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)kx, 0x128, 0xF, 0xF, false));
+            if ((v & 1) == 0) {
+                atomicMin(&slots[set * 2 * NRX + 8 * i + r], kn2);
+                atomicMax(&slots[set * 2 * NRX + NRX + 8 * i + r], kx2);
             }
         }
     };
-    auto advance = [&](RowsCursor &c) -> bool {
+    auto advance = [&](RowsCursor<NIT> &c) -> bool {
         if (++c.ql < c.g1)
             return true;
         c.ql = c.g0;
-        c.m0 += NRX;
-        if (c.m0 < P.M)
+        take_blocks(c, c.blk[NIT - 1] + 1);
+        if (c.blk[0] < nblk)
             return true;
-        c.m0 = 0;
+        take_blocks(c, 0);
         c.g0 = c.g1;
         c.g1 = min(c.g0 + P.q_group, P.q_count);
         c.ql = c.g0;
@@ -265,21 +358,20 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     // exceeds a region (`overflow`: its terms come from direct loads).
     auto make_window = [&](const RowsStep (&st)[NIT], int set, int buf) -> RowsWin<NIT> {
         RowsWin<NIT> wdw;
-        int kmn[NIT];
+        uint32_t kmn[NIT];
         bool over = false;
 #pragma unroll
         for (int i = 0; i < NIT; ++i) {
             kmn[i] = slots[set * 2 * NRX + 8 * i + r];
-            const int kmx = slots[set * 2 * NRX + NRX + 8 * i + r];
-            const int np = (kmn[i] <= kmx) ? kmx - kmn[i] + 1 : 0;
-            over = over || np > G::W_MAX;
+            const uint32_t kmx = slots[set * 2 * NRX + NRX + 8 * i + r];
+            over = over || (kmx - kmn[i] >= (uint32_t)G::W_MAX);     // empty: kmx - kmn = 1
         }
         // every wave covers all receivers of the step, so the vote agrees across the workgroup
         wdw.overflow = __any(over) ? 1u : 0u;
 #pragma unroll
         for (int i = 0; i < NIT; ++i) {
-            const bool on = st[i].k != 0xffffffffu && !wdw.overflow;
-            const uint32_t rel = on ? (uint32_t)((int)st[i].k - kmn[i]) : 0u;
+            const bool on = !wdw.overflow;
+            const uint32_t rel = min(st[i].k - kmn[i], (uint32_t)(G::RW - 2));
             const uint32_t first = (rel + vpar) & 1u;       // 1: row k + 1 first
             const uint32_t base = (uint32_t)(buf * G::BUF + (8 * i + r) * G::REGION);
             wdw.be[i] = base + (rel + first) * WR_ROWB;
@@ -293,7 +385,8 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     };
 
     // Copy of one receiver's rows by LDS-DMA: waves S w' .. S w' + S - 1
-    // copy receiver m0 + w', taking every S-th round.  A round moves 8 rows:
+    // copy receiver w' of the step (receiver 8 blk[w' / 8] + w' % 8), taking
+    // every S-th round.  A round moves 8 rows:
     // lane (rho, c) fetches 16 bytes (chunk c of the frame tile's part) of row
     // kmin + 8 round + rho, which the DMA writes at 16 lane past the round's
     // LDS base, i.e. row rho, chunk c of the region.  KQMB: every offset is
@@ -305,21 +398,22 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     const int wrx = wave / G::S, wpart = wave % G::S;
     const int crow = lane >> 3;
     const uint32_t coff = (uint32_t)crow * kstride32 + (uint32_t)(lane & 7) * 16u + (uint32_t)b0 * E;
-    auto copy_prepare = [&](const RowsCursor &c, int set, int buf) -> RowsCopy {
-        const int kmn = __builtin_amdgcn_readfirstlane(slots[set * 2 * NRX + wrx]);
-        const int kmx = __builtin_amdgcn_readfirstlane(slots[set * 2 * NRX + NRX + wrx]);
-        const int np = (kmn <= kmx) ? kmx - kmn + 1 : 0;
-        const int rows = (np > 0 && np <= G::W_MAX) ? np + 1 : 0;         // rows kmin .. kmax + 1
+    auto copy_prepare = [&](const RowsCursor<NIT> &c, int set, int buf) -> RowsCopy {
+        const uint32_t kmn = __builtin_amdgcn_readfirstlane(slots[set * 2 * NRX + wrx]);
+        const uint32_t kmx = __builtin_amdgcn_readfirstlane(slots[set * 2 * NRX + NRX + wrx]);
+        const uint32_t span = kmx - kmn;
+        const int rows = (kmn <= kmx && span < (uint32_t)G::W_MAX) ? (int)span + 2 : 0;   // rows kmin .. kmax + 1
         const int nr = (rows + 7) / 8;
         const uint32_t dst = (uint32_t)(buf * G::BUF + wrx * G::REGION);
         const uint32_t kmin = (uint32_t)(rows ? kmn : 0);
+        const int cb = (NIT == 1 || wrx < 8) ? c.blk[0] : c.blk[NIT - 1];
+        const int m = min(8 * cb + (wrx & 7), P.M - 1);    // (a receiver past M copies nothing)
         if constexpr (LAYOUT == DAS_LAYOUT_QMKB) {
-            const int64_t plane = ((int64_t)c.ql * P.M + c.m0) * m_stride;
-            return RowsCopy{nr, rows, (uint32_t)wrx * m_stride + kmin * kstride32, dst,
+            const int64_t plane = ((int64_t)c.ql * P.M + m) * m_stride;
+            return RowsCopy{nr, rows, kmin * kstride32, dst,
                             das::make_rsrc(rf_bytes + plane, (uint64_t)(chunk_bytes - plane))};
         } else {
-            return RowsCopy{nr, rows,
-                            ((uint32_t)c.ql * (uint32_t)P.M + (uint32_t)(c.m0 + wrx)) * m_stride + kmin * kstride32,
+            return RowsCopy{nr, rows, ((uint32_t)c.ql * (uint32_t)P.M + (uint32_t)m) * m_stride + kmin * kstride32,
                             dst, rs_chunk};
         }
     };
@@ -414,14 +508,15 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     };
     // A step by direct loads from the permuted buffer (a window too wide for
     // the regions): each item with a non-zero weight reads its two rows.
-    auto compute_direct = [&](const RowsStep (&st)[NIT], const RowsCursor &c) {
-        const int64_t pos = ((int64_t)c.ql * P.M + c.m0) * m_stride;
-        const das::BufRsrc rd = das::make_rsrc(rf_bytes + pos, (uint64_t)(chunk_bytes - pos));
+    auto compute_direct = [&](const RowsStep (&st)[NIT], const RowsCursor<NIT> &c) {
 #pragma unroll
         for (int i = 0; i < NIT; ++i) {
+            // (an item of a block past the last has weight 0 and k all ones)
+            const int64_t pos = ((int64_t)c.ql * P.M + 8 * min(c.blk[i], nblk - 1)) * m_stride;
+            const das::BufRsrc rd = das::make_rsrc(rf_bytes + pos, (uint64_t)(chunk_bytes - pos));
             if (st[i].k == 0xffffffffu)
                 continue;
-            const uint32_t o0 = (uint32_t)(8 * i + r) * m_stride + st[i].k * kstride32 + (uint32_t)b0 * E;
+            const uint32_t o0 = (uint32_t)r * m_stride + st[i].k * kstride32 + (uint32_t)b0 * E;
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 const f4_t x0 = das::buffer_load_f32x4(rd, (int)(o0 + 16u * s), 0, 0);
@@ -438,18 +533,24 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     // step i + 1, and the set of step i - 1 is cleared: its last reads were
     // in step i - 1 and its next publication is in step i + 1, each on the
     // other side of a barrier.
-    RowsCursor cur{0, 0, 0, min(P.q_group, P.q_count)};
-    load_geometry(cur.m0);
+    // (a tile outside every receiver's aperture has no step: its sums stay 0)
+    if (nlive > 0) {
+    RowsCursor<NIT> cur;
+    cur.ql = 0;
+    cur.g0 = 0;
+    cur.g1 = min(P.q_group, P.q_count);
+    take_blocks(cur, 0);
+    load_geometry(cur);
     RowsStep s_cur[NIT], s_nxt[NIT], s_spare[NIT];
     make_steps(load_tx(cur), s_cur);
     publish(s_cur, 0);
-    RowsCursor nxt = cur;
+    RowsCursor<NIT> nxt = cur;
     bool has_next = advance(nxt);
-    RowsCursor nxt2 = nxt;
+    RowsCursor<NIT> nxt2 = nxt;
     bool has_next2 = has_next && advance(nxt2);
     if (has_next) {
-        if (nxt.m0 != cur.m0)
-            load_geometry(nxt.m0);
+        if (nxt.blk[0] != cur.blk[0])
+            load_geometry(nxt);
         make_steps(load_tx(nxt), s_nxt);
         publish(s_nxt, 1);
     }
@@ -486,11 +587,11 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
         // The step after next: geometry (a new receiver block), sample split,
         // window publication.  Latency-bound fp64 work, done while all waves
         // of a SIMD are busy with it.
-        RowsCursor nxt3 = nxt2;
+        RowsCursor<NIT> nxt3 = nxt2;
         const bool has_next3 = has_next2 && advance(nxt3);
         if (has_next2) {
-            if (nxt2.m0 != nxt.m0)
-                load_geometry(nxt2.m0);
+            if (nxt2.blk[0] != nxt.blk[0])
+                load_geometry(nxt2);
             make_steps(t2, sn2);
             publish(sn2, set2);
             if (has_next3)
@@ -507,7 +608,7 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
         if (hn)
             w_cur = make_window(sn, set1, buf ^ 1);
         if (tid < 2 * NRX)                               // the previous step's slots
-            slots[set3 * 2 * NRX + tid] = (tid < NRX) ? INT_MAX : INT_MIN;
+            slots[set3 * 2 * NRX + tid] = (tid < NRX) ? 0xffffffffu : 0u;
         cur = nxt;
         nxt = nxt2;
         nxt2 = nxt3;
@@ -522,7 +623,7 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
         return true;
     };
     using das::ic;
-    const int nsteps = P.q_count * ((P.M + NRX - 1) / NRX);
+    const int nsteps = P.q_count * ((nlive + NIT - 1) / NIT);
     for (int left = nsteps; left >= 7; left -= 6) {
         step(ic<0>{}, s_cur, s_nxt, s_spare, tx_a, tx_b);
         step(ic<0>{}, s_nxt, s_spare, s_cur, tx_b, tx_a);
@@ -542,6 +643,8 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
         const RowsTx tt = tx_a;
         tx_a = tx_b;
         tx_b = tt;
+    }
+
     }
 
     // ---- output ----------------------------------------------------------------
@@ -604,8 +707,9 @@ hipError_t launch_rows_nit(const das_plan_t &plan, const DasKParams &kp, const f
 
 bool das_rows_supported(const das_plan_t &plan) {
     // native samples, 128-byte frame tiles (fp32: B a multiple of 32;
-    // complex64: of 16), sample indices below 2^16 in the window keys
-    if (plan.h16 || plan.p.K > 65535)
+    // complex64: of 16), records of at most 65535 samples, and at most
+    // 8 WR_LIVE_BLOCKS receivers (the aperture mask)
+    if (plan.h16 || plan.p.K > 65535 || plan.p.M > 8 * WR_LIVE_BLOCKS)
         return false;
     return (plan.p.dtype == DAS_F32 && plan.p.B % 32 == 0) || (plan.p.dtype == DAS_C64 && plan.p.B % 16 == 0);
 }

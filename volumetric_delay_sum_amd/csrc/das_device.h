@@ -215,13 +215,6 @@ __device__ __forceinline__ BufRsrc make_rsrc(const char *base, uint64_t bytes) {
     return r;
 }
 
-// Packed unsigned 16-bit minimum of two dwords (both halves at once).
-__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
-    uint32_t r;
-    asm("v_pk_min_u16 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-    return r;
-}
-
 // ---------------------------------------------------------------------------
 // Row broadcast on wave64: DPP row_newbcast:J hands lane J of each 16-lane row
 // to every lane of that row (gfx90a and later).
