@@ -116,9 +116,9 @@ def test_plan_info_and_sizes():
     pl = das.Plan(**_problem(B=32, dtype="c64", f_demod=5e6))
     assert pl.info["algorithm"] == das.ALG_BATCH_INNER
     assert pl.info["elem_bytes"] == 8
-    assert pl.info["frames_per_lane"] == 2                  # IQ, B % 32 == 0: LDS-staged DPP rows, split, 2 frames a lane
-    assert pl.info["lanes_per_voxel"] == 16
-    assert pl.info["whole_rows"] == 0 and pl.info["receivers_per_step"] == 8
+    assert pl.info["frames_per_lane"] == 16                 # IQ, B % 16 == 0: whole-row lanes, 16 complex frames a lane
+    assert pl.info["lanes_per_voxel"] == 8
+    assert pl.info["whole_rows"] == 1 and pl.info["receivers_per_step"] == 8
     assert pl.info["N"] == 32
     assert pl.permuted_bytes(1) == 64 * 1 * 8 * 32 * 8
     assert pl.permuted_bytes(2) == 2 * pl.permuted_bytes(1)
@@ -216,14 +216,23 @@ def test_frames_per_lane_choice_direct(B, fl, monkeypatch):
     assert pl.info["staged"] == 0
 
 
-@pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (31, 1), (32, 2), (40, 2), (48, 1), (64, 2), (34, 2)])
+@pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 16), (31, 1), (32, 16), (40, 2), (48, 16), (64, 16), (34, 2)])
 def test_frames_per_lane_choice_iq(B, fl):
-    # complex64 batch-inner: the LDS-staged DPP-row kernel wherever B % 16 ==
-    # 0 (2 frames per lane in split rows when B % 32 == 0, else 1)
+    # complex64 batch-inner: the LDS-staged whole-row kernel wherever B % 16
+    # == 0 (16 complex frames a lane), direct loads otherwise
     pl = das.Plan(**_problem(B=B, dtype="c64", f_demod=5e6))
     assert pl.info["frames_per_lane"] == fl
     assert pl.info["staged"] == (1 if B % 16 == 0 else 0)
-    assert pl.info["whole_rows"] == 0
+    assert pl.info["whole_rows"] == (1 if B % 16 == 0 else 0)
+
+
+@pytest.mark.parametrize("B,fl", [(16, 1), (32, 2), (48, 1), (64, 2)])
+def test_frames_per_lane_choice_iq_dpp_rows(B, fl, monkeypatch):
+    # DAS_STAGED_ROWS=0: the DPP-row kernel, 2 complex frames a lane in split
+    # rows when B % 32 == 0, else 1
+    monkeypatch.setenv("DAS_STAGED_ROWS", "0")
+    pl = das.Plan(**_problem(B=B, dtype="c64", f_demod=5e6))
+    assert pl.info["frames_per_lane"] == fl and pl.info["staged"] == 1 and pl.info["whole_rows"] == 0
 
 
 def test_error_strings(lib):

@@ -71,8 +71,10 @@ def test_start_time_binary16(gpu, monkeypatch, t0, kernel, iq):
 @pytest.mark.parametrize("B", [16, 64], ids=["one_frame_per_lane", "split_rows"])
 @pytest.mark.parametrize("storage", ["native", "f16"])
 def test_start_time_other_staged_shapes(gpu, B, iq, storage):
-    """B = 16 (one frame per lane) and B = 64 (split rows: two voxels per DPP row,
-    16 bytes per lane) at a fractional negative t0."""
+    """B = 16 and B = 64 at a fractional negative t0: with binary16 storage the
+    DPP-row kernel with one frame per lane and with split rows (two voxels per
+    DPP row, 16 bytes per lane); with native samples fp32 B = 16 runs the
+    DPP-row kernel with one frame per lane, the others whole-row lanes."""
     import volumetric_delay_sum_amd as das
     inp = Inputs(_cfg(-0.83e-6, iq=iq, B=B), w_tx="uniform")
     assert das.plan_from_fields(inp.fields, "batch_inner", "qmkb", storage=storage).info["staged"] == 1

@@ -368,15 +368,15 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
         pl->split = 2;
         pl->fl *= 2;
     }
-    // Whole-row lanes where they are built, for fp32 samples: 16 receivers a
-    // step (Main 8.2 ms against 9.2 with DPP rows).  Complex samples keep the
-    // DPP-row kernel (Main complex 21.8 ms against 28.9).  DAS_STAGED_ROWS
-    // selects explicitly: 1 or 2 receiver groups of 8 a step (complex: 1),
-    // 0 the DPP-row kernel.
+    // Whole-row lanes where they are built: 16 receivers a step for fp32
+    // samples, 8 for complex ones (with the receive-aperture skipping, Main
+    // 6.35 ms against 9.2 with DPP rows; Main complex 19.8 ms against 21.3).
+    // DAS_STAGED_ROWS selects explicitly: 1 or 2 receiver blocks of 8 a step
+    // (complex: 1), 0 the DPP-row kernel.
     pl->rows = 0;
     if (pl->staged && das_rows_supported(*pl)) {
         const char *rv = std::getenv("DAS_STAGED_ROWS");
-        const int g = rv ? std::atoi(rv) : (p.dtype == DAS_C64 ? 0 : 2);
+        const int g = rv ? std::atoi(rv) : (p.dtype == DAS_C64 ? 1 : 2);
         pl->rows = (g == 1 || g == 2) ? g : 0;
         if (p.dtype == DAS_C64 && pl->rows == 2)
             pl->rows = 1;                            // complex items hold twice the weights: 8 receivers a step
