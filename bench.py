@@ -40,6 +40,8 @@ LDS_BCLK = {
     "two ds_read_b64 (8-byte lanes)": 160.0,
     "two ds_read_b128 (16-byte lanes, split rows)": 219.0,
     "16 ds_read_b128 per lane, two whole 128-B rows, bank-group order": 238.0,
+    # the same instructions and bank groups over 128-byte slots, half the rows' bytes
+    "8 ds_read_b128 per lane, two 64-B binary16 rows in 128-B slots, bank-group order": 238.0,
 }
 
 
@@ -136,7 +138,8 @@ def delivery_ceiling(plan, iq: bool, h16: bool):
     sample = (8 if iq else 4) // (2 if h16 else 1)        # bytes of one stored sample
     lane = sample * plan.info["frames_per_lane"]           # bytes of one lane's tap
     if plan.info["whole_rows"]:
-        pattern = "16 ds_read_b128 per lane, two whole 128-B rows, bank-group order"
+        pattern = ("8 ds_read_b128 per lane, two 64-B binary16 rows in 128-B slots, bank-group order" if h16
+                   else "16 ds_read_b128 per lane, two whole 128-B rows, bank-group order")
     else:
         pattern = ("two ds_read_b128 (16-byte lanes, split rows)" if lane == 16
                    else "two ds_read_b64 (8-byte lanes)" if lane == 8 else None)

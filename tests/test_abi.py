@@ -202,10 +202,14 @@ def test_whole_row_receivers_per_step(rows, iq, per_step, monkeypatch):
     assert pl.info["lanes_per_voxel"] == 8 and pl.info["frames_per_lane"] == (16 if iq else 32)
 
 
-def test_whole_rows_need_native_samples_and_short_records():
-    assert das.Plan(**_problem(B=32, storage="f16")).info["whole_rows"] == 0
+def test_whole_rows_limits():
+    # both storages; records of at most 65535 samples; at most 4096 receivers
+    # (the kernel's receive-aperture mask)
+    assert das.Plan(**_problem(B=32, storage="f16")).info["whole_rows"] == 1
     assert das.Plan(**_problem(B=32, K=65535)).info["whole_rows"] == 1
     assert das.Plan(**_problem(B=32, K=65536)).info["whole_rows"] == 0
+    assert das.Plan(**_problem(B=32, M=4096)).info["whole_rows"] == 1
+    assert das.Plan(**_problem(B=32, M=4097)).info["whole_rows"] == 0
 
 
 @pytest.mark.parametrize("B,fl", [(32, 2), (64, 4), (96, 4), (160, 4)])
@@ -413,12 +417,14 @@ def test_binary16_storage_needs_batch_inner():
     assert _status(storage="f16", dtype="c128", f_demod=5e6, algorithm="baseline") == UNSUPPORTED
 
 
-@pytest.mark.parametrize("dtype,B,store,fl,staged", [
-    ("f32", 32, 2, 2, 1), ("f32", 64, 2, 4, 1), ("f32", 128, 2, 4, 1), ("f32", 96, 2, 2, 1), ("f32", 16, 2, 1, 1),
-    ("f32", 48, 2, 1, 1),
-    ("f32", 24, 2, 2, 0), ("f32", 68, 2, 4, 0), ("f32", 7, 2, 1, 0), ("c64", 32, 4, 2, 1),
-    ("c64", 64, 4, 2, 1), ("c64", 16, 4, 1, 1), ("c64", 48, 4, 1, 1), ("c64", 34, 4, 2, 0)])
-def test_binary16_plan_info(dtype, B, store, fl, staged):
+@pytest.mark.parametrize("dtype,B,store,fl,staged,rows", [
+    ("f32", 32, 2, 32, 1, 1), ("f32", 64, 2, 32, 1, 1), ("f32", 128, 2, 32, 1, 1), ("f32", 96, 2, 32, 1, 1),
+    ("f32", 16, 2, 1, 1, 0), ("f32", 48, 2, 1, 1, 0),
+    ("f32", 24, 2, 2, 0, 0), ("f32", 68, 2, 4, 0, 0), ("f32", 7, 2, 1, 0, 0), ("c64", 32, 4, 16, 1, 1),
+    ("c64", 64, 4, 16, 1, 1), ("c64", 16, 4, 16, 1, 1), ("c64", 48, 4, 16, 1, 1), ("c64", 34, 4, 2, 0, 0)])
+def test_binary16_plan_info(dtype, B, store, fl, staged, rows):
+    # binary16 rows run the whole-row kernel where its frame tiles fit (32
+    # fp32 or 16 complex frames), the DPP-row kernel for fp32 B = 16 and 48
     iq = dtype == "c64"
     pl = das.Plan(**_problem(B=B, dtype=dtype, f_demod=5e6 if iq else 0.0, storage="f16"))
     assert pl.store_f16
@@ -426,6 +432,7 @@ def test_binary16_plan_info(dtype, B, store, fl, staged):
     assert pl.info["store_bytes"] == store
     assert pl.info["frames_per_lane"] == fl
     assert pl.info["staged"] == staged
+    assert pl.info["whole_rows"] == rows
     native = das.Plan(**_problem(B=B, dtype=dtype, f_demod=5e6 if iq else 0.0))
     assert native.info["store_bytes"] == native.info["elem_bytes"]
     assert pl.permuted_bytes(1) * 2 == native.permuted_bytes(1)

@@ -81,26 +81,34 @@ def test_binary16_direct_kernel(gpu, monkeypatch, iq):
     assert_parity(y, oracle_ref(inp, storage="f16"), f"f16 direct iq={iq}")
 
 
-# frames per lane of the binary16 staged instances: B a multiple of 32 takes
-# two (complex: one pair of halves per frame, two frames), a multiple of 16
-# only takes one, and fp32 data with B a multiple of 64 takes four
-FPL16 = {(False, 16): 1, (False, 32): 2, (False, 48): 1, (False, 64): 4,
-         (True, 16): 1, (True, 32): 2, (True, 48): 1, (True, 64): 2}
+# frames per lane of the binary16 staged instances.  Whole-row lanes (the
+# default where B is a multiple of 32 fp32 or 16 complex frames): 32 or 16.
+# DPP rows (fp32 B = 16 and 48, or DAS_STAGED_ROWS=0): B a multiple of 32
+# takes two (complex: one pair of halves per frame, two frames), a multiple of
+# 16 only takes one, and fp32 data with B a multiple of 64 takes four
+FPL16_ROWS = {(False, 32): 32, (False, 64): 32, (True, 16): 16, (True, 32): 16, (True, 48): 16, (True, 64): 16}
+FPL16_DPP = {(False, 16): 1, (False, 32): 2, (False, 48): 1, (False, 64): 4,
+             (True, 16): 1, (True, 32): 2, (True, 48): 1, (True, 64): 2}
 
 
+@pytest.mark.parametrize("kernel", ["default", "dpp_rows"])
 @pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])
 @pytest.mark.parametrize("voxel", [0.2e-3, 1.2e-3])
 @pytest.mark.parametrize("B", [16, 32, 48, 64])
-def test_binary16_staged_windows_and_fallback(gpu, iq, voxel, B):
+def test_binary16_staged_windows_and_fallback(gpu, monkeypatch, iq, voxel, B, kernel):
     # coarse voxels make windows too wide for LDS: the direct-load fallback inside the staged kernel
     import volumetric_delay_sum_amd as das
+    if kernel == "dpp_rows":
+        monkeypatch.setenv("DAS_STAGED_ROWS", "0")
     cfg = das_synth.custom_config("tiny", name="win16", seed=29, array=(19, 3), grid=(11, 10, 3), K=700, B=B,
                                   tx="diverging", sources=((0.0, 0.0), (2e-3, 1e-3)), iq=iq, n_scatterers=0,
                                   voxel=voxel, z0=3e-3)
     inp = Inputs(cfg, w_tx="uniform")
     info = das.plan_from_fields(inp.fields, "batch_inner", "qmkb", storage="f16").info
     assert info["staged"] == 1
-    assert info["frames_per_lane"] == FPL16[(iq, B)], info
+    rows = kernel == "default" and (iq, B) in FPL16_ROWS
+    assert info["whole_rows"] == (1 if rows else 0), info
+    assert info["frames_per_lane"] == (FPL16_ROWS if rows else FPL16_DPP)[(iq, B)], info
     y = to_numpy(run_gpu(inp, "batch_inner", "qmkb", storage="f16", q_chunk=1), iq)
     assert_parity(y, oracle_ref(inp, storage="f16"), f"f16 windows voxel={voxel} iq={iq}")
 

@@ -1,8 +1,9 @@
 """GPU: the LDS-staged batch-inner kernel with whole-row lanes ("ffdas:
 volumetric ultrasound reconstruction at warp speed", Section 3, batch-inner
-tiling and spatial locality), in the variants the default plan does not
-pick: 8 receivers a step (fp32) and complex64 samples.  The default (fp32,
-16 receivers a step) runs in every fp32 parity test with B a multiple of 32.
+tiling and spatial locality; FP16 paragraph for binary16 storage): 8 or 16
+receivers a step (fp32), complex64 samples, native and binary16 storage.
+The default (fp32, 16 receivers a step, native) also runs in every fp32
+parity test with B a multiple of 32.
 
 Each case meets the same bar as every other kernel against the fp64 oracle
 (max|err| <= 1e-4 max|oracle|, relative L2 <= 1e-5): ragged grids and
@@ -34,43 +35,46 @@ def _ragged(iq, B=32, K=300, **kw):
     return das_synth.custom_config("tiny", **base)
 
 
-def _info(inp):
+def _info(inp, storage="native"):
     import volumetric_delay_sum_amd as das
-    return das.plan_from_fields(inp.fields, "batch_inner", "qmkb").info
+    return das.plan_from_fields(inp.fields, "batch_inner", "qmkb", storage=storage).info
 
 
+@pytest.mark.parametrize("storage", ["native", "f16"])
 @pytest.mark.parametrize("layout", ["kqmb", "qmkb"])
 @pytest.mark.parametrize("B", [32, 64, 96])
 @pytest.mark.parametrize("rows,iq", VARIANTS, ids=IDS)
-def test_ragged(gpu, monkeypatch, rows, iq, B, layout):
+def test_ragged(gpu, monkeypatch, rows, iq, B, layout, storage):
     _use(monkeypatch, rows)
     inp = Inputs(_ragged(iq, B=B), w_tx="uniform")
-    info = _info(inp)
+    info = _info(inp, storage)
     assert info["whole_rows"] == 1 and info["receivers_per_step"] == 8 * int(rows)
-    y = to_numpy(run_gpu(inp, "batch_inner", layout), iq)
-    assert_parity(y, oracle_ref(inp), f"rows={rows} iq={iq} B={B} {layout}")
+    y = to_numpy(run_gpu(inp, "batch_inner", layout, storage=storage), iq)
+    assert_parity(y, oracle_ref(inp, storage=storage), f"rows={rows} iq={iq} B={B} {layout} {storage}")
 
 
+@pytest.mark.parametrize("storage", ["native", "f16"])
 @pytest.mark.parametrize("t0", [3.0 / 20e6, 1.37e-6, -0.83e-6], ids=["3_periods", "plus_1.37us", "minus_0.83us"])
 @pytest.mark.parametrize("rows,iq", VARIANTS, ids=IDS)
-def test_start_time(gpu, monkeypatch, rows, iq, t0):
+def test_start_time(gpu, monkeypatch, rows, iq, t0, storage):
     _use(monkeypatch, rows)
     inp = Inputs(_ragged(iq, t0=t0, K=320), w_tx="uniform")
-    y = to_numpy(run_gpu(inp, "batch_inner", "qmkb"), iq)
-    assert_parity(y, oracle_ref(inp), f"rows={rows} iq={iq} t0={t0}")
+    y = to_numpy(run_gpu(inp, "batch_inner", "qmkb", storage=storage), iq)
+    assert_parity(y, oracle_ref(inp, storage=storage), f"rows={rows} iq={iq} t0={t0} {storage}")
 
 
+@pytest.mark.parametrize("storage", ["native", "f16"])
 @pytest.mark.parametrize("voxel", [0.6e-3, 1.5e-3], ids=["mixed", "coarse"])
 @pytest.mark.parametrize("rows,iq", VARIANTS, ids=IDS)
-def test_windows_wider_than_the_regions(gpu, monkeypatch, rows, iq, voxel):
+def test_windows_wider_than_the_regions(gpu, monkeypatch, rows, iq, voxel, storage):
     """Coarse voxels: some steps' windows exceed a region (38 positions with
     16 receivers a step, 78 with 8), and those steps read the permuted buffer."""
     _use(monkeypatch, rows)
     cfg = _ragged(iq, K=900, voxel=voxel, z0=3e-3, grid=(19, 10, 3), array=(19, 3), f_number=0.0,
                   sources=((0.0, 0.0), (2e-3, 1e-3)))
     inp = Inputs(cfg, w_tx="uniform")
-    y = to_numpy(run_gpu(inp, "batch_inner", "kqmb"), iq)
-    assert_parity(y, oracle_ref(inp), f"rows={rows} iq={iq} voxel={voxel}")
+    y = to_numpy(run_gpu(inp, "batch_inner", "kqmb", storage=storage), iq)
+    assert_parity(y, oracle_ref(inp, storage=storage), f"rows={rows} iq={iq} voxel={voxel} {storage}")
 
 
 @pytest.mark.parametrize("rows,iq", VARIANTS, ids=IDS)
@@ -97,8 +101,9 @@ def test_main_sampled(gpu, monkeypatch, rows, iq):
     assert_parity(to_numpy(out, iq)[:, vox], oracle_ref(inp, voxels=vox), f"main rows={rows} iq={iq}")
 
 
+@pytest.mark.parametrize("storage", ["native", "f16"])
 @pytest.mark.parametrize("rows,iq", VARIANTS, ids=IDS)
-def test_tiles_outside_every_aperture(gpu, monkeypatch, rows, iq):
+def test_tiles_outside_every_aperture(gpu, monkeypatch, rows, iq, storage):
     """A volume much wider than the array: the outer tiles (8 voxels wide
     along x) see no receiver inside their cones and skip every receiver
     block, the next ones keep a few blocks, the central ones all.  Every voxel whose receive weights
@@ -109,15 +114,27 @@ def test_tiles_outside_every_aperture(gpu, monkeypatch, rows, iq):
     cfg = _ragged(iq, B=32, K=400, array=(16, 4), grid=(40, 9, 4), voxel=0.5e-3, z0=2e-3, f_number=2.0,
                   sources=((0.0, 0.0), (1e-3, 0.0)))
     inp = Inputs(cfg, w_tx="uniform")
-    ref = oracle_ref(inp)
-    y = to_numpy(run_gpu(inp, "batch_inner", "qmkb"), iq)
+    ref = oracle_ref(inp, storage=storage)
+    y = to_numpy(run_gpu(inp, "batch_inner", "qmkb", storage=storage), iq)
     zero = ref == 0.0
     assert 0.5 < zero.mean() < 0.99, zero.mean()
     assert np.array_equal(y == 0.0, zero)
     assert_parity(y, ref, f"rows={rows} iq={iq} apertures")
     shape = (cfg.B, cfg.N, 2) if iq else (cfg.B, cfg.N)
     start = torch.linspace(-3.0, 3.0, int(np.prod(shape)), device="cuda").reshape(shape)
-    out = run_gpu(inp, "batch_inner", "qmkb", out=start.clone(), accumulate_into=True)
+    out = run_gpu(inp, "batch_inner", "qmkb", out=start.clone(), accumulate_into=True, storage=storage)
     got, base = to_numpy(out, iq), to_numpy(start, iq)
     assert np.array_equal(got[zero], base[zero])
     assert_parity(got - base, ref, f"rows={rows} iq={iq} apertures accumulate")
+
+
+@pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])
+def test_main_binary16_default(gpu, iq):
+    """The default binary16 plans on Main (16 receivers a step fp32, 8
+    complex), sampled, against the oracle of the rounded samples."""
+    inp = Inputs(das_synth.get_config("main-c64" if iq else "main"))
+    assert _info(inp, "f16")["whole_rows"] == 1
+    vox = sample_voxels(inp.cfg, 128, seed=6)
+    out = run_gpu(inp, "batch_inner", "qmkb", storage="f16")
+    assert_all_written(out, f"main f16 iq={iq}")
+    assert_parity(to_numpy(out, iq)[:, vox], oracle_ref(inp, voxels=vox, storage="f16"), f"main f16 iq={iq}")

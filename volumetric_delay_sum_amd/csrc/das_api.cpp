@@ -369,8 +369,9 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
         pl->fl *= 2;
     }
     // Whole-row lanes where they are built: 16 receivers a step for fp32
-    // samples, 8 for complex ones (with the receive-aperture skipping, Main
-    // 6.35 ms against 9.2 with DPP rows; Main complex 19.8 ms against 21.3).
+    // samples, 8 for complex ones, native or binary16 (with the
+    // receive-aperture skipping, Main 6.35 ms against 9.2 with DPP rows; Main
+    // complex 19.8 ms against 21.3).
     // DAS_STAGED_ROWS selects explicitly: 1 or 2 receiver blocks of 8 a step
     // (complex: 1), 0 the DPP-row kernel.
     pl->rows = 0;

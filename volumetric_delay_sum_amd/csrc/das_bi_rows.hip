@@ -47,7 +47,7 @@ namespace {
 
 constexpr int WR_THREADS = 1024;
 constexpr int WR_TX = 8, WR_TY = 8, WR_TZ = 2;   // voxel tile of a workgroup
-constexpr int WR_ROWB = 128;                     // bytes of one staged sample row (the frame tile's part)
+constexpr int WR_ROWB = 128;                     // LDS bytes of one staged sample row (the frame tile's part)
 constexpr int WR_LDS_TOTAL = 163840;             // LDS of one workgroup on gfx950 (160 KiB)
 constexpr int WR_LIVE_BLOCKS = 512;              // 8-receiver blocks a launch may have (M <= 4096)
 
@@ -109,7 +109,7 @@ struct RowsCopy {
     das::BufRsrc rs;
 };
 
-template <bool IQ, int LAYOUT, int NIT>
+template <bool IQ, int LAYOUT, int NIT, bool H>
 __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, const float *__restrict__ rfp,
                                                                  const float *__restrict__ rx,
                                                                  const float *__restrict__ tau_tx,
@@ -118,8 +118,10 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     using G = RowsGeo<NIT>;
     constexpr int NRX = G::NRX;
     constexpr int C = IQ ? 2 : 1;
-    constexpr int E = 4 * C;                     // bytes per sample
-    constexpr int FR = WR_ROWB / E;              // frames of a frame tile
+    constexpr int E = (H ? 2 : 4) * C;           // bytes per stored sample (H: binary16)
+    constexpr int FR = IQ ? 16 : 32;             // frames of a frame tile
+    constexpr int NCH = FR * E / 16;             // 16-byte chunks of a row's frame tile (8; binary16: 4)
+    constexpr int APC = 32 / NCH;                // sums a chunk feeds
     constexpr int DEPTH = 3;                     // units whose reads are in flight
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + 2 * G::BUF);
@@ -389,7 +391,9 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     // every S-th round.  A round moves 8 rows:
     // lane (rho, c) fetches 16 bytes (chunk c of the frame tile's part) of row
     // kmin + 8 round + rho, which the DMA writes at 16 lane past the round's
-    // LDS base, i.e. row rho, chunk c of the region.  KQMB: every offset is
+    // LDS base, i.e. row rho, chunk c of the region.  Binary16 rows are 64
+    // bytes: lanes c and c + 4 fetch the same chunk, so each row fills its
+    // 128-byte slot twice over and the reads keep the fp32 rows' bank pattern.  KQMB: every offset is
     // 32-bit (the launch keeps the chunk under 4 GiB).  QMKB: the resource is
     // rebased per step on the (event, receiver block) plane, in 64-bit scalar
     // arithmetic.  A receiver whose window exceeds its region is not copied
@@ -397,7 +401,7 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     const das::BufRsrc rs_chunk = das::make_rsrc(rf_bytes, (uint64_t)chunk_bytes);
     const int wrx = wave / G::S, wpart = wave % G::S;
     const int crow = lane >> 3;
-    const uint32_t coff = (uint32_t)crow * kstride32 + (uint32_t)(lane & 7) * 16u + (uint32_t)b0 * E;
+    const uint32_t coff = (uint32_t)crow * kstride32 + (uint32_t)((lane & 7) % NCH) * 16u + (uint32_t)b0 * E;
     auto copy_prepare = [&](const RowsCursor<NIT> &c, int set, int buf) -> RowsCopy {
         const uint32_t kmn = __builtin_amdgcn_readfirstlane(slots[set * 2 * NRX + wrx]);
         const uint32_t kmx = __builtin_amdgcn_readfirstlane(slots[set * 2 * NRX + NRX + wrx]);
@@ -426,9 +430,11 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     };
 
     // ---- interpolate-weight-accumulate ------------------------------------
-    // acc[4 s + j]: fp32 frame 4 s + j of the frame tile; complex: (re, im)
-    // of frames 2 s and 2 s + 1.  Unit u = 8 i + s of a step is chunk s (16
-    // bytes) of item i's two rows: two reads, 8 (complex: 16) FMAs.
+    // acc[j]: fp32 frame j of the frame tile; complex: (re, im) of frame j / 2.
+    // Unit u = NCH i + s of a step is chunk s (16 bytes) of item i's two rows:
+    // two reads and 8 (complex: 16) FMAs, twice that for binary16 chunks,
+    // whose FMAs take the halves straight from the loaded dwords
+    // (v_fma_mix_f32, one rounding as for a widened sample).
     float acc[32];
 #pragma unroll
     for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
@@ -437,12 +443,58 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
         f4_t e[DEPTH], o[DEPTH];
     };
     auto issue_unit = [&](auto U, const RowsWin<NIT> &wd, Ring &ring) {
-        constexpr int u = decltype(U)::value, i = u / 8, s = u % 8;
+        constexpr int u = decltype(U)::value, i = u / NCH, s = u % NCH;
         ring.e[u % DEPTH] = *(LdsF4)(lds + wd.be[i] + 16 * s);
         ring.o[u % DEPTH] = *(LdsF4)(lds + wd.bo[i] + 16 * s);
     };
     auto fma_chunk = [&](int s, float we, float wei, float wo, float woi, const f4_t &xe, const f4_t &xo) {
-        if constexpr (IQ) {
+        if constexpr (H && IQ) {
+            // dword j: (re, im) halves of complex frame 4 s + j, one term of
+            // all eight sums a pass
+            uint32_t e[4], o[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float fe = xe[j], fo = xo[j];  // (a bit cast of a vector element expression reads element 0)
+                e[j] = __builtin_bit_cast(uint32_t, fe);
+                o[j] = __builtin_bit_cast(uint32_t, fo);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                das::fma_half<false>(acc[8 * s + 2 * j], we, e[j]);
+                das::fma_half<true>(acc[8 * s + 2 * j + 1], we, e[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                das::fma_half<true>(acc[8 * s + 2 * j], -wei, e[j]);
+                das::fma_half<false>(acc[8 * s + 2 * j + 1], wei, e[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                das::fma_half<false>(acc[8 * s + 2 * j], wo, o[j]);
+                das::fma_half<true>(acc[8 * s + 2 * j + 1], wo, o[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                das::fma_half<true>(acc[8 * s + 2 * j], -woi, o[j]);
+                das::fma_half<false>(acc[8 * s + 2 * j + 1], woi, o[j]);
+            }
+        } else if constexpr (H) {
+            // dword j: frames 8 s + 2 j (low half) and 8 s + 2 j + 1 (high)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float fe = xe[j];
+                const uint32_t e = __builtin_bit_cast(uint32_t, fe);
+                das::fma_half<false>(acc[8 * s + 2 * j], we, e);
+                das::fma_half<true>(acc[8 * s + 2 * j + 1], we, e);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float fo = xo[j];
+                const uint32_t o = __builtin_bit_cast(uint32_t, fo);
+                das::fma_half<false>(acc[8 * s + 2 * j], wo, o);
+                das::fma_half<true>(acc[8 * s + 2 * j + 1], wo, o);
+            }
+        } else if constexpr (IQ) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 float &re = acc[4 * s + 2 * j], &im = acc[4 * s + 2 * j + 1];
@@ -463,13 +515,13 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
         }
     };
     auto fma_unit = [&](auto U, const RowsWin<NIT> &wd, const f4_t &xe, const f4_t &xo) {
-        constexpr int u = decltype(U)::value, i = u / 8, s = u % 8;
+        constexpr int u = decltype(U)::value, i = u / NCH, s = u % NCH;
         float (&ac)[32] = acc;                   // (a non-dependent use, so the generic lambda captures it)
         fma_chunk(s, wd.we[i], wd.wei[i], wd.wo[i], wd.woi[i], xe, xo);
         // pin the chunk's sums here: left alone the compiler sinks the FMAs
         // to the end of the step and keeps every unit's rows live
 #pragma unroll
-        for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(ac[4 * s + j]));
+        for (int j = 0; j < APC; ++j) asm volatile("" : "+v"(ac[APC * s + j]));
     };
     // Units U0 .. U1 - 1 in one pipeline, the reads running DEPTH units ahead
     // of their FMAs (the scheduling fences keep the compiler from sinking
@@ -479,8 +531,10 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     // catch up and all reach the barrier together.
     auto pipeline = [&](auto U0, auto U1, const RowsWin<NIT> &wd, const RowsCopy &cp) {
         constexpr int u0 = decltype(U0)::value, nu = decltype(U1)::value - u0;
+        // copy rounds: one every `spread` units, or (fewer units than
+        // rounds) round j at unit j mod nu
         constexpr int spread = (nu / G::MAXR) > 3 ? 3 : (nu / G::MAXR);
-        static_assert(spread >= 1 && spread * (G::MAXR - 1) + spread / 2 < nu, "every copy round is issued");
+        static_assert(spread == 0 || spread * (G::MAXR - 1) + spread / 2 < nu, "every copy round is issued");
         Ring ring;
         das::unroll<DEPTH>([&](auto U) { issue_unit(das::ic<u0 + decltype(U)::value>{}, wd, ring); });
         __builtin_amdgcn_sched_barrier(0);
@@ -489,8 +543,13 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
             fma_unit(das::ic<u>{}, wd, ring.e[u % DEPTH], ring.o[u % DEPTH]);
             if constexpr (l + DEPTH < nu)
                 issue_unit(das::ic<u + DEPTH>{}, wd, ring);
-            if constexpr (l % spread == spread / 2 && l / spread < G::MAXR)
-                copy_round(cp, l / spread);
+            if constexpr (spread > 0) {
+                if constexpr (l % spread == spread / 2 && l / spread < G::MAXR)
+                    copy_round(cp, l / spread);
+            } else {
+#pragma unroll
+                for (int j = l; j < G::MAXR; j += nu) copy_round(cp, j);
+            }
             if constexpr ((l + 1) % (nu / 4) == 0 && l + 1 < nu)
                 __builtin_amdgcn_s_setprio(3 - (l + 1) / (nu / 4));
             __builtin_amdgcn_sched_barrier(0);
@@ -504,7 +563,7 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     // copy of the sums: they spill.)
     auto compute_lds = [&](const RowsWin<NIT> &wd, const RowsCopy &cp) {
         using das::ic;
-        pipeline(ic<0>{}, ic<8 * NIT>{}, wd, cp);
+        pipeline(ic<0>{}, ic<NCH * NIT>{}, wd, cp);
     };
     // A step by direct loads from the permuted buffer (a window too wide for
     // the regions): each item with a non-zero weight reads its two rows.
@@ -518,7 +577,7 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
                 continue;
             const uint32_t o0 = (uint32_t)r * m_stride + st[i].k * kstride32 + (uint32_t)b0 * E;
 #pragma unroll
-            for (int s = 0; s < 8; ++s) {
+            for (int s = 0; s < NCH; ++s) {
                 const f4_t x0 = das::buffer_load_f32x4(rd, (int)(o0 + 16u * s), 0, 0);
                 const f4_t x1 = das::buffer_load_f32x4(rd, (int)(o0 + kstride32 + 16u * s), 0, 0);
                 fma_chunk(s, st[i].a, st[i].ai, st[i].b, st[i].bi, x0, x1);
@@ -683,33 +742,40 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     }
 }
 
-template <bool IQ, int LAYOUT, int NIT>
+template <bool IQ, int LAYOUT, int NIT, bool H>
 hipError_t launch_rows(const DasKParams &kp, const float *rf, const float *rx, const float *tau, const float *w,
                        float *out, hipStream_t stream) {
-    constexpr int FR = WR_ROWB / (IQ ? 8 : 4);
+    constexpr int FR = IQ ? 16 : 32;
     const int tiles = ((kp.nx + WR_TX - 1) / WR_TX) * ((kp.ny + WR_TY - 1) / WR_TY) * ((kp.nz + WR_TZ - 1) / WR_TZ);
-    hipLaunchKernelGGL((das_bi_rows_kernel<IQ, LAYOUT, NIT>), dim3(tiles, kp.B / FR), dim3(WR_THREADS), 0, stream, kp,
+    hipLaunchKernelGGL((das_bi_rows_kernel<IQ, LAYOUT, NIT, H>), dim3(tiles, kp.B / FR), dim3(WR_THREADS), 0, stream, kp,
                        rf, rx, tau, w, out);
     return hipGetLastError();
 }
 
-template <bool IQ, int LAYOUT>
+template <bool IQ, int LAYOUT, bool H>
 hipError_t launch_rows_nit(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
                            const float *tau, const float *w, float *out, hipStream_t stream) {
     if constexpr (IQ)                                    // complex plans take 8 receivers a step
-        return launch_rows<IQ, LAYOUT, 1>(kp, rf, rx, tau, w, out, stream);
+        return launch_rows<IQ, LAYOUT, 1, H>(kp, rf, rx, tau, w, out, stream);
     else
-        return plan.rows == 2 ? launch_rows<IQ, LAYOUT, 2>(kp, rf, rx, tau, w, out, stream)
-                              : launch_rows<IQ, LAYOUT, 1>(kp, rf, rx, tau, w, out, stream);
+        return plan.rows == 2 ? launch_rows<IQ, LAYOUT, 2, H>(kp, rf, rx, tau, w, out, stream)
+                              : launch_rows<IQ, LAYOUT, 1, H>(kp, rf, rx, tau, w, out, stream);
+}
+
+template <bool IQ, int LAYOUT>
+hipError_t launch_rows_h(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
+                         const float *tau, const float *w, float *out, hipStream_t stream) {
+    return plan.h16 ? launch_rows_nit<IQ, LAYOUT, true>(plan, kp, rf, rx, tau, w, out, stream)
+                    : launch_rows_nit<IQ, LAYOUT, false>(plan, kp, rf, rx, tau, w, out, stream);
 }
 
 }  // namespace
 
 bool das_rows_supported(const das_plan_t &plan) {
-    // native samples, 128-byte frame tiles (fp32: B a multiple of 32;
-    // complex64: of 16), records of at most 65535 samples, and at most
-    // 8 WR_LIVE_BLOCKS receivers (the aperture mask)
-    if (plan.h16 || plan.p.K > 65535 || plan.p.M > 8 * WR_LIVE_BLOCKS)
+    // frame tiles of 32 fp32 or 16 complex frames (B a multiple of that),
+    // native or binary16 samples, records of at most 65535 samples, and at
+    // most 8 WR_LIVE_BLOCKS receivers (the aperture mask)
+    if (plan.p.K > 65535 || plan.p.M > 8 * WR_LIVE_BLOCKS)
         return false;
     return (plan.p.dtype == DAS_F32 && plan.p.B % 32 == 0) || (plan.p.dtype == DAS_C64 && plan.p.B % 16 == 0);
 }
@@ -718,8 +784,8 @@ hipError_t das_launch_bi_rows(const das_plan_t &plan, const DasKParams &kp, cons
                               const float *tau_tx, const float *w_tx, float *out, hipStream_t stream) {
     const bool iq = plan.p.dtype == DAS_C64;
     if (plan.p.layout == DAS_LAYOUT_KQMB)
-        return iq ? launch_rows_nit<true, DAS_LAYOUT_KQMB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream)
-                  : launch_rows_nit<false, DAS_LAYOUT_KQMB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream);
-    return iq ? launch_rows_nit<true, DAS_LAYOUT_QMKB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream)
-              : launch_rows_nit<false, DAS_LAYOUT_QMKB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream);
+        return iq ? launch_rows_h<true, DAS_LAYOUT_KQMB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream)
+                  : launch_rows_h<false, DAS_LAYOUT_KQMB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream);
+    return iq ? launch_rows_h<true, DAS_LAYOUT_QMKB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream)
+              : launch_rows_h<false, DAS_LAYOUT_QMKB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream);
 }
