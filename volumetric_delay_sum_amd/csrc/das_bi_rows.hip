@@ -181,39 +181,48 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     // ---- receive aperture of the tile ------------------------------------------
     // A block of 8 receivers whose receive weight is zero for every voxel of
     // the tile adds nothing: the sweep skips it, and a step takes the next NIT
-    // live blocks.  A pair counts as
-    // zero only when it is clearly outside the aperture or behind the array,
-    // by a margin far above the rounding of this fp32 test and of the
-    // weight's own: cos^2 theta <= cos^2 theta_max / (1 + 1e-3 (1 - cos^2
-    // theta_max)), i.e. dz^2 (1 - c^2)(1 + 1e-3) <= c^2 rho^2 with dz > 0, or
-    // dz below zero by more than its rounding.  Lane (v, r) tests receiver
-    // r of each block against its voxel; a wave's vote goes to the mask by
-    // one atomic per block.
+    // live blocks.  A pair counts as zero only when it is clearly outside the
+    // aperture or behind the array, by a margin far above the rounding of
+    // this fp32 test and of the weight's own: cos^2 theta <= cos^2 theta_max
+    // / (1 + 1e-3 (1 - cos^2 theta_max)), i.e. dz^2 (1 - c^2)(1 + 1e-3) <=
+    // c^2 rho^2 with dz > 0, or dz below zero by more than its rounding.
+    // Lateral distance and depth separate, so over the tile's voxels the
+    // pair nearest to the inside of the cone is the voxel nearest to the
+    // receiver laterally on the tile's plane farthest in front of it: if that
+    // one counts as zero, so does every voxel of the tile.  Lane t tests
+    // receiver t (and t + 1024, ...) against it; the 8 lanes of a block vote.
     if (P.apod) {
         const float ctm = 1.0f - 1.0f / P.apod_inv_vmax;                 // cos theta_max
         const float ca = (1.0f - ctm * ctm) * 1.001f, cb = ctm * ctm;
-        const float fvx = (float)(P.ox + (double)ixc * P.sx), fvy = (float)(P.oy + (double)iyc * P.sy);
-        const float fvz = (float)(P.oz + (double)izc * P.sz);
-        constexpr int UNR = 4;
-        for (int b0 = 0; b0 < nblk; b0 += UNR) {
-            bool any[UNR];
-#pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-                any[u] = false;
-                const int m = (b0 + u) * 8 + r;
-                const int mc = min(m, P.M - 1);
-                const float dx = fvx - rx[3 * mc], dy = fvy - rx[3 * mc + 1], dz = fvz - rx[3 * mc + 2];
+        const int x0 = tx * WR_TX, x1 = min(x0 + WR_TX, P.nx) - 1;
+        const int y0 = ty * WR_TY, y1 = min(y0 + WR_TY, P.ny) - 1;
+        const int z0 = tz * WR_TZ, z1 = min(z0 + WR_TZ, P.nz) - 1;
+        // nearest index in [lo, hi] of a grid axis to coordinate p
+        auto nearest = [](double p, double o, double sp, int lo, int hi) -> int {
+            if (sp == 0.0)
+                return lo;
+            const double t = __builtin_rint((p - o) / sp);
+            return t <= (double)lo ? lo : (t >= (double)hi ? hi : (int)t);
+        };
+        for (int mb = 0; mb < nblk * 8; mb += WR_THREADS) {
+            const int m = mb + tid;
+            bool on = false;
+            if (m < P.M) {
+                const float px = rx[3 * m], py = rx[3 * m + 1], pz = rx[3 * m + 2];
+                const int ixn = nearest(px, P.ox, P.sx, x0, x1), iyn = nearest(py, P.oy, P.sy, y0, y1);
+                const float dx = (float)(P.ox + (double)ixn * P.sx) - px;
+                const float dy = (float)(P.oy + (double)iyn * P.sy) - py;
+                const float za = (float)(P.oz + (double)z0 * P.sz), zb = (float)(P.oz + (double)z1 * P.sz);
+                const float vz = fmaxf(za, zb), dz = vz - pz;
                 const float rho2 = __builtin_fmaf(dx, dx, dy * dy), dz2 = dz * dz;
-                const float ez = 1e-5f * (fabsf(fvz) + fabsf(rx[3 * mc + 2])) + 1e-30f;
+                const float ez = 1e-5f * (fabsf(vz) + fabsf(pz)) + 1e-30f;
                 const bool zero = (dz < -ez) || (dz > ez && dz2 * ca <= rho2 * cb);
-                any[u] = m < P.M && vox_ok && !zero;
+                on = !zero;
             }
-#pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-                const int b = b0 + u;
-                if (b < nblk && __any(any[u]) && lane == 0)
-                    atomicOr(&live[b >> 5], 1u << (b & 31));
-            }
+            const uint64_t vote = __ballot(on);
+            const int b = (mb + 64 * wave) / 8 + lane;                   // lane < 8: block b of this wave
+            if (lane < 8 && b < nblk && ((vote >> (8 * lane)) & 0xffu))
+                atomicOr(&live[b >> 5], 1u << (b & 31));
         }
         __syncthreads();
     }
