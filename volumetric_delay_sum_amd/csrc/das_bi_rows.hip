@@ -8,14 +8,16 @@
 // differs is the lane mapping:
 //
 //   - A lane owns one voxel of the 8 x 8 x 2 tile, ALL frames of the frame
-//     tile (128 bytes of a sample row: 32 fp32 or 16 complex frames) and, in
-//     each step, one receiver of every block of 8 the step takes.  Each (voxel, receiver)
-//     item is the lane's own: it computes the item's sample split and weights
-//     and applies them itself, so the item's 64 (complex: 128) FMAs take
-//     register weights (plain FMAs, nothing crosses lanes in the inner loop),
-//     and the per-item work is shared by 32 (16) frames.
-//   - The lane reads its item's two sample rows whole: 16 reads of 16 bytes,
-//     the LDS's widest access, from two base registers with immediate offsets.
+//     tile (32 fp32 or 16 complex frames: 128 bytes of a sample row, 64 with
+//     binary16 storage) and, in each step, one receiver of every block of 8
+//     the step takes.  Each (voxel, receiver) item is the lane's own: it
+//     computes the item's sample split and weights and applies them itself,
+//     so the item's 64 (complex: 128) FMAs take register weights (plain FMAs,
+//     nothing crosses lanes in the inner loop), and the per-item work is
+//     shared by 32 (16) frames.
+//   - The lane reads its item's two sample rows whole: 16 reads of 16 bytes
+//     (binary16: 8), the LDS's widest access, from two base registers with
+//     immediate offsets.  A staged row takes a 128-byte slot either way.
 //   - Bank conflicts.  The 16 lanes of one read are 8 receivers x 2 voxels.
 //     Receiver regions are padded by 16 bytes, so the 8 regions of a group
 //     start in 8 different 16-byte bank groups modulo 8; and a lane reads
