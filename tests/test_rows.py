@@ -138,3 +138,39 @@ def test_main_binary16_default(gpu, iq):
     out = run_gpu(inp, "batch_inner", "qmkb", storage="f16")
     assert_all_written(out, f"main f16 iq={iq}")
     assert_parity(to_numpy(out, iq)[:, vox], oracle_ref(inp, voxels=vox, storage="f16"), f"main f16 iq={iq}")
+
+
+def test_many_receivers(gpu, monkeypatch):
+    """A 48 x 48 array (2304 receivers: 288 blocks of 8, a nine-word aperture
+    mask, three rounds of the per-receiver test) over a small grid."""
+    cfg = _ragged(False, B=32, K=500, array=(48, 48), grid=(12, 9, 3), sources=((0.0, 0.0), (1e-3, 1e-3)))
+    inp = Inputs(cfg, w_tx="uniform")
+    assert _info(inp)["whole_rows"] == 1
+    y = to_numpy(run_gpu(inp, "batch_inner", "qmkb"), False)
+    assert_parity(y, oracle_ref(inp), "2304 receivers")
+
+
+@pytest.mark.parametrize("rows,iq", VARIANTS, ids=IDS)
+def test_grid_with_negative_spacing(gpu, monkeypatch, rows, iq):
+    """The same voxels indexed from the far corner (negative pitch on every
+    axis): the aperture test must take the plane farthest in front of each
+    receiver from either end of the z axis.  The result is the ordinary one
+    with the voxel index reversed."""
+    import copy
+    import torch
+    _use(monkeypatch, rows)
+    cfg = _ragged(iq, K=320, f_number=1.5)
+    inp = Inputs(cfg, w_tx="uniform")
+    nx, ny, nz = cfg.grid
+    (ox, oy, oz), (sx, sy, sz) = inp.fields["origin"], inp.fields["spacing"]
+    flip = copy.copy(inp)
+    flip.fields = dict(inp.fields, origin=(ox + (nx - 1) * sx, oy + (ny - 1) * sy, oz + (nz - 1) * sz),
+                       spacing=(-sx, -sy, -sz))
+    rev = np.arange(cfg.N)[::-1].copy()                 # flipped voxel n is ordinary voxel N - 1 - n
+    flip.tau, flip.w = inp.tau[:, rev].copy(), inp.w[:, rev].copy()
+    flip.tau_d, flip.w_d = torch.from_numpy(flip.tau).cuda(), torch.from_numpy(flip.w).cuda()
+    ref = oracle_ref(flip)
+    y = to_numpy(run_gpu(flip, "batch_inner", "qmkb"), iq)
+    assert_parity(y, ref, f"negative pitch rows={rows} iq={iq}")
+    y0 = to_numpy(run_gpu(inp, "batch_inner", "qmkb"), iq)
+    assert_parity(y, y0[:, rev], f"negative pitch against ordinary rows={rows} iq={iq}")
