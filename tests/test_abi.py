@@ -170,16 +170,16 @@ def test_auto_selection(dtype, B, alg):
                                algorithm="default")).info["algorithm"] == das.ALG_BASELINE
 
 
-@pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 1), (24, 1), (32, 32), (48, 1), (64, 32), (96, 32), (66, 1),
+@pytest.mark.parametrize("B,fl", [(1, 1), (8, 1), (16, 16), (24, 1), (32, 32), (48, 16), (64, 32), (96, 32), (66, 1),
                                   (160, 32), (192, 32), (68, 4)])
 def test_frames_per_lane_choice(B, fl):
-    # fp32 batch-inner: the LDS-staged kernel wherever B % 16 == 0, with
-    # whole-row lanes (all 32 frames of a frame tile per lane) when B % 32 == 0
-    # and one frame per lane of a DPP row otherwise
+    # fp32 batch-inner: the LDS-staged whole-row kernel wherever B % 16 == 0
+    # (all 32 frames of a frame tile per lane when B % 32 == 0, else 16),
+    # direct loads otherwise
     pl = das.Plan(**_problem(B=B))
     assert pl.info["frames_per_lane"] == fl
     assert pl.info["staged"] == (1 if B % 16 == 0 else 0)
-    assert pl.info["whole_rows"] == (1 if B % 32 == 0 else 0)
+    assert pl.info["whole_rows"] == (1 if B % 16 == 0 else 0)
     assert pl.info["receivers_per_step"] == (16 if B % 16 == 0 else 0)
 
 
@@ -419,12 +419,12 @@ def test_binary16_storage_needs_batch_inner():
 
 @pytest.mark.parametrize("dtype,B,store,fl,staged,rows", [
     ("f32", 32, 2, 32, 1, 1), ("f32", 64, 2, 32, 1, 1), ("f32", 128, 2, 32, 1, 1), ("f32", 96, 2, 32, 1, 1),
-    ("f32", 16, 2, 1, 1, 0), ("f32", 48, 2, 1, 1, 0),
+    ("f32", 16, 2, 16, 1, 1), ("f32", 48, 2, 16, 1, 1),
     ("f32", 24, 2, 2, 0, 0), ("f32", 68, 2, 4, 0, 0), ("f32", 7, 2, 1, 0, 0), ("c64", 32, 4, 16, 1, 1),
     ("c64", 64, 4, 16, 1, 1), ("c64", 16, 4, 16, 1, 1), ("c64", 48, 4, 16, 1, 1), ("c64", 34, 4, 2, 0, 0)])
 def test_binary16_plan_info(dtype, B, store, fl, staged, rows):
-    # binary16 rows run the whole-row kernel where its frame tiles fit (32
-    # fp32 or 16 complex frames), the DPP-row kernel for fp32 B = 16 and 48
+    # binary16 rows run the whole-row kernel where its frame tiles fit (32 or
+    # 16 fp32 or 16 complex frames: B a multiple of 16)
     iq = dtype == "c64"
     pl = das.Plan(**_problem(B=B, dtype=dtype, f_demod=5e6 if iq else 0.0, storage="f16"))
     assert pl.store_f16

@@ -82,11 +82,12 @@ def test_binary16_direct_kernel(gpu, monkeypatch, iq):
 
 
 # frames per lane of the binary16 staged instances.  Whole-row lanes (the
-# default where B is a multiple of 32 fp32 or 16 complex frames): 32 or 16.
-# DPP rows (fp32 B = 16 and 48, or DAS_STAGED_ROWS=0): B a multiple of 32
+# default where B is a multiple of 16): 32 fp32 frames (B a multiple of 32),
+# else 16 fp32 or complex frames.  DPP rows (DAS_STAGED_ROWS=0): B a multiple of 32
 # takes two (complex: one pair of halves per frame, two frames), a multiple of
 # 16 only takes one, and fp32 data with B a multiple of 64 takes four
-FPL16_ROWS = {(False, 32): 32, (False, 64): 32, (True, 16): 16, (True, 32): 16, (True, 48): 16, (True, 64): 16}
+FPL16_ROWS = {(False, 16): 16, (False, 32): 32, (False, 48): 16, (False, 64): 32,
+              (True, 16): 16, (True, 32): 16, (True, 48): 16, (True, 64): 16}
 FPL16_DPP = {(False, 16): 1, (False, 32): 2, (False, 48): 1, (False, 64): 4,
              (True, 16): 1, (True, 32): 2, (True, 48): 1, (True, 64): 2}
 

@@ -113,10 +113,9 @@ def test_q_chunks_sum_to_the_whole(gpu, alg, layout):
 @pytest.mark.parametrize("voxel", [0.25e-3, 0.6e-3, 1.5e-3], ids=["fine", "mixed", "coarse"])
 @pytest.mark.parametrize("B", [16, 32, 64])
 def test_staged_windows_and_fallback(gpu, monkeypatch, layout, voxel, iq, B, kernel):
-    """The LDS-staged kernels.  Default: fp32 with B a multiple of 32 and
-    complex64 with B a multiple of 16 run whole-row lanes (all 32 fp32 or 16
-    complex frames of a frame tile per lane, 16 or 8 receivers a step), fp32
-    B = 16 the DPP-row kernel; "dpp_rows" forces the DPP-row
+    """The LDS-staged kernels.  Default: whole-row lanes (all 32 or 16 fp32
+    or 16 complex frames of a frame tile per lane, 16 or 8 receivers a step);
+    "dpp_rows" forces the DPP-row
     kernel: fp32 B = 32, 2 frames per lane, one 32-frame tile of 16 receivers
     a step; fp32 B = 64 and complex64 B = 32 and 64: split rows (two voxels
     per DPP row, 16 bytes per lane, 8 receivers a step, 256-byte rows).

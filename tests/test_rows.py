@@ -42,7 +42,7 @@ def _info(inp, storage="native"):
 
 @pytest.mark.parametrize("storage", ["native", "f16"])
 @pytest.mark.parametrize("layout", ["kqmb", "qmkb"])
-@pytest.mark.parametrize("B", [32, 64, 96])
+@pytest.mark.parametrize("B", [16, 32, 48, 64, 96])
 @pytest.mark.parametrize("rows,iq", VARIANTS, ids=IDS)
 def test_ragged(gpu, monkeypatch, rows, iq, B, layout, storage):
     _use(monkeypatch, rows)

@@ -67,19 +67,23 @@ def test_start_time_binary16(gpu, monkeypatch, t0, kernel, iq):
     assert_parity(y, oracle_ref(inp, storage="f16"), f"t0={t0} f16 {alg}/{layout}/{override} iq={iq}")
 
 
+@pytest.mark.parametrize("kernel", ["default", "dpp_rows"])
 @pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])
-@pytest.mark.parametrize("B", [16, 64], ids=["one_frame_per_lane", "split_rows"])
+@pytest.mark.parametrize("B", [16, 64], ids=["B16", "B64"])
 @pytest.mark.parametrize("storage", ["native", "f16"])
-def test_start_time_other_staged_shapes(gpu, B, iq, storage):
-    """B = 16 and B = 64 at a fractional negative t0: with binary16 storage the
-    DPP-row kernel with one frame per lane and with split rows (two voxels per
-    DPP row, 16 bytes per lane); with native samples fp32 B = 16 runs the
-    DPP-row kernel with one frame per lane, the others whole-row lanes."""
+def test_start_time_other_staged_shapes(gpu, monkeypatch, B, iq, storage, kernel):
+    """B = 16 and B = 64 at a fractional negative t0.  Default: whole-row
+    lanes with 16- and 32-frame tiles.  "dpp_rows" (DAS_STAGED_ROWS=0): the
+    DPP-row kernel with one frame per lane (B = 16) and, for B = 64, split
+    rows (two voxels per DPP row, 16 bytes per lane)."""
     import volumetric_delay_sum_amd as das
+    if kernel == "dpp_rows":
+        monkeypatch.setenv("DAS_STAGED_ROWS", "0")
     inp = Inputs(_cfg(-0.83e-6, iq=iq, B=B), w_tx="uniform")
-    assert das.plan_from_fields(inp.fields, "batch_inner", "qmkb", storage=storage).info["staged"] == 1
+    info = das.plan_from_fields(inp.fields, "batch_inner", "qmkb", storage=storage).info
+    assert info["staged"] == 1 and info["whole_rows"] == (1 if kernel == "default" else 0)
     y = to_numpy(run_gpu(inp, "batch_inner", "qmkb", storage=storage), iq)
-    assert_parity(y, oracle_ref(inp, storage=storage), f"t0<0 B={B} {storage} iq={iq}")
+    assert_parity(y, oracle_ref(inp, storage=storage), f"t0<0 B={B} {storage} iq={iq} {kernel}")
 
 
 @pytest.mark.parametrize("kernel", KERNELS, ids=KERNEL_IDS)

@@ -397,7 +397,7 @@ das_status das_plan_get_info(const das_plan_t *plan, das_plan_info *info) {
     const bool bi = plan->alg == DAS_ALG_BATCH_INNER;
     const bool rp = plan->alg == DAS_ALG_REPACK;
     const bool wr = bi && plan->rows != 0;
-    const int32_t wr_frames = plan->p.dtype == DAS_C64 ? 16 : 32;
+    const int32_t wr_frames = (plan->p.dtype == DAS_C64 || plan->p.B % 32 != 0) ? 16 : 32;
     info->frames_per_lane = rp ? (plan->p.B % 64 == 0 ? 32 : 16) : (wr ? wr_frames : (bi ? plan->fl : plan->bt));
     info->lanes_per_voxel = rp ? 2 : (wr ? 8 : (bi ? 16 : 1));
     info->voxels_per_group = rp ? 256 : (wr ? 128 : (bi ? 16 : 256));

@@ -8,16 +8,17 @@
 // differs is the lane mapping:
 //
 //   - A lane owns one voxel of the 8 x 8 x 2 tile, ALL frames of the frame
-//     tile (32 fp32 or 16 complex frames: 128 bytes of a sample row, 64 with
+//     tile (32 fp32 frames, or 16 when B is a multiple of 16 only, or 16
+//     complex frames: 128 or 64 bytes of a sample row, half that with
 //     binary16 storage) and, in each step, one receiver of every block of 8
 //     the step takes.  Each (voxel, receiver) item is the lane's own: it
 //     computes the item's sample split and weights and applies them itself,
-//     so the item's 64 (complex: 128) FMAs take register weights (plain FMAs,
-//     nothing crosses lanes in the inner loop), and the per-item work is
-//     shared by 32 (16) frames.
-//   - The lane reads its item's two sample rows whole: 16 reads of 16 bytes
-//     (binary16: 8), the LDS's widest access, from two base registers with
-//     immediate offsets.  A staged row takes a 128-byte slot either way.
+//     so the item's 2 FMAs per fp32 frame (8 per complex frame) take register
+//     weights (plain FMAs, nothing crosses lanes in the inner loop), and the
+//     per-item work is shared by the tile's frames.
+//   - The lane reads its item's two sample rows whole: up to 16 reads of 16
+//     bytes, the LDS's widest access, from two base registers with immediate
+//     offsets.  A staged row takes a 128-byte slot whatever its size.
 //   - Bank conflicts.  The 16 lanes of one read are 8 receivers x 2 voxels.
 //     Receiver regions are padded by 16 bytes, so the 8 regions of a group
 //     start in 8 different 16-byte bank groups modulo 8; and a lane reads
@@ -111,7 +112,7 @@ struct RowsCopy {
     das::BufRsrc rs;
 };
 
-template <bool IQ, int LAYOUT, int NIT, bool H>
+template <bool IQ, int LAYOUT, int NIT, bool H, int FRT>
 __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, const float *__restrict__ rfp,
                                                                  const float *__restrict__ rx,
                                                                  const float *__restrict__ tau_tx,
@@ -121,9 +122,11 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     constexpr int NRX = G::NRX;
     constexpr int C = IQ ? 2 : 1;
     constexpr int E = (H ? 2 : 4) * C;           // bytes per stored sample (H: binary16)
-    constexpr int FR = IQ ? 16 : 32;             // frames of a frame tile
-    constexpr int NCH = FR * E / 16;             // 16-byte chunks of a row's frame tile (8; binary16: 4)
-    constexpr int APC = 32 / NCH;                // sums a chunk feeds
+    constexpr int FR = FRT;                      // frames of a frame tile: 32 or 16 fp32, 16 complex
+    static_assert(IQ ? FRT == 16 : (FRT == 32 || FRT == 16), "frame tile");
+    constexpr int NACC = FR * C;                 // sums per lane
+    constexpr int NCH = FR * E / 16;             // 16-byte chunks of a row's frame tile (8, 4 or 2)
+    constexpr int APC = NACC / NCH;              // sums a chunk feeds
     constexpr int DEPTH = 3;                     // units whose reads are in flight
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + 2 * G::BUF);
@@ -441,14 +444,15 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     };
 
     // ---- interpolate-weight-accumulate ------------------------------------
-    // acc[j]: fp32 frame j of the frame tile; complex: (re, im) of frame j / 2.
+    // acc[j], j < NACC: fp32 frame j of the frame tile; complex: (re, im) of
+    // frame j / 2.
     // Unit u = NCH i + s of a step is chunk s (16 bytes) of item i's two rows:
     // two reads and 8 (complex: 16) FMAs, twice that for binary16 chunks,
     // whose FMAs take the halves straight from the loaded dwords
     // (v_fma_mix_f32, one rounding as for a widened sample).
-    float acc[32];
+    float acc[NACC];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
+    for (int j = 0; j < NACC; ++j) acc[j] = 0.0f;
     using LdsF4 = const volatile __attribute__((address_space(3))) f4_t *;
     struct Ring {
         f4_t e[DEPTH], o[DEPTH];
@@ -527,7 +531,7 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     };
     auto fma_unit = [&](auto U, const RowsWin<NIT> &wd, const f4_t &xe, const f4_t &xo) {
         constexpr int u = decltype(U)::value, i = u / NCH, s = u % NCH;
-        float (&ac)[32] = acc;                   // (a non-dependent use, so the generic lambda captures it)
+        float (&ac)[NACC] = acc;                 // (a non-dependent use, so the generic lambda captures it)
         fma_chunk(s, wd.we[i], wd.wei[i], wd.wo[i], wd.woi[i], xe, xo);
         // pin the chunk's sums here: left alone the compiler sinks the FMAs
         // to the end of the step and keeps every unit's rows live
@@ -545,9 +549,10 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
         // copy rounds: one every `spread` units, or (fewer units than
         // rounds) round j at unit j mod nu
         constexpr int spread = (nu / G::MAXR) > 3 ? 3 : (nu / G::MAXR);
+        constexpr int q4 = nu >= 4 ? nu / 4 : 1;                  // units per quarter of the loop
         static_assert(spread == 0 || spread * (G::MAXR - 1) + spread / 2 < nu, "every copy round is issued");
         Ring ring;
-        das::unroll<DEPTH>([&](auto U) { issue_unit(das::ic<u0 + decltype(U)::value>{}, wd, ring); });
+        das::unroll<(DEPTH < nu ? DEPTH : nu)>([&](auto U) { issue_unit(das::ic<u0 + decltype(U)::value>{}, wd, ring); });
         __builtin_amdgcn_sched_barrier(0);
         das::unroll<nu>([&](auto L) {
             constexpr int l = decltype(L)::value, u = u0 + l;
@@ -561,8 +566,8 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
 #pragma unroll
                 for (int j = l; j < G::MAXR; j += nu) copy_round(cp, j);
             }
-            if constexpr ((l + 1) % (nu / 4) == 0 && l + 1 < nu)
-                __builtin_amdgcn_s_setprio(3 - (l + 1) / (nu / 4));
+            if constexpr ((l + 1) % q4 == 0 && l + 1 < nu)
+                __builtin_amdgcn_s_setprio(3 - (l + 1) * 4 / nu);
             __builtin_amdgcn_sched_barrier(0);
         });
     };
@@ -719,9 +724,11 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
 
     // ---- output ----------------------------------------------------------------
     // The 8 lanes of a voxel (r = 0..7) hold sums over different receivers:
-    // add them (pair, quad and half-row DPP), then lane r writes chunk r.
+    // add them (pair, quad and half-row DPP), then lane r writes the r-th
+    // eighth of the sums (VPL of them).
+    constexpr int VPL = NACC / 8;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
+    for (int j = 0; j < NACC; ++j) {
         float x = acc[j];
         x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
         x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
@@ -730,12 +737,12 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     }
     if (!vox_ok)
         return;
-    float val[4];
+    float val[VPL];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < VPL; ++j) {
         val[j] = acc[j];
 #pragma unroll
-        for (int s = 1; s < 8; ++s) val[j] = (r == s) ? acc[4 * s + j] : val[j];
+        for (int s = 1; s < 8; ++s) val[j] = (r == s) ? acc[VPL * s + j] : val[j];
     }
     if constexpr (IQ) {
 #pragma unroll
@@ -746,19 +753,18 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float *o = out + (int64_t)(b0 + 4 * r + j) * P.N + n;
+        for (int j = 0; j < VPL; ++j) {
+            float *o = out + (int64_t)(b0 + VPL * r + j) * P.N + n;
             *o = P.accumulate ? *o + val[j] : val[j];
         }
     }
 }
 
-template <bool IQ, int LAYOUT, int NIT, bool H>
+template <bool IQ, int LAYOUT, int NIT, bool H, int FRT>
 hipError_t launch_rows(const DasKParams &kp, const float *rf, const float *rx, const float *tau, const float *w,
                        float *out, hipStream_t stream) {
-    constexpr int FR = IQ ? 16 : 32;
     const int tiles = ((kp.nx + WR_TX - 1) / WR_TX) * ((kp.ny + WR_TY - 1) / WR_TY) * ((kp.nz + WR_TZ - 1) / WR_TZ);
-    hipLaunchKernelGGL((das_bi_rows_kernel<IQ, LAYOUT, NIT, H>), dim3(tiles, kp.B / FR), dim3(WR_THREADS), 0, stream, kp,
+    hipLaunchKernelGGL((das_bi_rows_kernel<IQ, LAYOUT, NIT, H, FRT>), dim3(tiles, kp.B / FRT), dim3(WR_THREADS), 0, stream, kp,
                        rf, rx, tau, w, out);
     return hipGetLastError();
 }
@@ -766,11 +772,16 @@ hipError_t launch_rows(const DasKParams &kp, const float *rf, const float *rx, c
 template <bool IQ, int LAYOUT, bool H>
 hipError_t launch_rows_nit(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
                            const float *tau, const float *w, float *out, hipStream_t stream) {
-    if constexpr (IQ)                                    // complex plans take 8 receivers a step
-        return launch_rows<IQ, LAYOUT, 1, H>(kp, rf, rx, tau, w, out, stream);
+    // complex plans take 8 receivers a step and 16-frame tiles; fp32 ones
+    // 32-frame tiles where B allows, else 16
+    if constexpr (IQ)
+        return launch_rows<IQ, LAYOUT, 1, H, 16>(kp, rf, rx, tau, w, out, stream);
+    else if (plan.p.B % 32 == 0)
+        return plan.rows == 2 ? launch_rows<IQ, LAYOUT, 2, H, 32>(kp, rf, rx, tau, w, out, stream)
+                              : launch_rows<IQ, LAYOUT, 1, H, 32>(kp, rf, rx, tau, w, out, stream);
     else
-        return plan.rows == 2 ? launch_rows<IQ, LAYOUT, 2, H>(kp, rf, rx, tau, w, out, stream)
-                              : launch_rows<IQ, LAYOUT, 1, H>(kp, rf, rx, tau, w, out, stream);
+        return plan.rows == 2 ? launch_rows<IQ, LAYOUT, 2, H, 16>(kp, rf, rx, tau, w, out, stream)
+                              : launch_rows<IQ, LAYOUT, 1, H, 16>(kp, rf, rx, tau, w, out, stream);
 }
 
 template <bool IQ, int LAYOUT>
@@ -783,12 +794,12 @@ hipError_t launch_rows_h(const das_plan_t &plan, const DasKParams &kp, const flo
 }  // namespace
 
 bool das_rows_supported(const das_plan_t &plan) {
-    // frame tiles of 32 fp32 or 16 complex frames (B a multiple of that),
-    // native or binary16 samples, records of at most 65535 samples, and at
-    // most 8 WR_LIVE_BLOCKS receivers (the aperture mask)
+    // frame tiles of 32 or 16 fp32 or 16 complex frames (B a multiple of
+    // 16), native or binary16 samples, records of at most 65535 samples, and
+    // at most 8 WR_LIVE_BLOCKS receivers (the aperture mask)
     if (plan.p.K > 65535 || plan.p.M > 8 * WR_LIVE_BLOCKS)
         return false;
-    return (plan.p.dtype == DAS_F32 && plan.p.B % 32 == 0) || (plan.p.dtype == DAS_C64 && plan.p.B % 16 == 0);
+    return (plan.p.dtype == DAS_F32 || plan.p.dtype == DAS_C64) && plan.p.B % 16 == 0;
 }
 
 hipError_t das_launch_bi_rows(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
