@@ -461,6 +461,9 @@ def main():
             "traffic": traffic,
             "kernel": kernel_name,
             "kernel_ms_per_step": kern_avg,
+            "kernel_basis": ("HIP events around each das_beamform call on the bench stream: for whole-row "
+                             "plans the tile-order pass (rows_cost_kernel, rows_order_kernel) and the beamform "
+                             "kernel"),
             "kernel_ms_per_launch": launch_avg,
             "launches_per_step": len(chunks),
             "kernel_gacc_s": accs / (kern_avg * 1e-3) / 1e9,

@@ -23,8 +23,11 @@
  *   r_n    = origin + (ix, iy, iz) * spacing,  n = (iz*ny + iy)*nx + ix.
  *
  * Conventions for every entry point:
- *  - All data pointers are DEVICE pointers owned by the caller; the library
- *    allocates no device memory.  Base pointers must be 16-byte aligned.
+ *  - All data pointers are DEVICE pointers owned by the caller.  Base
+ *    pointers must be 16-byte aligned.  The library allocates device memory
+ *    only for the work areas das_beamform sorts whole-row tiles in (6 bytes
+ *    per 8 x 8 x 2 voxel tile): a pool per device, kept until the process
+ *    ends, one area per call in flight (see das_beamform).
  *  - Work is enqueued on `hip_stream` (a hipStream_t; NULL = the default
  *    stream) and the call returns without synchronizing.  A device fault
  *    surfaces at the caller's next synchronization.
@@ -231,6 +234,14 @@ das_status das_permute(const das_plan_t *plan, const void *rf_bqmk, void *rf_per
  *            float64 pairs (DAS_C128); rf holds samples of the same type
  *   accumulate  0: out is overwritten; 1: the chunk's sum is added to out
  *               (to sum a volume over several q chunks)
+ * Whole-row batch-inner plans (das_plan_info.whole_rows) launch their voxel
+ * tiles by decreasing count of live receiver blocks when the launch has more
+ * workgroups than the device has CUs: two small kernels count and sort the
+ * tiles in a work area first.  The area comes from the device's pool: one
+ * last used on this stream, or one whose last launches have completed, or
+ * a new one (hipMalloc, on the first calls).  Under stream capture, or if no
+ * area can be had, the tiles go in their plain order.  The order changes no
+ * result: each tile's sums are computed alone.
  * Errors: DAS_ERR_INVALID_ARGUMENT (null pointer, bad q range, accumulate not
  * 0/1); DAS_ERR_UNSUPPORTED (batch-inner KQMB chunk larger than 4 GiB: use
  * a smaller q_count or the QMKB layout); DAS_ERR_ALIGNMENT;

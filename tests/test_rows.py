@@ -174,3 +174,72 @@ def test_grid_with_negative_spacing(gpu, monkeypatch, rows, iq):
     assert_parity(y, ref, f"negative pitch rows={rows} iq={iq}")
     y0 = to_numpy(run_gpu(inp, "batch_inner", "qmkb"), iq)
     assert_parity(y, y0[:, rev], f"negative pitch against ordinary rows={rows} iq={iq}")
+
+
+ORDER_CASES = {
+    # 4 x 2 lateral tiles (a multiple of 8: die chunks), 3 depths
+    "die_chunks": dict(grid=(32, 16, 6), array=(24, 6)),
+    # 3 x 2 lateral tiles, ragged on every axis
+    "ragged": dict(grid=(19, 13, 5)),
+    # outer tiles with no live block, inner ones with all
+    "apertures": dict(array=(16, 4), grid=(40, 9, 4), voxel=0.5e-3, z0=2e-3, f_number=2.0),
+    # no receive apodization: every tile has every block
+    "no_apodization": dict(grid=(24, 17, 4), f_number=0.0),
+}
+
+
+@pytest.mark.parametrize("storage", ["native", "f16"])
+@pytest.mark.parametrize("B", [32, 48])
+@pytest.mark.parametrize("case", list(ORDER_CASES))
+@pytest.mark.parametrize("rows,iq", VARIANTS, ids=IDS)
+def test_tile_order(gpu, monkeypatch, rows, iq, case, B, storage):
+    """Tiles launched by decreasing live receiver count (DAS_ROWS_ORDER=2
+    sorts at any size) give the sums of the sequence-order launch
+    (DAS_ROWS_ORDER=0) bit for bit, and meet the oracle bar."""
+    _use(monkeypatch, rows)
+    inp = Inputs(_ragged(iq, B=B, K=400, **ORDER_CASES[case]), w_tx="uniform")
+    got = {}
+    for mode in ("0", "2"):
+        monkeypatch.setenv("DAS_ROWS_ORDER", mode)
+        out = run_gpu(inp, "batch_inner", "qmkb", storage=storage)
+        assert_all_written(out, f"order {mode} {case}")
+        got[mode] = out.cpu().numpy()
+    assert np.array_equal(got["0"], got["2"]), f"rows={rows} iq={iq} {case} B={B} {storage}"
+    import torch
+    assert_parity(to_numpy(torch.from_numpy(got["2"]), iq), oracle_ref(inp, storage=storage),
+                  f"ordered rows={rows} iq={iq} {case} B={B} {storage}")
+
+
+def test_tile_order_two_streams(gpu, monkeypatch):
+    """Calls in flight on two streams at once, with different receiver
+    positions (so different tile orders), each take a work area of their
+    own: every result equals the one computed alone, bit for bit."""
+    import torch
+    import volumetric_delay_sum_amd as das
+    monkeypatch.setenv("DAS_ROWS_ORDER", "2")
+    inp = Inputs(_ragged(False, B=32, K=500, array=(24, 6), grid=(40, 24, 8), f_number=1.5,
+                         sources=((0.0, 0.0), (1e-3, 0.0))), w_tx="uniform")
+    plan = das.plan_from_fields(inp.fields, "batch_inner", "qmkb")
+    Q = inp.cfg.Q
+    perm = torch.empty(plan.permuted_shape(Q), dtype=plan.permuted_dtype(), device="cuda")
+    plan.permute(inp.rf_d, perm, 0, Q)
+    rx_b = inp.rx_d.clone()
+    rx_b[:, 0] += 2.5e-3                                  # the array moved along x: other live counts
+    rxs = (inp.rx_d, rx_b)
+    ref = []
+    for rx in rxs:
+        o = torch.empty(plan.output_shape(), dtype=torch.float32, device="cuda")
+        plan.beamform(perm, rx, inp.tau_d, inp.w_d, o, 0, Q)
+        torch.cuda.synchronize()
+        ref.append(o.cpu().numpy())
+    assert not np.array_equal(ref[0], ref[1])
+    streams = (torch.cuda.Stream(), torch.cuda.Stream())
+    outs = [[torch.full(plan.output_shape(), float("nan"), device="cuda") for _ in range(6)] for _ in range(2)]
+    torch.cuda.synchronize()
+    for i in range(6):
+        for j in (0, 1):
+            plan.beamform(perm, rxs[j], inp.tau_d, inp.w_d, outs[j][i], 0, Q, stream=streams[j])
+    torch.cuda.synchronize()
+    for j in (0, 1):
+        for i in range(6):
+            assert np.array_equal(outs[j][i].cpu().numpy(), ref[j]), f"stream {j} call {i}"

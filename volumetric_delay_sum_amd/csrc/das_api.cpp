@@ -1,6 +1,7 @@
 // Host side of libdas: problem validation, plans, device checks and launches.
-// Every argument is checked before anything is enqueued; no device memory is
-// allocated here.
+// Every argument is checked before anything is enqueued.  The only device
+// memory allocated here is the pool of small work areas the whole-row kernel
+// sorts its tiles in.
 #include <algorithm>
 #include <hip/hip_runtime.h>
 
@@ -9,7 +10,9 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
+#include <vector>
 
 #include "das.h"
 #include "das_internal.h"
@@ -42,6 +45,110 @@ das_status check_device() {
         g_device_state[dev].store(st, std::memory_order_relaxed);
     }
     return st == 1 ? DAS_OK : DAS_ERR_NO_DEVICE;
+}
+
+// compute units of device dev (a device check has passed)
+std::atomic<int> g_device_cus[kMaxDevices];
+int device_cus(int dev) {
+    int n = g_device_cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        g_device_cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// ---- work areas of the whole-row kernel's tile order ----------------------------
+// Each device keeps a pool of small device buffers for the life of the
+// process.  A call takes an area that no launch in flight can still read:
+// one last used on the same stream (its launches run after those), or one
+// whose event, recorded after its last launches, has completed; else it
+// allocates one.  So calls in flight on any streams and threads never share
+// an area.  The per-thread default stream is one handle for many streams and
+// is matched by events only.
+struct WorkArea {
+    void *ptr;
+    size_t bytes;
+    hipEvent_t done;        // recorded after the last launches that used the area
+    hipStream_t stream;     // the stream of those launches
+    bool taken;             // a call between taking and giving back
+};
+struct WorkPool {
+    std::mutex mu;
+    std::vector<WorkArea> areas;
+};
+WorkPool g_pools[kMaxDevices];
+constexpr size_t kMinAreaBytes = 1 << 16;
+constexpr size_t kMaxAreas = 64;
+
+// index of an area of at least `bytes` on device dev for launches on stream
+// s, its pointer in *ptr; -1 when none can be had
+int take_area(int dev, size_t bytes, hipStream_t s, void **ptr) {
+    WorkPool &pool = g_pools[dev];
+    std::lock_guard<std::mutex> lock(pool.mu);
+    const size_t n = pool.areas.size();
+    int pick = -1;
+    if (s != hipStreamPerThread)
+        for (size_t i = 0; i < n && pick < 0; ++i) {
+            const WorkArea &a = pool.areas[i];
+            if (!a.taken && a.bytes >= bytes && a.stream == s)
+                pick = (int)i;
+        }
+    for (size_t i = 0; i < n && pick < 0; ++i) {
+        const WorkArea &a = pool.areas[i];
+        if (a.taken || a.bytes < bytes)
+            continue;
+        const hipError_t q = hipEventQuery(a.done);
+        if (q == hipSuccess)
+            pick = (int)i;
+        else if (q != hipErrorNotReady)
+            (void)hipGetLastError();
+    }
+    if (pick < 0) {
+        if (n >= kMaxAreas)
+            return -1;
+        WorkArea a{nullptr, std::max(bytes, kMinAreaBytes), nullptr, nullptr, false};
+        if (hipMalloc(&a.ptr, a.bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            return -1;
+        }
+        if (hipEventCreateWithFlags(&a.done, hipEventDisableTiming) != hipSuccess) {
+            (void)hipGetLastError();
+            (void)hipFree(a.ptr);
+            return -1;
+        }
+        pool.areas.push_back(a);
+        pick = (int)n;
+    }
+    pool.areas[pick].taken = true;
+    *ptr = pool.areas[pick].ptr;
+    return pick;
+}
+
+// give area i of device dev back after launches on stream s that use it
+void give_area(int dev, int i, hipStream_t s) {
+    WorkPool &pool = g_pools[dev];
+    std::lock_guard<std::mutex> lock(pool.mu);
+    WorkArea &a = pool.areas[i];
+    if (hipEventRecord(a.done, s) != hipSuccess) {
+        (void)hipGetLastError();
+        return;                  // not known to be free again: stays taken
+    }
+    a.stream = s;
+    a.taken = false;
+}
+
+// whether stream s is being captured into a graph (an error counts as yes)
+bool capturing(hipStream_t s) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;
+    }
+    return cs != hipStreamCaptureStatusNone;
 }
 
 // Frames per lane of the batch-inner kernel.  fp32: 4 adjacent frames (one
@@ -382,6 +489,11 @@ das_status das_plan(const das_problem *problem, das_plan_t **out) {
         if (p.dtype == DAS_C64 && pl->rows == 2)
             pl->rows = 1;                            // complex items hold twice the weights: 8 receivers a step
     }
+    // whole-row tiles by decreasing work where the launch outgrows the device
+    // (Main 6.9 -> 6.7 ms a step); DAS_ROWS_ORDER=0 keeps the sequence order,
+    // 2 sorts at any size (comparisons and tests)
+    const char *ov = std::getenv("DAS_ROWS_ORDER");
+    pl->order = ov ? (std::atoi(ov) == 0 ? 0 : (std::atoi(ov) == 2 ? 2 : 1)) : 1;
     *out = pl;
     return DAS_OK;
 }
@@ -473,9 +585,20 @@ das_status das_beamform(const das_plan_t *plan, const void *rf, const float *rx_
         const int64_t tables = (int64_t)plan->p.Q * plan->N * 4;
         const bool chunk_ok = plan->p.layout == DAS_LAYOUT_QMKB || chunk < ((int64_t)1 << 32);
         const bool staged = plan->staged && chunk_ok && tables < ((int64_t)1 << 32);
-        if (staged && plan->rows)
-            e = das_launch_bi_rows(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s);
-        else
+        if (staged && plan->rows) {
+            // tiles by decreasing work, sorted in a work area from the pool
+            // (none under graph capture: the plain order, the same sums)
+            int dev = 0, area = -1;
+            void *work = nullptr;
+            if (hipGetDevice(&dev) != hipSuccess)
+                return DAS_ERR_NO_DEVICE;
+            const int64_t wb = das_rows_work_bytes(*plan, device_cus(dev));
+            if (wb > 0 && !capturing(s))
+                area = take_area(dev, (size_t)wb, s, &work);
+            e = das_launch_bi_rows(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, area >= 0 ? work : nullptr, s);
+            if (area >= 0)
+                give_area(dev, area, s);
+        } else
             e = staged ? das_launch_batch_inner_staged(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s)
                        : das_launch_batch_inner(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s);
     }

@@ -112,12 +112,70 @@ struct RowsCopy {
     das::BufRsrc rs;
 };
 
+// Tile u of the launch sequence (u < tiles_x tiles_y tiles_z).  Workgroup
+// b runs on die b % 8 (of the MI355X's eight, each with its own L2).  The
+// sequence goes deepest first (with the receive aperture a tile's work grows
+// with depth).  Within a depth, die x takes a chunk of lat / 8 neighbouring
+// tiles (a row of tiles when the rows are 8 long), the chunk rotating with
+// depth so that every die gets as much edge and centre of the volume as the
+// others.
+__device__ __forceinline__ void rows_tile_of(const DasKParams &P, int u, int &tx, int &ty, int &tz) {
+    const int tiles_x = (P.nx + WR_TX - 1) / WR_TX, tiles_y = (P.ny + WR_TY - 1) / WR_TY;
+    const int tiles_z = (P.nz + WR_TZ - 1) / WR_TZ;
+    const int lat = tiles_x * tiles_y;
+    const int bd = u / lat, bw = u % lat;
+    int bj = bw;
+    if (lat % 8 == 0) {
+        const int per = lat / 8, x = bw % 8, k = bw / 8;
+        bj = ((x + bd) % 8) * per + (k + bd) % per;
+    }
+    tz = tiles_z - 1 - bd;
+    ty = bj / tiles_x;
+    tx = bj % tiles_x;
+}
+
+// Whether receiver m may have a non-zero receive weight for some voxel of
+// tile (tx, ty, tz).  A pair counts as zero only when it is clearly outside
+// the aperture or behind the array, by a margin far above the rounding of
+// this fp32 test and of the weight's own: cos^2 theta <= cos^2 theta_max /
+// (1 + 1e-3 (1 - cos^2 theta_max)), i.e. dz^2 (1 - c^2)(1 + 1e-3) <= c^2
+// rho^2 with dz > 0, or dz below zero by more than its rounding.  Lateral
+// distance and depth separate, so over the tile's voxels the pair nearest to
+// the inside of the cone is the voxel nearest to the receiver laterally on
+// the tile's plane farthest in front of it: if that one counts as zero, so
+// does every voxel of the tile.
+__device__ __forceinline__ bool rows_rx_on(const DasKParams &P, const float *rx, int m, int tx, int ty, int tz) {
+    const float ctm = 1.0f - 1.0f / P.apod_inv_vmax;                     // cos theta_max
+    const float ca = (1.0f - ctm * ctm) * 1.001f, cb = ctm * ctm;
+    const int x0 = tx * WR_TX, x1 = min(x0 + WR_TX, P.nx) - 1;
+    const int y0 = ty * WR_TY, y1 = min(y0 + WR_TY, P.ny) - 1;
+    const int z0 = tz * WR_TZ, z1 = min(z0 + WR_TZ, P.nz) - 1;
+    // nearest index in [lo, hi] of a grid axis to coordinate p
+    auto nearest = [](double p, double o, double sp, int lo, int hi) -> int {
+        if (sp == 0.0)
+            return lo;
+        const double t = __builtin_rint((p - o) / sp);
+        return t <= (double)lo ? lo : (t >= (double)hi ? hi : (int)t);
+    };
+    const float px = rx[3 * m], py = rx[3 * m + 1], pz = rx[3 * m + 2];
+    const int ixn = nearest(px, P.ox, P.sx, x0, x1), iyn = nearest(py, P.oy, P.sy, y0, y1);
+    const float dx = (float)(P.ox + (double)ixn * P.sx) - px;
+    const float dy = (float)(P.oy + (double)iyn * P.sy) - py;
+    const float za = (float)(P.oz + (double)z0 * P.sz), zb = (float)(P.oz + (double)z1 * P.sz);
+    const float vz = fmaxf(za, zb), dz = vz - pz;
+    const float rho2 = __builtin_fmaf(dx, dx, dy * dy), dz2 = dz * dz;
+    const float ez = 1e-5f * (fabsf(vz) + fabsf(pz)) + 1e-30f;
+    const bool zero = (dz < -ez) || (dz > ez && dz2 * ca <= rho2 * cb);
+    return !zero;
+}
+
 template <bool IQ, int LAYOUT, int NIT, bool H, int FRT>
 __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, const float *__restrict__ rfp,
                                                                  const float *__restrict__ rx,
                                                                  const float *__restrict__ tau_tx,
                                                                  const float *__restrict__ w_tx,
-                                                                 float *__restrict__ out) {
+                                                                 float *__restrict__ out,
+                                                                 const uint32_t *__restrict__ order) {
     using G = RowsGeo<NIT>;
     constexpr int NRX = G::NRX;
     constexpr int C = IQ ? 2 : 1;
@@ -141,22 +199,12 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
 
     const int tiles_x = (P.nx + WR_TX - 1) / WR_TX, tiles_y = (P.ny + WR_TY - 1) / WR_TY;
     const int tiles_z = (P.nz + WR_TZ - 1) / WR_TZ;
-    const int lat = tiles_x * tiles_y;
-    // Workgroup b runs on die b % 8 (of the MI355X's eight, each with its
-    // own L2).  Tiles go deepest first (with the receive aperture a tile's
-    // work grows with depth).  Within a depth, die x takes a chunk of
-    // lat / 8 neighbouring tiles (a row of tiles when the rows are 8 long),
-    // the chunk rotating with depth so that every die gets as much edge and
-    // centre of the volume as the others, and so about the same work.
-    const int bd = (int)blockIdx.x / lat, bw = (int)blockIdx.x % lat;
-    int bj = bw;
-    if (lat % 8 == 0) {
-        const int per = lat / 8, x = bw % 8, k = bw / 8;
-        bj = ((x + bd) % 8) * per + (k + bd) % per;
-    }
-    const int tz = tiles_z - 1 - bd;
-    const int ty = bj / tiles_x;
-    const int tx = bj % tiles_x;
+    // the tile: sequence position blockIdx.x, or the one the list of tiles
+    // by decreasing work puts there
+    const int ntiles = tiles_x * tiles_y * tiles_z;
+    const int u = order ? min((int)order[blockIdx.x], ntiles - 1) : (int)blockIdx.x;
+    int tx, ty, tz;
+    rows_tile_of(P, u, tx, ty, tz);
     const int ix = tx * WR_TX + v, iy = ty * WR_TY + (wave & 7), iz = tz * WR_TZ + (wave >> 3);
     const bool vox_ok = ix < P.nx && iy < P.ny && iz < P.nz;
     const int ixc = min(ix, P.nx - 1), iyc = min(iy, P.ny - 1), izc = min(iz, P.nz - 1);
@@ -186,44 +234,12 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     // ---- receive aperture of the tile ------------------------------------------
     // A block of 8 receivers whose receive weight is zero for every voxel of
     // the tile adds nothing: the sweep skips it, and a step takes the next NIT
-    // live blocks.  A pair counts as zero only when it is clearly outside the
-    // aperture or behind the array, by a margin far above the rounding of
-    // this fp32 test and of the weight's own: cos^2 theta <= cos^2 theta_max
-    // / (1 + 1e-3 (1 - cos^2 theta_max)), i.e. dz^2 (1 - c^2)(1 + 1e-3) <=
-    // c^2 rho^2 with dz > 0, or dz below zero by more than its rounding.
-    // Lateral distance and depth separate, so over the tile's voxels the
-    // pair nearest to the inside of the cone is the voxel nearest to the
-    // receiver laterally on the tile's plane farthest in front of it: if that
-    // one counts as zero, so does every voxel of the tile.  Lane t tests
-    // receiver t (and t + 1024, ...) against it; the 8 lanes of a block vote.
+    // live blocks.  Lane t tests receiver t (and t + 1024, ...) by
+    // rows_rx_on; the 8 lanes of a block vote.
     if (P.apod) {
-        const float ctm = 1.0f - 1.0f / P.apod_inv_vmax;                 // cos theta_max
-        const float ca = (1.0f - ctm * ctm) * 1.001f, cb = ctm * ctm;
-        const int x0 = tx * WR_TX, x1 = min(x0 + WR_TX, P.nx) - 1;
-        const int y0 = ty * WR_TY, y1 = min(y0 + WR_TY, P.ny) - 1;
-        const int z0 = tz * WR_TZ, z1 = min(z0 + WR_TZ, P.nz) - 1;
-        // nearest index in [lo, hi] of a grid axis to coordinate p
-        auto nearest = [](double p, double o, double sp, int lo, int hi) -> int {
-            if (sp == 0.0)
-                return lo;
-            const double t = __builtin_rint((p - o) / sp);
-            return t <= (double)lo ? lo : (t >= (double)hi ? hi : (int)t);
-        };
         for (int mb = 0; mb < nblk * 8; mb += WR_THREADS) {
             const int m = mb + tid;
-            bool on = false;
-            if (m < P.M) {
-                const float px = rx[3 * m], py = rx[3 * m + 1], pz = rx[3 * m + 2];
-                const int ixn = nearest(px, P.ox, P.sx, x0, x1), iyn = nearest(py, P.oy, P.sy, y0, y1);
-                const float dx = (float)(P.ox + (double)ixn * P.sx) - px;
-                const float dy = (float)(P.oy + (double)iyn * P.sy) - py;
-                const float za = (float)(P.oz + (double)z0 * P.sz), zb = (float)(P.oz + (double)z1 * P.sz);
-                const float vz = fmaxf(za, zb), dz = vz - pz;
-                const float rho2 = __builtin_fmaf(dx, dx, dy * dy), dz2 = dz * dz;
-                const float ez = 1e-5f * (fabsf(vz) + fabsf(pz)) + 1e-30f;
-                const bool zero = (dz < -ez) || (dz > ez && dz2 * ca <= rho2 * cb);
-                on = !zero;
-            }
+            const bool on = m < P.M && rows_rx_on(P, rx, m, tx, ty, tz);
             const uint64_t vote = __ballot(on);
             const int b = (mb + 64 * wave) / 8 + lane;                   // lane < 8: block b of this wave
             if (lane < 8 && b < nblk && ((vote >> (8 * lane)) & 0xffu))
@@ -760,35 +776,140 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     }
 }
 
+// ---- tile order ---------------------------------------------------------------
+// A launch's workgroups go to the dies in turn and, on a die, to its shader
+// engines in turn and in order, one tile per CU: a CU that frees up waits
+// while the next tile is bound for an engine that is still busy.  A tile's
+// work is its live receiver blocks, which vary by a factor of 30 over one
+// depth (edge against centre).  Launched by decreasing live count, the
+// engines of a die stay in step and the last tiles to start are the cheapest.
+// rows_cost_kernel counts the live blocks of every tile (the workgroup's own
+// test, one wave per tile); rows_order_kernel sorts each die's tiles (those
+// of sequence positions u = x mod 8 for die x, so a die keeps its
+// neighbouring tiles and their L2 reuse) by that count, largest first and in
+// sequence order within a count, and puts die x's j-th tile at launch
+// position 8 j + x.  The list is a permutation of the sequence, so the sums
+// are those of the plain launch, bit for bit.
+
+constexpr int WR_DIES = 8;
+
+__global__ __launch_bounds__(256) void rows_cost_kernel(DasKParams P, const float *__restrict__ rx,
+                                                        uint16_t *__restrict__ cost, int ntiles) {
+    const int u = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (u >= ntiles)
+        return;
+    int tx, ty, tz;
+    rows_tile_of(P, u, tx, ty, tz);
+    const int nblk = (P.M + 7) / 8;
+    int nlive = nblk;
+    if (P.apod) {
+        nlive = 0;
+        for (int mb = 0; mb < P.M; mb += 64) {
+            const int m = mb + lane;
+            const uint64_t vote = __ballot(m < P.M && rows_rx_on(P, rx, m, tx, ty, tz));
+#pragma unroll
+            for (int g = 0; g < 8; ++g)
+                nlive += ((vote >> (8 * g)) & 0xffu) != 0;
+        }
+    }
+    if (lane == 0)
+        cost[u] = (uint16_t)nlive;
+}
+
+// One workgroup: a counting sort with one list per die.  cur holds per (die,
+// key) first the count, then the next free position in the die's list.  The
+// scatter runs in one wave, 64 tiles at a time in sequence order; a lane's
+// rank among the lanes with its (die, key) comes from ballots over the key's
+// 13 bits, and the lowest of them moves the position on after every lane has
+// read it (the write depends on the read).
+__global__ __launch_bounds__(1024) void rows_order_kernel(const uint16_t *__restrict__ cost, int ntiles, int nkeys,
+                                                          uint32_t *__restrict__ order) {
+    __shared__ int cur[WR_DIES * (WR_LIVE_BLOCKS + 1)];
+    const int tid = threadIdx.x;
+    for (int k = tid; k < WR_DIES * nkeys; k += 1024)
+        cur[k] = 0;
+    __syncthreads();
+    for (int u = tid; u < ntiles; u += 1024)
+        atomicAdd(&cur[(u % WR_DIES) * nkeys + min((int)cost[u], nkeys - 1)], 1);
+    __syncthreads();
+    if (tid < WR_DIES) {                         // die tid's list, largest key first
+        int pos = 0;
+        for (int k = nkeys - 1; k >= 0; --k) {
+            const int c = cur[tid * nkeys + k];
+            cur[tid * nkeys + k] = pos;
+            pos += c;
+        }
+    }
+    __syncthreads();
+    if (tid >= 64)
+        return;
+    for (int base = 0; base < ntiles; base += 64) {
+        const int u = base + tid;
+        const bool valid = u < ntiles;
+        const int key = valid ? (u % WR_DIES) * nkeys + min((int)cost[u], nkeys - 1) : 0;
+        uint64_t same = __ballot(valid);
+#pragma unroll
+        for (int bit = 0; bit < 13; ++bit) {
+            const bool set = (key >> bit) & 1;
+            const uint64_t b = __ballot(set);
+            same &= set ? b : ~b;
+        }
+        const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(same >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)same, 0));
+        const int cnt = __builtin_popcountll(same);
+        const int pos = valid ? cur[key] : 0;
+        if (valid && rank == 0)
+            cur[key] = pos + cnt;
+        if (valid)
+            order[(pos + rank) * WR_DIES + u % WR_DIES] = (uint32_t)u;
+    }
+}
+
+int rows_tiles(const DasKParams &kp) {
+    return ((kp.nx + WR_TX - 1) / WR_TX) * ((kp.ny + WR_TY - 1) / WR_TY) * ((kp.nz + WR_TZ - 1) / WR_TZ);
+}
+
+// byte offset of the order list in the work area (after the counts)
+int64_t rows_order_offset(int64_t tiles) { return (2 * tiles + 255) / 256 * 256; }
+
 template <bool IQ, int LAYOUT, int NIT, bool H, int FRT>
 hipError_t launch_rows(const DasKParams &kp, const float *rf, const float *rx, const float *tau, const float *w,
-                       float *out, hipStream_t stream) {
-    const int tiles = ((kp.nx + WR_TX - 1) / WR_TX) * ((kp.ny + WR_TY - 1) / WR_TY) * ((kp.nz + WR_TZ - 1) / WR_TZ);
+                       float *out, void *work, hipStream_t stream) {
+    const int tiles = rows_tiles(kp);
+    const uint32_t *order = nullptr;
+    if (work) {
+        uint16_t *cost = static_cast<uint16_t *>(work);
+        uint32_t *ord = reinterpret_cast<uint32_t *>(static_cast<char *>(work) + rows_order_offset(tiles));
+        hipLaunchKernelGGL(rows_cost_kernel, dim3((tiles + 3) / 4), dim3(256), 0, stream, kp, rx, cost, tiles);
+        hipLaunchKernelGGL(rows_order_kernel, dim3(1), dim3(1024), 0, stream, (const uint16_t *)cost, tiles,
+                           (kp.M + 7) / 8 + 1, ord);
+        order = ord;
+    }
     hipLaunchKernelGGL((das_bi_rows_kernel<IQ, LAYOUT, NIT, H, FRT>), dim3(tiles, kp.B / FRT), dim3(WR_THREADS), 0, stream, kp,
-                       rf, rx, tau, w, out);
+                       rf, rx, tau, w, out, order);
     return hipGetLastError();
 }
 
 template <bool IQ, int LAYOUT, bool H>
 hipError_t launch_rows_nit(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
-                           const float *tau, const float *w, float *out, hipStream_t stream) {
+                           const float *tau, const float *w, float *out, void *work, hipStream_t stream) {
     // complex plans take 8 receivers a step and 16-frame tiles; fp32 ones
     // 32-frame tiles where B allows, else 16
     if constexpr (IQ)
-        return launch_rows<IQ, LAYOUT, 1, H, 16>(kp, rf, rx, tau, w, out, stream);
+        return launch_rows<IQ, LAYOUT, 1, H, 16>(kp, rf, rx, tau, w, out, work, stream);
     else if (plan.p.B % 32 == 0)
-        return plan.rows == 2 ? launch_rows<IQ, LAYOUT, 2, H, 32>(kp, rf, rx, tau, w, out, stream)
-                              : launch_rows<IQ, LAYOUT, 1, H, 32>(kp, rf, rx, tau, w, out, stream);
+        return plan.rows == 2 ? launch_rows<IQ, LAYOUT, 2, H, 32>(kp, rf, rx, tau, w, out, work, stream)
+                              : launch_rows<IQ, LAYOUT, 1, H, 32>(kp, rf, rx, tau, w, out, work, stream);
     else
-        return plan.rows == 2 ? launch_rows<IQ, LAYOUT, 2, H, 16>(kp, rf, rx, tau, w, out, stream)
-                              : launch_rows<IQ, LAYOUT, 1, H, 16>(kp, rf, rx, tau, w, out, stream);
+        return plan.rows == 2 ? launch_rows<IQ, LAYOUT, 2, H, 16>(kp, rf, rx, tau, w, out, work, stream)
+                              : launch_rows<IQ, LAYOUT, 1, H, 16>(kp, rf, rx, tau, w, out, work, stream);
 }
 
 template <bool IQ, int LAYOUT>
 hipError_t launch_rows_h(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
-                         const float *tau, const float *w, float *out, hipStream_t stream) {
-    return plan.h16 ? launch_rows_nit<IQ, LAYOUT, true>(plan, kp, rf, rx, tau, w, out, stream)
-                    : launch_rows_nit<IQ, LAYOUT, false>(plan, kp, rf, rx, tau, w, out, stream);
+                         const float *tau, const float *w, float *out, void *work, hipStream_t stream) {
+    return plan.h16 ? launch_rows_nit<IQ, LAYOUT, true>(plan, kp, rf, rx, tau, w, out, work, stream)
+                    : launch_rows_nit<IQ, LAYOUT, false>(plan, kp, rf, rx, tau, w, out, work, stream);
 }
 
 }  // namespace
@@ -802,12 +923,29 @@ bool das_rows_supported(const das_plan_t &plan) {
     return (plan.p.dtype == DAS_F32 || plan.p.dtype == DAS_C64) && plan.p.B % 16 == 0;
 }
 
+int64_t das_rows_work_bytes(const das_plan_t &plan, int cus) {
+    // plan.order: 0 plain sequence, 1 sorted when the launch has more
+    // workgroups than the device has CUs (else every tile starts at once),
+    // 2 sorted always
+    if (!plan.rows || plan.order == 0)
+        return 0;
+    DasKParams kp{};
+    kp.nx = plan.p.nx;
+    kp.ny = plan.p.ny;
+    kp.nz = plan.p.nz;
+    const int64_t tiles = rows_tiles(kp);
+    const int64_t frt = (plan.p.dtype == DAS_C64 || plan.p.B % 32 != 0) ? 16 : 32;
+    if (plan.order == 1 && tiles * (plan.p.B / frt) <= cus)
+        return 0;
+    return rows_order_offset(tiles) + 4 * tiles;
+}
+
 hipError_t das_launch_bi_rows(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
-                              const float *tau_tx, const float *w_tx, float *out, hipStream_t stream) {
+                              const float *tau_tx, const float *w_tx, float *out, void *work, hipStream_t stream) {
     const bool iq = plan.p.dtype == DAS_C64;
     if (plan.p.layout == DAS_LAYOUT_KQMB)
-        return iq ? launch_rows_h<true, DAS_LAYOUT_KQMB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream)
-                  : launch_rows_h<false, DAS_LAYOUT_KQMB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream);
-    return iq ? launch_rows_h<true, DAS_LAYOUT_QMKB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream)
-              : launch_rows_h<false, DAS_LAYOUT_QMKB>(plan, kp, rf, rx, tau_tx, w_tx, out, stream);
+        return iq ? launch_rows_h<true, DAS_LAYOUT_KQMB>(plan, kp, rf, rx, tau_tx, w_tx, out, work, stream)
+                  : launch_rows_h<false, DAS_LAYOUT_KQMB>(plan, kp, rf, rx, tau_tx, w_tx, out, work, stream);
+    return iq ? launch_rows_h<true, DAS_LAYOUT_QMKB>(plan, kp, rf, rx, tau_tx, w_tx, out, work, stream)
+              : launch_rows_h<false, DAS_LAYOUT_QMKB>(plan, kp, rf, rx, tau_tx, w_tx, out, work, stream);
 }

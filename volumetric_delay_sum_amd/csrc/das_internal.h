@@ -51,6 +51,9 @@ struct das_plan {
     int32_t store_bytes;      // bytes per sample in the permuted buffer (elem_bytes, or half that with h16)
     int32_t rows;             // staged kernel: 0 = DPP-row lanes; 1 or 2 = whole-row lanes with 8 or 16
                               // receivers a step
+    int32_t order;            // whole-row lanes: tiles launched 0 = in sequence order; 1 = by decreasing
+                              // work when the launch has more workgroups than the device has CUs; 2 = by
+                              // decreasing work always
 };
 
 // Launchers (defined next to their kernels).  They assume validated input.
@@ -66,8 +69,13 @@ bool das_staged_supported(const das_plan_t &plan);
 // Whole-row lanes (das_bi_rows.hip): native fp32 with B a multiple of 32 or
 // complex64 with B a multiple of 16, K below 2^16.
 bool das_rows_supported(const das_plan_t &plan);
+// Bytes of the work area a whole-row launch sorts its tiles in (0: the plan
+// launches them in sequence order), on a device with `cus` compute units.
+int64_t das_rows_work_bytes(const das_plan_t &plan, int cus);
+// work: a device work area of das_rows_work_bytes bytes that no other launch
+// uses until this one has finished, or null for the sequence order.
 hipError_t das_launch_bi_rows(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
-                              const float *tau_tx, const float *w_tx, float *out, hipStream_t stream);
+                              const float *tau_tx, const float *w_tx, float *out, void *work, hipStream_t stream);
 hipError_t das_launch_batch_inner_staged(const das_plan_t &plan, const DasKParams &kp, const float *rf,
                                          const float *rx, const float *tau_tx, const float *w_tx, float *out,
                                          hipStream_t stream);
