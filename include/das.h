@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define DAS_ABI_VERSION 7
+#define DAS_ABI_VERSION 8
 
 typedef enum das_status {
     DAS_OK = 0,
@@ -57,7 +57,9 @@ typedef enum das_status {
     DAS_ERR_UNSUPPORTED = 2,      /* valid request this build cannot serve          */
     DAS_ERR_ALIGNMENT = 3,        /* a base pointer is not 16-byte aligned          */
     DAS_ERR_NO_DEVICE = 4,        /* no HIP device, or the device is not gfx950     */
-    DAS_ERR_LAUNCH = 5            /* the HIP runtime refused a launch               */
+    DAS_ERR_LAUNCH = 5,           /* the HIP runtime refused a launch               */
+    DAS_ERR_WORK_AREA = 6         /* das_beamform_noalloc: more voxel tiles than its
+                                     fixed work area holds                          */
 } das_status;
 
 /* Sample type.  DAS_F32: real float32 RF.  DAS_C64: complex64 IQ data, stored
@@ -250,6 +252,23 @@ das_status das_beamform(const das_plan_t *plan, const void *rf, const float *rx_
                         const float *tau_tx, const float *w_tx, void *out,
                         int32_t q_begin, int32_t q_count, int32_t accumulate,
                         void *hip_stream);
+
+/* das_beamform for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, hosts that forbid hipMalloc.  Same
+ * arguments, result and errors as das_beamform, and it never allocates: a
+ * whole-row plan sorts its tiles in a fixed device array of the library
+ * (384 KiB per device, one copy per device, looked up once per device),
+ * also under stream capture.  Every call on a device shares that device's
+ * array, so calls that overlap in time on one device race (their tile lists
+ * mix and sums go missing or twice): order them on one stream, or use
+ * das_beamform.  Nothing in the array needs clearing between calls.
+ * Extra error: DAS_ERR_WORK_AREA when a whole-row plan that sorts its tiles
+ * has more than 65536 voxel tiles of 8 x 8 x 2 (checked before any HIP call;
+ * such volumes take das_beamform). */
+das_status das_beamform_noalloc(const das_plan_t *plan, const void *rf, const float *rx_pos,
+                                const float *tau_tx, const float *w_tx, void *out,
+                                int32_t q_begin, int32_t q_count, int32_t accumulate,
+                                void *hip_stream);
 
 /* Streamed batch-inner pass over all Q transmit events (a volume too large
  * to permute at once).  Events are taken in chunks of q_chunk; chunk c is

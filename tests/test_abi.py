@@ -13,7 +13,7 @@ import volumetric_delay_sum_amd as das
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "das.h")
 
-OK, INVALID, UNSUPPORTED, ALIGNMENT, NO_DEVICE, LAUNCH = 0, 1, 2, 3, 4, 5
+OK, INVALID, UNSUPPORTED, ALIGNMENT, NO_DEVICE, LAUNCH, WORK_AREA = 0, 1, 2, 3, 4, 5, 6
 
 
 @pytest.fixture(scope="module")
@@ -240,7 +240,7 @@ def test_frames_per_lane_choice_iq_dpp_rows(B, fl, monkeypatch):
 
 
 def test_error_strings(lib):
-    for code in range(0, 7):
+    for code in range(0, 8):
         s = lib.das_error_string(code)
         assert isinstance(s, bytes) and len(s) > 0
     assert lib.das_error_string(-3) == b"unknown status"
@@ -281,6 +281,22 @@ def test_beamform_argument_errors(lib):
         args = [g] * 5
         args[i] = bad
         assert lib.das_beamform(h, *args, 0, 1, 0, None) == ALIGNMENT
+
+
+def test_noalloc_work_area_limit(lib):
+    """das_beamform_noalloc rejects a whole-row plan that sorts more voxel
+    tiles than its fixed work area holds (65536 of 8 x 8 x 2) with its own
+    status, before any HIP call (so fake pointers are safe here), and checks
+    its arguments as das_beamform does."""
+    g, bad = _fake(0x10000), _fake(0x10004)
+    big = _problem(B=32, Q=1, M=64, K=64, nx=1024, ny=1024, nz=18, layout="qmkb")   # 128 x 128 x 9 tiles
+    pl = das.Plan(**big)
+    assert pl.info["whole_rows"] == 1
+    assert lib.das_beamform_noalloc(pl._h, g, g, g, g, g, 0, 1, 0, None) == WORK_AREA
+    assert b"65536" in lib.das_error_string(WORK_AREA)
+    assert lib.das_beamform_noalloc(None, g, g, g, g, g, 0, 1, 0, None) == INVALID
+    assert lib.das_beamform_noalloc(pl._h, g, g, g, g, g, 0, 2, 0, None) == INVALID       # past Q
+    assert lib.das_beamform_noalloc(pl._h, g, bad, g, g, g, 0, 1, 0, None) == ALIGNMENT
 
 
 def test_streamed_argument_errors(lib):

@@ -109,6 +109,8 @@ def load_library():
     lib.das_permute.restype = ctypes.c_int
     lib.das_beamform.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
     lib.das_beamform.restype = ctypes.c_int
+    lib.das_beamform_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
+    lib.das_beamform_noalloc.restype = ctypes.c_int
     lib.das_beamform_streamed.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp]
     lib.das_beamform_streamed.restype = ctypes.c_int
     lib.das_tx_tables.argtypes = [vp, ctypes.POINTER(_TxEvent), i32, i32, vp, vp, vp]
@@ -271,8 +273,12 @@ class Plan:
         return out
 
     def beamform(self, rf, rx_pos, tau_tx, w_tx, out, q_begin: int = 0, q_count: Optional[int] = None,
-                 accumulate: bool = False, stream=None):
-        """Sum events [q_begin, q_begin+q_count) into out (B x N, or B x N x 2 for IQ)."""
+                 accumulate: bool = False, stream=None, noalloc: bool = False):
+        """Sum events [q_begin, q_begin+q_count) into out (B x N, or B x N x 2 for IQ).
+
+        noalloc: call das_beamform_noalloc (no device allocation; the library's
+        fixed work area, shared by every such call on the device).
+        """
         p = self.problem
         q_begin, q_count = self._q_range(q_begin, q_count)
         c = 2 if self.iq else 1
@@ -282,10 +288,10 @@ class Plan:
         tau_tx = self._tensor(tau_tx, p.Q * self.N, "tau_tx")
         w_tx = self._tensor(w_tx, p.Q * self.N, "w_tx")
         out = self._tensor(out, p.B * self.N * c, "out", samples=True)
-        _check(self._lib.das_beamform(self._h, rf.data_ptr(), rx_pos.data_ptr(), tau_tx.data_ptr(),
-                                      w_tx.data_ptr(), out.data_ptr(), q_begin, q_count,
-                                      1 if accumulate else 0, _stream_handle(stream, rf.device)),
-               "das_beamform")
+        fn, name = ((self._lib.das_beamform_noalloc, "das_beamform_noalloc") if noalloc
+                    else (self._lib.das_beamform, "das_beamform"))
+        _check(fn(self._h, rf.data_ptr(), rx_pos.data_ptr(), tau_tx.data_ptr(), w_tx.data_ptr(), out.data_ptr(),
+                  q_begin, q_count, 1 if accumulate else 0, _stream_handle(stream, rf.device)), name)
         return out
 
     def beamform_streamed(self, rf, rx_pos, tau_tx, w_tx, out, perm_a, perm_b, q_chunk: int,

@@ -19,7 +19,7 @@
 
 namespace {
 
-constexpr int kMaxDevices = 64;
+constexpr int kMaxDevices = DAS_MAX_DEVICES;
 // 0 unknown, 1 usable gfx950, 2 not usable
 std::atomic<int> g_device_state[kMaxDevices];
 
@@ -363,6 +363,9 @@ const char *das_error_string(int status) {
         return "no usable HIP device (a gfx950 GPU is required)";
     case DAS_ERR_LAUNCH:
         return "kernel launch failed";
+    case DAS_ERR_WORK_AREA:
+        return "das_beamform_noalloc: the volume has more 8 x 8 x 2 voxel tiles than its fixed work area "
+               "holds (65536); use das_beamform";
     default:
         return "unknown status";
     }
@@ -554,9 +557,15 @@ das_status das_permute(const das_plan_t *plan, const void *rf_bqmk, void *rf_per
     return e == hipSuccess ? DAS_OK : DAS_ERR_LAUNCH;
 }
 
-das_status das_beamform(const das_plan_t *plan, const void *rf, const float *rx_pos, const float *tau_tx,
-                        const float *w_tx, void *out, int32_t q_begin, int32_t q_count, int32_t accumulate,
-                        void *hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// das_beamform, and with noalloc das_beamform_noalloc: the whole-row tile
+// order in the fixed device array instead of a pooled work area
+das_status beamform_impl(const das_plan_t *plan, const void *rf, const float *rx_pos, const float *tau_tx,
+                         const float *w_tx, void *out, int32_t q_begin, int32_t q_count, int32_t accumulate,
+                         void *hip_stream, bool noalloc) {
     if (!valid_plan(plan) || !rf || !rx_pos || !tau_tx || !w_tx || !out)
         return DAS_ERR_INVALID_ARGUMENT;
     if (q_begin < 0 || q_count < 1 || (int64_t)q_begin + q_count > plan->p.Q)
@@ -567,6 +576,9 @@ das_status das_beamform(const das_plan_t *plan, const void *rf, const float *rx_
         return DAS_ERR_ALIGNMENT;
     if (q_count > max_q_chunk(plan))
         return DAS_ERR_UNSUPPORTED;
+    if (noalloc && plan->alg == DAS_ALG_BATCH_INNER && plan->rows && plan->order != 0 &&
+        das_rows_tiles(*plan) > DAS_NOALLOC_MAX_TILES)
+        return DAS_ERR_WORK_AREA;
     das_status st = check_device();
     if (st != DAS_OK)
         return st;
@@ -593,11 +605,19 @@ das_status das_beamform(const das_plan_t *plan, const void *rf, const float *rx_
             if (hipGetDevice(&dev) != hipSuccess)
                 return DAS_ERR_NO_DEVICE;
             const int64_t wb = das_rows_work_bytes(*plan, device_cus(dev));
-            if (wb > 0 && !capturing(s))
-                area = take_area(dev, (size_t)wb, s, &work);
-            e = das_launch_bi_rows(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, area >= 0 ? work : nullptr, s);
-            if (area >= 0)
-                give_area(dev, area, s);
+            if (noalloc) {
+                // the fixed array (its size was checked above); the plain
+                // order if its address cannot be had
+                if (wb > 0)
+                    work = das_rows_static_work(dev);
+                e = das_launch_bi_rows(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, work, s);
+            } else {
+                if (wb > 0 && !capturing(s))
+                    area = take_area(dev, (size_t)wb, s, &work);
+                e = das_launch_bi_rows(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, area >= 0 ? work : nullptr, s);
+                if (area >= 0)
+                    give_area(dev, area, s);
+            }
         } else
             e = staged ? das_launch_batch_inner_staged(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s)
                        : das_launch_batch_inner(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s);
@@ -608,6 +628,22 @@ das_status das_beamform(const das_plan_t *plan, const void *rf, const float *rx_
     else
         e = das_launch_baseline(*plan, kp, rff, rx_pos, tau_tx, w_tx, o, s);
     return e == hipSuccess ? DAS_OK : DAS_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+das_status das_beamform(const das_plan_t *plan, const void *rf, const float *rx_pos, const float *tau_tx,
+                        const float *w_tx, void *out, int32_t q_begin, int32_t q_count, int32_t accumulate,
+                        void *hip_stream) {
+    return beamform_impl(plan, rf, rx_pos, tau_tx, w_tx, out, q_begin, q_count, accumulate, hip_stream, false);
+}
+
+das_status das_beamform_noalloc(const das_plan_t *plan, const void *rf, const float *rx_pos, const float *tau_tx,
+                                const float *w_tx, void *out, int32_t q_begin, int32_t q_count, int32_t accumulate,
+                                void *hip_stream) {
+    return beamform_impl(plan, rf, rx_pos, tau_tx, w_tx, out, q_begin, q_count, accumulate, hip_stream, true);
 }
 
 das_status das_beamform_streamed(const das_plan_t *plan, const void *rf_bqmk, const float *rx_pos,

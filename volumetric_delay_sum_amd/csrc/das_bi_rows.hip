@@ -46,6 +46,9 @@
 // rows straight from the permuted buffer.
 #include "das_device.h"
 
+#include <atomic>
+#include <mutex>
+
 namespace {
 
 constexpr int WR_THREADS = 1024;
@@ -870,7 +873,9 @@ int rows_tiles(const DasKParams &kp) {
 }
 
 // byte offset of the order list in the work area (after the counts)
-int64_t rows_order_offset(int64_t tiles) { return (2 * tiles + 255) / 256 * 256; }
+constexpr int64_t rows_order_offset(int64_t tiles) { return (2 * tiles + 255) / 256 * 256; }
+static_assert(rows_order_offset(DAS_NOALLOC_MAX_TILES) + 4 * DAS_NOALLOC_MAX_TILES <= DAS_NOALLOC_WORK_BYTES,
+              "fixed work area");
 
 template <bool IQ, int LAYOUT, int NIT, bool H, int FRT>
 hipError_t launch_rows(const DasKParams &kp, const float *rf, const float *rx, const float *tau, const float *w,
@@ -913,6 +918,42 @@ hipError_t launch_rows_h(const das_plan_t &plan, const DasKParams &kp, const flo
 }
 
 }  // namespace
+
+// ---- fixed work area of das_beamform_noalloc --------------------------------------
+// For callers that cannot allocate: the tile order of a whole-row launch in
+// a file-scope device array instead of a pooled area.  Every such call on a
+// device shares that device's copy (calls that overlap on one device race),
+// and nothing in it needs clearing: the counting kernel writes every count
+// and the sorting kernel every list entry before the beamform kernel reads.
+// Host code takes the array's address per device from hipGetSymbolAddress
+// (the array's name on the host is no device address).
+static __device__ __align__(256) unsigned char scratch[DAS_NOALLOC_WORK_BYTES];
+
+int64_t das_rows_tiles(const das_plan_t &plan) {
+    return ((int64_t)(plan.p.nx + WR_TX - 1) / WR_TX) * ((plan.p.ny + WR_TY - 1) / WR_TY) *
+           ((plan.p.nz + WR_TZ - 1) / WR_TZ);
+}
+
+void *das_rows_static_work(int dev) {
+    static std::atomic<void *> ptr[DAS_MAX_DEVICES];
+    static std::mutex mu;
+    if (dev < 0 || dev >= DAS_MAX_DEVICES)
+        return nullptr;
+    void *p = ptr[dev].load(std::memory_order_acquire);
+    if (p)
+        return p;
+    std::lock_guard<std::mutex> lock(mu);
+    p = ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        // the current device is dev: this gives its copy of the array
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        ptr[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
 
 bool das_rows_supported(const das_plan_t &plan) {
     // frame tiles of 32 or 16 fp32 or 16 complex frames (B a multiple of

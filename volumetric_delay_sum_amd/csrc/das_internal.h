@@ -76,6 +76,16 @@ int64_t das_rows_work_bytes(const das_plan_t &plan, int cus);
 // uses until this one has finished, or null for the sequence order.
 hipError_t das_launch_bi_rows(const das_plan_t &plan, const DasKParams &kp, const float *rf, const float *rx,
                               const float *tau_tx, const float *w_tx, float *out, void *work, hipStream_t stream);
+// Voxel tiles (8 x 8 x 2) of a whole-row launch.
+int64_t das_rows_tiles(const das_plan_t &plan);
+// das_beamform_noalloc: a fixed device array holds the tile order of
+// launches of at most DAS_NOALLOC_MAX_TILES tiles (counts, then the list).
+constexpr int DAS_MAX_DEVICES = 64;
+constexpr int64_t DAS_NOALLOC_MAX_TILES = 65536;
+constexpr int64_t DAS_NOALLOC_WORK_BYTES = 6 * DAS_NOALLOC_MAX_TILES;
+// The array's address on device dev (the current device), looked up once
+// per device; null if the lookup fails.
+void *das_rows_static_work(int dev);
 hipError_t das_launch_batch_inner_staged(const das_plan_t &plan, const DasKParams &kp, const float *rf,
                                          const float *rx, const float *tau_tx, const float *w_tx, float *out,
                                          hipStream_t stream);
