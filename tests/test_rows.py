@@ -177,8 +177,11 @@ def test_grid_with_negative_spacing(gpu, monkeypatch, rows, iq):
 
 
 ORDER_CASES = {
-    # 4 x 2 lateral tiles (a multiple of 8: die chunks), 3 depths
+    # 4 x 2 lateral tiles (a multiple of 8: chunks of one tile shared out to
+    # the dies by work), 3 depths
     "die_chunks": dict(grid=(32, 16, 6), array=(24, 6)),
+    # 4 x 4 lateral tiles (chunks of two), 4 depths
+    "die_chunks_2": dict(grid=(32, 32, 8), array=(20, 8)),
     # 3 x 2 lateral tiles, ragged on every axis
     "ragged": dict(grid=(19, 13, 5)),
     # outer tiles with no live block, inner ones with all
