@@ -787,7 +787,7 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
 // depth (edge against centre).  Launched by decreasing live count, the
 // engines of a die stay in step and the last tiles to start are the cheapest.
 // rows_cost_kernel counts the live blocks of every tile (the workgroup's own
-// test, one wave per tile); rows_order_kernel sorts each die's tiles (those
+// test, one 256-thread workgroup per tile); rows_order_kernel sorts each die's tiles (those
 // of sequence positions u = x mod 8 for die x, so a die keeps its
 // neighbouring tiles and their L2 reuse) by that count, largest first and in
 // sequence order within a count, and puts die x's j-th tile at launch
@@ -797,74 +797,116 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
 constexpr int WR_DIES = 8;
 
 __global__ __launch_bounds__(256) void rows_cost_kernel(DasKParams P, const float *__restrict__ rx,
-                                                        uint16_t *__restrict__ cost, int ntiles) {
-    const int u = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (u >= ntiles)
-        return;
+                                                        uint16_t *__restrict__ cost) {
+    __shared__ int live;
+    const int u = (int)blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    if (tid == 0)
+        live = 0;
+    __syncthreads();
     int tx, ty, tz;
     rows_tile_of(P, u, tx, ty, tz);
     const int nblk = (P.M + 7) / 8;
-    int nlive = nblk;
     if (P.apod) {
-        nlive = 0;
-        for (int mb = 0; mb < P.M; mb += 64) {
-            const int m = mb + lane;
+        // thread t tests receivers t, t + 256, ...; a wave's 64 receivers are
+        // 8 whole blocks (bytes of its vote)
+        for (int mb = 0; mb < P.M; mb += 256) {
+            const int m = mb + tid;
             const uint64_t vote = __ballot(m < P.M && rows_rx_on(P, rx, m, tx, ty, tz));
+            if (lane == 0) {
+                int n = 0;
 #pragma unroll
-            for (int g = 0; g < 8; ++g)
-                nlive += ((vote >> (8 * g)) & 0xffu) != 0;
+                for (int g = 0; g < 8; ++g)
+                    n += ((vote >> (8 * g)) & 0xffu) != 0;
+                atomicAdd(&live, n);
+            }
         }
     }
-    if (lane == 0)
-        cost[u] = (uint16_t)nlive;
+    __syncthreads();
+    if (tid == 0)
+        cost[u] = (uint16_t)(P.apod ? live : nblk);
 }
 
 // One workgroup: a counting sort with one list per die.  cur holds per (die,
-// key) first the count, then the next free position in the die's list.  The
-// scatter runs in one wave, 64 tiles at a time in sequence order; a lane's
-// rank among the lanes with its (die, key) comes from ballots over the key's
-// 13 bits, and the lowest of them moves the position on after every lane has
-// read it (the write depends on the read).
+// count) first the number of tiles, then the next free position in the
+// die's list.  Wave x scatters die x's tiles, 64 at a time in sequence
+// order, from the counts copied to LDS first (up to WR_ORDER_LDS_TILES
+// tiles); a lane's rank among the lanes with its count comes from ballots
+// over the count's 10 bits, and the lowest of them moves the position on
+// after every lane has read it (the write depends on the read).
+constexpr int WR_ORDER_LDS_TILES = 32768;         // tiles whose counts the sort keeps in LDS
+
 __global__ __launch_bounds__(1024) void rows_order_kernel(const uint16_t *__restrict__ cost, int ntiles, int nkeys,
                                                           uint32_t *__restrict__ order) {
     __shared__ int cur[WR_DIES * (WR_LIVE_BLOCKS + 1)];
+    __shared__ uint16_t key_of[WR_ORDER_LDS_TILES];  // the counts again, for the scatter
     const int tid = threadIdx.x;
+    const bool staged = ntiles <= WR_ORDER_LDS_TILES;
     for (int k = tid; k < WR_DIES * nkeys; k += 1024)
         cur[k] = 0;
     __syncthreads();
-    for (int u = tid; u < ntiles; u += 1024)
-        atomicAdd(&cur[(u % WR_DIES) * nkeys + min((int)cost[u], nkeys - 1)], 1);
+    for (int u = tid; u < ntiles; u += 1024) {
+        const int c = min((int)cost[u], nkeys - 1);
+        if (staged)
+            key_of[u] = (uint16_t)c;
+        atomicAdd(&cur[(u % WR_DIES) * nkeys + c], 1);
+    }
     __syncthreads();
-    if (tid < WR_DIES) {                         // die tid's list, largest key first
-        int pos = 0;
-        for (int k = nkeys - 1; k >= 0; --k) {
-            const int c = cur[tid * nkeys + k];
-            cur[tid * nkeys + k] = pos;
-            pos += c;
+    // first position of each (die, key) in the die's list, largest key
+    // first: wave x scans die x, lane l taking keys nkeys - 1 - (l per ..
+    // l per + per - 1) in turn
+    if (tid < 64 * WR_DIES) {
+        const int x = tid >> 6, l = tid & 63;
+        const int per = (nkeys + 63) / 64;
+        int sum = 0;
+        for (int i = 0; i < per; ++i) {
+            const int k = nkeys - 1 - (l * per + i);
+            if (k >= 0)
+                sum += cur[x * nkeys + k];
+        }
+        int incl = sum;                          // inclusive prefix over the lanes
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int o = __shfl_up(incl, d, 64);
+            if (l >= d)
+                incl += o;
+        }
+        int pos = incl - sum;
+        for (int i = 0; i < per; ++i) {
+            const int k = nkeys - 1 - (l * per + i);
+            if (k >= 0) {
+                const int c = cur[x * nkeys + k];
+                cur[x * nkeys + k] = pos;
+                pos += c;
+            }
         }
     }
     __syncthreads();
-    if (tid >= 64)
+    if (tid >= 64 * WR_DIES)
         return;
-    for (int base = 0; base < ntiles; base += 64) {
-        const int u = base + tid;
-        const bool valid = u < ntiles;
-        const int key = valid ? (u % WR_DIES) * nkeys + min((int)cost[u], nkeys - 1) : 0;
+    // wave x scatters die x's tiles (positions u = x + 8 j), 64 at a time
+    const int x = tid >> 6, l = tid & 63;
+    const int nd = (ntiles - x + WR_DIES - 1) / WR_DIES;
+    for (int base = 0; base < nd; base += 64) {
+        const int j = base + l;
+        const bool valid = j < nd;
+        const int u = x + WR_DIES * j;
+        const int c = valid ? (staged ? (int)key_of[u] : min((int)cost[u], nkeys - 1)) : 0;
+        // lanes holding the same count as this one
         uint64_t same = __ballot(valid);
 #pragma unroll
-        for (int bit = 0; bit < 13; ++bit) {
-            const bool set = (key >> bit) & 1;
-            const uint64_t b = __ballot(set);
-            same &= set ? b : ~b;
+        for (int bit = 0; bit < 10; ++bit) {
+            const bool set = (c >> bit) & 1;
+            const uint64_t v = __ballot(set);
+            same &= set ? v : ~v;
         }
         const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(same >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)same, 0));
         const int cnt = __builtin_popcountll(same);
-        const int pos = valid ? cur[key] : 0;
+        const int pos = valid ? cur[x * nkeys + c] : 0;
         if (valid && rank == 0)
-            cur[key] = pos + cnt;
+            cur[x * nkeys + c] = pos + cnt;
         if (valid)
-            order[(pos + rank) * WR_DIES + u % WR_DIES] = (uint32_t)u;
+            order[(pos + rank) * WR_DIES + x] = (uint32_t)u;
     }
 }
 
@@ -885,7 +927,7 @@ hipError_t launch_rows(const DasKParams &kp, const float *rf, const float *rx, c
     if (work) {
         uint16_t *cost = static_cast<uint16_t *>(work);
         uint32_t *ord = reinterpret_cast<uint32_t *>(static_cast<char *>(work) + rows_order_offset(tiles));
-        hipLaunchKernelGGL(rows_cost_kernel, dim3((tiles + 3) / 4), dim3(256), 0, stream, kp, rx, cost, tiles);
+        hipLaunchKernelGGL(rows_cost_kernel, dim3(tiles), dim3(256), 0, stream, kp, rx, cost);
         hipLaunchKernelGGL(rows_order_kernel, dim3(1), dim3(1024), 0, stream, (const uint16_t *)cost, tiles,
                            (kp.M + 7) / 8 + 1, ord);
         order = ord;
