@@ -198,6 +198,9 @@ def main():
                     help="samples in the permuted buffer: as given, or rounded to binary16 by the permute "
                          "(batch-inner; the arithmetic stays fp32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-f16-compare", action="store_true",
+                    help="skip the side line that times the same step with binary16 storage (native-storage "
+                         "batch-inner runs only)")
     ap.add_argument("--cpu-voxels", type=int, default=0, help="oracle sample size (0: one depth slab)")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="threads of the multi-core oracle rate (0: the host's cores available to this process, "
@@ -322,6 +325,49 @@ def main():
         wall = time.perf_counter() - t0
         streamed_desc = ", streamed: permute of chunk c+1 on a second stream overlaps beamform of chunk c"
         print(f"[bench] streamed: {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    # The same step with binary16 storage, for comparison (not the metric: its
+    # samples are rounded): permute into half the bytes, same kernels widening
+    # the halves.  Timed like the steps above, after them.
+    f16_compare = None
+    if bi and not h16 and not plan.repack and not args.no_f16_compare and not args.streamed:
+        plan16 = das.plan_from_fields(fields, algorithm=args.algorithm, layout=args.layout, storage="f16")
+        perm16 = torch.empty(plan16.permuted_shape(qc), dtype=plan16.permuted_dtype(), device=dev)
+        pe16 = perm16.numel() // qc
+        out16 = torch.empty_like(out)
+
+        def step16(e=None):
+            for i, (q0, n) in enumerate(chunks):
+                if e is not None:
+                    e[i][0].record(stream)
+                view16 = perm16.view(-1)[: pe16 * n]
+                plan16.permute(rf, view16, q0, n, stream=stream)
+                if e is not None:
+                    e[i][1].record(stream)
+                plan16.beamform(view16, rx_d, tau_d, w_d, out16, q0, n, accumulate=(i > 0), stream=stream)
+                if e is not None:
+                    e[i][2].record(stream)
+
+        for _ in range(args.warmup):
+            step16()
+        torch.cuda.synchronize()
+        ev16 = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in chunks] for _ in range(args.steps)]
+        t16 = time.perf_counter()
+        for i in range(args.steps):
+            step16(ev16[i])
+        torch.cuda.synchronize()
+        wall16 = time.perf_counter() - t16
+        k16 = float(np.mean([sum(e[1].elapsed_time(e[2]) for e in ev) for ev in ev16]))
+        p16 = float(np.mean([sum(e[0].elapsed_time(e[1]) for e in ev) for ev in ev16]))
+        ms16 = wall16 * 1e3 / args.steps
+        f16_compare = {"ms_per_step": ms16, "kernel_ms_per_step": k16, "permute_ms": p16,
+                       "value": das_synth.accumulations(cfg) / (ms16 * 1e-3) / 1e9,
+                       "kernel_gacc_s": das_synth.accumulations(cfg) / (k16 * 1e-3) / 1e9,
+                       "note": "the same step with binary16 samples in the permuted buffer (rounded by the "
+                               "permute, widened to fp32 in the kernel), timed after the steps above; a "
+                               "comparison, not the metric"}
+        del perm16, out16
+        print(f"[bench] binary16 storage: {args.steps} steps in {wall16:.3f} s", file=sys.stderr, flush=True)
 
     # the transmit-table generator on this workload's events (not part of a
     # step: the tables are inputs); HBM-write bound, 8 bytes per (event, voxel)
@@ -477,6 +523,7 @@ def main():
                                  "it executes this fraction of them, at this rate"},
         },
         "permute_ms": perm_avg if bi else None,
+        "binary16_storage": f16_compare,
         "tx_tables": tx_tables,
         "cpu_baseline": cpu,
     }

@@ -361,10 +361,12 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
 #pragma unroll
         for (int i = 0; i < NIT; ++i) {
             // pairs of voxels first (lanes r and r + 8 of a row), by DPP
-            const uint32_t k = st[i].k;
-            const uint32_t kx = (k != 0xffffffffu) ? k : 0u;
-            const uint32_t kn2 = min(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, 0x128, 0xF, 0xF, false));
-            const uint32_t kx2 = max(kx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)kx, 0x128, 0xF, 0xF, false));
+            // (row_ror:8 gives every lane a source, so no old value is kept).
+            // The maximum slot holds kmax + 1: a weight-0 item's all-ones k
+            // wraps to 0 there, which no maximum takes.
+            const uint32_t k = st[i].k, k1 = k + 1u;
+            const uint32_t kn2 = min(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, 0x128, 0xF, 0xF, false));
+            const uint32_t kx2 = max(k1, (uint32_t)__builtin_amdgcn_mov_dpp((int)k1, 0x128, 0xF, 0xF, false));
             if ((v & 1) == 0) {
                 atomicMin(&slots[set * 2 * NRX + 8 * i + r], kn2);
                 atomicMax(&slots[set * 2 * NRX + NRX + 8 * i + r], kx2);
@@ -398,8 +400,8 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
 #pragma unroll
         for (int i = 0; i < NIT; ++i) {
             kmn[i] = slots[set * 2 * NRX + 8 * i + r];
-            const uint32_t kmx = slots[set * 2 * NRX + NRX + 8 * i + r];
-            over = over || (kmx - kmn[i] >= (uint32_t)G::W_MAX);     // empty: kmx - kmn = 1
+            const uint32_t kmx1 = slots[set * 2 * NRX + NRX + 8 * i + r];    // kmax + 1
+            over = over || (kmx1 - kmn[i] > (uint32_t)G::W_MAX);     // empty: kmx1 - kmn = 1
         }
         // every wave covers all receivers of the step, so the vote agrees across the workgroup
         wdw.overflow = __any(over) ? 1u : 0u;
@@ -437,9 +439,9 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     const uint32_t coff = (uint32_t)crow * kstride32 + (uint32_t)((lane & 7) % NCH) * 16u + (uint32_t)b0 * E;
     auto copy_prepare = [&](const RowsCursor<NIT> &c, int set, int buf) -> RowsCopy {
         const uint32_t kmn = __builtin_amdgcn_readfirstlane(slots[set * 2 * NRX + wrx]);
-        const uint32_t kmx = __builtin_amdgcn_readfirstlane(slots[set * 2 * NRX + NRX + wrx]);
-        const uint32_t span = kmx - kmn;
-        const int rows = (kmn <= kmx && span < (uint32_t)G::W_MAX) ? (int)span + 2 : 0;   // rows kmin .. kmax + 1
+        const uint32_t kmx1 = __builtin_amdgcn_readfirstlane(slots[set * 2 * NRX + NRX + wrx]);   // kmax + 1
+        const uint32_t span1 = kmx1 - kmn;
+        const int rows = (kmn < kmx1 && span1 <= (uint32_t)G::W_MAX) ? (int)span1 + 1 : 0;   // rows kmin .. kmax + 1
         const int nr = (rows + 7) / 8;
         const uint32_t dst = (uint32_t)(buf * G::BUF + wrx * G::REGION);
         const uint32_t kmin = (uint32_t)(rows ? kmn : 0);
@@ -559,15 +561,17 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     };
     // Units U0 .. U1 - 1 in one pipeline, the reads running DEPTH units ahead
     // of their FMAs (the scheduling fences keep the compiler from sinking
-    // each read next to its use), the next step's copy rounds spread over it.
+    // each read next to its use), the next step's copy rounds issued over its first units.
     // A SIMD issues from its oldest ready wave first; each wave lowers its
     // own priority as it gets through the loop, so that the waves behind
     // catch up and all reach the barrier together.
     auto pipeline = [&](auto U0, auto U1, const RowsWin<NIT> &wd, const RowsCopy &cp) {
         constexpr int u0 = decltype(U0)::value, nu = decltype(U1)::value - u0;
-        // copy rounds: one every `spread` units, or (fewer units than
-        // rounds) round j at unit j mod nu
-        constexpr int spread = (nu / G::MAXR) > 3 ? 3 : (nu / G::MAXR);
+        // copy rounds: one a unit from the first on, so that the last has
+        // most of the step to land (spread over the loop, one every third
+        // unit, Large took 1.2% longer); with fewer units than rounds, round
+        // j at unit j mod nu
+        constexpr int spread = (nu / G::MAXR) > 1 ? 1 : (nu / G::MAXR);
         constexpr int q4 = nu >= 4 ? nu / 4 : 1;                  // units per quarter of the loop
         static_assert(spread == 0 || spread * (G::MAXR - 1) + spread / 2 < nu, "every copy round is issued");
         Ring ring;
