@@ -90,3 +90,19 @@ def test_auto_plan_runs_the_chosen_kernel(gpu, oracle_mod):
     y = T.to_numpy(T.run_gpu(inp, "auto"), False)
     vox = T.sample_voxels(cfg, 1500)
     T.assert_parity(y[:, vox], T.oracle_ref(inp, voxels=vox), "mid auto")
+
+
+@pytest.mark.parametrize("f_number", [0.3, 1.0, 3.0, 0.0, 1e-7])
+@pytest.mark.parametrize("iq", [False, True])
+def test_receive_aperture_f_numbers(gpu, oracle_mod, f_number, iq):
+    # The kernel skips receivers outside a voxel's aperture, deciding most of
+    # them by a tangent test with a margin before atan2; a 37 x 3 array over
+    # a 13 x 7 x 3 grid puts many pairs on both sides of the aperture edge.
+    # f# 0 switches apodization off (nothing skipped); at f# 1e-7 the
+    # aperture is wider than atan(1e6) and only the exact test runs.
+    cfg = das_synth.custom_config("tiny", name="f64-apod", seed=31, iq=iq, B=4, array=(37, 3),
+                                  grid=(13, 7, 3), f_number=f_number, n_scatterers=0)
+    inp = T.Inputs(cfg, w_tx="uniform")
+    x = _wide_rf(inp, 4)
+    ref = oracle_mod.das_sum(inp.fields, x, inp.rx, inp.tau, inp.w)
+    _assert_f64(_run(inp, x), ref, f"f# {f_number} iq={iq}")

@@ -51,6 +51,12 @@ __global__ __launch_bounds__(THREADS) void das_baseline_f64_kernel(DasKParams P,
     const double vy = P.oy + (double)iy * P.sy;
     const double vz = P.oz + (double)iz * P.sz;
     const double theta_max = P.f_number > 0.0 ? atan(1.0 / (2.0 * P.f_number)) : 0.0;
+    // tan(theta_max) with a relative margin: a pair with rho beyond dz times
+    // it is outside the aperture by far more than the rounding of atan2, so
+    // its weight is 0 without evaluating atan2 (apertures wider than
+    // atan(1e6) skip this test)
+    const double tan_out = 1.0 / (2.0 * P.f_number) * (1.0 + 1e-6);
+    const bool pretest = P.f_number > 0.0 && 1.0 / (2.0 * P.f_number) <= 1e6;
 
     double acc[BT][C];
 #pragma unroll
@@ -64,10 +70,16 @@ __global__ __launch_bounds__(THREADS) void das_baseline_f64_kernel(DasKParams P,
         const double rho = sqrt(dx * dx + dy * dy);
         const double dist = sqrt(rho * rho + dz * dz);
         double wrx = 1.0;
-        if (P.f_number > 0.0) {
+        if (pretest && (!(dz > 0.0) || rho > dz * tan_out)) {
+            wrx = 0.0;
+        } else if (P.f_number > 0.0) {
             const double th = atan2(rho, dz);
             wrx = (dz > 0.0 && th < theta_max) ? 0.5 * (1.0 + cos(PI * th / theta_max)) : 0.0;
         }
+        // a receiver outside this voxel's aperture adds only zero terms
+        // (the wave skips it when none of its voxels sees the receiver)
+        if (wrx == 0.0)
+            continue;
         const double trx = dist / P.c;
         for (int qq = 0; qq < P.q_count; ++qq) {
             const int q = P.q_begin + qq;
