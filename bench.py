@@ -93,9 +93,9 @@ def stored_traffic(kernel: str, workload: str):
 
 def executed_fraction(cfg, info):
     """Share of the sum's terms the whole-row kernel executes.  Each 8 x 8 x 2
-    voxel tile sweeps only the blocks of 8 receivers with a non-zero receive
-    weight for one of its voxels (the f-number cone), NIT blocks a step; the
-    rest are exact zeros it skips.  Per tile and receiver the cone test is
+    voxel tile lists the receivers with a non-zero receive weight for one of
+    its voxels (the f-number cone) and sweeps the list in blocks of 8, NIT
+    blocks a step; the rest are exact zeros it skips.  Per tile and receiver the cone test is
     taken at the tile's voxel nearest to the receiver laterally on its
     deepest plane (where the cone is widest), which is where the kernel's
     per-voxel test first passes.  Returns executed term slots (steps x NIT
@@ -120,10 +120,7 @@ def executed_fraction(cfg, info):
     for z in dz:
         rho2 = dy2[:, None, :] + dx2[None, :, :]       # tiles_y x tiles_x x M
         live = (z - rx[:, 2][None, None, :] > 0) & (b_ * rho2 < a_ * (z - rx[:, 2][None, None, :]) ** 2)
-        mb = (cfg.M + 7) // 8
-        pad = np.zeros(live.shape[:2] + (mb * 8,), bool)
-        pad[..., :cfg.M] = live
-        blocks = pad.reshape(live.shape[:2] + (mb, 8)).any(-1).sum(-1)   # live blocks per tile
+        blocks = np.ceil(live.sum(-1) / 8)              # blocks of each tile's receiver list
         slots += (np.ceil(blocks / nit) * nit * 8).sum()
     return float(slots * 128 / (cfg.N * cfg.M))
 

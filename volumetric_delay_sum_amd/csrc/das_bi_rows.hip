@@ -30,13 +30,14 @@
 //
 // Receive aperture.  The receive weight is zero outside the f-number cone of
 // a receiver, and for a tile near the surface most of the array's receivers
-// see none of its voxels.  At its start a workgroup marks the blocks of 8
-// receivers that have a non-zero weight for some voxel of the tile (a test
-// with a margin, so no block with a non-zero weight is left out); its sweep
-// then takes only those blocks, NIT a step.  Skipped terms are exact zeros,
-// so the sums are those of the full sweep up to the order of addition.
+// see none of its voxels.  At its start a workgroup lists the receivers
+// that have a non-zero weight for some voxel of the tile (a test with a
+// margin, so no receiver with a non-zero weight is left out); its sweep then
+// takes the list in blocks of 8 entries, NIT blocks a step.  Skipped terms
+// are exact zeros, so the sums are those of the full sweep up to the order of
+// addition.
 //
-// Per step (transmit event, NIT blocks of 8 receivers): the window [kmin,
+// Per step (transmit event, NIT blocks of 8 listed receivers): the window [kmin,
 // kmax] of k over the tile's voxels with a non-zero weight is reduced per
 // receiver (over voxel pairs by DPP, across the tile by LDS atomics) two
 // steps ahead; the receivers' rows kmin .. kmax + 1 are copied by LDS-DMA
@@ -55,7 +56,8 @@ constexpr int WR_THREADS = 1024;
 constexpr int WR_TX = 8, WR_TY = 8, WR_TZ = 2;   // voxel tile of a workgroup
 constexpr int WR_ROWB = 128;                     // LDS bytes of one staged sample row (the frame tile's part)
 constexpr int WR_LDS_TOTAL = 163840;             // LDS of one workgroup on gfx950 (160 KiB)
-constexpr int WR_LIVE_BLOCKS = 512;              // 8-receiver blocks a launch may have (M <= 4096)
+constexpr int WR_MAX_RX = 4096;                  // receivers a launch may have (the tile's list in LDS)
+constexpr int WR_LIVE_BLOCKS = WR_MAX_RX / 8;    // 8-receiver blocks of a full list
 
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
@@ -64,11 +66,11 @@ template <int NIT>
 struct RowsGeo {
     static constexpr int NRX = 8 * NIT;                                      // receivers per step
     static constexpr int SLOTS = 4 * 2 * NRX * 4;                            // window slots [4 sets][min, max][NRX]
-    static constexpr int LIVE_WORDS = WR_LIVE_BLOCKS / 32;                   // receiver-block mask
-    static constexpr int RW = ((WR_LDS_TOTAL - SLOTS - 4 * LIVE_WORDS) / (2 * NRX) - 16) / WR_ROWB;   // sample rows per region
+    static constexpr int LIST = 2 * WR_MAX_RX + 4 * 16;                      // the tile's live receivers, per-wave counts
+    static constexpr int RW = ((WR_LDS_TOTAL - SLOTS - LIST) / (2 * NRX) - 16) / WR_ROWB;   // sample rows per region
     static constexpr int REGION = RW * WR_ROWB + 16;                         // one receiver's rows, padded
     static constexpr int BUF = NRX * REGION;                                 // one row buffer
-    static constexpr int LDS_BYTES = 2 * BUF + SLOTS + 4 * LIVE_WORDS;
+    static constexpr int LDS_BYTES = 2 * BUF + SLOTS + LIST;
     static constexpr int W_MAX = RW - 1;                                     // k positions of a window
     static constexpr int S = 16 / NRX;                                       // waves sharing one receiver's copy
     static constexpr int MAXR = (RW + 8 * S - 1) / (8 * S);                  // copy rounds of one wave
@@ -86,8 +88,9 @@ struct RowsStep {
     float a, b, ai, bi;
 };
 
-// Position in the sweep: event ql of the group [g0, g1), and the live
-// 8-receiver blocks of the step (blk[i] >= the block count: none).
+// Position in the sweep: event ql of the group [g0, g1), and the blocks of
+// 8 entries of the tile's receiver list the step takes (blk[i] >= the block
+// count: none).
 template <int NIT>
 struct RowsCursor {
     int ql, g0, g1;
@@ -191,12 +194,13 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     constexpr int DEPTH = 3;                     // units whose reads are in flight
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + 2 * G::BUF);
-    uint32_t *live = reinterpret_cast<uint32_t *>(lds + 2 * G::BUF + G::SLOTS);
+    uint16_t *rxlist = reinterpret_cast<uint16_t *>(lds + 2 * G::BUF + G::SLOTS);
+    int *wcount = reinterpret_cast<int *>(lds + 2 * G::BUF + G::SLOTS + 2 * WR_MAX_RX);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int r = lane & 7;                      // receiver of each block: item i is receiver 8 blk[i] + r
+    const int r = lane & 7;                      // receiver of each block: item i is list entry 8 blk[i] + r
     const int v = lane >> 3;                     // voxel in the wave's row of 8
     const uint32_t vpar = (uint32_t)v & 1u;
 
@@ -229,50 +233,43 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
         *reinterpret_cast<int4 *>(lds + i) = make_int4(0, 0, 0, 0);
     if (tid < 4 * 2 * NRX)
         slots[tid] = ((tid / NRX) & 1) ? 0u : 0xffffffffu;
-    const int nblk = (P.M + 7) / 8;
-    for (int i = tid; i < G::LIVE_WORDS; i += WR_THREADS)
-        live[i] = P.apod ? 0u : 0xffffffffu;
-    __syncthreads();
 
     // ---- receive aperture of the tile ------------------------------------------
-    // A block of 8 receivers whose receive weight is zero for every voxel of
-    // the tile adds nothing: the sweep skips it, and a step takes the next NIT
-    // live blocks.  Lane t tests receiver t (and t + 1024, ...) by
-    // rows_rx_on; the 8 lanes of a block vote.
-    if (P.apod) {
-        for (int mb = 0; mb < nblk * 8; mb += WR_THREADS) {
-            const int m = mb + tid;
-            const bool on = m < P.M && rows_rx_on(P, rx, m, tx, ty, tz);
-            const uint64_t vote = __ballot(on);
-            const int b = (mb + 64 * wave) / 8 + lane;                   // lane < 8: block b of this wave
-            if (lane < 8 && b < nblk && ((vote >> (8 * lane)) & 0xffu))
-                atomicOr(&live[b >> 5], 1u << (b & 31));
-        }
+    // A receiver whose receive weight is zero for every voxel of the tile
+    // adds nothing.  Lane t tests receiver t (and t + 1024, ...) by
+    // rows_rx_on, and the receivers that pass are listed in increasing order
+    // (a prefix count over the waves' ballots); the sweep takes the list in
+    // blocks of 8 entries, NIT blocks a step.  Without apodization every
+    // receiver is listed.
+    int nrx = 0;                                 // entries of the list (wave-uniform)
+    for (int mb = 0; mb < P.M; mb += WR_THREADS) {
+        const int m = mb + tid;
+        const bool on = m < P.M && (!P.apod || rows_rx_on(P, rx, m, tx, ty, tz));
+        const uint64_t vote = __ballot(on);
+        if (lane == 0)
+            wcount[wave] = __builtin_popcountll(vote);
         __syncthreads();
-    }
-    // first live block at or after block b, or the block count if none
-    auto next_live = [&](int b) -> int {
-        while (b < nblk) {
-            const uint32_t wd = (uint32_t)__builtin_amdgcn_readfirstlane(live[b >> 5]) >> (b & 31);
-            if (wd)
-                return b + __builtin_ctz(wd);
-            b = (b | 31) + 1;
+        int before = 0, all = 0;
+        for (int w = 0; w < WR_THREADS / 64; ++w) {
+            const int c = wcount[w];
+            before += (w < wave) ? c : 0;
+            all += c;
         }
-        return nblk;
-    };
-    // the step's blocks: the NIT live blocks from block b on
+        const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(vote >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)vote, 0));
+        if (on)
+            rxlist[nrx + before + rank] = (uint16_t)m;
+        nrx += __builtin_amdgcn_readfirstlane(all);
+        __syncthreads();                         // the counts are read before the next pass writes them
+    }
+    const int nblk = (nrx + 7) / 8;              // blocks of the list
+    // the step's blocks: the NIT blocks from block b on (nblk: none)
     auto take_blocks = [&](RowsCursor<NIT> &c, int b) {
 #pragma unroll
-        for (int i = 0; i < NIT; ++i) {
-            c.blk[i] = next_live(b);
-            b = c.blk[i] + 1;
-        }
+        for (int i = 0; i < NIT; ++i) c.blk[i] = min(b + i, nblk);
     };
-    int nlive = 0;
-    for (int w = 0; w < (nblk + 31) / 32; ++w) {
-        const uint32_t wd = (uint32_t)__builtin_amdgcn_readfirstlane(live[w]);
-        nlive += __builtin_popcount(w == nblk / 32 ? wd & ((1u << (nblk & 31)) - 1u) : wd);
-    }
+    // list entry e of the tile (receiver index); entries past the end repeat
+    // the last one, whose items then carry weight 0
+    auto rx_at = [&](int e) -> int { return (int)rxlist[min(e, nrx - 1)]; };
 
     // ---- per-step work ---------------------------------------------------
     // Launch constants used once per receiver block are read afresh from the
@@ -291,17 +288,17 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
         const float *rxg = *(const float *const *)(ka + sizeof(DasKParams) + sizeof(void *));
         // the voxel indices converted afresh at each use: held as doubles
         // across the loop they would take four registers
-        int ixv = ixc, iyv = iyc;
-        asm volatile("" : "+v"(ixv), "+v"(iyv));
+        int ixv = ixc, iyv = iyc, izv = izc;
+        asm volatile("" : "+v"(ixv), "+v"(iyv), "+v"(izv));
         double vx, vy, vz;
-        das::voxel_centre(Pg, ixv, iyv, izc, vx, vy, vz);
+        das::voxel_centre(Pg, ixv, iyv, izv, vx, vy, vz);
 #pragma unroll
         for (int i = 0; i < NIT; ++i) {
-            const int mm = 8 * c.blk[i] + r;
-            const int m = min(mm, Pg.M - 1);
+            const int e = 8 * c.blk[i] + r;
+            const int m = rx_at(e);
             R[i] = das::rx_term<IQ>(Pg, vx, vy, vz, rxg[3 * m], rxg[3 * m + 1], rxg[3 * m + 2]);
             R[i].s_rx += 1.0 - Pg.t0fs;          // the sample split takes s + 1
-            R[i].w = (mm < Pg.M && vox_ok) ? R[i].w : 0.0f;
+            R[i].w = (e < nrx && vox_ok) ? R[i].w : 0.0f;
         }
     };
     // transmit tables of the lane's voxel (the launch keeps Q N 4 < 2^32)
@@ -446,7 +443,8 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
         const uint32_t dst = (uint32_t)(buf * G::BUF + wrx * G::REGION);
         const uint32_t kmin = (uint32_t)(rows ? kmn : 0);
         const int cb = (NIT == 1 || wrx < 8) ? c.blk[0] : c.blk[NIT - 1];
-        const int m = min(8 * cb + (wrx & 7), P.M - 1);    // (a receiver past M copies nothing)
+        // (an entry past the list's end has an empty window and copies nothing)
+        const int m = __builtin_amdgcn_readfirstlane(rx_at(8 * cb + (wrx & 7)));
         if constexpr (LAYOUT == DAS_LAYOUT_QMKB) {
             const int64_t plane = ((int64_t)c.ql * P.M + m) * m_stride;
             return RowsCopy{nr, rows, kmin * kstride32, dst,
@@ -605,21 +603,28 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
         pipeline(ic<0>{}, ic<NCH * NIT>{}, wd, cp);
     };
     // A step by direct loads from the permuted buffer (a window too wide for
-    // the regions): each item with a non-zero weight reads its two rows.
+    // the regions): each item with a non-zero weight reads its two rows.  The
+    // 8 receivers of a block are taken one at a time (a receiver is one list
+    // entry, the same for the wave), so each resource starts at its (event,
+    // receiver) plane and the lanes' offsets stay 32-bit.
     auto compute_direct = [&](const RowsStep (&st)[NIT], const RowsCursor<NIT> &c) {
 #pragma unroll
         for (int i = 0; i < NIT; ++i) {
-            // (an item of a block past the last has weight 0 and k all ones)
-            const int64_t pos = ((int64_t)c.ql * P.M + 8 * min(c.blk[i], nblk - 1)) * m_stride;
-            const das::BufRsrc rd = das::make_rsrc(rf_bytes + pos, (uint64_t)(chunk_bytes - pos));
-            if (st[i].k == 0xffffffffu)
-                continue;
-            const uint32_t o0 = (uint32_t)r * m_stride + st[i].k * kstride32 + (uint32_t)b0 * E;
+#pragma unroll 1
+            for (int j = 0; j < 8; ++j) {
+                // (an item past the list's end has weight 0 and k all ones)
+                const int m = __builtin_amdgcn_readfirstlane(rx_at(8 * c.blk[i] + j));
+                const int64_t pos = ((int64_t)c.ql * P.M + m) * m_stride;
+                const das::BufRsrc rd = das::make_rsrc(rf_bytes + pos, (uint64_t)(chunk_bytes - pos));
+                if (r != j || st[i].k == 0xffffffffu)
+                    continue;
+                const uint32_t o0 = st[i].k * kstride32 + (uint32_t)b0 * E;
 #pragma unroll
-            for (int s = 0; s < NCH; ++s) {
-                const f4_t x0 = das::buffer_load_f32x4(rd, (int)(o0 + 16u * s), 0, 0);
-                const f4_t x1 = das::buffer_load_f32x4(rd, (int)(o0 + kstride32 + 16u * s), 0, 0);
-                fma_chunk(s, st[i].a, st[i].ai, st[i].b, st[i].bi, x0, x1);
+                for (int s = 0; s < NCH; ++s) {
+                    const f4_t x0 = das::buffer_load_f32x4(rd, (int)(o0 + 16u * s), 0, 0);
+                    const f4_t x1 = das::buffer_load_f32x4(rd, (int)(o0 + kstride32 + 16u * s), 0, 0);
+                    fma_chunk(s, st[i].a, st[i].ai, st[i].b, st[i].bi, x0, x1);
+                }
             }
         }
     };
@@ -632,7 +637,7 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     // in step i - 1 and its next publication is in step i + 1, each on the
     // other side of a barrier.
     // (a tile outside every receiver's aperture has no step: its sums stay 0)
-    if (nlive > 0) {
+    if (nblk > 0) {
     RowsCursor<NIT> cur;
     cur.ql = 0;
     cur.g0 = 0;
@@ -721,7 +726,7 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
         return true;
     };
     using das::ic;
-    const int nsteps = P.q_count * ((nlive + NIT - 1) / NIT);
+    const int nsteps = P.q_count * ((nblk + NIT - 1) / NIT);
     for (int left = nsteps; left >= 7; left -= 6) {
         step(ic<0>{}, s_cur, s_nxt, s_spare, tx_a, tx_b);
         step(ic<0>{}, s_nxt, s_spare, s_cur, tx_b, tx_a);
@@ -787,10 +792,10 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
 // A launch's workgroups go to the dies in turn and, on a die, to its shader
 // engines in turn and in order, one tile per CU: a CU that frees up waits
 // while the next tile is bound for an engine that is still busy.  A tile's
-// work is its live receiver blocks, which vary by a factor of 30 over one
-// depth (edge against centre).  Launched by decreasing live count, the
+// work is its blocks of 8 live receivers, which vary by a factor of 30 over
+// one depth (edge against centre).  Launched by decreasing count, the
 // engines of a die stay in step and the last tiles to start are the cheapest.
-// rows_cost_kernel counts the live blocks of every tile (the workgroup's own
+// rows_cost_kernel counts the blocks of every tile (the workgroup's own
 // test, one 256-thread workgroup per tile); rows_order_kernel sorts each die's tiles (those
 // of sequence positions u = x mod 8 for die x, so a die keeps its
 // neighbouring tiles and their L2 reuse) by that count, largest first and in
@@ -810,25 +815,19 @@ __global__ __launch_bounds__(256) void rows_cost_kernel(DasKParams P, const floa
     __syncthreads();
     int tx, ty, tz;
     rows_tile_of(P, u, tx, ty, tz);
-    const int nblk = (P.M + 7) / 8;
     if (P.apod) {
-        // thread t tests receivers t, t + 256, ...; a wave's 64 receivers are
-        // 8 whole blocks (bytes of its vote)
+        // thread t tests receivers t, t + 256, ...
         for (int mb = 0; mb < P.M; mb += 256) {
             const int m = mb + tid;
             const uint64_t vote = __ballot(m < P.M && rows_rx_on(P, rx, m, tx, ty, tz));
-            if (lane == 0) {
-                int n = 0;
-#pragma unroll
-                for (int g = 0; g < 8; ++g)
-                    n += ((vote >> (8 * g)) & 0xffu) != 0;
-                atomicAdd(&live, n);
-            }
+            if (lane == 0)
+                atomicAdd(&live, __builtin_popcountll(vote));
         }
     }
     __syncthreads();
+    // the tile's blocks of 8 listed receivers
     if (tid == 0)
-        cost[u] = (uint16_t)(P.apod ? live : nblk);
+        cost[u] = (uint16_t)(((P.apod ? live : P.M) + 7) / 8);
 }
 
 // One workgroup: a counting sort with one list per die.  cur holds per (die,
@@ -1004,8 +1003,8 @@ void *das_rows_static_work(int dev) {
 bool das_rows_supported(const das_plan_t &plan) {
     // frame tiles of 32 or 16 fp32 or 16 complex frames (B a multiple of
     // 16), native or binary16 samples, records of at most 65535 samples, and
-    // at most 8 WR_LIVE_BLOCKS receivers (the aperture mask)
-    if (plan.p.K > 65535 || plan.p.M > 8 * WR_LIVE_BLOCKS)
+    // at most WR_MAX_RX receivers (the tile's receiver list)
+    if (plan.p.K > 65535 || plan.p.M > WR_MAX_RX)
         return false;
     return (plan.p.dtype == DAS_F32 || plan.p.dtype == DAS_C64) && plan.p.B % 16 == 0;
 }
