@@ -246,3 +246,19 @@ def test_tile_order_two_streams(gpu, monkeypatch):
     for j in (0, 1):
         for i in range(6):
             assert np.array_equal(outs[j][i].cpu().numpy(), ref[j]), f"stream {j} call {i}"
+
+
+@pytest.mark.parametrize("storage", ["native", "f16"])
+@pytest.mark.parametrize("layout", ["kqmb", "qmkb"])
+@pytest.mark.parametrize("q_chunk", [16, 17, 20])
+def test_complex_transmit_phasors_many_events(gpu, layout, storage, q_chunk):
+    # A complex launch of up to 16 events keeps each voxel's w_tx exp(+j 2 pi
+    # f0 tau_tx) in LDS; a launch of more events forms the phasor per step.
+    # 20 diverging events with random transmit weights, called in chunks of
+    # 16 (the table: 16 + 4), 17 (17 events without it, then 3 with it) and
+    # 20 (without it), against the oracle.
+    src = tuple((x * 1e-3, y * 1e-3) for x in (-1.5, -0.5, 0.5, 1.5) for y in (-1.0, -0.5, 0.0, 0.5, 1.0))
+    inp = Inputs(_ragged(True, B=32, sources=src), w_tx="uniform")
+    assert inp.cfg.Q == 20
+    y = to_numpy(run_gpu(inp, "batch_inner", layout, storage=storage, q_chunk=q_chunk), True)
+    assert_parity(y, oracle_ref(inp, storage=storage), f"Q=20 chunks of {q_chunk} {layout} {storage}")

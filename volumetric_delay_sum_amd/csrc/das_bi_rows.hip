@@ -61,16 +61,21 @@ constexpr int WR_LIVE_BLOCKS = WR_MAX_RX / 8;    // 8-receiver blocks of a full 
 
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
-// Sizes of one instance: NIT items (receiver groups of 8) per lane and step.
-template <int NIT>
+constexpr int WR_PT_EVENTS = 16;                 // events of a launch whose phases an IQ workgroup keeps in LDS
+constexpr int WR_PT_STRIDE = WR_PT_EVENTS + 1;   // float2 per voxel of that table (padded against bank conflicts)
+
+// Sizes of one instance: NIT items (receiver groups of 8) per lane and step;
+// PT: the table of weighted transmit phasors (IQ).
+template <int NIT, bool PT>
 struct RowsGeo {
     static constexpr int NRX = 8 * NIT;                                      // receivers per step
     static constexpr int SLOTS = 4 * 2 * NRX * 4;                            // window slots [4 sets][min, max][NRX]
     static constexpr int LIST = 2 * WR_MAX_RX + 4 * 16;                      // the tile's live receivers, per-wave counts
-    static constexpr int RW = ((WR_LDS_TOTAL - SLOTS - LIST) / (2 * NRX) - 16) / WR_ROWB;   // sample rows per region
+    static constexpr int PTAB = PT ? 8 * 128 * WR_PT_STRIDE : 0;             // [128 voxels][events] float2
+    static constexpr int RW = ((WR_LDS_TOTAL - SLOTS - LIST - PTAB) / (2 * NRX) - 16) / WR_ROWB;   // sample rows per region
     static constexpr int REGION = RW * WR_ROWB + 16;                         // one receiver's rows, padded
     static constexpr int BUF = NRX * REGION;                                 // one row buffer
-    static constexpr int LDS_BYTES = 2 * BUF + SLOTS + LIST;
+    static constexpr int LDS_BYTES = 2 * BUF + SLOTS + LIST + PTAB;
     static constexpr int W_MAX = RW - 1;                                     // k positions of a window
     static constexpr int S = 16 / NRX;                                       // waves sharing one receiver's copy
     static constexpr int MAXR = (RW + 8 * S - 1) / (8 * S);                  // copy rounds of one wave
@@ -97,8 +102,11 @@ struct RowsCursor {
     int blk[NIT];
 };
 
+// The transmit table entries of the lane's voxel for one event; with the
+// phase table (IQ), w and ws are w_tx times the cosine and sine of the
+// event's phase.
 struct RowsTx {
-    float tau, w;
+    float tau, w, ws;
 };
 
 // Per item: LDS byte address of the row read first (be) and second (bo) and
@@ -175,14 +183,15 @@ __device__ __forceinline__ bool rows_rx_on(const DasKParams &P, const float *rx,
     return !zero;
 }
 
-template <bool IQ, int LAYOUT, int NIT, bool H, int FRT>
+template <bool IQ, int LAYOUT, int NIT, bool H, int FRT, bool PT>
 __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, const float *__restrict__ rfp,
                                                                  const float *__restrict__ rx,
                                                                  const float *__restrict__ tau_tx,
                                                                  const float *__restrict__ w_tx,
                                                                  float *__restrict__ out,
                                                                  const uint32_t *__restrict__ order) {
-    using G = RowsGeo<NIT>;
+    static_assert(IQ || !PT, "phase table");
+    using G = RowsGeo<NIT, PT>;
     constexpr int NRX = G::NRX;
     constexpr int C = IQ ? 2 : 1;
     constexpr int E = (H ? 2 : 4) * C;           // bytes per stored sample (H: binary16)
@@ -196,6 +205,7 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + 2 * G::BUF);
     uint16_t *rxlist = reinterpret_cast<uint16_t *>(lds + 2 * G::BUF + G::SLOTS);
     int *wcount = reinterpret_cast<int *>(lds + 2 * G::BUF + G::SLOTS + 2 * WR_MAX_RX);
+    float2 *ptab = reinterpret_cast<float2 *>(lds + 2 * G::BUF + G::SLOTS + G::LIST);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -306,7 +316,13 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     const char *w_base = reinterpret_cast<const char *>(w_tx);
     auto load_tx = [&](const RowsCursor<NIT> &c) -> RowsTx {
         const uint32_t o = ((uint32_t)(P.q_begin + c.ql) * (uint32_t)P.N + (uint32_t)n) * 4u;
-        return RowsTx{*reinterpret_cast<const float *>(tau_base + o), *reinterpret_cast<const float *>(w_base + o)};
+        if constexpr (PT) {
+            const float2 wp = ptab[(wave * 8 + v) * WR_PT_STRIDE + c.ql];
+            return RowsTx{*reinterpret_cast<const float *>(tau_base + o), wp.x, wp.y};
+        } else {
+            return RowsTx{*reinterpret_cast<const float *>(tau_base + o), *reinterpret_cast<const float *>(w_base + o),
+                          0.0f};
+        }
     };
     // Sample split of the lane's items for one event: s = (tau_tx - t0) fs +
     // d fs / c in fp64; the receive part folds in 1 - t0 fs, so s1 = s + 1.
@@ -317,7 +333,7 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     // on the absolute delay, event part times receive part.
     auto make_steps = [&](RowsTx tx, RowsStep (&st)[NIT]) {
         float epc = 1.0f, eps = 0.0f;
-        if constexpr (IQ) {
+        if constexpr (IQ && !PT) {
             double cyc = (double)tx.tau * P.f0;
             cyc -= __builtin_floor(cyc);
             sincospif(2.0f * (float)cyc, &eps, &epc);
@@ -330,6 +346,19 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
             const uint32_t k = k1 - 1u;
             const bool valid = k <= (uint32_t)(P.K - 2);
             const float f = (float)__builtin_amdgcn_fract(s1);
+            if constexpr (PT) {
+                // the table's w_tx exp(+j 2 pi f0 tau_tx) times the receive
+                // part; a zero transmit weight keeps its k (zero weights)
+                const float wr = valid ? R[i].w : 0.0f;
+                const float bw = wr * f, aw = wr - bw;
+                st[i].k = (wr != 0.0f) ? k : 0xffffffffu;
+                const float pc = tx.w * R[i].pc - tx.ws * R[i].ps, ps = tx.ws * R[i].pc + tx.w * R[i].ps;
+                st[i].a = aw * pc;
+                st[i].ai = aw * ps;
+                st[i].b = bw * pc;
+                st[i].bi = bw * ps;
+                continue;
+            }
             const float w = valid ? tx.w * R[i].w : 0.0f;
             const float bw = w * f, aw = w - bw;
             st[i].k = (w != 0.0f) ? k : 0xffffffffu;
@@ -637,6 +666,24 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     // in step i - 1 and its next publication is in step i + 1, each on the
     // other side of a barrier.
     // (a tile outside every receiver's aperture has no step: its sums stay 0)
+    if constexpr (PT) {
+        // IQ: w_tx exp(+j 2 pi f0 tau_tx) of every (voxel, event) of the
+        // launch, the phase taken on the absolute tau_tx as the sum defines
+        // it (cycles reduced in fp64); lane (v, r) fills events r, r + 8
+        if (nblk > 0) {
+            for (int e = r; e < P.q_count; e += 8) {
+                const uint32_t o = ((uint32_t)(P.q_begin + e) * (uint32_t)P.N + (uint32_t)n) * 4u;
+                const float tau = *reinterpret_cast<const float *>(tau_base + o);
+                const float wt = *reinterpret_cast<const float *>(w_base + o);
+                double cyc = (double)tau * P.f0;
+                cyc -= __builtin_floor(cyc);
+                float sn, cs;
+                sincospif(2.0f * (float)cyc, &sn, &cs);
+                ptab[(wave * 8 + v) * WR_PT_STRIDE + e] = make_float2(wt * cs, wt * sn);
+            }
+        }
+        __syncthreads();
+    }
     if (nblk > 0) {
     RowsCursor<NIT> cur;
     cur.ql = 0;
@@ -658,7 +705,7 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
         publish(s_nxt, 1);
     }
     // transmit tables of step i + 2, read a step ahead
-    RowsTx tx_a{0.0f, 0.0f}, tx_b{0.0f, 0.0f};
+    RowsTx tx_a{0.0f, 0.0f, 0.0f}, tx_b{0.0f, 0.0f, 0.0f};
     if (has_next2)
         tx_a = load_tx(nxt2);
     __syncthreads();
@@ -925,6 +972,8 @@ static_assert(rows_order_offset(DAS_NOALLOC_MAX_TILES) + 4 * DAS_NOALLOC_MAX_TIL
 template <bool IQ, int LAYOUT, int NIT, bool H, int FRT>
 hipError_t launch_rows(const DasKParams &kp, const float *rf, const float *rx, const float *tau, const float *w,
                        float *out, void *work, hipStream_t stream) {
+    // IQ launches of up to WR_PT_EVENTS events keep their transmit phasors in LDS
+    constexpr bool PT_OK = IQ;
     const int tiles = rows_tiles(kp);
     const uint32_t *order = nullptr;
     if (work) {
@@ -935,8 +984,12 @@ hipError_t launch_rows(const DasKParams &kp, const float *rf, const float *rx, c
                            (kp.M + 7) / 8 + 1, ord);
         order = ord;
     }
-    hipLaunchKernelGGL((das_bi_rows_kernel<IQ, LAYOUT, NIT, H, FRT>), dim3(tiles, kp.B / FRT), dim3(WR_THREADS), 0, stream, kp,
-                       rf, rx, tau, w, out, order);
+    if (PT_OK && kp.q_count <= WR_PT_EVENTS)
+        hipLaunchKernelGGL((das_bi_rows_kernel<IQ, LAYOUT, NIT, H, FRT, PT_OK>), dim3(tiles, kp.B / FRT), dim3(WR_THREADS), 0,
+                           stream, kp, rf, rx, tau, w, out, order);
+    else
+        hipLaunchKernelGGL((das_bi_rows_kernel<IQ, LAYOUT, NIT, H, FRT, false>), dim3(tiles, kp.B / FRT), dim3(WR_THREADS), 0,
+                           stream, kp, rf, rx, tau, w, out, order);
     return hipGetLastError();
 }
 
