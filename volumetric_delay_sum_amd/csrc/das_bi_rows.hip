@@ -76,7 +76,12 @@ struct RowsGeo {
     static constexpr int REGION = RW * WR_ROWB + 16;                         // one receiver's rows, padded
     static constexpr int BUF = NRX * REGION;                                 // one row buffer
     static constexpr int LDS_BYTES = 2 * BUF + SLOTS + LIST + PTAB;
-    static constexpr int W_MAX = RW - 1;                                     // k positions of a window
+    // With room for 40 rows or more a copy moves whole rounds of 8 rows (no
+    // per-lane test; the rows past a window are never read) into at most
+    // ROWS rows; else exactly the window's rows, up to RW
+    static constexpr bool FULL = (RW / 8) * 8 >= 40;
+    static constexpr int ROWS = FULL ? (RW / 8) * 8 : RW;
+    static constexpr int W_MAX = ROWS - 1;                                   // k positions of a window
     static constexpr int S = 16 / NRX;                                       // waves sharing one receiver's copy
     static constexpr int MAXR = (RW + 8 * S - 1) / (8 * S);                  // copy rounds of one wave
     static_assert(LDS_BYTES <= WR_LDS_TOTAL, "LDS budget");
@@ -485,7 +490,7 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     };
     auto copy_round = [&](const RowsCopy &cp, int j) {
         const int rr = j * G::S + wpart;                       // round of the receiver's copy
-        if (rr < cp.nr && rr * 8 + crow < cp.rows) {
+        if (rr < cp.nr && (G::FULL || rr * 8 + crow < cp.rows)) {
             const das::lds_ptr dst = (das::lds_ptr)(lds + cp.dst + (uint32_t)(rr * 8 * WR_ROWB));
             das::buffer_load_lds(cp.rs, dst, 16, (int)coff, (int)(cp.start + (uint32_t)(rr * 8) * kstride32), 0, 0);
         }
