@@ -516,7 +516,7 @@ def main():
             "executed": {"fraction_of_terms": executed, "tflops": achieved * executed,
                          "frac": achieved * executed / peak,
                          "note": "achieved and frac count every term of the sum; the kernel skips the "
-                                 "receiver blocks outside each tile's receive aperture (exact zeros), so "
+                                 "receivers outside each tile's receive aperture (exact zeros), so "
                                  "it executes this fraction of them, at this rate"},
         },
         "permute_ms": perm_avg if bi else None,
