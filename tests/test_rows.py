@@ -140,14 +140,20 @@ def test_main_binary16_default(gpu, iq):
     assert_parity(to_numpy(out, iq)[:, vox], oracle_ref(inp, voxels=vox, storage="f16"), f"main f16 iq={iq}")
 
 
-def test_many_receivers(gpu, monkeypatch):
-    """A 48 x 48 array (2304 receivers: 288 blocks of 8, a nine-word aperture
-    mask, three rounds of the per-receiver test) over a small grid."""
-    cfg = _ragged(False, B=32, K=500, array=(48, 48), grid=(12, 9, 3), sources=((0.0, 0.0), (1e-3, 1e-3)))
+@pytest.mark.parametrize("iq", [False, True], ids=["f32", "c64"])
+@pytest.mark.parametrize("array", [(48, 48), (64, 64)], ids=["2304rx", "4096rx"])
+def test_many_receivers(gpu, monkeypatch, array, iq):
+    """A 48 x 48 array (2304 receivers: three rounds of the per-receiver
+    test) and the largest array the kernel lists, 64 x 64 = 4096 receivers,
+    without apodization so that every receiver is listed (the whole 8 KB
+    list, 512 blocks), over a small grid."""
+    f_number = 1.0 if array[0] < 64 else 0.0
+    cfg = _ragged(iq, B=32 if not iq else 16, K=500, array=array, grid=(12, 9, 3),
+                  sources=((0.0, 0.0), (1e-3, 1e-3)), f_number=f_number)
     inp = Inputs(cfg, w_tx="uniform")
     assert _info(inp)["whole_rows"] == 1
-    y = to_numpy(run_gpu(inp, "batch_inner", "qmkb"), False)
-    assert_parity(y, oracle_ref(inp), "2304 receivers")
+    y = to_numpy(run_gpu(inp, "batch_inner", "qmkb"), iq)
+    assert_parity(y, oracle_ref(inp), f"{array[0] * array[1]} receivers iq={iq}")
 
 
 @pytest.mark.parametrize("rows,iq", VARIANTS, ids=IDS)

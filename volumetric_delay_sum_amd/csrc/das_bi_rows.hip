@@ -62,7 +62,7 @@ constexpr int WR_LIVE_BLOCKS = WR_MAX_RX / 8;    // 8-receiver blocks of a full 
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
 constexpr int WR_PT_EVENTS = 16;                 // events of a launch whose phases an IQ workgroup keeps in LDS
-constexpr int WR_PT_STRIDE = WR_PT_EVENTS + 1;   // float2 per voxel of that table (padded against bank conflicts)
+constexpr int WR_PT_STRIDE = WR_PT_EVENTS + 1;   // entries per voxel of that table (padded against bank conflicts)
 
 // Sizes of one instance: NIT items (receiver groups of 8) per lane and step;
 // PT: the table of weighted transmit phasors (IQ).
@@ -71,7 +71,7 @@ struct RowsGeo {
     static constexpr int NRX = 8 * NIT;                                      // receivers per step
     static constexpr int SLOTS = 4 * 2 * NRX * 4;                            // window slots [4 sets][min, max][NRX]
     static constexpr int LIST = 2 * WR_MAX_RX + 4 * 16;                      // the tile's live receivers, per-wave counts
-    static constexpr int PTAB = PT ? 8 * 128 * WR_PT_STRIDE : 0;             // [128 voxels][events] float2
+    static constexpr int PTAB = PT ? 16 * 128 * WR_PT_STRIDE : 0;            // [128 voxels][events] float4
     static constexpr int RW = ((WR_LDS_TOTAL - SLOTS - LIST - PTAB) / (2 * NRX) - 16) / WR_ROWB;   // sample rows per region
     static constexpr int REGION = RW * WR_ROWB + 16;                         // one receiver's rows, padded
     static constexpr int BUF = NRX * REGION;                                 // one row buffer
@@ -109,7 +109,7 @@ struct RowsCursor {
 
 // The transmit table entries of the lane's voxel for one event; with the
 // phase table (IQ), w and ws are w_tx times the cosine and sine of the
-// event's phase.
+// event's phase, and all three come from LDS.
 struct RowsTx {
     float tau, w, ws;
 };
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     uint32_t *slots = reinterpret_cast<uint32_t *>(lds + 2 * G::BUF);
     uint16_t *rxlist = reinterpret_cast<uint16_t *>(lds + 2 * G::BUF + G::SLOTS);
     int *wcount = reinterpret_cast<int *>(lds + 2 * G::BUF + G::SLOTS + 2 * WR_MAX_RX);
-    float2 *ptab = reinterpret_cast<float2 *>(lds + 2 * G::BUF + G::SLOTS + G::LIST);
+    float4 *ptab = reinterpret_cast<float4 *>(lds + 2 * G::BUF + G::SLOTS + G::LIST);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -320,11 +320,11 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     const char *tau_base = reinterpret_cast<const char *>(tau_tx);
     const char *w_base = reinterpret_cast<const char *>(w_tx);
     auto load_tx = [&](const RowsCursor<NIT> &c) -> RowsTx {
-        const uint32_t o = ((uint32_t)(P.q_begin + c.ql) * (uint32_t)P.N + (uint32_t)n) * 4u;
         if constexpr (PT) {
-            const float2 wp = ptab[(wave * 8 + v) * WR_PT_STRIDE + c.ql];
-            return RowsTx{*reinterpret_cast<const float *>(tau_base + o), wp.x, wp.y};
+            const float4 wp = ptab[(wave * 8 + v) * WR_PT_STRIDE + c.ql];     // (w cos, w sin, tau, -)
+            return RowsTx{wp.z, wp.x, wp.y};
         } else {
+            const uint32_t o = ((uint32_t)(P.q_begin + c.ql) * (uint32_t)P.N + (uint32_t)n) * 4u;
             return RowsTx{*reinterpret_cast<const float *>(tau_base + o), *reinterpret_cast<const float *>(w_base + o),
                           0.0f};
         }
@@ -672,9 +672,10 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
     // other side of a barrier.
     // (a tile outside every receiver's aperture has no step: its sums stay 0)
     if constexpr (PT) {
-        // IQ: w_tx exp(+j 2 pi f0 tau_tx) of every (voxel, event) of the
-        // launch, the phase taken on the absolute tau_tx as the sum defines
-        // it (cycles reduced in fp64); lane (v, r) fills events r, r + 8
+        // IQ: w_tx exp(+j 2 pi f0 tau_tx) and tau_tx of every (voxel,
+        // event) of the launch, the phase taken on the absolute tau_tx as the
+        // sum defines it (cycles reduced in fp64); lane (v, r) fills events
+        // r, r + 8
         if (nblk > 0) {
             for (int e = r; e < P.q_count; e += 8) {
                 const uint32_t o = ((uint32_t)(P.q_begin + e) * (uint32_t)P.N + (uint32_t)n) * 4u;
@@ -684,7 +685,7 @@ __global__ __launch_bounds__(WR_THREADS) void das_bi_rows_kernel(DasKParams P, c
                 cyc -= __builtin_floor(cyc);
                 float sn, cs;
                 sincospif(2.0f * (float)cyc, &sn, &cs);
-                ptab[(wave * 8 + v) * WR_PT_STRIDE + e] = make_float2(wt * cs, wt * sn);
+                ptab[(wave * 8 + v) * WR_PT_STRIDE + e] = make_float4(wt * cs, wt * sn, tau, 0.0f);
             }
         }
         __syncthreads();
