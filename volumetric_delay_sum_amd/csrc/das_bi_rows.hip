@@ -45,6 +45,11 @@
 // step.  A lane's sums cover its receivers; the 8 lanes of a voxel add them
 // up once at the end (DPP).  A step whose window exceeds a region reads its
 // rows straight from the permuted buffer.
+//
+// Complex data (IQ).  A launch of up to WR_PT_EVENTS events keeps, per voxel
+// of the tile and event, w_tx exp(+j 2 pi f0 tau_tx) and tau_tx in LDS,
+// filled once per tile; a step reads them there instead of loading the
+// transmit tables and evaluating a sine and cosine.
 #include "das_device.h"
 
 #include <atomic>
