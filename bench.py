@@ -125,9 +125,9 @@ def executed_fraction(cfg, info):
     return float(slots * 128 / (cfg.N * cfg.M))
 
 
-def executed_fraction_wide_baseline(cfg):
-    """Share of the sum's terms the float64 / complex128 baseline kernel
-    executes.  A wave holds an 8 x 8 lateral patch of voxels on one plane and
+def executed_fraction_baseline(cfg):
+    """Share of the sum's terms the baseline kernels (fp32 / complex64 and
+    float64 / complex128) execute.  A wave holds an 8 x 8 lateral patch of voxels on one plane and
     skips a receiver (all its events and frames) when the receiver's cone
     contains none of the patch's voxels; per patch and receiver the test is
     taken at the patch's voxel nearest to the receiver laterally.  Returns
@@ -489,8 +489,8 @@ def main():
     info = plan.info
     if bi and not plan.repack:
         executed = executed_fraction(cfg, info)
-    elif args.wide:
-        executed = executed_fraction_wide_baseline(cfg)
+    elif not bi:
+        executed = executed_fraction_baseline(cfg)
     else:
         executed = 1.0
     delivery = delivery_ceiling(plan, cfg.iq, h16) if not args.wide else None
@@ -551,7 +551,7 @@ def main():
                          "frac": achieved * executed / peak,
                          "note": ("achieved and frac count every term of the sum; the kernel skips the "
                                   + ("receivers outside all the apertures of a wave's 8 x 8 voxels"
-                                     if args.wide else "receivers outside each tile's receive aperture")
+                                     if not bi else "receivers outside each tile's receive aperture")
                                   + " (exact zeros), so it executes this fraction of them, at this rate")
                                  if executed < 1.0 else "the kernel executes every term"},
         },

@@ -9,7 +9,9 @@
 // stacks four such patches in depth, so neighbouring lanes ask for nearly the
 // same sample index of every (q, m) row and hit the same cache lines.  The
 // receive geometry (fp64 distance, Hann weight) is computed once per
-// (voxel, receiver) and reused over all transmit events and frames.
+// (voxel, receiver) and reused over all transmit events and frames; a wave
+// skips the events and frames of a receiver whose weight is zero for all its
+// voxels.
 #include "das_device.h"
 
 namespace {
@@ -60,6 +62,10 @@ __global__ __launch_bounds__(THREADS) void das_baseline_kernel(DasKParams P, con
         const int me = min(mb + MBLK, P.M);
         for (int m = mb; m < me; ++m) {
             const das::RxTerm R = das::rx_term<IQ>(P, vx, vy, vz, rx[3 * m], rx[3 * m + 1], rx[3 * m + 2]);
+            // a receiver outside this voxel's aperture adds only zero terms
+            // (the wave skips it when none of its voxels sees the receiver)
+            if (R.w == 0.0f)
+                continue;
             for (int qq = 0; qq < P.q_count; ++qq) {
                 const int q = P.q_begin + qq;
                 const das::TxTerm T = das::tx_term<IQ>(P, tau_tx[(int64_t)q * P.N + n],
