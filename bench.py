@@ -76,6 +76,33 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
+def stored_counter(kernel: str, workload: str, field: str):
+    """A reading of the committed counter summary (profiles/traffic.json) for
+    a kernel and workload, if it was taken on these sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{kernel}:{workload}")
+        if rec and rec.get("source_hash") == kernel_source_hash(kernel):
+            return rec.get(field)
+    except Exception:
+        return None
+    return None
+
+
+def pick_bound(t_hbm: float, t_alu: float, hbm_frac, valu_busy) -> str:
+    """Which roof binds a launch: HBM if its algorithmic bytes at 8 TB/s take
+    longer than its flops at the vector peak, or if the HBM bytes the
+    counters saw keep HBM busier (fraction of 8 TB/s) than the VALU is busy
+    (VALUBusy read on the same sources); else the ALU."""
+    if t_hbm > t_alu:
+        return "hbm"
+    if hbm_frac is not None and valu_busy is not None and hbm_frac > valu_busy:
+        return "hbm"
+    return "alu"
+
+
 def stored_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed counter summary, if it matches these sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -445,12 +472,15 @@ def main():
     launch_flops = accs * flops_per_acc * q_l / cfg.Q
     t_hbm, t_alu = alg_bytes / (PEAK_HBM_GBS * 1e9), launch_flops / (peak * 1e12)
     hbm_frac_measured = traffic / (launch_avg * 1e-3) / (PEAK_HBM_GBS * 1e9) if traffic else None
-    bound = "hbm" if (t_hbm > t_alu or (hbm_frac_measured or 0.0) > achieved / peak) else "alu"
+    valu_busy = stored_counter(kernel_name, cfg.name + ("-f16" if h16 else ""), "valu_busy")
+    bound = pick_bound(t_hbm, t_alu, hbm_frac_measured, valu_busy)
     bound_basis = {"algorithmic_bytes_per_launch": alg_bytes, "hbm_time_ms_at_peak": t_hbm * 1e3,
                    "alu_time_ms_at_peak": t_alu * 1e3,
                    "hbm_frac_from_counters": hbm_frac_measured,
+                   "valu_busy_from_counters": valu_busy,
                    "rule": "hbm if the launch's algorithmic bytes at 8 TB/s take longer than its flops at the "
-                           "vector peak, or if the counted HBM bytes per launch time exceed the ALU fraction; "
+                           "vector peak, or if the counted HBM bytes per launch time, as a fraction of 8 TB/s, "
+                           "exceed the VALU busy fraction (VALUBusy) the counters read on the same sources; "
                            "else alu"}
 
     cpu = None

@@ -34,3 +34,16 @@ def test_source_hash_ignores_comments_and_layout():
 def test_stored_traffic_is_none_for_an_unmeasured_workload():
     assert bench.stored_traffic("das_bi_staged_kernel", "no-such-workload") is None
     assert bench.stored_traffic("no_such_kernel", "main") is None
+
+
+def test_pick_bound():
+    import bench
+    # algorithmic bytes slower than the flops: HBM
+    assert bench.pick_bound(2.0, 1.0, None, None) == "hbm"
+    # counted bytes keep HBM at 48% while the VALU is 83% busy: ALU
+    assert bench.pick_bound(0.3, 2.0, 0.48, 0.83) == "alu"
+    # counted bytes keep HBM busier than the VALU: HBM
+    assert bench.pick_bound(0.3, 2.0, 0.9, 0.6) == "hbm"
+    # no counters on these sources: the algorithmic rule alone
+    assert bench.pick_bound(0.3, 2.0, 0.9, None) == "alu"
+    assert bench.pick_bound(0.3, 2.0, None, 0.6) == "alu"
