@@ -236,8 +236,10 @@ das_status das_permute(const das_plan_t *plan, const void *rf_bqmk, void *rf_per
  *            float64 pairs (DAS_C128); rf holds samples of the same type
  *   accumulate  0: out is overwritten; 1: the chunk's sum is added to out
  *               (to sum a volume over several q chunks)
- * Whole-row batch-inner plans (das_plan_info.whole_rows) launch their voxel
- * tiles by decreasing count of live receiver blocks when the launch has more
+ * Whole-row batch-inner plans (das_plan_info.whole_rows) sweep, per voxel
+ * tile, only the receivers whose receive weight is non-zero for some voxel
+ * of the tile (the skipped terms are exact zeros), and launch their voxel
+ * tiles by decreasing count of those receivers when the launch has more
  * workgroups than the device has CUs: two small kernels count and sort the
  * tiles in a work area first.  The area comes from the device's pool: one
  * last used on this stream, or one whose last launches have completed, or
