@@ -181,6 +181,25 @@ def executed_fraction_baseline(cfg):
     return float(live * 64 / (cfg.N * cfg.M))
 
 
+def repack_mfma(cfg, plan, h16: bool, launch_ms: float, launches: int, q_launch: int):
+    """Matrix-core side of the repack variant: each (32-voxel group, event,
+    receiver, 32-frame tile) issues at least one 16-position block of
+    products, each a 32 x 32 x 16 fp16 matrix product (2 x 16,384 flops),
+    three per block with float32 samples (hi and lo parts), two with
+    binary16 samples; windows wider than 16 positions add blocks, so these
+    are lower bounds of the flops the matrix cores run, against their dense
+    fp16 peak."""
+    groups = -(-cfg.grid[0] // 16) * -(-cfg.grid[1] // 16) * cfg.grid[2] * 8   # 8 x 4 groups of 16 x 16 tiles
+    ftiles = -(-cfg.B // 32)
+    products = 2 if h16 else 3
+    flops = groups * q_launch * cfg.M * ftiles * products * 2 * 32 * 32 * 16
+    tf = flops / (launch_ms * 1e-3) / 1e12
+    return {"peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s", "issued_flops_per_launch_min": flops,
+            "achieved_min": tf, "frac_min": tf / PEAK_F16_MFMA_TFLOPS, "products_per_block": products,
+            "note": "lower bounds: one 16-position block per (group, event, receiver, frame tile); the useful "
+                    "flops are in achieved / frac above"}
+
+
 def delivery_ceiling(plan, iq: bool, h16: bool):
     """On-chip delivery roofline of the LDS-staged batch-inner kernels: every
     accumulation (voxel, receiver, event, frame) needs its two samples in
@@ -577,6 +596,7 @@ def main():
             "flops_per_accumulation": flops_per_acc,
             "bound_basis": bound_basis,
             "delivery": delivery,
+            "mfma": repack_mfma(cfg, plan, h16, launch_avg, len(chunks), q_l) if plan.repack else None,
             "executed": {"fraction_of_terms": executed, "tflops": achieved * executed,
                          "frac": achieved * executed / peak,
                          "note": ("achieved and frac count every term of the sum; the kernel skips the "
