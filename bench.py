@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 PEAK_FP32_TFLOPS = 157.3        # MI355X vector fp32 (published)
 PEAK_FP64_TFLOPS = 78.6         # MI355X vector fp64 (published)
 PEAK_F16_MFMA_TFLOPS = 2500.0   # MI355X dense fp16 matrix (published)
+REPACK_MAX_LISTED = 4096        # receivers up to which the repack kernel lists each tile's live ones
 PEAK_HBM_GBS = 8000.0
 CUS, SCLK_HZ = 256, 2.4e9
 
@@ -118,38 +119,54 @@ def stored_traffic(kernel: str, workload: str):
     return None
 
 
-def executed_fraction(cfg, info):
-    """Share of the sum's terms the whole-row kernel executes.  Each 8 x 8 x 2
-    voxel tile lists the receivers with a non-zero receive weight for one of
-    its voxels (the f-number cone) and sweeps the list in blocks of 8, NIT
-    blocks a step; the rest are exact zeros it skips.  Per tile and receiver the cone test is
-    taken at the tile's voxel nearest to the receiver laterally on its
-    deepest plane (where the cone is widest), which is where the kernel's
-    per-voxel test first passes.  Returns executed term slots (steps x NIT
-    x 8 receivers x 128 voxels x events x frames) over N M Q B."""
+def listed_slots(cfg, tile, block):
+    """Receiver slots a kernel that lists each voxel tile's receivers sweeps.
+    Each tile of tile = (tx, ty, tz) voxels lists the receivers with a
+    non-zero receive weight for one of its voxels (the f-number cone) and
+    sweeps the list in steps of `block` entries; the rest are exact zeros it
+    skips.  Per tile and receiver the cone test is taken at the tile's voxel
+    nearest to the receiver laterally on its deepest plane (where the cone is
+    widest), which is where the kernel's per-voxel test first passes.  Returns
+    the sum over tiles of (steps x block) times the tile's voxel count."""
     import numpy as np
     import das_synth
-    if not info["whole_rows"] or cfg.f_number <= 0:
-        return 1.0
-    nit = info["receivers_per_step"] // 8
+    px, py, pz = tile
     rx = das_synth.array_positions(cfg).astype(np.float64)
     (ox, oy, oz), (sx, sy, sz), (nx, ny, nz) = das_synth.voxel_grid(cfg)
     ct = np.cos(np.arctan(1.0 / (2.0 * cfg.f_number)))
     a_, b_ = (1.0 - ct * ct) * 1.001, ct * ct
-    txs, tys, tzs = np.arange(0, nx, 8), np.arange(0, ny, 8), np.arange(0, nz, 2)
-    def nearest(p, o, s, lo, n):                       # nearest voxel centre of [lo, lo + span) to p
-        i = np.clip(np.rint((p[None, :] - o) / s), lo[:, None], np.minimum(lo + 8, n)[:, None] - 1)
+    txs, tys, tzs = np.arange(0, nx, px), np.arange(0, ny, py), np.arange(0, nz, pz)
+    def nearest(p, o, s, lo, span, n):                 # nearest voxel centre of [lo, lo + span) to p
+        i = np.clip(np.rint((p[None, :] - o) / s), lo[:, None], np.minimum(lo + span, n)[:, None] - 1)
         return o + i * s - p[None, :]
-    dx2 = nearest(rx[:, 0], ox, sx, txs, nx) ** 2      # tiles_x x M
-    dy2 = nearest(rx[:, 1], oy, sy, tys, ny) ** 2      # tiles_y x M
-    dz = oz + (np.minimum(tzs + 2, nz) - 1) * sz       # deepest plane of each tile depth (array at z = 0)
+    dx2 = nearest(rx[:, 0], ox, sx, txs, px, nx) ** 2  # tiles_x x M
+    dy2 = nearest(rx[:, 1], oy, sy, tys, py, ny) ** 2  # tiles_y x M
+    dz = oz + (np.minimum(tzs + pz, nz) - 1) * sz      # deepest plane of each tile depth (array at z = 0)
     slots = 0
     for z in dz:
         rho2 = dy2[:, None, :] + dx2[None, :, :]       # tiles_y x tiles_x x M
         live = (z - rx[:, 2][None, None, :] > 0) & (b_ * rho2 < a_ * (z - rx[:, 2][None, None, :]) ** 2)
-        blocks = np.ceil(live.sum(-1) / 8)              # blocks of each tile's receiver list
-        slots += (np.ceil(blocks / nit) * nit * 8).sum()
-    return float(slots * 128 / (cfg.N * cfg.M))
+        slots += (np.ceil(live.sum(-1) / block) * block).sum()
+    return float(slots * px * py * pz)
+
+
+def executed_fraction(cfg, info):
+    """Share of the sum's terms the whole-row kernel executes: 8 x 8 x 2 voxel
+    tiles, each sweeping its receiver list in blocks of 8, NIT blocks a step.
+    Returns executed term slots (steps x NIT x 8 receivers x 128 voxels x
+    events x frames) over N M Q B."""
+    if not info["whole_rows"] or cfg.f_number <= 0:
+        return 1.0
+    return listed_slots(cfg, (8, 8, 2), info["receivers_per_step"]) / (cfg.N * cfg.M)
+
+
+def executed_fraction_repack(cfg, receivers_per_step):
+    """Share of the sum's terms the repack kernel executes: 16 x 16 x 1 voxel
+    tiles, each sweeping its receiver list a step of 8 (one 32-frame tile
+    a wave) or 4 (two) receivers at a time."""
+    if cfg.f_number <= 0 or cfg.M > REPACK_MAX_LISTED:
+        return 1.0
+    return listed_slots(cfg, (16, 16, 1), receivers_per_step) / (cfg.N * cfg.M)
 
 
 def executed_fraction_baseline(cfg):
@@ -181,22 +198,24 @@ def executed_fraction_baseline(cfg):
     return float(live * 64 / (cfg.N * cfg.M))
 
 
-def repack_mfma(cfg, plan, h16: bool, launch_ms: float, launches: int, q_launch: int):
+def repack_mfma(cfg, plan, h16: bool, launch_ms: float, launches: int, q_launch: int, executed: float):
     """Matrix-core side of the repack variant: each (32-voxel group, event,
-    receiver, 32-frame tile) issues at least one 16-position block of
-    products, each a 32 x 32 x 16 fp16 matrix product (2 x 16,384 flops),
-    three per block with float32 samples (hi and lo parts), two with
+    swept receiver slot, 32-frame tile) issues at least one 16-position
+    block of products, each a 32 x 32 x 16 fp16 matrix product (2 x 16,384
+    flops), three per block with float32 samples (hi and lo parts), two with
     binary16 samples; windows wider than 16 positions add blocks, so these
     are lower bounds of the flops the matrix cores run, against their dense
-    fp16 peak."""
+    fp16 peak.  `executed`: the share of (voxel, receiver) slots the tiles'
+    receiver lists sweep (1: every receiver)."""
     groups = -(-cfg.grid[0] // 16) * -(-cfg.grid[1] // 16) * cfg.grid[2] * 8   # 8 x 4 groups of 16 x 16 tiles
+    group_rx = groups * cfg.M if executed >= 1.0 else executed * cfg.N * cfg.M / 32
     ftiles = -(-cfg.B // 32)
     products = 2 if h16 else 3
-    flops = groups * q_launch * cfg.M * ftiles * products * 2 * 32 * 32 * 16
+    flops = group_rx * q_launch * ftiles * products * 2 * 32 * 32 * 16
     tf = flops / (launch_ms * 1e-3) / 1e12
     return {"peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s", "issued_flops_per_launch_min": flops,
             "achieved_min": tf, "frac_min": tf / PEAK_F16_MFMA_TFLOPS, "products_per_block": products,
-            "note": "lower bounds: one 16-position block per (group, event, receiver, frame tile); the useful "
+            "note": "lower bounds: one 16-position block per (group, event, listed receiver, frame tile); the useful "
                     "flops are in achieved / frac above"}
 
 
@@ -541,7 +560,7 @@ def main():
     elif not bi:
         executed = executed_fraction_baseline(cfg)
     else:
-        executed = 1.0
+        executed = executed_fraction_repack(cfg, 4 if cfg.B % 64 == 0 else 8)
     delivery = delivery_ceiling(plan, cfg.iq, h16) if not args.wide else None
     if delivery and delivery.get("ceiling_gacc_s"):
         kg = accs / (kern_avg * 1e-3) / 1e9
@@ -596,7 +615,7 @@ def main():
             "flops_per_accumulation": flops_per_acc,
             "bound_basis": bound_basis,
             "delivery": delivery,
-            "mfma": repack_mfma(cfg, plan, h16, launch_avg, len(chunks), q_l) if plan.repack else None,
+            "mfma": repack_mfma(cfg, plan, h16, launch_avg, len(chunks), q_l, executed) if plan.repack else None,
             "executed": {"fraction_of_terms": executed, "tflops": achieved * executed,
                          "frac": achieved * executed / peak,
                          "note": ("achieved and frac count every term of the sum; the kernel skips the "

@@ -10,7 +10,9 @@ storage, of the rounded samples with binary16 storage.  Cases cover ragged
 grids and receiver counts, 32, 64 and 96 frames, records that end inside the
 window, start times of both signs, several f-numbers, coarse voxels (windows
 wider than the staged rows: the direct-read path), one event per call,
-accumulation, and the named Main and Large workloads at full size.
+accumulation, tiles whose receiver lists are empty or short, receiver counts
+up to and past the listed maximum, and the named Main and Large workloads at
+full size.
 """
 import numpy as np
 import pytest
@@ -159,6 +161,45 @@ def test_degenerate_single_voxel(gpu):
     inp = Inputs(cfg, w_tx="uniform")
     y = to_numpy(run_gpu(inp, "repack"), False)
     assert_parity(y, oracle_ref(inp), "repack one voxel")
+
+
+@pytest.mark.parametrize("storage", ["native", "f16"])
+@pytest.mark.parametrize("B", [32, 64])
+def test_tiles_outside_every_aperture(gpu, storage, B):
+    """A volume much wider than the array: the outer 16 x 16 tiles see no
+    receiver inside their cones (an empty receiver list, no step), the next
+    ones list a few receivers, the central ones most.  Every voxel whose
+    receive weights are all zero comes out exactly 0 (and exactly unchanged
+    when accumulating), the rest meet the usual bar."""
+    import torch
+    cfg = _ragged(B=B, K=400, array=(16, 4), grid=(56, 9, 4), voxel=0.5e-3, z0=2e-3, f_number=2.0,
+                  sources=((0.0, 0.0), (1e-3, 0.0)))
+    inp = Inputs(cfg, w_tx="uniform")
+    ref = oracle_ref(inp, storage=storage)
+    y = to_numpy(run_gpu(inp, "repack", storage=storage), False)
+    zero = ref == 0.0
+    assert 0.5 < zero.mean() < 0.99, zero.mean()
+    assert np.array_equal(y == 0.0, zero)
+    assert_parity(y, ref, f"repack apertures B={B} {storage}")
+    start = torch.linspace(-3.0, 3.0, cfg.B * cfg.N, device="cuda").reshape(cfg.B, cfg.N)
+    out = run_gpu(inp, "repack", out=start.clone(), accumulate_into=True, storage=storage)
+    got, base = to_numpy(out, False), to_numpy(start, False)
+    assert np.array_equal(got[zero], base[zero])
+    assert_parity(got - base, ref, f"repack apertures accumulate B={B} {storage}")
+
+
+@pytest.mark.parametrize("array,f_number", [((48, 48), 1.0), ((64, 64), 0.0), ((65, 64), 1.0)],
+                         ids=["2304rx", "4096rx_all", "4160rx_unlisted"])
+def test_many_receivers(gpu, array, f_number):
+    """2304 receivers (five rounds of the per-receiver test), 4096 without
+    apodization (every receiver, one step per 8), and 4160 with apodization,
+    past the 4096 entries a tile lists: then every receiver is swept, those
+    outside a tile's apertures with zero weights."""
+    cfg = _ragged(B=32, K=500, array=array, grid=(20, 9, 2), sources=((0.0, 0.0), (1e-3, 1e-3)),
+                  f_number=f_number)
+    inp = Inputs(cfg, w_tx="uniform")
+    y = to_numpy(run_gpu(inp, "repack"), False)
+    assert_parity(y, oracle_ref(inp), f"repack {array[0] * array[1]} receivers f#={f_number}")
 
 
 def test_repack_and_batch_inner_agree(gpu):

@@ -136,61 +136,19 @@ struct RowsCopy {
     das::BufRsrc rs;
 };
 
-// Tile u of the launch sequence (u < tiles_x tiles_y tiles_z).  Workgroup
-// b runs on die b % 8 (of the MI355X's eight, each with its own L2).  The
-// sequence goes deepest first (with the receive aperture a tile's work grows
-// with depth).  Within a depth, die x takes a chunk of lat / 8 neighbouring
-// tiles (a row of tiles when the rows are 8 long), the chunk rotating with
-// depth so that every die gets as much edge and centre of the volume as the
-// others.
+// Tile u of the launch sequence (u < tiles_x tiles_y tiles_z): deepest
+// first, each die a rotating chunk of every depth (das::deep_first_tile).
 __device__ __forceinline__ void rows_tile_of(const DasKParams &P, int u, int &tx, int &ty, int &tz) {
-    const int tiles_x = (P.nx + WR_TX - 1) / WR_TX, tiles_y = (P.ny + WR_TY - 1) / WR_TY;
-    const int tiles_z = (P.nz + WR_TZ - 1) / WR_TZ;
-    const int lat = tiles_x * tiles_y;
-    const int bd = u / lat, bw = u % lat;
-    int bj = bw;
-    if (lat % 8 == 0) {
-        const int per = lat / 8, x = bw % 8, k = bw / 8;
-        bj = ((x + bd) % 8) * per + (k + bd) % per;
-    }
-    tz = tiles_z - 1 - bd;
-    ty = bj / tiles_x;
-    tx = bj % tiles_x;
+    das::deep_first_tile(u, (P.nx + WR_TX - 1) / WR_TX, (P.ny + WR_TY - 1) / WR_TY, (P.nz + WR_TZ - 1) / WR_TZ, tx,
+                         ty, tz);
 }
 
 // Whether receiver m may have a non-zero receive weight for some voxel of
-// tile (tx, ty, tz).  A pair counts as zero only when it is clearly outside
-// the aperture or behind the array, by a margin far above the rounding of
-// this fp32 test and of the weight's own: cos^2 theta <= cos^2 theta_max /
-// (1 + 1e-3 (1 - cos^2 theta_max)), i.e. dz^2 (1 - c^2)(1 + 1e-3) <= c^2
-// rho^2 with dz > 0, or dz below zero by more than its rounding.  Lateral
-// distance and depth separate, so over the tile's voxels the pair nearest to
-// the inside of the cone is the voxel nearest to the receiver laterally on
-// the tile's plane farthest in front of it: if that one counts as zero, so
-// does every voxel of the tile.
+// tile (tx, ty, tz) (das::box_rx_on over the tile's voxels).
 __device__ __forceinline__ bool rows_rx_on(const DasKParams &P, const float *rx, int m, int tx, int ty, int tz) {
-    const float ctm = 1.0f - 1.0f / P.apod_inv_vmax;                     // cos theta_max
-    const float ca = (1.0f - ctm * ctm) * 1.001f, cb = ctm * ctm;
-    const int x0 = tx * WR_TX, x1 = min(x0 + WR_TX, P.nx) - 1;
-    const int y0 = ty * WR_TY, y1 = min(y0 + WR_TY, P.ny) - 1;
-    const int z0 = tz * WR_TZ, z1 = min(z0 + WR_TZ, P.nz) - 1;
-    // nearest index in [lo, hi] of a grid axis to coordinate p
-    auto nearest = [](double p, double o, double sp, int lo, int hi) -> int {
-        if (sp == 0.0)
-            return lo;
-        const double t = __builtin_rint((p - o) / sp);
-        return t <= (double)lo ? lo : (t >= (double)hi ? hi : (int)t);
-    };
-    const float px = rx[3 * m], py = rx[3 * m + 1], pz = rx[3 * m + 2];
-    const int ixn = nearest(px, P.ox, P.sx, x0, x1), iyn = nearest(py, P.oy, P.sy, y0, y1);
-    const float dx = (float)(P.ox + (double)ixn * P.sx) - px;
-    const float dy = (float)(P.oy + (double)iyn * P.sy) - py;
-    const float za = (float)(P.oz + (double)z0 * P.sz), zb = (float)(P.oz + (double)z1 * P.sz);
-    const float vz = fmaxf(za, zb), dz = vz - pz;
-    const float rho2 = __builtin_fmaf(dx, dx, dy * dy), dz2 = dz * dz;
-    const float ez = 1e-5f * (fabsf(vz) + fabsf(pz)) + 1e-30f;
-    const bool zero = (dz < -ez) || (dz > ez && dz2 * ca <= rho2 * cb);
-    return !zero;
+    const int x0 = tx * WR_TX, y0 = ty * WR_TY, z0 = tz * WR_TZ;
+    return das::box_rx_on(P, rx, m, x0, min(x0 + WR_TX, P.nx) - 1, y0, min(y0 + WR_TY, P.ny) - 1, z0,
+                          min(z0 + WR_TZ, P.nz) - 1);
 }
 
 template <bool IQ, int LAYOUT, int NIT, bool H, int FRT, bool PT>

@@ -31,6 +31,26 @@ __device__ __forceinline__ int xcd_tile(int b, int nblocks) {
     return (b % NXCD) * (full / NXCD) + b / NXCD;
 }
 
+// Tile u of a deepest-first launch sequence over tiles_x x tiles_y x
+// tiles_z tiles (u < their product).  Workgroup b runs on die b % 8, and
+// with the receive aperture a tile's work grows with depth, so the sequence
+// goes deepest first; within a depth, die x takes a chunk of lat / 8
+// neighbouring tiles, the chunk rotating with depth so that every die gets
+// as much edge and centre of the volume as the others.
+__device__ __forceinline__ void deep_first_tile(int u, int tiles_x, int tiles_y, int tiles_z, int &tx, int &ty,
+                                                int &tz) {
+    const int lat = tiles_x * tiles_y;
+    const int bd = u / lat, bw = u % lat;
+    int bj = bw;
+    if (lat % 8 == 0) {
+        const int per = lat / 8, x = bw % 8, k = bw / 8;
+        bj = ((x + bd) % 8) * per + (k + bd) % per;
+    }
+    tz = tiles_z - 1 - bd;
+    ty = bj / tiles_x;
+    tx = bj % tiles_x;
+}
+
 // Voxel centre in fp64: origin + index * pitch.
 __device__ __forceinline__ void voxel_centre(const DasKParams &P, int ix, int iy, int iz,
                                              double &x, double &y, double &z) {
@@ -63,6 +83,40 @@ __device__ __forceinline__ float rx_weight(const DasKParams &P, double rho2, dou
     for (int i = DAS_APOD_TERMS - 2; i >= 0; --i) w = __builtin_fmaf(w, y, P.apod_c[i]);
     w = (dz > 0.0 && y < 1.0f) ? w : 0.0f;
     return P.apod ? w : 1.0f;
+}
+
+// Whether receiver m may have a non-zero receive weight for some voxel of
+// the box of voxel indices [x0, x1] x [y0, y1] x [z0, z1] (inclusive, array
+// in front of the box's planes).  A pair counts as zero only when it is
+// clearly outside the aperture or behind the array, by a margin far above
+// the rounding of this fp32 test and of the weight's own: cos^2 theta <=
+// cos^2 theta_max / (1 + 1e-3 (1 - cos^2 theta_max)), i.e. dz^2 (1 - c^2)
+// (1 + 1e-3) <= c^2 rho^2 with dz > 0, or dz below zero by more than its
+// rounding.  Lateral distance and depth separate, so over the box the pair
+// nearest to the inside of the cone is the voxel nearest to the receiver
+// laterally on the box's plane farthest in front of it: if that one counts
+// as zero, so does every voxel of the box.
+__device__ __forceinline__ bool box_rx_on(const DasKParams &P, const float *rx, int m, int x0, int x1, int y0,
+                                          int y1, int z0, int z1) {
+    const float ctm = 1.0f - 1.0f / P.apod_inv_vmax;                     // cos theta_max
+    const float ca = (1.0f - ctm * ctm) * 1.001f, cb = ctm * ctm;
+    // nearest index in [lo, hi] of a grid axis to coordinate p
+    auto nearest = [](double p, double o, double sp, int lo, int hi) -> int {
+        if (sp == 0.0)
+            return lo;
+        const double t = __builtin_rint((p - o) / sp);
+        return t <= (double)lo ? lo : (t >= (double)hi ? hi : (int)t);
+    };
+    const float px = rx[3 * m], py = rx[3 * m + 1], pz = rx[3 * m + 2];
+    const int ixn = nearest(px, P.ox, P.sx, x0, x1), iyn = nearest(py, P.oy, P.sy, y0, y1);
+    const float dx = (float)(P.ox + (double)ixn * P.sx) - px;
+    const float dy = (float)(P.oy + (double)iyn * P.sy) - py;
+    const float za = (float)(P.oz + (double)z0 * P.sz), zb = (float)(P.oz + (double)z1 * P.sz);
+    const float vz = fmaxf(za, zb), dz = vz - pz;
+    const float rho2 = __builtin_fmaf(dx, dx, dy * dy), dz2 = dz * dz;
+    const float ez = 1e-5f * (fabsf(vz) + fabsf(pz)) + 1e-30f;
+    const bool zero = (dz < -ez) || (dz > ez && dz2 * ca <= rho2 * cb);
+    return !zero;
 }
 
 // Receive part of one (voxel, receiver) pair: fp64 sample offset, weight,

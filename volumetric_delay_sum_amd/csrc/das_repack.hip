@@ -39,8 +39,11 @@
 // l % 32; lanes l and l + 32 hold positions 0-7 and 8-15 of the window in the
 // weight operand (the MFMA's operand layout).  For the per-pair work (sample
 // split, weights) the two lane halves take two receivers at once, lane half h
-// receiver m0 + 2p + h, and v_permlane32_swap hands each half the other's.
-// Work goes in steps of (transmit event, block of NRX receivers):
+// the receiver at entry l0 + 2p + h of the tile's list, and v_permlane32_swap
+// hands each half the other's.  With apodization the list holds only the
+// receivers whose weight can be non-zero for a voxel of the tile (the others
+// add exact zeros); without it, every receiver.
+// Work goes in steps of (transmit event, block of NRX listed receivers):
 //   - setup: every lane computes k, the weights and their halves for its
 //     pairs; each lane half reduces its receiver's [kmin, kmax] over the
 //     group's voxels with a non-zero weight (DPP row rotations and a row
@@ -66,6 +69,7 @@ constexpr int RP_THREADS = 512;
 constexpr int RP_TX = 16, RP_TY = 16;          // voxel tile of a workgroup (one depth plane)
 constexpr int RP_LDS_TOTAL = 163840;           // LDS of one workgroup on gfx950 (160 KiB)
 constexpr int RP_FLUSH = 4;                    // steps per partial sum
+constexpr int RP_MAX_RX = 4096;                // receivers up to which a tile lists its live ones
 
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f16v_t __attribute__((ext_vector_type(16)));
@@ -101,11 +105,12 @@ struct RGeo {
     static constexpr int PARTS = (RP_THREADS / 64) / NRX; // waves sharing one receiver's copy
     static constexpr int SEL = 11 * 16;                   // selector table
     static constexpr int SLOTS = 4 * 2 * NRX * 4;         // [4 sets][min, max][NRX]
-    static constexpr int LDS_BYTES = 2 * BUF + SEL + SLOTS;
+    static constexpr int LIST = 2 * RP_MAX_RX + 4 * (RP_THREADS / 64);   // receiver list, per-wave counts
+    static constexpr int LDS_BYTES = 2 * BUF + SEL + SLOTS + LIST;
     static_assert(LDS_BYTES <= RP_LDS_TOTAL, "LDS budget");
 };
 
-// One step's per-lane state: pair p of this lane half (receiver m0 + 2p + h).
+// One step's per-lane state: pair p of this lane half (list entry l0 + 2p + h).
 template <int NP>
 struct RStep {
     int32_t e[NP];        // k - kb of the half's receiver (meaningful where the weight is non-zero)
@@ -118,9 +123,10 @@ struct Tx {
     float tau, w;
 };
 
-// (transmit event, first receiver) of a step; steps run events fastest
+// (transmit event, first entry of the tile's receiver list) of a step;
+// steps run events fastest
 struct Cur {
-    int ql, m0;
+    int ql, l0;
 };
 
 __device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
@@ -165,6 +171,8 @@ __global__ __launch_bounds__(RP_THREADS) void das_repack_kernel(DasKParams P, co
     __shared__ __attribute__((aligned(16))) char lds[G::LDS_BYTES];
     constexpr uint32_t SEL_AT = 2 * G::BUF;
     int *slots = reinterpret_cast<int *>(lds + SEL_AT + G::SEL);    // [set][min, max][NRX]
+    uint16_t *rxlist = reinterpret_cast<uint16_t *>(lds + SEL_AT + G::SEL + G::SLOTS);
+    int *wcount = reinterpret_cast<int *>(lds + SEL_AT + G::SEL + G::SLOTS + 2 * RP_MAX_RX);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -173,11 +181,19 @@ __global__ __launch_bounds__(RP_THREADS) void das_repack_kernel(DasKParams P, co
 
     // voxel of this lane
     const int tiles_x = (P.nx + RP_TX - 1) / RP_TX, tiles_y = (P.ny + RP_TY - 1) / RP_TY;
-    int t = das::xcd_tile(blockIdx.x, gridDim.x);
-    const int tx = t % tiles_x;
-    t /= tiles_x;
-    const int ty = t % tiles_y;
-    const int iz = t / tiles_y;
+    // With the receivers listed, a tile's work grows with depth: deepest
+    // tiles first, spread over the dies; else each die a contiguous range.
+    const bool listed = P.apod && P.M <= RP_MAX_RX;
+    int tx, ty, iz;
+    if (listed) {
+        das::deep_first_tile(blockIdx.x, tiles_x, tiles_y, P.nz, tx, ty, iz);
+    } else {
+        int t = das::xcd_tile(blockIdx.x, gridDim.x);
+        tx = t % tiles_x;
+        t /= tiles_x;
+        ty = t % tiles_y;
+        iz = t / tiles_y;
+    }
     const int ix = tx * RP_TX + (wave & 1) * 8 + (j & 7);
     const int iy = ty * RP_TY + (wave >> 1) * 4 + (j >> 3);
     const bool vox_ok = ix < P.nx && iy < P.ny;
@@ -204,17 +220,58 @@ __global__ __launch_bounds__(RP_THREADS) void das_repack_kernel(DasKParams P, co
         slots[tid] = ((tid / NRX) & 1) ? INT_MIN : INT_MAX;
     __syncthreads();
 
-    const int nmb = (P.M + NRX - 1) / NRX;
+    // ---- the tile's receivers -------------------------------------------------
+    // With apodization a receiver whose weight is zero for every voxel of the
+    // tile adds only zero terms: the tile lists the others (das::box_rx_on,
+    // a conservative test) in increasing order, by a prefix count over the
+    // waves' ballots, and the steps take the list NRX entries at a time.
+    // Without apodization, or past RP_MAX_RX receivers, entry e is receiver e.
+    int nrx = P.M;                               // entries of the list (workgroup-uniform)
+    if (listed) {
+        nrx = 0;
+        if (tid == 0)
+            rxlist[0] = 0;                       // read (weight 0) when the list stays empty
+        const int x0 = tx * RP_TX, y0 = ty * RP_TY;
+        const int x1 = min(x0 + RP_TX, P.nx) - 1, y1 = min(y0 + RP_TY, P.ny) - 1;
+        for (int mb = 0; mb < P.M; mb += RP_THREADS) {
+            const int m = mb + tid;
+            const bool on = m < P.M && das::box_rx_on(P, rx, m, x0, x1, y0, y1, iz, iz);
+            const uint64_t vote = __ballot(on);
+            if (lane == 0)
+                wcount[wave] = __builtin_popcountll(vote);
+            __syncthreads();
+            int before = 0, all = 0;
+            for (int w = 0; w < RP_THREADS / 64; ++w) {
+                const int cnt = wcount[w];
+                before += (w < wave) ? cnt : 0;
+                all += cnt;
+            }
+            const int rank =
+                __builtin_amdgcn_mbcnt_hi((uint32_t)(vote >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)vote, 0));
+            if (on)
+                rxlist[nrx + before + rank] = (uint16_t)m;
+            nrx += __builtin_amdgcn_readfirstlane(all);
+            __syncthreads();                     // the counts are read before the next pass writes them
+        }
+    }
+    // receiver of list entry e; entries past the end repeat the last one (their
+    // pairs carry weight 0).  A tile whose list is empty has no step; its
+    // prologue reads entry 0.
+    auto rx_at = [&](int e) -> int {
+        return listed ? (int)rxlist[max(min(e, nrx - 1), 0)] : min(e, P.M - 1);
+    };
+
+    const int nmb = (nrx + NRX - 1) / NRX;
     const int nsteps = P.q_count * nmb;
     auto advance = [&](Cur c) -> Cur {
         if (++c.ql == P.q_count) {
             c.ql = 0;
-            c.m0 += NRX;
+            c.l0 += NRX;
         }
         return c;
     };
 
-    // ---- receive geometry of this lane's pairs (receiver m0 + 2p + h) -------
+    // ---- receive geometry of this lane's pairs (list entry l0 + 2p + h) ------
     // Its launch constants are read afresh from the kernel arguments (held
     // across the step loop they would crowd the scalar registers); receiver
     // positions are loaded one receiver block ahead.
@@ -226,32 +283,30 @@ __global__ __launch_bounds__(RP_THREADS) void das_repack_kernel(DasKParams P, co
     double s_rx[NP];     // d fs / c + 1 - t0 fs: the sample split takes s + 1
     float w_rx[NP];
     float px[NP], py[NP], pz[NP];
-    auto load_positions = [&](int m0) {
+    auto load_positions = [&](int l0) {
         const kptr ka = kargs();
         const float *rxg = *(const float *const *)(ka + sizeof(DasKParams) + sizeof(void *));
-        const int M = ((const DasKParams *)ka)->M;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            const int m = min(m0 + 2 * p + h, M - 1);
+            const int m = rx_at(l0 + 2 * p + h);
             px[p] = rxg[3 * m];
             py[p] = rxg[3 * m + 1];
             pz[p] = rxg[3 * m + 2];
         }
     };
-    auto geometry = [&](int m0) {
+    auto geometry = [&](int l0) {
         const kptr ka = kargs();
         const DasKParams &Pg = *(const DasKParams *)ka;
         double vx, vy, vz;
         das::voxel_centre(Pg, min(ix, Pg.nx - 1), min(iy, Pg.ny - 1), iz, vx, vy, vz);
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            const int mm = m0 + 2 * p + h;
             const das::RxTerm R = das::rx_term<false>(Pg, vx, vy, vz, px[p], py[p], pz[p]);
             s_rx[p] = R.s_rx + (1.0 - Pg.t0fs);
-            w_rx[p] = (mm < Pg.M && vox_ok) ? R.w : 0.0f;
+            w_rx[p] = (l0 + 2 * p + h < nrx && vox_ok) ? R.w : 0.0f;
         }
-        if (m0 + NRX < Pg.M)
-            load_positions(m0 + NRX);
+        if (l0 + NRX < nrx)
+            load_positions(l0 + NRX);
     };
     // transmit tables of a step for this lane's voxel (loaded three steps ahead)
     auto load_tx = [&](Cur c, bool ok) -> Tx {
@@ -308,9 +363,9 @@ __global__ __launch_bounds__(RP_THREADS) void das_repack_kernel(DasKParams P, co
     auto stage = [&](Cur c, int set, int buf) {
         const int kmn = __builtin_amdgcn_readfirstlane(slots[set * 2 * NRX + crx]);
         const int kmx = __builtin_amdgcn_readfirstlane(slots[set * 2 * NRX + NRX + crx]);
-        const int m = c.m0 + crx;
-        if (kmn == INT_MAX || m >= P.M)
+        if (kmn == INT_MAX || c.l0 + crx >= nrx)
             return;
+        const int m = __builtin_amdgcn_readfirstlane(rx_at(c.l0 + crx));
         const int kw0 = kmn & ~7;
         const int need = min((kmx + 2 - kw0 + 7) / 8, G::DPF);       // pieces
         const int nr = (need + G::PPR - 1) / G::PPR;                    // rounds per plane
@@ -465,8 +520,7 @@ __global__ __launch_bounds__(RP_THREADS) void das_repack_kernel(DasKParams P, co
         };
 #pragma unroll
         for (int r = 0; r < NRX; ++r) {
-            const int m = c.m0 + r;
-            if (m >= P.M)
+            if (c.l0 + r >= nrx)
                 continue;
             if (wn[r].lds) {
                 for (int blk = 1; blk < wn[r].nblk; ++blk) {
@@ -480,6 +534,7 @@ __global__ __launch_bounds__(RP_THREADS) void das_repack_kernel(DasKParams P, co
                     }
                 }
             } else {
+                const int m = __builtin_amdgcn_readfirstlane(rx_at(c.l0 + r));
                 const das::BufRsrc rs = das::make_rsrc(perm + ((uint64_t)c.ql * P.M + m) * qm_bytes, qm_bytes);
                 // positions kb .. kb + 3 and kb + 4 .. kb + 7 of the lane's slot: one
                 // piece, or the end of one and the start of the next
@@ -525,12 +580,12 @@ __global__ __launch_bounds__(RP_THREADS) void das_repack_kernel(DasKParams P, co
     setup(txa, st0);
     publish(st0, 0);
     if (1 < nsteps && c1.ql == 0)
-        geometry(c1.m0);
+        geometry(c1.l0);
     txa = load_tx(c1, 1 < nsteps);
     setup(txa, st1);
     publish(st1, 1);
     if (2 < nsteps && c2.ql == 0)
-        geometry(c2.m0);
+        geometry(c2.l0);
     txa = load_tx(c2, 2 < nsteps);            // tables of step s + 2, loaded during step s - 1
     __syncthreads();
     stage(c0, 0, 0);
@@ -551,7 +606,7 @@ __global__ __launch_bounds__(RP_THREADS) void das_repack_kernel(DasKParams P, co
         if (more)
             publish(st2, set2);
         if (s + 3 < nsteps && c3.ql == 0)
-            geometry(c3.m0);
+            geometry(c3.l0);
         if ((s + 1) % RP_FLUSH == 0 || s + 1 == nsteps) {
 #pragma unroll
             for (int f = 0; f < FT; ++f)
