@@ -91,9 +91,13 @@ enum { DAS_F32 = 0, DAS_C64 = 1, DAS_F64 = 2, DAS_C128 = 3 };
  *                       and receiver, the 32 frames x 16 sample positions of
  *                       the group's window times the 16 x 32 interpolation
  *                       weights, one v_mfma_f32_32x32x16_f16 per 16
- *                       positions.  Operands are binary16 halves: float32
- *                       samples and all weights are split into hi + lo halves
- *                       (three products, or two with DAS_STORE_F16 samples),
+ *                       positions.  With receive apodization each 16 x 16
+ *                       voxel tile sweeps only the receivers whose weight
+ *                       can be non-zero for one of its voxels (up to 4096
+ *                       receivers; past that, all).  Operands are binary16
+ *                       halves: float32 samples and all weights are split
+ *                       into hi + lo halves (three products, or two with
+ *                       DAS_STORE_F16 samples),
  *                       so the result meets the float32 bar of the other
  *                       kernels (relative error about 2^-21 per term), for
  *                       |x| and |w_tx w_rx| below 65504 (the binary16 range).
